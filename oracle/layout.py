@@ -1,0 +1,121 @@
+"""Byte layout of a pool page, written out as plain packing loops.
+
+A page holds 64 tokens of every layer and every KV head ("Pages hold 64
+tokens", KV at 9 KB a token, How it works; one ``kv_page_bytes`` figure per
+pool, section "See it, control it").  Inside a page, the data of one
+(layer, KV head) pair is one contiguous block at
+``((layer * Hkv) + head) * block_bytes``.
+
+2-bit block (D dims; 72 B per token per head at D = 256, as the page's table):
+    [0,        16*D)   K codes, token-major: row t (D/4 bytes) at t*D/4
+    [16*D,     32*D)   V codes, dim-major:   row d (16 bytes = 64 tokens) at 16*d
+    [32*D,     32*D+512)  K metadata: 64 x [fp32 scale, fp32 min]
+    [32*D+512, 32*D+1024) V metadata: 64 x [fp32 scale, fp32 min]
+  Codes are packed least-significant-bits first: element j of a packed row
+  sits in byte j // 4 at bit 2 * (j % 4).  For a K row the elements are dims;
+  for a V row they are the page's 64 token slots.
+
+8-bit block (D dims):
+    [0,      64*D)   K codes int8, token-major: row t at t*D
+    [64*D,  128*D)   V codes int8, dim-major:   row d (64 bytes) at 64*d
+    [128*D, 132*D)   K scales: fp32 per channel (one set per page)
+    [132*D, 132*D+256) V scales: fp32 per token slot
+
+The arrangement inside a block is not fixed by the pages (they give only the
+bytes per head per token); the byte totals match them exactly.  Pinned by
+closed forms: block sizes reproduce 9,216 B/token at the 27B geometry and the
+pack/unpack pair is checked element by element on seeded codes with a loop
+reference in tests/test_oracle_layout.py.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64
+
+
+def q2_block_bytes(D: int) -> int:
+    return 32 * D + 1024
+
+
+def q8_block_bytes(D: int) -> int:
+    return 132 * D + 256
+
+
+def block_bytes(fmt: str, D: int) -> int:
+    return q2_block_bytes(D) if fmt == "q2" else q8_block_bytes(D)
+
+
+def block_offset(fmt: str, layer: int, head: int, n_kv_heads: int, D: int) -> int:
+    return (layer * n_kv_heads + head) * block_bytes(fmt, D)
+
+
+# --------------------------------------------------------- 2-bit packing --
+
+def pack2(codes) -> np.ndarray:
+    """codes uint8 [..., n] in 0..3 (n % 4 == 0) -> bytes [..., n/4], element j at bits 2*(j%4) of byte j//4."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 4 == 0 and c.max(initial=0) <= 3
+    g = c.reshape(c.shape[:-1] + (c.shape[-1] // 4, 4)).astype(np.uint32)
+    b = g[..., 0] | (g[..., 1] << 2) | (g[..., 2] << 4) | (g[..., 3] << 6)
+    return b.astype(np.uint8)
+
+
+def unpack2(packed, n: int) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    assert p.shape[-1] * 4 == n
+    out = np.empty(p.shape[:-1] + (n,), dtype=np.uint8)
+    for j in range(4):
+        out[..., j::4] = (p >> (2 * j)) & 3
+    return out
+
+
+class Q2Block:
+    """Views into one 2-bit (layer, head) block of a page (a uint8 array of block_bytes)."""
+
+    def __init__(self, buf: np.ndarray, D: int):
+        assert buf.dtype == np.uint8 and buf.size == q2_block_bytes(D)
+        self.D = D
+        self.k_codes = buf[0:16 * D].reshape(PAGE, D // 4)
+        self.v_codes = buf[16 * D:32 * D].reshape(D, 16)
+        self.k_meta = buf[32 * D:32 * D + 512].view(np.float32).reshape(PAGE, 2)
+        self.v_meta = buf[32 * D + 512:32 * D + 1024].view(np.float32).reshape(PAGE, 2)
+
+    def write_k(self, slot: int, codes_row, scale, mn):
+        self.k_codes[slot] = pack2(codes_row)
+        self.k_meta[slot] = (scale, mn)
+
+    def write_v(self, slot: int, codes_row, scale, mn):
+        """Set the 2 bits of token ``slot`` in every dim row, leaving other slots untouched."""
+        byte, shift = slot // 4, 2 * (slot % 4)
+        keep = np.uint8(0xFF ^ (3 << shift))
+        col = self.v_codes[:, byte]
+        self.v_codes[:, byte] = (col & keep) | (np.asarray(codes_row, np.uint8) << shift)
+        self.v_meta[slot] = (scale, mn)
+
+    def read_k(self, n: int):
+        codes = unpack2(self.k_codes[:n], self.D)
+        return codes, self.k_meta[:n, 0].copy(), self.k_meta[:n, 1].copy()
+
+    def read_v(self, n: int):
+        codes = unpack2(self.v_codes, PAGE)[:, :n].T.copy()   # [n][D]
+        return codes, self.v_meta[:n, 0].copy(), self.v_meta[:n, 1].copy()
+
+
+class Q8Block:
+    """Views into one 8-bit (layer, head) block of a page."""
+
+    def __init__(self, buf: np.ndarray, D: int):
+        assert buf.dtype == np.uint8 and buf.size == q8_block_bytes(D)
+        self.D = D
+        self.k_codes = buf[0:64 * D].view(np.int8).reshape(PAGE, D)
+        self.v_codes = buf[64 * D:128 * D].view(np.int8).reshape(D, PAGE)
+        self.k_scale = buf[128 * D:132 * D].view(np.float32)
+        self.v_scale = buf[132 * D:132 * D + 256].view(np.float32)
+
+    def read_k(self, n: int):
+        return self.k_codes[:n].copy(), self.k_scale.copy()
+
+    def read_v(self, n: int):
+        return self.v_codes[:, :n].T.copy(), self.v_scale[:n].copy()

@@ -1,0 +1,136 @@
+"""A byte image of the page pool on the host, with append and gather.
+
+Follows "KV at 9 KB a token" (How it works: fixed-size 64-token pages, a pool
+that is a byte budget) and "The KV cache and prompt reuse" (What a sequence is
+made of: one pool shared by all lanes; the window of exact recent keys the
+compressed format keeps).  A sequence owns a block table: logical page i of the
+sequence lives in physical page ``bt[i]``; token t sits in slot t % 64 of page
+``bt[t // 64]``.
+
+append writes each new token's K and V rows quantized into its slot, leaving
+every other slot of the pool untouched.  For the 8-bit variant, K is scaled per
+channel over the tokens present in the open page; the exact K rows of that page
+are kept aside (the exact window), and each append re-derives the page's K codes
+and scales from the exact rows present, so a full page equals the plain
+per-channel quantization of its 64 tokens.
+
+Pins: append-then-gather returns exactly the codec's dequantized rows for any
+block table (permutation invariance) and slots outside the appended range keep
+their fill bytes (tests/test_oracle_pool.py).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import codec
+from .accounting import page_bytes
+from .layout import PAGE, Q2Block, Q8Block, block_bytes, block_offset
+
+
+class OraclePool:
+    def __init__(self, fmt: str, n_layers: int, n_kv_heads: int, head_dim: int, n_pages: int, fill: int = 0xA5):
+        assert fmt in ("q2", "q8")
+        self.fmt, self.L, self.H, self.D = fmt, n_layers, n_kv_heads, head_dim
+        self.page_bytes = page_bytes(fmt, n_layers, n_kv_heads, head_dim)
+        self.data = np.full((n_pages, self.page_bytes), fill, dtype=np.uint8)
+        self._exact_k = {}  # (seq, layer) -> fp32 [64][H][D] exact K rows of the open page (8-bit only)
+
+    def block(self, page: int, layer: int, head: int):
+        off = block_offset(self.fmt, layer, head, self.H, self.D)
+        buf = self.data[page, off:off + block_bytes(self.fmt, self.D)]
+        return Q2Block(buf, self.D) if self.fmt == "q2" else Q8Block(buf, self.D)
+
+    # ------------------------------------------------------------ append --
+    def append(self, layer: int, seq: int, bt, start: int, k_rows, v_rows):
+        """Quantize-append rows k_rows/v_rows [n][H][D] (fp32 values of bf16) at positions start..start+n-1."""
+        k = np.asarray(k_rows, np.float32)
+        v = np.asarray(v_rows, np.float32)
+        n = k.shape[0]
+        if n == 0:
+            return
+        assert k.shape == (n, self.H, self.D) and v.shape == k.shape
+        if self.fmt == "q2":
+            ck, sk, mk = codec.q2_quantize(k)
+            cv, sv, mv = codec.q2_quantize(v)
+            for i in range(n):
+                pos = start + i
+                page, slot = int(bt[pos // PAGE]), pos % PAGE
+                for h in range(self.H):
+                    blk = self.block(page, layer, h)
+                    blk.write_k(slot, ck[i, h], sk[i, h], mk[i, h])
+                    blk.write_v(slot, cv[i, h], sv[i, h], mv[i, h])
+            return
+        # 8-bit: V per token; K per channel over the open page's exact rows
+        cv, sv = codec.q8_quantize_v(v)
+        for i in range(n):
+            pos = start + i
+            page, slot = int(bt[pos // PAGE]), pos % PAGE
+            for h in range(self.H):
+                blk = self.block(page, layer, h)
+                blk.v_codes[:, slot] = cv[i, h]
+                blk.v_scale[slot] = sv[i, h]
+        pos, end = start, start + n
+        while pos < end:
+            lp = pos // PAGE
+            page_end = min(end, (lp + 1) * PAGE)
+            key = (seq, layer)
+            if pos % PAGE == 0 or key not in self._exact_k:
+                exact = np.zeros((PAGE, self.H, self.D), np.float32)
+                if pos % PAGE != 0:
+                    raise ValueError("8-bit append into a page whose exact rows were not kept")
+            else:
+                exact = self._exact_k[key]
+            exact[pos % PAGE:page_end - lp * PAGE] = k[pos - start:page_end - start]
+            present = page_end - lp * PAGE
+            codes, scales = codec.q8_quantize_k_page(exact[:present])
+            page = int(bt[lp])
+            for h in range(self.H):
+                blk = self.block(page, layer, h)
+                blk.k_codes[:present] = codes[:, h]
+                blk.k_scale[:] = scales[h]
+            self._exact_k[key] = exact
+            pos = page_end
+
+    # ------------------------------------------------------------ gather --
+    def gather(self, layer: int, bt, ctx_len: int):
+        """Dequantized K^ and V^ [ctx_len][H][D] (fp32) read through the block table."""
+        K = np.empty((ctx_len, self.H, self.D), np.float32)
+        V = np.empty_like(K)
+        for lp in range(-(-ctx_len // PAGE)):
+            n = min(PAGE, ctx_len - lp * PAGE)
+            page = int(bt[lp])
+            for h in range(self.H):
+                blk = self.block(page, layer, h)
+                if self.fmt == "q2":
+                    c, s, m = blk.read_k(n)
+                    K[lp * PAGE:lp * PAGE + n, h] = codec.q2_dequantize(c, s, m)
+                    c, s, m = blk.read_v(n)
+                    V[lp * PAGE:lp * PAGE + n, h] = codec.q2_dequantize(c, s, m)
+                else:
+                    c, s = blk.read_k(n)
+                    K[lp * PAGE:lp * PAGE + n, h] = codec.q8_dequantize(c, s[None, :])
+                    c, s = blk.read_v(n)
+                    V[lp * PAGE:lp * PAGE + n, h] = codec.q8_dequantize(c, s[:, None])
+        return K, V
+
+
+def dequantized_rows(fmt: str, k_rows, v_rows):
+    """K^, V^ of a whole sequence quantized page by page, without a pool image.
+
+    Same arithmetic as append + gather for a sequence appended from position 0
+    (used for the large workloads, where a full pool image does not fit).
+    """
+    k = np.asarray(k_rows, np.float32)
+    v = np.asarray(v_rows, np.float32)
+    if fmt == "q2":
+        K = codec.q2_dequantize(*codec.q2_quantize(k))
+        V = codec.q2_dequantize(*codec.q2_quantize(v))
+        return K, V
+    cv, sv = codec.q8_quantize_v(v)
+    V = codec.q8_dequantize(cv, sv[..., None])
+    K = np.empty_like(k)
+    for p0 in range(0, k.shape[0], PAGE):
+        c, s = codec.q8_quantize_k_page(k[p0:p0 + PAGE])
+        K[p0:p0 + PAGE] = codec.q8_dequantize(c, s[None])
+    return K, V

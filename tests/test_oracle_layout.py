@@ -1,0 +1,60 @@
+"""Oracle pins: page layout (packing) against loop references and byte totals."""
+
+import numpy as np
+
+from oracle import accounting, layout
+
+
+def _pack_loop(codes):
+    n = len(codes)
+    out = []
+    for b in range(n // 4):
+        v = 0
+        for j in range(4):
+            v |= int(codes[4 * b + j]) << (2 * j)
+        out.append(v)
+    return out
+
+
+def test_pack2_matches_loop():
+    rng = np.random.default_rng(21)
+    for n in (64, 128, 256):
+        c = rng.integers(0, 4, (5, n)).astype(np.uint8)
+        p = layout.pack2(c)
+        for r in range(5):
+            assert list(p[r]) == _pack_loop(c[r])
+        assert np.array_equal(layout.unpack2(p, n), c)
+
+
+def test_block_sizes_match_token_bytes():
+    for L, H, D in ((16, 4, 256), (1, 4, 256), (2, 2, 128)):
+        assert L * H * layout.q2_block_bytes(D) == accounting.page_bytes("q2", L, H, D)
+    assert 32 * 8 * layout.q8_block_bytes(128) == accounting.page_bytes("q8", 32, 8, 128)
+    assert layout.q2_block_bytes(256) == 2 * 64 * 72  # K and V rows of 64 tokens
+
+
+def test_v_plane_write_touches_only_its_slot():
+    buf = np.full(layout.q2_block_bytes(256), 0xA5, np.uint8)
+    blk = layout.Q2Block(buf, 256)
+    rng = np.random.default_rng(22)
+    before = buf.copy()
+    c = rng.integers(0, 4, 256).astype(np.uint8)
+    blk.write_v(37, c, np.float32(0.5), np.float32(-1.0))
+    codes = layout.unpack2(blk.v_codes, 64)            # [D][64]
+    old = layout.unpack2(before[16 * 256:32 * 256].reshape(256, 16), 64)
+    assert np.array_equal(codes[:, 37], c)
+    mask = np.ones(64, bool)
+    mask[37] = False
+    assert np.array_equal(codes[:, mask], old[:, mask])
+    assert np.array_equal(buf[:16 * 256], before[:16 * 256])  # K plane untouched
+
+
+def test_k_row_layout_positions():
+    buf = np.zeros(layout.q2_block_bytes(128), np.uint8)
+    blk = layout.Q2Block(buf, 128)
+    c = np.zeros(128, np.uint8)
+    c[5] = 3  # dim 5 -> byte 1, bits 2..3
+    blk.write_k(2, c, np.float32(1.0), np.float32(0.0))
+    row_off = 2 * 128 // 4
+    assert buf[row_off + 1] == 3 << 2 and buf[row_off:row_off + 32].sum() == 12
+    assert np.frombuffer(buf[32 * 128 + 16:32 * 128 + 24].tobytes(), np.float32).tolist() == [1.0, 0.0]
