@@ -1,0 +1,207 @@
+/*
+ * kvq.h — C ABI of a paged, quantized KV cache with attention that reads the
+ * compressed pages directly, for AMD Instinct MI355X (gfx950).
+ *
+ * What it implements, by source page:
+ *  - "KV at 9 KB a token" (ignis, why-ignis/kv-in-bytes), section "How it
+ *    works": a per-token byte cost of 64 B of 2-bit code plus an 8-byte
+ *    metadata row per head per token (9,216 B a token at 16 layers x 4 KV
+ *    heads x 256 dims); the pool is a byte budget of 64-token pages; a request
+ *    reserves pages for its whole bound when admitted; prefill attention reads
+ *    the compressed cache; every workspace byte a launch reads it writes first.
+ *    Section "See it, control it": pool size in bytes or tokens, and the pool
+ *    figures (pages, used pages, page bytes).
+ *  - "The KV cache and prompt reuse" (ignis, concepts), section "What a
+ *    sequence is made of": one pool shared by all lanes, a lane is charged for
+ *    the pages it holds; the window of exact recent keys the compressed format
+ *    keeps.  Section "When reuse misses": a format mismatch is refused before
+ *    any byte moves.
+ *  - "Half the Cache, Twice the Context" (ml.co.ke): the symmetric absmax
+ *    quantizer with per-channel K and per-token V scaling (section "What the
+ *    cache loses when you round it"), accumulation in real FP32 (section "The
+ *    cliff is in the accumulator"), and failing loudly rather than falling
+ *    back (section "How to apply this", item 6).
+ *
+ * Conventions for every call:
+ *  - Every entry point returns kv_status.  On any status other than KV_OK the
+ *    call has launched nothing and written nothing (host checks run first),
+ *    and kv_last_error() returns a message for the calling thread.
+ *  - There is no fallback path: an unsupported geometry, format or size is an
+ *    error, never a slower route.
+ *  - Pointers named d_* are device pointers owned by the caller (for example
+ *    torch tensors); all other pointers are host pointers read during the
+ *    call only.  A kv_stream_t is a hipStream_t (NULL = the null stream).
+ *    Kernels run asynchronously on that stream; host-side pool metadata
+ *    (reservations, block tables) is updated synchronously.
+ *  - A kv_pool is not thread-safe: calls on one pool must not overlap.
+ *  - Token positions and lengths are < 2^31; head_dim is 128 or 256; the GQA
+ *    group G = n_q_heads / n_kv_heads must be 1, 2, 4 or 8.
+ *  - A batch holds at most KV_MAX_BATCH sequences per call.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KV_PAGE_TOKENS 64
+#define KV_MAX_BATCH 128
+
+typedef void* kv_stream_t; /* hipStream_t */
+typedef struct kv_pool kv_pool;
+
+typedef enum {
+    /* 2-bit rows sized like hq-e8-2b: per (token, KV head) D/4 bytes of
+     * uniform 2-bit codes plus an 8-byte [fp32 scale, fp32 min] row; the
+     * dequantized value is fmaf(code, scale, min). */
+    KV_FMT_Q2 = 1,
+    /* int8 codes: K scaled per channel over the tokens of its 64-token page,
+     * V scaled per token (fp32 scales, symmetric, codes in [-127, 127]). */
+    KV_FMT_Q8 = 2
+} kv_format;
+
+typedef enum {
+    KV_OK = 0,
+    KV_ERR_ARG = -1,         /* null pointer, negative size, bad index */
+    KV_ERR_NO_SPACE = -2,    /* not enough free pages (or sequence slots) */
+    KV_ERR_BOUND = -3,       /* position or length beyond a sequence's reserved bound */
+    KV_ERR_FORMAT = -4,      /* operation does not match the pool's format */
+    KV_ERR_UNSUPPORTED = -5, /* geometry / batch size this library does not implement */
+    KV_ERR_WORKSPACE = -6,   /* workspace null or smaller than kv_workspace_bytes() */
+    KV_ERR_DEVICE = -7       /* a HIP runtime call failed */
+} kv_status;
+
+typedef struct {
+    int32_t n_layers;   /* attention layers that keep a cache */
+    int32_t n_kv_heads; /* Hkv */
+    int32_t head_dim;   /* D: 128 or 256 */
+    int32_t n_q_heads;  /* Hq, a multiple of Hkv; query head h reads KV head h / (Hq/Hkv) */
+} kv_geom;
+
+typedef struct {
+    int64_t pages;          /* pages the byte budget bought */
+    int64_t free_pages;     /* pages not reserved by any sequence */
+    int64_t reserved_pages; /* pages reserved by live sequences */
+    int64_t used_pages;     /* reserved pages that hold at least one appended token */
+    int64_t page_bytes;     /* 64 x token_bytes */
+    int64_t token_bytes;    /* e.g. 9,216 for 2-bit at 16 x 4 x 256 */
+    int64_t tokens;         /* pages x 64 */
+    int64_t n_seqs;         /* live sequences */
+} kv_pool_stats_t;
+
+/* Bytes one token costs in a format, and the bytes of one 64-token page.
+ * 2-bit: 2 x L x Hkv x (D/4 + 8).  8-bit: L x Hkv x (2D + 4 + 4D/64). */
+kv_status kv_token_bytes(const kv_geom* geom, kv_format fmt, int64_t* token_bytes, int64_t* page_bytes);
+
+/* Byte budget that holds `tokens` tokens in whole pages (the pool size can be
+ * given in tokens as well as bytes). */
+kv_status kv_pool_bytes_for_tokens(const kv_geom* geom, kv_format fmt, int64_t tokens, int64_t* bytes);
+
+/* Create a pool of floor(bytes / page_bytes) pages.  d_mem: NULL to let the
+ * library allocate device memory (freed by kv_pool_destroy), or caller-owned
+ * device memory of at least pages x page_bytes bytes.  max_seqs and
+ * max_seq_tokens size the device block tables (and, for KV_FMT_Q8, the
+ * per-sequence exact-key window of one page per layer and head).  Prints one
+ * line with the page and token counts to stderr.  Errors: KV_ERR_ARG,
+ * KV_ERR_UNSUPPORTED (geometry), KV_ERR_NO_SPACE (budget below one page),
+ * KV_ERR_DEVICE. */
+kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int32_t max_seqs,
+                         int64_t max_seq_tokens, void* d_mem, kv_pool** out);
+
+/* Destroy a pool; frees only memory the library allocated. */
+kv_status kv_pool_destroy(kv_pool* pool);
+
+kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
+
+/* Device address and size of the page array (page p starts at p x page_bytes);
+ * for inspection and tests. */
+kv_status kv_pool_device_ptr(const kv_pool* pool, void** d_pages, int64_t* bytes);
+
+/* Admission: reserve ceil(max_tokens / 64) pages for a new sequence's whole
+ * bound and upload its block table once.  pages: NULL to take free pages, or
+ * an explicit list of that many distinct free page ids (logical page i ->
+ * physical pages[i]).  Errors: KV_ERR_ARG, KV_ERR_BOUND (max_tokens above the
+ * pool's max_seq_tokens), KV_ERR_NO_SPACE (not enough free pages or no free
+ * sequence slot), KV_ERR_DEVICE. */
+kv_status kv_seq_reserve(kv_pool* pool, int64_t max_tokens, const int32_t* pages, int32_t* seq);
+
+/* Return a sequence's pages to the free list. */
+kv_status kv_seq_release(kv_pool* pool, int32_t seq);
+
+/* Host copy of a sequence's block table: writes up to cap page ids. */
+kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t cap, int32_t* n_pages);
+
+/* Quantize-on-append for one layer.  For entry i, rows
+ * d_k[row_i .. row_i + n_new[i]) (bf16 [rows][Hkv][D], row_i = sum of earlier
+ * n_new) go to positions start_pos[i] .. start_pos[i] + n_new[i] - 1 of
+ * sequence seqs[i]; same for d_v.  Each token's K and V rows are quantized in
+ * fp32 (2-bit: min, scale = (max - min) / 3 correctly rounded, codes
+ * rint((x - min) / scale) clamped to 0..3; 8-bit: V per token; K per channel
+ * over the exact rows present in the token's page) and written into slot
+ * pos % 64 of page block_table[pos / 64].  No other slot of the pool changes,
+ * except that an 8-bit append re-derives the K codes and channel scales of the
+ * pages it touches.  The sequences of one call must be distinct.  Errors:
+ * KV_ERR_ARG, KV_ERR_BOUND (a position beyond the reserved bound; nothing is
+ * written), KV_ERR_UNSUPPORTED (more than KV_MAX_BATCH entries),
+ * KV_ERR_DEVICE. */
+kv_status kv_append_quant(kv_pool* pool, int32_t layer, int32_t n, const int32_t* seqs,
+                          const int64_t* start_pos, const int32_t* n_new, const uint16_t* d_k,
+                          const uint16_t* d_v, kv_stream_t stream);
+
+enum { KV_OP_DECODE = 0, KV_OP_PREFILL = 1 };
+
+/* Workspace bytes for an attention call: decode with n_rows sequences, or
+ * prefill with n_rows chunk queries, and n_splits splits of the context
+ * (0 = the split count the library would choose; for decode that choice
+ * also needs the context lengths, so pass the same n_splits to both calls). */
+kv_status kv_workspace_bytes(const kv_pool* pool, int32_t op, int32_t n_rows, int32_t n_splits, int64_t* bytes);
+
+/* Split-count the library picks for a decode batch when n_splits = 0. */
+kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_len, int32_t* n_splits);
+
+/* One decode step for n sequences of one layer.  d_q: bf16 [n][Hq][D], one
+ * query per sequence; sequence i attends to its tokens 0 .. ctx_len[i]-1
+ * (ctx_len >= 1, within the reserved bound).  Scores are sm_scale x q.k^ over
+ * the dequantized keys; softmax and all sums are kept in fp32; the context is
+ * split into n_splits page ranges (flash-decoding) whose partial results
+ * (max, sum, unnormalised output) go to d_ws and are merged in fp32.
+ * d_out: fp32 [n][Hq][D].  d_scores: NULL, or fp32 [n][Hq][scores_stride]
+ * receiving the raw logits (scores_stride >= max ctx_len).  Every workspace
+ * byte read is written first within the call.  Errors: KV_ERR_ARG,
+ * KV_ERR_BOUND, KV_ERR_FORMAT, KV_ERR_UNSUPPORTED, KV_ERR_WORKSPACE,
+ * KV_ERR_DEVICE. */
+kv_status kv_attn_decode(kv_pool* pool, int32_t layer, int32_t n, const int32_t* seqs, const int64_t* ctx_len,
+                         const uint16_t* d_q, float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes,
+                         float* d_out, float* d_scores, int64_t scores_stride, kv_stream_t stream);
+
+/* Causal prefill of a chunk of n_q queries of one sequence that sit at
+ * positions q_start .. q_start + n_q - 1, after the chunk's own K/V have been
+ * appended: query i attends to tokens 0 .. q_start + i, all read from the
+ * compressed pool.  d_q: bf16 [n_q][Hq][D]; d_out: fp32 [n_q][Hq][D].  The
+ * workspace needs no clearing: every byte read is written first.  Errors as
+ * for decode. */
+kv_status kv_attn_prefill(kv_pool* pool, int32_t layer, int32_t seq, int64_t q_start, int32_t n_q,
+                          const uint16_t* d_q, float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes,
+                          float* d_out, kv_stream_t stream);
+
+/* Dequantize the 64 token slots of one (page, layer, KV head, K or V) plane
+ * into d_out fp32 [64][D] (kv: 0 = K, 1 = V).  Slots never written hold
+ * whatever the decoding of their bytes gives. */
+kv_status kv_dequant_page(const kv_pool* pool, int32_t page, int32_t layer, int32_t head, int32_t kv, float* d_out,
+                          kv_stream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kv_last_error(void);
+
+/* Name of a status code. */
+const char* kv_status_str(kv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

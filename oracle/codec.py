@@ -4,7 +4,7 @@
 it works": 64 B of 2-bit code plus an 8-byte metadata row per head per token).
 The pages size the row but do not give its codebook; this library uses
 uniform asymmetric codes per (token, head) row, in emulated fp32:
-    mn = min x, mx = max x                         (exact)
+    mn = min x, mx = max x                         (exact; a zero is taken as +0)
     scale = fl32(fl32(mx - mn) / 3);  scale == 0 -> 1.0
     c_i = clamp(rint(fl32(fl32(x_i - mn) / scale)), 0, 3)   (rint = nearest even)
     dequantized x_i = fl32(c_i * scale + mn)       (one rounding, as fmaf)
@@ -44,8 +44,8 @@ def q2_quantize(x):
     """Rows x[..., D] (fp32 values) -> (codes uint8[..., D], scale f32[...], mn f32[...])."""
     x = np.asarray(x, dtype=F32)
     _check_finite(x)
-    mn = x.min(axis=-1)
-    mx = x.max(axis=-1)
+    mn = np.add(x.min(axis=-1), F32(0), dtype=F32)   # a zero min or max is taken as +0
+    mx = np.add(x.max(axis=-1), F32(0), dtype=F32)
     span = np.subtract(mx, mn, dtype=F32)
     scale = np.divide(span, F32(3), dtype=F32)
     scale = np.where(scale == F32(0), F32(1), scale).astype(F32)

@@ -1,0 +1,165 @@
+// Quantize-on-append for the 2-bit format, and page dequantization.
+//
+// The row format follows the byte budget of "KV at 9 KB a token" (section "How
+// it works", table): per (token, KV head), D/4 bytes of 2-bit code plus an
+// 8-byte metadata row [fp32 scale, fp32 min].  The codebook is uniform over
+// the row's range:
+//     mn = min x, mx = max x, scale = (mx - mn) / 3 (correctly rounded fp32),
+//     scale == 0 -> 1.0, code = clamp(rint((x - mn) / scale), 0, 3)
+// and the dequantized value is fmaf(code, scale, mn).  Every step is a single
+// IEEE fp32 operation with round-to-nearest-even, so the codes and metadata are
+// a pure function of the bf16 inputs (min and max do not depend on reduction
+// order).  A zero min or max is canonicalised to +0.
+//
+// Layout of one (layer, KV head) block of a page: K codes token-major (row t =
+// D/4 bytes), V codes dim-major (row d = 16 bytes holding the 64 token slots),
+// then 64 K metadata rows and 64 V metadata rows.  Packing is
+// least-significant-bits first: element j of a row is at bit 2*(j%4) of byte
+// j/4.  K rows are read by token for the q.k contraction over dims; V rows by
+// dim for the p.v contraction over tokens.
+//
+// Work split: one workgroup of four waves per (sequence, page touched, KV
+// head); wave w owns token slots [16w, 16w+16) of the page, which is exactly
+// one 32-bit word of every dim-major V row, so the V plane is written with one
+// read-modify-write per (dim, word) and no two workgroups share a byte.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+// Quantize one row spread over a wavefront, DPL consecutive elements per lane.
+// Returns the lane's codes; scale and mn are the same in every lane.
+template <int DPL>
+__device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t (&c)[DPL], float& scale, float& mn) {
+#pragma clang fp contract(off)
+    float lo = x[0], hi = x[0];
+#pragma unroll
+    for (int k = 1; k < DPL; ++k) {
+        lo = fminf(lo, x[k]);
+        hi = fmaxf(hi, x[k]);
+    }
+    lo = wave_min(lo) + 0.0f;
+    hi = wave_max(hi) + 0.0f;
+    float sc = (hi - lo) / 3.0f;
+    if (sc == 0.0f) sc = 1.0f;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        float t = (x[k] - lo) / sc;
+        float r = fminf(fmaxf(rintf(t), 0.0f), 3.0f);
+        c[k] = (uint32_t)r;
+    }
+    scale = sc;
+    mn = lo;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                        const uint16_t* __restrict__ kin,
+                                                        const uint16_t* __restrict__ vin) {
+    constexpr int DPL = D / 64;
+    const int x = blockIdx.x, head = blockIdx.y;
+    int e = 0;
+    while (e + 1 < bd.n && bd.work0[e + 1] <= x) ++e;
+    const int start = bd.pos[e], cnt = bd.cnt[e];
+    const int lp = start / PAGE + (x - bd.work0[e]);
+    const int slot_lo = max(start, lp * PAGE) - lp * PAGE;
+    const int slot_hi = min(start + cnt, (lp + 1) * PAGE) - lp * PAGE;
+    const int phys = pv.bt[(int64_t)bd.seq[e] * pv.bt_stride + lp];
+    uint8_t* blk = pv.pages + (int64_t)phys * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
+
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int s0 = max(slot_lo, wave * 16), s1 = min(slot_hi, wave * 16 + 16);
+    if (s0 >= s1) return;
+
+    uint32_t vw[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) vw[k] = 0;
+    uint32_t vmask = 0;
+    for (int s = s0; s < s1; ++s) {
+        const int64_t row = (int64_t)bd.row0[e] + (lp * PAGE + s - start);
+        const int64_t off = (row * pv.Hkv + head) * D + lane * DPL;
+        float xk[DPL], xv[DPL];
+        load_bf16<DPL>(kin + off, xk);
+        load_bf16<DPL>(vin + off, xv);
+        uint32_t ck[DPL], cv[DPL];
+        float sk, mk, sv, mv;
+        q2_quantize_row<DPL>(xk, ck, sk, mk);
+        q2_quantize_row<DPL>(xv, cv, sv, mv);
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) bits |= ck[k] << (2 * k);
+        uint8_t* krow = blk + (int64_t)s * (D / 4);
+        if constexpr (DPL == 4) {
+            krow[lane] = (uint8_t)bits;
+        } else {
+            uint32_t other = __shfl_down(bits, 1);
+            if ((lane & 1) == 0) krow[lane >> 1] = (uint8_t)(bits | (other << 4));
+        }
+        const int sh = 2 * (s & 15);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) vw[k] |= cv[k] << sh;
+        vmask |= 3u << sh;
+        if (lane == 0) {
+            *reinterpret_cast<float2*>(blk + q2_kmeta_off(D) + 8 * s) = make_float2(sk, mk);
+            *reinterpret_cast<float2*>(blk + q2_vmeta_off(D) + 8 * s) = make_float2(sv, mv);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        const int d = lane * DPL + k;
+        uint32_t* p = reinterpret_cast<uint32_t*>(blk + q2_vcodes_off(D) + 16 * d + 4 * wave);
+        uint32_t old = (vmask == 0xFFFFFFFFu) ? 0u : *p;
+        *p = (old & ~vmask) | vw[k];
+    }
+}
+
+hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, int work_items, const uint16_t* k,
+                            const uint16_t* v, hipStream_t s) {
+    dim3 grid(work_items, pv.Hkv);
+    if (pv.D == 256)
+        hipLaunchKernelGGL(append_q2_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+    else
+        hipLaunchKernelGGL(append_q2_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ dequant ----
+
+__global__ __launch_bounds__(256) void dequant_page_kernel(PoolView pv, int fmt, int page, int layer, int head, int kv,
+                                                           float* __restrict__ out) {
+    const int D = pv.D;
+    const uint8_t* blk = pv.pages + (int64_t)page * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
+    for (int i = threadIdx.x; i < PAGE * D; i += blockDim.x) {
+        const int t = i / D, d = i % D;
+        float r;
+        if (fmt == KV_FMT_Q2) {
+            uint32_t c;
+            float2 meta;
+            if (kv == 0) {
+                c = (blk[t * (D / 4) + d / 4] >> (2 * (d % 4))) & 3u;
+                meta = *reinterpret_cast<const float2*>(blk + q2_kmeta_off(D) + 8 * t);
+            } else {
+                c = (blk[q2_vcodes_off(D) + 16 * d + t / 4] >> (2 * (t % 4))) & 3u;
+                meta = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * t);
+            }
+            r = __fmaf_rn((float)c, meta.x, meta.y);
+        } else {
+            if (kv == 0) {
+                int8_t c = (int8_t)blk[t * D + d];
+                r = (float)c * *reinterpret_cast<const float*>(blk + q8_kscale_off(D) + 4 * d);
+            } else {
+                int8_t c = (int8_t)blk[q8_vcodes_off(D) + 64 * d + t];
+                r = (float)c * *reinterpret_cast<const float*>(blk + q8_vscale_off(D) + 4 * t);
+            }
+        }
+        out[i] = r;
+    }
+}
+
+hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(dequant_page_kernel, dim3(1), dim3(256), 0, s, pv, fmt, page, layer, head, kv, out);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

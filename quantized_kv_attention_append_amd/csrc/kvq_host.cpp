@@ -1,0 +1,475 @@
+// Host runtime of the paged, quantized KV cache: pool sizing, admission-time
+// page reservation, block tables, argument checks and kernel launch planning.
+//
+// The pool is a byte budget of 64-token pages shared by every sequence, and a
+// sequence reserves the pages of its whole bound when it is admitted, so an
+// append inside the bound can never run out of pages ("KV at 9 KB a token",
+// section "How it works"; "The KV cache and prompt reuse", section "What a
+// sequence is made of").  Every check runs before anything is launched, and a
+// mismatch is refused before any byte moves ("The KV cache and prompt reuse",
+// section "When reuse misses"); nothing falls back to another path ("Half the
+// Cache, Twice the Context", section "How to apply this", item 6).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kv_status fail(kv_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(kv_status_str(s)) + ": " + buf;
+    return s;
+}
+
+kv_status hip_fail(hipError_t e, const char* what) {
+    return fail(KV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+kv_status check_geom(const kv_geom* g, kv_format fmt) {
+    if (!g) return fail(KV_ERR_ARG, "geometry is NULL");
+    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8) return fail(KV_ERR_FORMAT, "unknown format %d", (int)fmt);
+    if (g->n_layers <= 0 || g->n_kv_heads <= 0 || g->n_q_heads <= 0 || g->head_dim <= 0)
+        return fail(KV_ERR_ARG, "geometry fields must be positive");
+    if (g->head_dim != 128 && g->head_dim != 256)
+        return fail(KV_ERR_UNSUPPORTED, "head_dim %d (supported: 128, 256)", g->head_dim);
+    if (g->n_q_heads % g->n_kv_heads != 0)
+        return fail(KV_ERR_UNSUPPORTED, "n_q_heads %d is not a multiple of n_kv_heads %d", g->n_q_heads,
+                    g->n_kv_heads);
+    int G = g->n_q_heads / g->n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(KV_ERR_UNSUPPORTED, "GQA group %d (supported: 1, 2, 4, 8)", G);
+    return KV_OK;
+}
+
+int64_t block_bytes_of(kv_format fmt, int D) { return fmt == KV_FMT_Q2 ? q2_block_bytes(D) : q8_block_bytes(D); }
+
+int64_t token_bytes_of(const kv_geom* g, kv_format fmt) {
+    return (int64_t)g->n_layers * g->n_kv_heads * block_bytes_of(fmt, g->head_dim) / PAGE;
+}
+
+}  // namespace
+
+struct kv_pool {
+    kv_geom geom;
+    kv_format fmt;
+    int64_t n_pages = 0;
+    int64_t page_bytes = 0, token_bytes = 0, block_bytes = 0;
+    uint8_t* d_pages = nullptr;
+    bool own_pages = false;
+    int32_t max_seqs = 0;
+    int32_t bt_stride = 0;       // max pages per sequence
+    int32_t* d_bt = nullptr;     // [max_seqs][bt_stride]
+    uint16_t* d_stage = nullptr; // 8-bit exact-K window
+    int device = 0;
+    // host metadata
+    std::vector<int32_t> owner;      // page -> seq slot or -1
+    std::vector<int32_t> free_stack; // may hold pages reserved explicitly since (skipped lazily)
+    int64_t free_count = 0;
+    struct Seq {
+        bool live = false;
+        int64_t bound = 0;     // reserved tokens
+        int64_t appended = 0;  // highest position appended + 1, over all layers
+        std::vector<int32_t> pages;
+    };
+    std::vector<Seq> seqs;
+
+    PoolView view() const {
+        PoolView v;
+        v.pages = d_pages;
+        v.page_bytes = page_bytes;
+        v.block_bytes = block_bytes;
+        v.L = geom.n_layers;
+        v.Hkv = geom.n_kv_heads;
+        v.D = geom.head_dim;
+        v.Hq = geom.n_q_heads;
+        v.bt = d_bt;
+        v.bt_stride = bt_stride;
+        v.stage = d_stage;
+        return v;
+    }
+};
+
+extern "C" {
+
+const char* kv_status_str(kv_status s) {
+    switch (s) {
+        case KV_OK: return "KV_OK";
+        case KV_ERR_ARG: return "KV_ERR_ARG";
+        case KV_ERR_NO_SPACE: return "KV_ERR_NO_SPACE";
+        case KV_ERR_BOUND: return "KV_ERR_BOUND";
+        case KV_ERR_FORMAT: return "KV_ERR_FORMAT";
+        case KV_ERR_UNSUPPORTED: return "KV_ERR_UNSUPPORTED";
+        case KV_ERR_WORKSPACE: return "KV_ERR_WORKSPACE";
+        case KV_ERR_DEVICE: return "KV_ERR_DEVICE";
+    }
+    return "KV_ERR_UNKNOWN";
+}
+
+const char* kv_last_error(void) { return g_last_error.c_str(); }
+
+kv_status kv_token_bytes(const kv_geom* geom, kv_format fmt, int64_t* token_bytes, int64_t* page_bytes) {
+    kv_status s = check_geom(geom, fmt);
+    if (s != KV_OK) return s;
+    if (!token_bytes || !page_bytes) return fail(KV_ERR_ARG, "output pointer is NULL");
+    *token_bytes = token_bytes_of(geom, fmt);
+    *page_bytes = *token_bytes * PAGE;
+    return KV_OK;
+}
+
+kv_status kv_pool_bytes_for_tokens(const kv_geom* geom, kv_format fmt, int64_t tokens, int64_t* bytes) {
+    kv_status s = check_geom(geom, fmt);
+    if (s != KV_OK) return s;
+    if (!bytes) return fail(KV_ERR_ARG, "output pointer is NULL");
+    if (tokens < 0) return fail(KV_ERR_ARG, "negative token count");
+    *bytes = ((tokens + PAGE - 1) / PAGE) * token_bytes_of(geom, fmt) * PAGE;
+    return KV_OK;
+}
+
+kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int32_t max_seqs, int64_t max_seq_tokens,
+                         void* d_mem, kv_pool** out) {
+    kv_status s = check_geom(geom, fmt);
+    if (s != KV_OK) return s;
+    if (!out) return fail(KV_ERR_ARG, "out is NULL");
+    if (bytes < 0 || max_seqs <= 0 || max_seq_tokens <= 0)
+        return fail(KV_ERR_ARG, "bytes, max_seqs and max_seq_tokens must be positive");
+    if (max_seq_tokens >= (int64_t)1 << 31) return fail(KV_ERR_UNSUPPORTED, "max_seq_tokens must be < 2^31");
+    int64_t tb = token_bytes_of(geom, fmt), pb = tb * PAGE;
+    int64_t n_pages = bytes / pb;
+    if (n_pages <= 0) return fail(KV_ERR_NO_SPACE, "budget of %lld B is below one page (%lld B)", (long long)bytes, (long long)pb);
+    if (n_pages >= ((int64_t)1 << 31)) return fail(KV_ERR_UNSUPPORTED, "more than 2^31 pages");
+
+    kv_pool* p = new kv_pool();
+    p->geom = *geom;
+    p->fmt = fmt;
+    p->n_pages = n_pages;
+    p->page_bytes = pb;
+    p->token_bytes = tb;
+    p->block_bytes = block_bytes_of(fmt, geom->head_dim);
+    p->max_seqs = max_seqs;
+    p->bt_stride = (int32_t)((max_seq_tokens + PAGE - 1) / PAGE);
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        delete p;
+        return hip_fail(e, "hipGetDevice");
+    }
+    if (d_mem) {
+        p->d_pages = (uint8_t*)d_mem;
+    } else {
+        e = hipMalloc((void**)&p->d_pages, (size_t)(n_pages * pb));
+        if (e != hipSuccess) {
+            delete p;
+            return hip_fail(e, "hipMalloc(pool pages)");
+        }
+        p->own_pages = true;
+    }
+    e = hipMalloc((void**)&p->d_bt, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(p->d_bt, 0, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
+    if (e == hipSuccess && fmt == KV_FMT_Q8) {
+        size_t sb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * PAGE * geom->head_dim * sizeof(uint16_t);
+        e = hipMalloc((void**)&p->d_stage, sb);
+    }
+    if (e != hipSuccess) {
+        kv_status r = hip_fail(e, "hipMalloc(block tables / window)");
+        kv_pool_destroy(p);
+        return r;
+    }
+    p->owner.assign((size_t)n_pages, -1);
+    p->free_stack.resize((size_t)n_pages);
+    for (int64_t i = 0; i < n_pages; ++i) p->free_stack[(size_t)i] = (int32_t)(n_pages - 1 - i);
+    p->free_count = n_pages;
+    p->seqs.resize((size_t)max_seqs);
+    fprintf(stderr, "kvq: pool %s kv_pool_pages=%lld kv_pool_tokens=%lld kv_page_bytes=%lld token_bytes=%lld\n",
+            fmt == KV_FMT_Q2 ? "q2" : "q8", (long long)n_pages, (long long)(n_pages * PAGE), (long long)pb,
+            (long long)tb);
+    *out = p;
+    return KV_OK;
+}
+
+kv_status kv_pool_destroy(kv_pool* p) {
+    if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+    if (p->own_pages && p->d_pages) (void)hipFree(p->d_pages);
+    if (p->d_bt) (void)hipFree(p->d_bt);
+    if (p->d_stage) (void)hipFree(p->d_stage);
+    delete p;
+    return KV_OK;
+}
+
+kv_status kv_pool_stats(const kv_pool* p, kv_pool_stats_t* o) {
+    if (!p || !o) return fail(KV_ERR_ARG, "NULL argument");
+    int64_t reserved = 0, used = 0, n = 0;
+    for (const auto& s : p->seqs) {
+        if (!s.live) continue;
+        ++n;
+        reserved += (int64_t)s.pages.size();
+        used += (s.appended + PAGE - 1) / PAGE;
+    }
+    o->pages = p->n_pages;
+    o->free_pages = p->free_count;
+    o->reserved_pages = reserved;
+    o->used_pages = used;
+    o->page_bytes = p->page_bytes;
+    o->token_bytes = p->token_bytes;
+    o->tokens = p->n_pages * PAGE;
+    o->n_seqs = n;
+    return KV_OK;
+}
+
+kv_status kv_pool_device_ptr(const kv_pool* p, void** d_pages, int64_t* bytes) {
+    if (!p || !d_pages || !bytes) return fail(KV_ERR_ARG, "NULL argument");
+    *d_pages = p->d_pages;
+    *bytes = p->n_pages * p->page_bytes;
+    return KV_OK;
+}
+
+kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, int32_t* seq) {
+    if (!p || !seq) return fail(KV_ERR_ARG, "NULL argument");
+    if (max_tokens <= 0) return fail(KV_ERR_ARG, "max_tokens must be positive");
+    int64_t need = (max_tokens + PAGE - 1) / PAGE;
+    if (need > p->bt_stride)
+        return fail(KV_ERR_BOUND, "bound of %lld tokens exceeds the pool's max_seq_tokens (%d pages)", (long long)max_tokens,
+                    p->bt_stride);
+    int32_t slot = -1;
+    for (int32_t i = 0; i < p->max_seqs; ++i)
+        if (!p->seqs[(size_t)i].live) {
+            slot = i;
+            break;
+        }
+    if (slot < 0) return fail(KV_ERR_NO_SPACE, "all %d sequence slots are live", p->max_seqs);
+    if (need > p->free_count)
+        return fail(KV_ERR_NO_SPACE, "need %lld pages, %lld free", (long long)need, (long long)p->free_count);
+    std::vector<int32_t> got;
+    got.reserve((size_t)need);
+    if (pages) {
+        std::vector<int32_t> sorted(pages, pages + need);
+        std::sort(sorted.begin(), sorted.end());
+        for (int64_t i = 0; i < need; ++i) {
+            int32_t pg = sorted[(size_t)i];
+            if (pg < 0 || pg >= p->n_pages) return fail(KV_ERR_ARG, "page id %d out of range", pg);
+            if (i > 0 && sorted[(size_t)i - 1] == pg) return fail(KV_ERR_ARG, "page id %d listed twice", pg);
+            if (p->owner[(size_t)pg] != -1) return fail(KV_ERR_NO_SPACE, "page %d is already reserved", pg);
+        }
+        got.assign(pages, pages + need);
+    } else {
+        while ((int64_t)got.size() < need) {
+            int32_t pg = p->free_stack.back();
+            p->free_stack.pop_back();
+            if (p->owner[(size_t)pg] == -1) got.push_back(pg);
+        }
+    }
+    hipError_t e = hipMemcpy(p->d_bt + (size_t)slot * p->bt_stride, got.data(), got.size() * sizeof(int32_t),
+                             hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (!pages)
+            for (int32_t pg : got) p->free_stack.push_back(pg);
+        return hip_fail(e, "hipMemcpy(block table)");
+    }
+    for (int32_t pg : got) p->owner[(size_t)pg] = slot;
+    p->free_count -= need;
+    auto& s = p->seqs[(size_t)slot];
+    s.live = true;
+    s.bound = max_tokens;
+    s.appended = 0;
+    s.pages = std::move(got);
+    *seq = slot;
+    return KV_OK;
+}
+
+kv_status kv_seq_release(kv_pool* p, int32_t seq) {
+    if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+    if (seq < 0 || seq >= p->max_seqs || !p->seqs[(size_t)seq].live) return fail(KV_ERR_ARG, "sequence %d is not live", seq);
+    auto& s = p->seqs[(size_t)seq];
+    for (int32_t pg : s.pages) {
+        p->owner[(size_t)pg] = -1;
+        p->free_stack.push_back(pg);
+    }
+    p->free_count += (int64_t)s.pages.size();
+    s = kv_pool::Seq();
+    return KV_OK;
+}
+
+kv_status kv_seq_pages(const kv_pool* p, int32_t seq, int32_t* pages, int32_t cap, int32_t* n_pages) {
+    if (!p || !n_pages) return fail(KV_ERR_ARG, "NULL argument");
+    if (seq < 0 || seq >= p->max_seqs || !p->seqs[(size_t)seq].live) return fail(KV_ERR_ARG, "sequence %d is not live", seq);
+    const auto& s = p->seqs[(size_t)seq];
+    *n_pages = (int32_t)s.pages.size();
+    if (pages)
+        for (int32_t i = 0; i < cap && i < *n_pages; ++i) pages[i] = s.pages[(size_t)i];
+    return KV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* what) {
+    if (seq < 0 || seq >= p->max_seqs || !p->seqs[(size_t)seq].live)
+        return fail(KV_ERR_ARG, "%s: sequence %d is not live", what, seq);
+    if (end_pos > p->seqs[(size_t)seq].bound)
+        return fail(KV_ERR_BOUND, "%s: position %lld beyond sequence %d's bound of %lld tokens", what,
+                    (long long)end_pos, seq, (long long)p->seqs[(size_t)seq].bound);
+    return KV_OK;
+}
+
+// Default split count for a decode batch: enough workgroups to cover the
+// chip several times (256 compute units), with at least four pages per split.
+int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
+    int64_t max_pages = 1;
+    for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
+    int64_t base = (int64_t)n * p->geom.n_kv_heads;
+    int64_t want = (2048 + base - 1) / base;
+    int64_t cap = std::max<int64_t>(1, max_pages / 4);
+    int64_t sp = std::min(want, cap);
+    sp = std::max<int64_t>(1, std::min<int64_t>(sp, 256));
+    return (int)sp;
+}
+
+}  // namespace
+
+extern "C" {
+
+kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* seqs, const int64_t* start_pos,
+                          const int32_t* n_new, const uint16_t* d_k, const uint16_t* d_v, kv_stream_t stream) {
+    if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+    if (n < 0) return fail(KV_ERR_ARG, "negative batch size");
+    if (n == 0) return KV_OK;
+    if (n > KV_MAX_BATCH) return fail(KV_ERR_UNSUPPORTED, "batch of %d exceeds KV_MAX_BATCH (%d)", n, KV_MAX_BATCH);
+    if (!seqs || !start_pos || !n_new || !d_k || !d_v) return fail(KV_ERR_ARG, "NULL argument");
+    if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
+    BatchDesc bd;
+    memset(&bd, 0, sizeof bd);
+    bd.n = n;
+    int64_t rows = 0, work = 0;
+    for (int i = 0; i < n; ++i) {
+        if (n_new[i] < 0 || start_pos[i] < 0) return fail(KV_ERR_ARG, "entry %d: negative position or count", i);
+        kv_status s = check_seq(p, seqs[i], start_pos[i] + n_new[i], "append");
+        if (s != KV_OK) return s;
+        for (int j = 0; j < i; ++j)
+            if (seqs[j] == seqs[i]) return fail(KV_ERR_ARG, "sequence %d appears twice in one append", seqs[i]);
+        bd.seq[i] = seqs[i];
+        bd.pos[i] = (int32_t)start_pos[i];
+        bd.cnt[i] = n_new[i];
+        bd.row0[i] = (int32_t)rows;
+        bd.work0[i] = (int32_t)work;
+        if (n_new[i] > 0) work += (start_pos[i] + n_new[i] - 1) / PAGE - start_pos[i] / PAGE + 1;
+        rows += n_new[i];
+        if (rows >= ((int64_t)1 << 31)) return fail(KV_ERR_UNSUPPORTED, "more than 2^31 rows in one append");
+    }
+    bd.work0[n] = (int32_t)work;
+    if (work == 0) return KV_OK;
+    hipError_t e = p->fmt == KV_FMT_Q2
+                       ? launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream)
+                       : launch_append_q8(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+    for (int i = 0; i < n; ++i) {
+        auto& s = p->seqs[(size_t)seqs[i]];
+        s.appended = std::max<int64_t>(s.appended, start_pos[i] + n_new[i]);
+    }
+    return KV_OK;
+}
+
+kv_status kv_decode_splits(const kv_pool* p, int32_t n, const int64_t* ctx_len, int32_t* n_splits) {
+    if (!p || !ctx_len || !n_splits || n <= 0) return fail(KV_ERR_ARG, "bad argument");
+    *n_splits = auto_splits(p, n, ctx_len);
+    return KV_OK;
+}
+
+kv_status kv_workspace_bytes(const kv_pool* p, int32_t op, int32_t n_rows, int32_t n_splits, int64_t* bytes) {
+    if (!p || !bytes) return fail(KV_ERR_ARG, "NULL argument");
+    if (n_rows < 0 || n_splits < 0) return fail(KV_ERR_ARG, "negative size");
+    if (op == KV_OP_DECODE) {
+        int sp = n_splits > 0 ? n_splits : 256;
+        *bytes = 4 * decode_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
+    } else if (op == KV_OP_PREFILL) {
+        int sp = n_splits > 0 ? n_splits : 1;
+        *bytes = 4 * prefill_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
+    } else {
+        return fail(KV_ERR_ARG, "unknown op %d", op);
+    }
+    return KV_OK;
+}
+
+kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* seqs, const int64_t* ctx_len,
+                         const uint16_t* d_q, float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes,
+                         float* d_out, float* d_scores, int64_t scores_stride, kv_stream_t stream) {
+    if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+    if (n <= 0) return fail(KV_ERR_ARG, "batch size must be positive");
+    if (n > KV_MAX_BATCH) return fail(KV_ERR_UNSUPPORTED, "batch of %d exceeds KV_MAX_BATCH (%d)", n, KV_MAX_BATCH);
+    if (!seqs || !ctx_len || !d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
+    if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
+    if (n_splits < 0 || n_splits > 1024) return fail(KV_ERR_ARG, "n_splits %d out of range", n_splits);
+    BatchDesc bd;
+    memset(&bd, 0, sizeof bd);
+    bd.n = n;
+    int64_t max_ctx = 0;
+    for (int i = 0; i < n; ++i) {
+        if (ctx_len[i] <= 0) return fail(KV_ERR_ARG, "entry %d: ctx_len must be >= 1", i);
+        kv_status s = check_seq(p, seqs[i], ctx_len[i], "decode");
+        if (s != KV_OK) return s;
+        bd.seq[i] = seqs[i];
+        bd.pos[i] = (int32_t)ctx_len[i];
+        max_ctx = std::max(max_ctx, ctx_len[i]);
+    }
+    if (d_scores && scores_stride < max_ctx) return fail(KV_ERR_ARG, "scores_stride %lld < max ctx_len %lld", (long long)scores_stride, (long long)max_ctx);
+    int sp = n_splits > 0 ? n_splits : auto_splits(p, n, ctx_len);
+    int64_t need = 4 * decode_ws_floats(n, p->geom.n_q_heads, p->geom.head_dim, sp);
+    if (!d_ws || ws_bytes < need)
+        return fail(KV_ERR_WORKSPACE, "decode needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
+    hipStream_t s = (hipStream_t)stream;
+    PoolView pv = p->view();
+    hipError_t e = p->fmt == KV_FMT_Q2 ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_scores, scores_stride, s)
+                                       : launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_scores, scores_stride, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    e = launch_merge_decode(pv, bd, sp, (const float*)d_ws, d_out, s);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return KV_OK;
+}
+
+kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_start, int32_t n_q, const uint16_t* d_q,
+                          float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes, float* d_out,
+                          kv_stream_t stream) {
+    if (!p) return fail(KV_ERR_ARG, "pool is NULL");
+    if (p->fmt != KV_FMT_Q2) return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit format only");
+    if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
+    if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
+    if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
+    kv_status st = check_seq(p, seq, q_start + n_q, "prefill");
+    if (st != KV_OK) return st;
+    if (n_splits < 0 || n_splits > 64) return fail(KV_ERR_ARG, "n_splits %d out of range", n_splits);
+    int sp = n_splits > 0 ? n_splits : 1;
+    int64_t need = 4 * prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim, sp);
+    if (!d_ws || ws_bytes < need)
+        return fail(KV_ERR_WORKSPACE, "prefill needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
+    hipError_t e = launch_prefill_q2(p->view(), layer, seq, (int)q_start, n_q, d_q, sm_scale, sp, (float*)d_ws, d_out,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return KV_OK;
+}
+
+kv_status kv_dequant_page(const kv_pool* p, int32_t page, int32_t layer, int32_t head, int32_t kv, float* d_out,
+                          kv_stream_t stream) {
+    if (!p || !d_out) return fail(KV_ERR_ARG, "NULL argument");
+    if (page < 0 || page >= p->n_pages) return fail(KV_ERR_ARG, "page %d out of range", page);
+    if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
+    if (head < 0 || head >= p->geom.n_kv_heads) return fail(KV_ERR_ARG, "head %d out of range", head);
+    if (kv != 0 && kv != 1) return fail(KV_ERR_ARG, "kv must be 0 (K) or 1 (V)");
+    hipError_t e = launch_dequant_page(p->view(), (int)p->fmt, page, layer, head, kv, d_out, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    return KV_OK;
+}
+
+}  // extern "C"

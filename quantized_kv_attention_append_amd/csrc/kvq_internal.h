@@ -1,0 +1,83 @@
+// Internal interface between the host runtime (kvq_host.cpp) and the HIP
+// kernels.  Not part of the public ABI (include/kvq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int PAGE = KV_PAGE_TOKENS;
+
+// Device view of a pool, passed by value to every kernel.
+struct PoolView {
+    uint8_t* pages;        // page p at pages + p * page_bytes
+    int64_t page_bytes;
+    int64_t block_bytes;   // one (layer, KV head) block inside a page
+    int32_t L, Hkv, D, Hq;
+    const int32_t* bt;     // device block tables [max_seqs][bt_stride]
+    int32_t bt_stride;
+    uint16_t* stage;       // 8-bit pools: exact K window, bf16 [max_seqs][L][Hkv][64][D]
+};
+
+// Per-call batch description, passed by value as a kernel argument (so it is
+// captured with the launch and needs no device copy).
+struct BatchDesc {
+    int32_t n;
+    int32_t seq[KV_MAX_BATCH];        // sequence slot -> block-table row
+    int32_t pos[KV_MAX_BATCH];        // append: first position; decode: context length
+    int32_t cnt[KV_MAX_BATCH];        // append: tokens appended
+    int32_t row0[KV_MAX_BATCH];       // append: first input row of the entry
+    int32_t work0[KV_MAX_BATCH + 1];  // prefix sum of work items per entry
+};
+
+// Byte offsets inside a 2-bit (layer, head) block of D dims.
+__host__ __device__ constexpr int64_t q2_block_bytes(int D) { return 32 * (int64_t)D + 1024; }
+__host__ __device__ constexpr int64_t q2_vcodes_off(int D) { return 16 * (int64_t)D; }
+__host__ __device__ constexpr int64_t q2_kmeta_off(int D) { return 32 * (int64_t)D; }
+__host__ __device__ constexpr int64_t q2_vmeta_off(int D) { return 32 * (int64_t)D + 512; }
+// Byte offsets inside an 8-bit (layer, head) block.
+__host__ __device__ constexpr int64_t q8_block_bytes(int D) { return 132 * (int64_t)D + 256; }
+__host__ __device__ constexpr int64_t q8_vcodes_off(int D) { return 64 * (int64_t)D; }
+__host__ __device__ constexpr int64_t q8_kscale_off(int D) { return 128 * (int64_t)D; }
+__host__ __device__ constexpr int64_t q8_vscale_off(int D) { return 132 * (int64_t)D; }
+
+// Launchers (defined in the .hip files).  Each returns the launch status.
+hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
+                            const uint16_t* k, const uint16_t* v, hipStream_t s);
+hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
+                            const uint16_t* k, const uint16_t* v, hipStream_t s);
+hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
+                            int splits, float* ws, float* scores, int64_t sstride, hipStream_t s);
+hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
+                            int splits, float* ws, float* scores, int64_t sstride, hipStream_t s);
+hipError_t launch_merge_decode(const PoolView& pv, const BatchDesc& bd, int splits, const float* ws, float* out,
+                               hipStream_t s);
+hipError_t launch_prefill_q2(const PoolView& pv, int layer, int seq, int q_start, int n_q, const uint16_t* q,
+                             float sm, int splits, float* ws, float* out, hipStream_t s);
+hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,
+                               hipStream_t s);
+
+// Decode workspace: partial outputs [n][Hq][splits][D] then (max, sum) pairs [n][Hq][splits][2].
+inline int64_t decode_ws_floats(int n, int Hq, int D, int splits) {
+    return (int64_t)n * Hq * splits * (D + 2);
+}
+// Prefill workspace: partial outputs [n_q][Hq][splits][D] then (max, sum) [n_q][Hq][splits][2].
+inline int64_t prefill_ws_floats(int n_q, int Hq, int D, int splits) {
+    return (int64_t)n_q * Hq * splits * (D + 2);
+}
+
+// Pages of a context of `ctx` tokens handled by split `p` of `splits`, in
+// whole pairs of pages (the decode kernels step two pages at a time).
+__host__ __device__ inline void split_range(int ctx, int splits, int p, int* pg0, int* pg1) {
+    int n_pages = (ctx + PAGE - 1) / PAGE;
+    int pairs = (n_pages + 1) / 2;
+    int per = (pairs + splits - 1) / splits;
+    int a = p * per * 2, b = a + per * 2;
+    *pg0 = a < n_pages ? a : n_pages;
+    *pg1 = b < n_pages ? b : n_pages;
+}
+
+}  // namespace kvq

@@ -1,0 +1,53 @@
+"""The C-ABI library loads on a machine without a GPU and exports every entry
+point include/kvq.h declares; the pure host functions answer without a device."""
+
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("kv_pool_create", "kv_append_quant", "kv_attn_decode", "kv_attn_prefill", "kv_dequant_page"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    import quantized_kv_attention_append_amd as kvq
+    for name in declared_functions():
+        assert hasattr(kvq.lib, name), name
+    from quantized_kv_attention_append_amd._lib import SIGNATURES
+    assert set(SIGNATURES) == set(declared_functions())
+
+
+def test_token_bytes_from_the_library():
+    import quantized_kv_attention_append_amd as kvq
+    assert kvq.token_bytes((16, 4, 256, 16), kvq.FMT_Q2) == (9216, 589824)
+    assert kvq.token_bytes((32, 8, 128, 32), kvq.FMT_Q8) == (68608, 4390912)
+    assert kvq.pool_bytes_for_tokens((16, 4, 256, 16), kvq.FMT_Q2, 8 * 40960) == 3_019_898_880
+    assert kvq.pool_bytes_for_tokens((1, 4, 256, 16), kvq.FMT_Q2, 65) == 2 * 36864
+
+
+@pytest.mark.parametrize("geom,fmt,status", [
+    ((16, 4, 96, 16), 1, "KV_ERR_UNSUPPORTED"),    # head_dim
+    ((16, 4, 256, 6), 1, "KV_ERR_UNSUPPORTED"),    # Hq not a multiple of Hkv
+    ((16, 4, 256, 64), 1, "KV_ERR_UNSUPPORTED"),   # group 16
+    ((0, 4, 256, 16), 1, "KV_ERR_ARG"),
+    ((16, 4, 256, 16), 3, "KV_ERR_FORMAT"),
+])
+def test_bad_geometry_is_refused(geom, fmt, status):
+    import quantized_kv_attention_append_amd as kvq
+    with pytest.raises(kvq.KvError) as ei:
+        kvq.token_bytes(geom, fmt)
+    assert ei.value.name == status
+    assert status in str(ei.value)
