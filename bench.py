@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Decode attention over a 2-bit paged KV pool, one MI355X.
+
+Workload (27B geometry): 16 attention layers x 4 KV heads x 256 dims, 16
+query heads; 8 lanes, each at 40,960 context tokens (640 pages of 64 tokens
+per lane, pages shuffled across lanes in one pool of 5,120 pages =
+3,019,898,880 B).  K/V are bf16 N(0,1) with every 16th key channel x4 and
+every 64th value token x6, drawn on the device from fixed seeds and
+quantize-appended once (untimed set-up, reported separately).  One step =
+one decode launch per layer for all 8 lanes (16 launches), one bf16 query per
+lane per layer.
+
+Prints one JSON line: KV tokens attended per second (lane x layer x token
+triples), the per-launch roofline of the decode kernel against 8 TB/s HBM, and
+the CPU oracle timed on a bounded sample of the same work.
+
+    python bench.py [--steps K] [--warmup W] [--splits P] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode attention: KV tokens attended/s and achieved HBM GB/s (% of peak), 2-bit"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--splits", type=int, default=0, help="split-K partitions per (lane, KV head); 0 = library choice")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def oracle_baseline(w, budget_s: float):
+    """The oracle's decode (dequantize the lane's codes, fp64 softmax attention)
+    timed on (layer, lane) units of the same workload until the budget is spent."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import attention, codec
+    from synth import kv_rows, queries
+
+    ctx = w.ctx
+    done_tokens, spent, units = 0, 0.0, []
+    for layer, lane in ((0, 0), (1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (6, 6), (7, 7)):
+        k, v = kv_rows(w, layer, lane, ctx, device="cuda")
+        kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
+        del k, v
+        ck = codec.q2_quantize(kf)
+        cv = codec.q2_quantize(vf)
+        q = queries(w, layer, w.lanes, device="cuda")[lane].float().cpu().numpy()
+        t0 = time.perf_counter()
+        K = codec.q2_dequantize(*ck)
+        V = codec.q2_dequantize(*cv)
+        attention.decode(q, K, V, w.sm_scale)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done_tokens += ctx
+        units.append((layer, lane))
+        log(f"oracle unit layer={layer} lane={lane}: {dt:.2f} s")
+        if spent >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": done_tokens / spent,
+        "unit": "KV tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(units)} (layer, lane) units of {ctx} tokens x 4 KV heads x 16 query heads "
+                  f"(dequantize + fp64 softmax attention), {spent:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this library runs on one GPU only (no multi-GPU path is built); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_kv_attention_append_amd as kvq
+    from synth import CONFIGS, kv_rows, page_permutation, queries
+
+    w = CONFIGS[1]
+    L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
+    geom = (L, H, D, Hq)
+    tb, pb = kvq.token_bytes(geom, kvq.FMT_Q2)
+    pages_per_lane = ctx // 64
+    n_pages = B * pages_per_lane
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q2, max_seqs=B, max_seq_tokens=ctx)
+    perm = page_permutation(w, n_pages)
+    seqs = [pool.reserve(ctx, pages=perm[i * pages_per_lane:(i + 1) * pages_per_lane]) for i in range(B)]
+    stream = torch.cuda.current_stream()
+
+    # ---- populate (quantize-append of every token, untimed for the metric) --
+    app_ms = 0.0
+    for layer in range(L):
+        ks, vs = [], []
+        for lane in range(B):
+            k, v = kv_rows(w, layer, lane, ctx, device="cuda")
+            ks.append(k); vs.append(v)
+        k, v = torch.cat(ks), torch.cat(vs)
+        del ks, vs
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pool.append(layer, seqs, [0] * B, [ctx] * B, k, v)
+        e1.record(stream)
+        e1.synchronize()
+        app_ms += e0.elapsed_time(e1)
+        del k, v
+    append_rows = L * B * ctx * H * 2
+    append_bytes = append_rows * (2 * D) + L * B * ctx * tb // L  # bf16 rows read + codes/metadata written
+    log(f"populate: {append_rows} rows in {app_ms:.2f} ms -> {append_bytes / app_ms / 1e6:.0f} GB/s")
+
+    # ---- decode ----------------------------------------------------------
+    qs = [queries(w, layer, B, device="cuda") for layer in range(L)]
+    sp = args.splits if args.splits > 0 else pool.decode_splits([ctx] * B)
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, B, sp), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device="cuda") for _ in range(L)]
+    ctxs = [ctx] * B
+
+    def step(events=None):
+        for layer in range(L):
+            if events is not None:
+                events[layer][0].record(stream)
+            pool.decode(layer, seqs, ctxs, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
+            if events is not None:
+                events[layer][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(args.steps) for l in range(L)]
+    region_ms = ev[0][0][0].elapsed_time(ev[-1][-1][1])
+    ms_per_step = region_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    kv_bytes_per_launch = B * pages_per_lane * H * 64 * (2 * (D // 4 + 8))   # K and V rows read
+    io_bytes_per_launch = B * Hq * D * 2 + B * Hq * D * 4                      # q in, fp32 out
+    bytes_per_launch = kv_bytes_per_launch + io_bytes_per_launch
+    achieved = bytes_per_launch / (avg_launch_ms * 1e-3) / 1e9
+    tokens_per_step = B * L * ctx
+    value = tokens_per_step / (ms_per_step * 1e-3)
+    log(f"splits={sp} avg decode launch {avg_launch_ms * 1e3:.1f} us, step {ms_per_step:.3f} ms, "
+        f"{achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s), wall {wall:.3f} s")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = oracle_baseline(w, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u2/f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "27B-geometry batched decode, 2-bit: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
+                        "8 lanes x 40960 tokens",
+            "layers": L, "kv_heads": H, "head_dim": D, "q_heads": Hq, "lanes": B, "ctx_tokens": ctx,
+            "splits": sp, "pool_bytes": n_pages * pb,
+        },
+        "hbm_gbs": achieved,
+        "hbm_pct_of_peak": 100 * achieved / HBM_PEAK_GBS,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "decode_q2 (one launch per layer, merge fused)",
+            "bytes_per_launch": bytes_per_launch,
+            "avg_launch_us": avg_launch_ms * 1e3,
+        },
+        "append": {"rows": append_rows, "ms": app_ms, "gbs": append_bytes / app_ms / 1e6},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

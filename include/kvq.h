@@ -155,9 +155,9 @@ kv_status kv_append_quant(kv_pool* pool, int32_t layer, int32_t n, const int32_t
 enum { KV_OP_DECODE = 0, KV_OP_PREFILL = 1 };
 
 /* Workspace bytes for an attention call: decode with n_rows sequences, or
- * prefill with n_rows chunk queries, and n_splits splits of the context
- * (0 = the split count the library would choose; for decode that choice
- * also needs the context lengths, so pass the same n_splits to both calls). */
+ * prefill with n_rows chunk queries, and n_splits splits of the context.
+ * n_splits = 0 asks for enough bytes for any split count the library picks
+ * by itself (decode: up to 256; prefill: 1). */
 kv_status kv_workspace_bytes(const kv_pool* pool, int32_t op, int32_t n_rows, int32_t n_splits, int64_t* bytes);
 
 /* Split-count the library picks for a decode batch when n_splits = 0. */
@@ -167,8 +167,10 @@ kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_le
  * query per sequence; sequence i attends to its tokens 0 .. ctx_len[i]-1
  * (ctx_len >= 1, within the reserved bound).  Scores are sm_scale x q.k^ over
  * the dequantized keys; softmax and all sums are kept in fp32; the context is
- * split into n_splits page ranges (flash-decoding) whose partial results
- * (max, sum, unnormalised output) go to d_ws and are merged in fp32.
+ * split into n_splits (1..256, 0 = kv_decode_splits' choice) ranges of
+ * whole page pairs (flash-decoding) whose partial results (max, sum,
+ * unnormalised output) go to d_ws; the last workgroup of each (sequence, KV
+ * head) merges them in fp32, so the call is a single kernel launch.
  * d_out: fp32 [n][Hq][D].  d_scores: NULL, or fp32 [n][Hq][scores_stride]
  * receiving the raw logits (scores_stride >= max ctx_len).  Every workspace
  * byte read is written first within the call.  Errors: KV_ERR_ARG,

@@ -11,23 +11,24 @@
 // materialising K^ and V^:
 //     q . k^_t = mn_t * sum(q) + scale_t * sum_d q_d c_td
 //     sum_t p_t v^_td = sum_t p_t mn_t + sum_t (p_t scale_t) c_td
-// Partial (m, l, o) go to the workspace and the merge kernel combines splits.
-#include "kvq_device.h"
-#include "kvq_internal.h"
+// Partial (m, l, o) go to the workspace; the last workgroup of a (sequence,
+// KV head) to finish merges the splits in fp32 (decode_common.h).
+#include "decode_common.h"
 
 namespace kvq {
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int layer, BatchDesc bd,
                                                              const uint16_t* __restrict__ q, float sm, int splits,
-                                                             float* __restrict__ ws, float* __restrict__ scores,
-                                                             int64_t sstride) {
+                                                             float* __restrict__ ws, float* __restrict__ out,
+                                                             float* __restrict__ scores, int64_t sstride) {
     const int Hkv = pv.Hkv, Hq = pv.Hq, G = Hq / Hkv;
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int ctx = bd.pos[e];
     int pg0, pg1;
     split_range(ctx, splits, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
+    const float LOG2E = 1.4426950408889634f;
 
     __shared__ float q_s[8][D];
     __shared__ float s_s[8][PAGE];
@@ -73,6 +74,7 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
                 float2 meta = *reinterpret_cast<const float2*>(blk + q2_kmeta_off(D) + 8 * t);
                 s = sm * (meta.y * qsum_s[j] + meta.x * acc);
                 if (scores) scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + t] = s;
+                s *= LOG2E;
             }
             s_s[j][t] = s;
         }
@@ -82,11 +84,11 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
             const float s = s_s[j][lane];
             const float m_old = m_s[j];
             const float m_new = fmaxf(m_old, wave_max(s));
-            const float alpha = expf(m_old - m_new);
+            const float alpha = exp2f(m_old - m_new);
             float p = 0.f, wv = 0.f, cv = 0.f;
             if (lane < n_tok) {
                 float2 vm = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * lane);
-                p = expf(s - m_new);
+                p = exp2f(s - m_new);
                 wv = p * vm.x;
                 cv = p * vm.y;
             }
@@ -116,64 +118,27 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
         }
         __syncthreads();
     }
-    const int64_t nrow = (int64_t)bd.n * Hq;
-    float* ws_o = ws;
-    float* ws_ml = ws + nrow * splits * D;
+    DecodeWs w(ws, bd.n, Hq, D, splits);
     if (tid < D)
         for (int j = 0; j < G; ++j) {
             const int64_t r = ((int64_t)e * Hq + g * G + j) * splits + sp;
-            ws_o[r * D + tid] = o[j] + c_s[j];
+            w.o[r * D + tid] = o[j] + c_s[j];
         }
     if (tid < G) {
         const int64_t r = ((int64_t)e * Hq + g * G + tid) * splits + sp;
-        ws_ml[2 * r] = m_s[tid];
-        ws_ml[2 * r + 1] = l_s[tid];
+        w.ml[2 * r] = m_s[tid];
+        w.ml[2 * r + 1] = l_s[tid];
     }
+    merge_if_last(pv, bd, e, g, splits, ws, out);
 }
 
 hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
-                                 int splits, float* ws, float* scores, int64_t sstride, hipStream_t s) {
+                                 int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
     dim3 grid(bd.n * pv.Hkv, splits);
     if (pv.D == 256)
-        hipLaunchKernelGGL(decode_q2_valu_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, scores, sstride);
+        hipLaunchKernelGGL(decode_q2_valu_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
     else
-        hipLaunchKernelGGL(decode_q2_valu_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, scores, sstride);
-    return hipGetLastError();
-}
-
-// ---------------------------------------------------------------- merge ----
-// out = sum_p e^{m_p - M} o_p / sum_p e^{m_p - M} l_p over the splits that hold
-// at least one page (the same partition the decode kernels use), in fp32.
-__global__ __launch_bounds__(256) void merge_decode_kernel(PoolView pv, BatchDesc bd, int splits,
-                                                           const float* __restrict__ ws, float* __restrict__ out) {
-    const int D = pv.D, Hq = pv.Hq;
-    const int row = blockIdx.x;  // e * Hq + h
-    const int e = row / Hq;
-    const int ctx = bd.pos[e];
-    const int64_t nrow = (int64_t)bd.n * Hq;
-    const float* ws_o = ws + (int64_t)row * splits * D;
-    const float* ws_ml = ws + nrow * splits * D + (int64_t)row * splits * 2;
-    int live = 0;
-    for (int p = 0; p < splits; ++p) {
-        int a, b;
-        split_range(ctx, splits, p, &a, &b);
-        if (a < b) live = p + 1;
-    }
-    float M = -INFINITY;
-    for (int p = 0; p < live; ++p) M = fmaxf(M, ws_ml[2 * p]);
-    float den = 0.f;
-    for (int p = 0; p < live; ++p) den += expf(ws_ml[2 * p] - M) * ws_ml[2 * p + 1];
-    const float inv = 1.0f / den;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float acc = 0.f;
-        for (int p = 0; p < live; ++p) acc += expf(ws_ml[2 * p] - M) * ws_o[(int64_t)p * D + d];
-        out[(int64_t)row * D + d] = acc * inv;
-    }
-}
-
-hipError_t launch_merge_decode(const PoolView& pv, const BatchDesc& bd, int splits, const float* ws, float* out,
-                               hipStream_t s) {
-    hipLaunchKernelGGL(merge_decode_kernel, dim3(bd.n * pv.Hq), dim3(256), 0, s, pv, bd, splits, ws, out);
+        hipLaunchKernelGGL(decode_q2_valu_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
     return hipGetLastError();
 }
 
@@ -181,7 +146,7 @@ hipError_t launch_merge_decode(const PoolView& pv, const BatchDesc& bd, int spli
 
 namespace kvq {
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
-                            float* ws, float* scores, int64_t sstride, hipStream_t s) {
-    return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, scores, sstride, s);
+                            float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
+    return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, s);
 }
 }  // namespace kvq

@@ -75,6 +75,7 @@ struct kv_pool {
     int32_t bt_stride = 0;       // max pages per sequence
     int32_t* d_bt = nullptr;     // [max_seqs][bt_stride]
     uint16_t* d_stage = nullptr; // 8-bit exact-K window
+    int32_t* d_sem = nullptr;    // split-arrival counters
     int device = 0;
     // host metadata
     std::vector<int32_t> owner;      // page -> seq slot or -1
@@ -100,6 +101,7 @@ struct kv_pool {
         v.bt = d_bt;
         v.bt_stride = bt_stride;
         v.stage = d_stage;
+        v.sem = d_sem;
         return v;
     }
 };
@@ -179,6 +181,9 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
     }
     e = hipMalloc((void**)&p->d_bt, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(p->d_bt, 0, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMalloc((void**)&p->d_sem, (size_t)KV_MAX_BATCH * geom->n_kv_heads * sizeof(int32_t));
+    if (e == hipSuccess) e = hipMemset(p->d_sem, 0, (size_t)KV_MAX_BATCH * geom->n_kv_heads * sizeof(int32_t));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e == hipSuccess && fmt == KV_FMT_Q8) {
         size_t sb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * PAGE * geom->head_dim * sizeof(uint16_t);
         e = hipMalloc((void**)&p->d_stage, sb);
@@ -205,6 +210,7 @@ kv_status kv_pool_destroy(kv_pool* p) {
     if (p->own_pages && p->d_pages) (void)hipFree(p->d_pages);
     if (p->d_bt) (void)hipFree(p->d_bt);
     if (p->d_stage) (void)hipFree(p->d_stage);
+    if (p->d_sem) (void)hipFree(p->d_sem);
     delete p;
     return KV_OK;
 }
@@ -411,7 +417,7 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
     if (n > KV_MAX_BATCH) return fail(KV_ERR_UNSUPPORTED, "batch of %d exceeds KV_MAX_BATCH (%d)", n, KV_MAX_BATCH);
     if (!seqs || !ctx_len || !d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
     if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
-    if (n_splits < 0 || n_splits > 1024) return fail(KV_ERR_ARG, "n_splits %d out of range", n_splits);
+    if (n_splits < 0 || n_splits > 256) return fail(KV_ERR_ARG, "n_splits %d out of range (0..256)", n_splits);
     BatchDesc bd;
     memset(&bd, 0, sizeof bd);
     bd.n = n;
@@ -431,11 +437,10 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
         return fail(KV_ERR_WORKSPACE, "decode needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
     hipStream_t s = (hipStream_t)stream;
     PoolView pv = p->view();
-    hipError_t e = p->fmt == KV_FMT_Q2 ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_scores, scores_stride, s)
-                                       : launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_scores, scores_stride, s);
+    hipError_t e = p->fmt == KV_FMT_Q2
+                       ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
+                       : launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-    e = launch_merge_decode(pv, bd, sp, (const float*)d_ws, d_out, s);
-    if (e != hipSuccess) return hip_fail(e, "merge launch");
     return KV_OK;
 }
 

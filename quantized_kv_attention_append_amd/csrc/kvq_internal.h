@@ -20,6 +20,7 @@ struct PoolView {
     const int32_t* bt;     // device block tables [max_seqs][bt_stride]
     int32_t bt_stride;
     uint16_t* stage;       // 8-bit pools: exact K window, bf16 [max_seqs][L][Hkv][64][D]
+    int32_t* sem;          // split-arrival counters [KV_MAX_BATCH][Hkv], zero between calls
 };
 
 // Per-call batch description, passed by value as a kernel argument (so it is
@@ -49,12 +50,12 @@ hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, 
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
+// Decode launchers write the fp32 output themselves: the last workgroup of a
+// (sequence, KV head) to finish merges that pair's splits.
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
-                            int splits, float* ws, float* scores, int64_t sstride, hipStream_t s);
+                            int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
-                            int splits, float* ws, float* scores, int64_t sstride, hipStream_t s);
-hipError_t launch_merge_decode(const PoolView& pv, const BatchDesc& bd, int splits, const float* ws, float* out,
-                               hipStream_t s);
+                            int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_prefill_q2(const PoolView& pv, int layer, int seq, int q_start, int n_q, const uint16_t* q,
                              float sm, int splits, float* ws, float* out, hipStream_t s);
 hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,

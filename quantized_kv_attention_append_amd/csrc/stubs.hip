@@ -4,8 +4,8 @@ namespace kvq {
 hipError_t launch_append_q8(const PoolView&, int, const BatchDesc&, int, const uint16_t*, const uint16_t*, hipStream_t) {
     return hipErrorNotSupported;
 }
-hipError_t launch_decode_q8(const PoolView&, int, const BatchDesc&, const uint16_t*, float, int, float*, float*, int64_t,
-                            hipStream_t) {
+hipError_t launch_decode_q8(const PoolView&, int, const BatchDesc&, const uint16_t*, float, int, float*, float*, float*,
+                            int64_t, hipStream_t) {
     return hipErrorNotSupported;
 }
 hipError_t launch_prefill_q2(const PoolView&, int, int, int, int, const uint16_t*, float, int, float*, float*,
