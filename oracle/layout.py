@@ -11,9 +11,12 @@ pool, section "See it, control it").  Inside a page, the data of one
     [16*D,     32*D)   V codes, dim-major:   row d (16 bytes = 64 tokens) at 16*d
     [32*D,     32*D+512)  K metadata: 64 x [fp32 scale, fp32 min]
     [32*D+512, 32*D+1024) V metadata: 64 x [fp32 scale, fp32 min]
-  Codes are packed least-significant-bits first: element j of a packed row
-  sits in byte j // 4 at bit 2 * (j % 4).  For a K row the elements are dims;
-  for a V row they are the page's 64 token slots.
+  K rows pack dims least-significant-bits first: dim j sits in byte j // 4 at
+  bit 2 * (j % 4).  A V row packs the page's 64 token slots as four 32-bit
+  little-endian words, word w holding slots 16w..16w+15: slot 16w + q (q < 8)
+  at bits 4q..4q+1 and slot 16w + 8 + q at bits 4q+2..4q+3 (each 4-bit
+  nibble holds one slot of each half-word), so masking a word with 0x33333333
+  yields eight slots in order, one per nibble.
 
 8-bit block (D dims):
     [0,      64*D)   K codes int8, token-major: row t at t*D
@@ -62,6 +65,35 @@ def pack2(codes) -> np.ndarray:
     return b.astype(np.uint8)
 
 
+def _vslot_field():
+    """2-bit field index (0..15) inside its 32-bit word of each of the word's 16 slots."""
+    return np.array([2 * q for q in range(8)] + [2 * q + 1 for q in range(8)])
+
+
+def pack2_vrow(codes) -> np.ndarray:
+    """codes uint8 [..., 64] (token slots) -> bytes [..., 16] in the V-row word layout."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] == 64 and c.max(initial=0) <= 3
+    field = _vslot_field()
+    words = np.zeros(c.shape[:-1] + (4,), dtype=np.uint32)
+    for w in range(4):
+        for q in range(16):
+            words[..., w] |= c[..., 16 * w + q].astype(np.uint32) << np.uint32(2 * field[q])
+    return words.view(np.uint8).reshape(c.shape[:-1] + (16,)) if words.flags.c_contiguous else \
+        np.ascontiguousarray(words).view(np.uint8).reshape(c.shape[:-1] + (16,))
+
+
+def unpack2_vrow(packed) -> np.ndarray:
+    p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    words = p.view(np.uint32).reshape(p.shape[:-1] + (4,))
+    field = _vslot_field()
+    out = np.empty(p.shape[:-1] + (64,), dtype=np.uint8)
+    for w in range(4):
+        for q in range(16):
+            out[..., 16 * w + q] = (words[..., w] >> np.uint32(2 * field[q])) & 3
+    return out
+
+
 def unpack2(packed, n: int) -> np.ndarray:
     p = np.asarray(packed, dtype=np.uint8)
     assert p.shape[-1] * 4 == n
@@ -88,7 +120,9 @@ class Q2Block:
 
     def write_v(self, slot: int, codes_row, scale, mn):
         """Set the 2 bits of token ``slot`` in every dim row, leaving other slots untouched."""
-        byte, shift = slot // 4, 2 * (slot % 4)
+        field = _vslot_field()[slot % 16]
+        bit = 32 * (slot // 16) + 2 * field
+        byte, shift = bit // 8, bit % 8
         keep = np.uint8(0xFF ^ (3 << shift))
         col = self.v_codes[:, byte]
         self.v_codes[:, byte] = (col & keep) | (np.asarray(codes_row, np.uint8) << shift)
@@ -99,7 +133,7 @@ class Q2Block:
         return codes, self.k_meta[:n, 0].copy(), self.k_meta[:n, 1].copy()
 
     def read_v(self, n: int):
-        codes = unpack2(self.v_codes, PAGE)[:, :n].T.copy()   # [n][D]
+        codes = unpack2_vrow(self.v_codes)[:, :n].T.copy()   # [n][D]
         return codes, self.v_meta[:n, 0].copy(), self.v_meta[:n, 1].copy()
 
 

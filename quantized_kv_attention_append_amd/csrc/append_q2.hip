@@ -12,11 +12,14 @@
 // order).  A zero min or max is canonicalised to +0.
 //
 // Layout of one (layer, KV head) block of a page: K codes token-major (row t =
-// D/4 bytes), V codes dim-major (row d = 16 bytes holding the 64 token slots),
-// then 64 K metadata rows and 64 V metadata rows.  Packing is
-// least-significant-bits first: element j of a row is at bit 2*(j%4) of byte
-// j/4.  K rows are read by token for the q.k contraction over dims; V rows by
-// dim for the p.v contraction over tokens.
+// D/4 bytes, dim j at bit 2*(j%4) of byte j/4), V codes dim-major (row d = 16
+// bytes = four 32-bit words holding the 64 token slots; in word w, slot
+// 16w+q sits at bit 4q for q < 8 and slot 16w+8+q at bit 4q+2), then 64 K
+// metadata rows and 64 V metadata rows.  K rows are read by token for the
+// q.k contraction over dims; V rows by dim for the p.v contraction over
+// tokens, and masking a V word with 0x33333333 yields eight consecutive slots,
+// one per 4-bit nibble, which is the matrix-core operand format the decode
+// kernel feeds from it.
 //
 // Work split: one workgroup of four waves per (sequence, page touched, KV
 // head); wave w owns token slots [16w, 16w+16) of the page, which is exactly
@@ -95,7 +98,8 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
             uint32_t other = __shfl_down(bits, 1);
             if ((lane & 1) == 0) krow[lane >> 1] = (uint8_t)(bits | (other << 4));
         }
-        const int sh = 2 * (s & 15);
+        const int q = s & 15;
+        const int sh = q < 8 ? 4 * q : 4 * (q - 8) + 2;
 #pragma unroll
         for (int k = 0; k < DPL; ++k) vw[k] |= cv[k] << sh;
         vmask |= 3u << sh;
@@ -139,7 +143,9 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(PoolView pv, int fmt,
                 c = (blk[t * (D / 4) + d / 4] >> (2 * (d % 4))) & 3u;
                 meta = *reinterpret_cast<const float2*>(blk + q2_kmeta_off(D) + 8 * t);
             } else {
-                c = (blk[q2_vcodes_off(D) + 16 * d + t / 4] >> (2 * (t % 4))) & 3u;
+                const uint32_t word = *reinterpret_cast<const uint32_t*>(blk + q2_vcodes_off(D) + 16 * d + 4 * (t / 16));
+                const int q = t & 15;
+                c = (word >> (q < 8 ? 4 * q : 4 * (q - 8) + 2)) & 3u;
                 meta = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * t);
             }
             r = __fmaf_rn((float)c, meta.x, meta.y);

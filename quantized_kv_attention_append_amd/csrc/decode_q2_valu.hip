@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
             for (int w = 0; w < 4; ++w) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const float c = (float)((words[w] >> (2 * i)) & 3u);
+                    const float c = (float)((words[w] >> (i < 8 ? 4 * i : 4 * (i - 8) + 2)) & 3u);
                     for (int j = 0; j < G; ++j) o[j] += w_s[j][16 * w + i] * c;
                 }
             }
@@ -142,11 +142,4 @@ hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc&
     return hipGetLastError();
 }
 
-}  // namespace kvq
-
-namespace kvq {
-hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
-                            float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
-    return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, s);
-}
 }  // namespace kvq

@@ -40,8 +40,8 @@ def test_v_plane_write_touches_only_its_slot():
     before = buf.copy()
     c = rng.integers(0, 4, 256).astype(np.uint8)
     blk.write_v(37, c, np.float32(0.5), np.float32(-1.0))
-    codes = layout.unpack2(blk.v_codes, 64)            # [D][64]
-    old = layout.unpack2(before[16 * 256:32 * 256].reshape(256, 16), 64)
+    codes = layout.unpack2_vrow(blk.v_codes)            # [D][64]
+    old = layout.unpack2_vrow(before[16 * 256:32 * 256].reshape(256, 16))
     assert np.array_equal(codes[:, 37], c)
     mask = np.ones(64, bool)
     mask[37] = False
@@ -58,3 +58,20 @@ def test_k_row_layout_positions():
     row_off = 2 * 128 // 4
     assert buf[row_off + 1] == 3 << 2 and buf[row_off:row_off + 32].sum() == 12
     assert np.frombuffer(buf[32 * 128 + 16:32 * 128 + 24].tobytes(), np.float32).tolist() == [1.0, 0.0]
+
+
+def test_v_row_word_layout_matches_loop():
+    """slot 16w+q (q<8) at bits 4q of word w; slot 16w+8+q at bits 4q+2."""
+    rng = np.random.default_rng(23)
+    c = rng.integers(0, 4, (7, 64)).astype(np.uint8)
+    p = layout.pack2_vrow(c)
+    for r in range(7):
+        for w in range(4):
+            word = 0
+            for q in range(8):
+                word |= int(c[r, 16 * w + q]) << (4 * q)
+                word |= int(c[r, 16 * w + 8 + q]) << (4 * q + 2)
+            assert int.from_bytes(bytes(p[r, 4 * w:4 * w + 4]), "little") == word
+            nibbles_lo = [(word >> (4 * q)) & 0xF & 3 for q in range(8)]
+            assert nibbles_lo == list(c[r, 16 * w:16 * w + 8])
+    assert np.array_equal(layout.unpack2_vrow(p), c)

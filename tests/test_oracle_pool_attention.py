@@ -5,7 +5,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention, codec, pool
+from oracle import attention, codec, layout, pool
 from synth import CONFIGS, kv_rows, page_permutation, queries
 
 F32 = np.float32
@@ -48,8 +48,8 @@ def test_append_leaves_other_slots_and_pages_alone():
         blk = p.block(1, 0, h)
         assert np.all(blk.k_codes[36:] == 0xA5)             # slots 36..63 of the 2nd page
         assert np.all(blk.k_meta[36:].view(np.uint8) == 0xA5)
-        assert np.all(blk.v_codes[:, 9:] == 0xA5)             # V bytes of slots 36..63
-        assert np.all((blk.v_codes[:, 9] & 0xF0) == (0xA5 & 0xF0))
+        fill_slots = layout.unpack2_vrow(np.full((1, 16), 0xA5, np.uint8))[0]
+        assert np.all(layout.unpack2_vrow(blk.v_codes)[:, 36:] == fill_slots[36:])   # V slots 36..63
 
 
 def test_q8_partial_page_then_full_page_equals_full_quantization():
