@@ -74,6 +74,7 @@ __device__ inline void merge_if_last(const PoolView& pv, const BatchDesc& bd, in
         const int64_t row = (int64_t)e * Hq + g * G + j;
         const float* o = w.o + row * splits * D + d;
         float acc = 0.f;
+#pragma unroll 8
         for (int p = 0; p < live; ++p) acc += wgt_s[j][p] * __builtin_nontemporal_load(o + (int64_t)p * D);
         out[row * D + d] = acc * inv_s[j];
     }

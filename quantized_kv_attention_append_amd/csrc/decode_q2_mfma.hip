@@ -27,8 +27,10 @@
 // accumulation "Half the Cache, Twice the Context" asks for in section "The
 // cliff is in the accumulator").
 //
-// One wavefront per (sequence, KV head, split) walks its pages two at a time
-// (128 tokens = one k-block of the instruction).  Token t of the pair sits at
+// One workgroup of four wavefronts per (sequence, KV head, split); wave w
+// takes every fourth pair of pages of the split (128 tokens = one k-block of
+// the instruction), loading the next pair while it computes the current one,
+// and the four waves combine their partial results in LDS.  Token t of the pair sits at
 // page t/64, slot t%64.  Operand lane layouts of the instruction (fp4: lane
 // group g holds k = 32g..32g+31; fp8: k = 16g..16g+15 and 64+16g..64+16g+15;
 // result: lane l holds column l%16, rows 4(l/16)..+3) let the q.k product
@@ -111,16 +113,175 @@ __device__ __forceinline__ int fp8_k(int grp, int s) { return s < 16 ? 16 * grp 
 
 }  // namespace
 
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+// A head's reference max moves only when a tile's max exceeds it by more than
+// 2^8 in weight, so the running sums are rescaled rarely (weights stay < 2^8).
+constexpr float RESCALE_LOG2 = 8.0f;
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
-                                                            const uint16_t* __restrict__ q, float sm, int splits,
-                                                            float* __restrict__ ws, float* __restrict__ out,
-                                                            float* __restrict__ scores, int64_t sstride) {
+struct Tile {
+    uint32_t kc[8][D / 64];  // K code words of this lane's row for the eight q.k token groups
+    uint2 vc[D / 16];        // V code words: 32 token slots of dim 16b + l%16
+    uint4 meta[2];           // this lane's two 16-byte chunks of the pair's metadata
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, const uint8_t* base1, int l) {
+    constexpr int NW = D / 64;
+    const int j = l & 15, grp = l >> 4;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int slot = 16 * (j >> 2) + 4 * (m & 3) + (j & 3);
+        const uint8_t* src = (m < 4 ? base0 : base1) + slot * (D / 4) + 4 * NW * grp;
+        if constexpr (NW == 4) {
+            const uint4 w = *reinterpret_cast<const uint4*>(src);
+            t.kc[m][0] = w.x; t.kc[m][1] = w.y; t.kc[m][2] = w.z; t.kc[m][3] = w.w;
+        } else {
+            const uint2 w = *reinterpret_cast<const uint2*>(src);
+            t.kc[m][0] = w.x; t.kc[m][1] = w.y;
+        }
+    }
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b)
+        t.vc[b] = *reinterpret_cast<const uint2*>((grp < 2 ? base0 : base1) + q2_vcodes_off(D) + 16 * (16 * b + j) +
+                                                  8 * (grp & 1));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ch = l + 64 * h, plane = ch >> 5;
+        t.meta[h] = *reinterpret_cast<const uint4*>(((plane & 1) ? base1 : base0) +
+                                                    (plane < 2 ? q2_kmeta_off(D) : q2_vmeta_off(D)) + (ch & 31) * 16);
+    }
+}
+
+template <int D>
+struct WaveState {
+    v4f acc[D / 16];  // p.v sums: block b, register r = head r, lane group = weight digit
+    float m_ref;      // reference max of this lane's head, in units of 1/cB
+    float cbm;        // cB * m_ref (log2 units)
+    float l_run;      // this lane's share of sum p
+    float c_run;      // this lane's share of sum p * min_v
+};
+
+struct QConst {
+    float qdig_w;  // 32^(3 - digit) of this lane's q.k column
+    float cAB;     // sum(q) / (2 * 2^-E): min_k's factor in units of the digit sum
+    float cB;      // log2(e) * sm * 2 * 2^-E: digit-sum units -> log2 logits
+};
+
+template <int D, bool FULL>
+__device__ __forceinline__ void compute_tile(const Tile<D>& t, float2 (*meta)[PAGE], int l, const v8i* qop,
+                                             const QConst& qc, WaveState<D>& st, int tok0, int ctx,
+                                             float* __restrict__ srow) {
+    constexpr int NC = D / 128, NB = D / 16;
+    const int j = l & 15, grp = l >> 4, piece = j >> 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int ch = l + 64 * h;
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&meta[ch >> 5][0]) + (ch & 31) * 16) = t.meta[h];
+    }
+    // ---- q.k: scores in units of 1/cB ----
+    float s2[8][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        v4f cq = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) cq = mma_fp4_fp8(fp4_operand(t.kc[m][2 * c], t.kc[m][2 * c + 1]), qop[c], cq);
+        const int pm = m >> 2, slot0 = 16 * grp + 4 * (m & 3);
+        const float4 km0 = *reinterpret_cast<const float4*>(&meta[pm][slot0]);
+        const float4 km1 = *reinterpret_cast<const float4*>(&meta[pm][slot0 + 2]);
+        const float ks[4] = {km0.x, km0.z, km1.x, km1.z};
+        const float kn[4] = {km0.y, km0.w, km1.y, km1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float s = fmaf(ks[r], row_sum4(cq[r] * qc.qdig_w), kn[r] * qc.cAB);
+            if (!FULL && tok0 + pm * PAGE + slot0 + r >= ctx) s = -INFINITY;
+            s2[m][r] = s;
+            mt = fmaxf(mt, s);
+        }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool need = (mt - st.m_ref) * qc.cB > RESCALE_LOG2;
+    if (__ballot(need)) {
+        const float m_new = need ? mt : st.m_ref;
+        const float cbm_new = qc.cB * m_new;
+        const float alpha = __builtin_amdgcn_exp2f(st.cbm - cbm_new);
+        st.l_run *= alpha;
+        st.c_run *= alpha;
+        float al[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, (l & ~3) | r);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st.acc[b][r] *= al[r];
+        st.m_ref = m_new;
+        st.cbm = cbm_new;
+    }
+    // ---- weights w = p * scale_v ----
+    float wv[8][4];
+    float wmax = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int pm = m >> 2, slot0 = 16 * grp + 4 * (m & 3);
+        const float4 vm0 = *reinterpret_cast<const float4*>(&meta[2 + pm][slot0]);
+        const float4 vm1 = *reinterpret_cast<const float4*>(&meta[2 + pm][slot0 + 2]);
+        const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};
+        const float vn[4] = {vm0.y, vm0.w, vm1.y, vm1.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s2[m][r], qc.cB, -st.cbm));
+            float w;
+            if (FULL) {
+                w = p * vs[r];
+                st.c_run = fmaf(p, vn[r], st.c_run);
+            } else {
+                const bool valid = tok0 + pm * PAGE + slot0 + r < ctx;
+                w = valid ? p * vs[r] : 0.f;
+                st.c_run += valid ? p * vn[r] : 0.f;
+            }
+            st.l_run += p;
+            wv[m][r] = w;
+            wmax = fmaxf(wmax, w);
+        }
+    }
+    if (srow != nullptr && piece == 0) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = tok0 + (m >> 2) * PAGE + 16 * grp + 4 * (m & 3) + r;
+                if (FULL || tok < ctx) srow[tok] = s2[m][r] * (qc.cB * LN2);
+            }
+    }
+    // ---- weight digits, per-head tile scale (lane l's scale byte serves row l%16) ----
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
+    wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
+    const int ew = wmax > 0.f ? (int)((__float_as_uint(wmax) >> 23) & 0xFF) - 127 : 0;
+    const int FW = 18 - ew;  // w * 2^FW < 2^19
+    const float wscale = pow2f(FW);
+    v8i wop;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        wop[m] = (int)pack4_fp8(digit_of(wv[m][0], wscale, piece), digit_of(wv[m][1], wscale, piece),
+                                digit_of(wv[m][2], wscale, piece), digit_of(wv[m][3], wscale, piece));
+    // ---- p.v ----
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+        st.acc[b] = mma_fp8_fp4(wop, fp4_operand(t.vc[b].x, t.vc[b].y), st.acc[b], 127 - FW);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                             const uint16_t* __restrict__ q, float sm, int splits,
+                                                             float* __restrict__ ws, float* __restrict__ out,
+                                                             float* __restrict__ scores, int64_t sstride) {
     constexpr int G = 4;
     constexpr int NC = D / 128;  // k-chunks of the q.k product
     constexpr int NB = D / 16;   // 16-dim blocks of the p.v product
-    constexpr int ROWB = D / 4;  // bytes of a K code row
-    const float LOG2E = 1.4426950408889634f;
     const int Hkv = pv.Hkv, Hq = pv.Hq;
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int ctx = bd.pos[e];
@@ -128,12 +289,13 @@ __global__ __launch_bounds__(64) void decode_q2_mfma_kernel(PoolView pv, int lay
     split_range(ctx, splits, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
 
-    const int l = threadIdx.x;
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = l & 15, grp = l >> 4;
-    const int hh = j & 3;     // head of this lane's q.k column and p.v row
-    const int piece = j >> 2; // weight piece of this lane's p.v row
+    const int hh = j & 3;  // head of this lane's q.k column and p.v row
 
-    __shared__ __align__(16) float2 meta_s[4][PAGE];  // (scale, min): K page 0, K page 1, V page 0, V page 1
+    __shared__ __align__(16) float2 meta_s[4][4][PAGE];  // per wave: K page 0, K page 1, V page 0, V page 1
+    __shared__ float o_s[4][G][D];
+    __shared__ float ml_s[4][G][2];
 
     // ---- query operand: 19-bit fixed point per head, digit (j >> 2) of head hh ----
     const uint16_t* qrow = q + ((int64_t)e * Hq + g * G + hh) * D;
@@ -158,9 +320,10 @@ __global__ __launch_bounds__(64) void decode_q2_mfma_kernel(PoolView pv, int lay
     const int EQ = 18 - ea;  // |q * 2^EQ| < 2^19
     const float qscale = pow2f(EQ);
     const int qdig = j >> 2;
-    const float qdig_w = pow2f(5 * (3 - qdig));
-    const float cA = LOG2E * sm * qsum;
-    const float cB = LOG2E * sm * pow2f(1 - EQ);  // sum_d q_d c_d = 2 * 2^-EQ * (sum of the digit products)
+    QConst qc;
+    qc.qdig_w = pow2f(5 * (3 - qdig));
+    qc.cB = LOG2E * sm * pow2f(1 - EQ);  // sum_d q_d c_d = 2 * 2^-EQ * (digit sum)
+    qc.cAB = qsum * pow2f(EQ - 1);
     v8i qop[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -169,135 +332,40 @@ __global__ __launch_bounds__(64) void decode_q2_mfma_kernel(PoolView pv, int lay
             qop[c][v] = (int)pack4_fp8(digit_of(qv[c][4 * v], qscale, qdig), digit_of(qv[c][4 * v + 1], qscale, qdig),
                                        digit_of(qv[c][4 * v + 2], qscale, qdig), digit_of(qv[c][4 * v + 3], qscale, qdig));
 
-    // this lane's p.v row is digit `piece` of its head's weights
-    v4f acc[NB];
+    WaveState<D> st;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f, c_run = 0.f;
+    for (int b = 0; b < NB; ++b) st.acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+    st.m_ref = -INFINITY;
+    st.cbm = -INFINITY;
+    st.l_run = 0.f;
+    st.c_run = 0.f;
 
     const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
     const int n_pages = (ctx + PAGE - 1) / PAGE;
-    const bool want_scores = scores != nullptr;
+    float* srow = scores ? scores + ((int64_t)e * Hq + g * G + hh) * sstride : nullptr;
+    float2(*meta)[PAGE] = meta_s[wave];
 
-    for (int pg = pg0; pg < pg1; pg += 2) {
-        const int phys0 = bt[pg];
-        const int phys1 = (pg + 1 < n_pages) ? bt[pg + 1] : phys0;
-        const uint8_t* base0 = pv.pages + (int64_t)phys0 * pv.page_bytes + lhoff;
-        const uint8_t* base1 = pv.pages + (int64_t)phys1 * pv.page_bytes + lhoff;
-
-        // metadata of both pages -> LDS (lane l moves 16-byte chunks l and l+64)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ch = l + 64 * h, plane = ch >> 5, off = (ch & 31) * 16;
-            const uint8_t* src = ((plane & 1) ? base1 : base0) + (plane < 2 ? q2_kmeta_off(D) : q2_vmeta_off(D)) + off;
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&meta_s[plane][0]) + off) =
-                *reinterpret_cast<const uint4*>(src);
-        }
-        // K code rows for the eight q.k token groups
-        uint32_t kc[8][NC * 2];
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int slot = 16 * (j >> 2) + 4 * (m & 3) + (j & 3);
-            const uint8_t* src = (m < 4 ? base0 : base1) + slot * ROWB + (NC * 8) * grp;
-            if constexpr (NC == 2) {
-                const uint4 w = *reinterpret_cast<const uint4*>(src);
-                kc[m][0] = w.x; kc[m][1] = w.y; kc[m][2] = w.z; kc[m][3] = w.w;
-            } else {
-                const uint2 w = *reinterpret_cast<const uint2*>(src);
-                kc[m][0] = w.x; kc[m][1] = w.y;
-            }
-        }
-        // V code words: dim 16b + j, 32 token slots of page grp/2
-        uint2 vc[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-            vc[b] = *reinterpret_cast<const uint2*>((grp < 2 ? base0 : base1) + q2_vcodes_off(D) + 16 * (16 * b + j) +
-                                                    8 * (grp & 1));
-        __syncthreads();
-
-        // ---- q.k on the matrix cores ----
-        const bool full = (pg + 2) * PAGE <= ctx;
-        float s2[8][4];
-        float mt = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            v4f cq = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) cq = mma_fp4_fp8(fp4_operand(kc[m][2 * c], kc[m][2 * c + 1]), qop[c], cq);
-            const int pm = m >> 2, slot0 = 16 * grp + 4 * (m & 3);
-            const float4 km0 = *reinterpret_cast<const float4*>(&meta_s[pm][slot0]);
-            const float4 km1 = *reinterpret_cast<const float4*>(&meta_s[pm][slot0 + 2]);
-            const float ks[4] = {km0.x, km0.z, km1.x, km1.z};
-            const float kn[4] = {km0.y, km0.w, km1.y, km1.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float s = fmaf(ks[r] * cB, row_sum4(cq[r] * qdig_w), kn[r] * cA);
-                if (!full && (pg + pm) * PAGE + slot0 + r >= ctx) s = -INFINITY;
-                s2[m][r] = s;
-                mt = fmaxf(mt, s);
-            }
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        c_run *= alpha;
-
-        // ---- weights ----
-        float wv[8][4];
-        float wmax = 0.f;
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int pm = m >> 2, slot0 = 16 * grp + 4 * (m & 3);
-            const float4 vm0 = *reinterpret_cast<const float4*>(&meta_s[2 + pm][slot0]);
-            const float4 vm1 = *reinterpret_cast<const float4*>(&meta_s[2 + pm][slot0 + 2]);
-            const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};
-            const float vn[4] = {vm0.y, vm0.w, vm1.y, vm1.w};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool valid = full || (pg + pm) * PAGE + slot0 + r < ctx;
-                const float p = exp2f(s2[m][r] - m_new);
-                const float w = valid ? p * vs[r] : 0.f;
-                l_run += p;
-                c_run += valid ? p * vn[r] : 0.f;
-                wv[m][r] = w;
-                wmax = fmaxf(wmax, w);
-                if (want_scores && piece == 0 && valid)
-                    scores[((int64_t)e * Hq + g * G + hh) * sstride + (pg + pm) * PAGE + slot0 + r] = s2[m][r] / LOG2E;
-            }
-        }
-        // per-head tile scale: the instruction applies lane l's scale byte to row l%16
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
-        wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
-        const int ew = wmax > 0.f ? (int)((__float_as_uint(wmax) >> 23) & 0xFF) - 127 : 0;
-        const int FW = 18 - ew;  // w * 2^FW < 2^19
-        const float wscale = pow2f(FW);
-        v8i wop;
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-            wop[m] = (int)pack4_fp8(digit_of(wv[m][0], wscale, piece), digit_of(wv[m][1], wscale, piece),
-                                    digit_of(wv[m][2], wscale, piece), digit_of(wv[m][3], wscale, piece));
-
-        // rescale the running p.v sums (register r of every block is head r)
-        if (__ballot(alpha != 1.0f)) {
-            float al[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, (l & ~3) | r);
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[b][r] *= al[r];
-        }
-        // ---- p.v on the matrix cores ----
-#pragma unroll
-        for (int b = 0; b < NB; ++b) acc[b] = mma_fp8_fp4(wop, fp4_operand(vc[b].x, vc[b].y), acc[b], 127 - FW);
-        __syncthreads();
+    // ---- this wave's page pairs: pr0 + wave, pr0 + wave + 4, ... ----
+    const int pr1 = (pg1 + 1) / 2;
+    int pr = pg0 / 2 + wave;
+    auto base_of = [&](int page) {
+        return pv.pages + (int64_t)bt[page < n_pages ? page : 2 * (page / 2)] * pv.page_bytes + lhoff;
+    };
+    Tile<D> cur, nxt;
+    if (pr < pr1) load_tile<D>(cur, base_of(2 * pr), base_of(2 * pr + 1), l);
+    for (; pr < pr1; pr += 4) {
+        const bool has_next = pr + 4 < pr1;
+        if (has_next) load_tile<D>(nxt, base_of(2 * pr + 8), base_of(2 * pr + 9), l);
+        if ((2 * pr + 2) * PAGE <= ctx)
+            compute_tile<D, true>(cur, meta, l, qop, qc, st, 2 * pr * PAGE, ctx, srow);
+        else
+            compute_tile<D, false>(cur, meta, l, qop, qc, st, 2 * pr * PAGE, ctx, srow);
+        if (has_next) cur = nxt;
     }
 
-    // ---- partials: sum the four weight pieces (lane groups) and the lanes' sums ----
+    // ---- this wave's partial: sum weight digits (lane groups) and lanes' sums ----
+    float l_run = st.l_run, c_run = st.c_run;
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     c_run += __shfl_xor(c_run, 16);
@@ -305,26 +373,51 @@ __global__ __launch_bounds__(64) void decode_q2_mfma_kernel(PoolView pv, int lay
     float cr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) cr[r] = __shfl(c_run, (l & ~3) | r);
-    DecodeWs w(ws, bd.n, Hq, D, splits);
-    const int64_t row = ((int64_t)e * Hq + g * G + grp) * splits + sp;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         float t[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             // digit row weight 32^(3 - grp), and 2 for the code/2 fp4 values
-            float v = acc[b][r] * pow2f(16 - 5 * grp);
+            float v = st.acc[b][r] * pow2f(16 - 5 * grp);
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
             t[r] = v + cr[r];
         }
-        const float mine = grp == 0 ? t[0] : grp == 1 ? t[1] : grp == 2 ? t[2] : t[3];
-        w.o[row * D + 16 * b + j] = mine;
+        o_s[wave][grp][16 * b + j] = grp == 0 ? t[0] : grp == 1 ? t[1] : grp == 2 ? t[2] : t[3];
     }
     if (l < 4) {
-        const int64_t r2 = ((int64_t)e * Hq + g * G + l) * splits + sp;
-        w.ml[2 * r2] = m_run;
-        w.ml[2 * r2 + 1] = l_run;
+        ml_s[wave][l][0] = st.cbm;  // log2 units
+        ml_s[wave][l][1] = l_run;
+    }
+    __syncthreads();
+
+    // ---- combine the four waves, write this split's partial ----
+    DecodeWs w(ws, bd.n, Hq, D, splits);
+    {
+        const int h = threadIdx.x >> 6;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_s[v][h][0]);
+        float f[4], lsum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            f[v] = __builtin_amdgcn_exp2f(ml_s[v][h][0] - M);
+            lsum += f[v] * ml_s[v][h][1];
+        }
+        const int64_t row = ((int64_t)e * Hq + g * G + h) * splits + sp;
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) {
+            const int d = l + 64 * k;
+            float o = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o += f[v] * o_s[v][h][d];
+            w.o[row * D + d] = o;
+        }
+        if (l == 0) {
+            w.ml[2 * row] = M;
+            w.ml[2 * row + 1] = lsum;
+        }
     }
     merge_if_last(pv, bd, e, g, splits, ws, out);
 }
@@ -337,10 +430,10 @@ hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, 
     if (pv.Hq != 4 * pv.Hkv) return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, s);
     dim3 grid(bd.n * pv.Hkv, splits);
     if (pv.D == 256)
-        hipLaunchKernelGGL(decode_q2_mfma_kernel<256>, grid, dim3(64), 0, s, pv, layer, bd, q, sm, splits, ws, out,
+        hipLaunchKernelGGL(decode_q2_mfma_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out,
                            scores, sstride);
     else
-        hipLaunchKernelGGL(decode_q2_mfma_kernel<128>, grid, dim3(64), 0, s, pv, layer, bd, q, sm, splits, ws, out,
+        hipLaunchKernelGGL(decode_q2_mfma_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out,
                            scores, sstride);
     return hipGetLastError();
 }

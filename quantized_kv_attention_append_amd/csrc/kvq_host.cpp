@@ -331,17 +331,16 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
     return KV_OK;
 }
 
-// Default split count for a decode batch: enough workgroups to cover the
-// chip several times (256 compute units), with at least four pages per split.
+// Default split count for a decode batch: about one workgroup per compute
+// unit (256 on MI355X) over all (sequence, KV head) pairs, with at least
+// eight page pairs per split (two per wavefront of a workgroup).
 int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     int64_t max_pages = 1;
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
-    int64_t base = (int64_t)n * p->geom.n_kv_heads;
-    int64_t want = (2048 + base - 1) / base;
-    int64_t cap = std::max<int64_t>(1, max_pages / 4);
-    int64_t sp = std::min(want, cap);
-    sp = std::max<int64_t>(1, std::min<int64_t>(sp, 256));
-    return (int)sp;
+    const int64_t base = (int64_t)n * p->geom.n_kv_heads;
+    const int64_t want = (256 + base - 1) / base;
+    const int64_t cap = std::max<int64_t>(1, ((max_pages + 1) / 2) / 8);
+    return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
 }
 
 }  // namespace
