@@ -169,8 +169,8 @@ kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_le
  * the dequantized keys; softmax and all sums are kept in fp32; the context is
  * split into n_splits (1..256, 0 = kv_decode_splits' choice) ranges of
  * whole page pairs (flash-decoding) whose partial results (max, sum,
- * unnormalised output) go to d_ws; the last workgroup of each (sequence, KV
- * head) merges them in fp32, so the call is a single kernel launch.
+ * unnormalised output) go to d_ws; a second kernel on the same stream merges
+ * them in fp32 (two launches per call).
  * d_out: fp32 [n][Hq][D].  d_scores: NULL, or fp32 [n][Hq][scores_stride]
  * receiving the raw logits (scores_stride >= max ctx_len).  Every workspace
  * byte read is written first within the call.  Errors: KV_ERR_ARG,

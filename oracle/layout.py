@@ -8,15 +8,18 @@ pool, section "See it, control it").  Inside a page, the data of one
 
 2-bit block (D dims; 72 B per token per head at D = 256, as the page's table):
     [0,        16*D)   K codes, token-major: row t (D/4 bytes) at t*D/4
-    [16*D,     32*D)   V codes, dim-major:   row d (16 bytes = 64 tokens) at 16*d
+    [16*D,     32*D)   V codes, dim-major, in two halves of 32 token slots
     [32*D,     32*D+512)  K metadata: 64 x [fp32 scale, fp32 min]
     [32*D+512, 32*D+1024) V metadata: 64 x [fp32 scale, fp32 min]
   K rows pack dims least-significant-bits first: dim j sits in byte j // 4 at
-  bit 2 * (j % 4).  A V row packs the page's 64 token slots as four 32-bit
-  little-endian words, word w holding slots 16w..16w+15: slot 16w + q (q < 8)
-  at bits 4q..4q+1 and slot 16w + 8 + q at bits 4q+2..4q+3 (each 4-bit
-  nibble holds one slot of each half-word), so masking a word with 0x33333333
-  yields eight slots in order, one per nibble.
+  bit 2 * (j % 4).  The V codes of a dim are four 32-bit little-endian words,
+  word w holding token slots 16w..16w+15: slot 16w + q (q < 8) at bits
+  4q..4q+1 and slot 16w + 8 + q at bits 4q+2..4q+3 (each 4-bit nibble holds
+  one slot of each half-word), so masking a word with 0x33333333 yields eight
+  slots in order, one per nibble.  Words 0-1 (slots 0-31) of every dim form
+  the first half of the V plane, words 2-3 the second; inside a half the 8
+  bytes of dims d and d + 16 (d % 32 < 16) are adjacent, so the 8-byte pieces
+  of dim d sit at  half * 8D + 16 * (16 * (d // 32) + d % 16) + 8 * ((d // 16) % 2).
 
 8-bit block (D dims):
     [0,      64*D)   K codes int8, token-major: row t at t*D
@@ -103,6 +106,41 @@ def unpack2(packed, n: int) -> np.ndarray:
     return out
 
 
+def v_word_offset(D: int, d: int, w: int) -> int:
+    """Byte offset, inside the V plane, of word w (slots 16w..16w+15) of dim d."""
+    half, word = w // 2, w % 2
+    return half * 8 * D + 16 * (16 * (d // 32) + d % 16) + 8 * ((d // 16) % 2) + 4 * word
+
+
+def v_plane_index(D: int) -> np.ndarray:
+    """[D][16] byte indices into the V plane: row d lists dim d's 16 bytes in slot order."""
+    idx = np.empty((D, 16), dtype=np.int64)
+    for d in range(D):
+        for w in range(4):
+            o = v_word_offset(D, d, w)
+            idx[d, 4 * w:4 * w + 4] = np.arange(o, o + 4)
+    return idx
+
+
+class _VRows:
+    """[D][16] view of a V plane: row d = dim d's four words in slot order (a gather/scatter)."""
+
+    def __init__(self, plane: np.ndarray, D: int):
+        self.plane, self.idx = plane, v_plane_index(D)
+
+    def __getitem__(self, key):
+        return self.plane[self.idx][key]
+
+    def __setitem__(self, key, value):
+        rows = self.plane[self.idx]
+        rows[key] = value
+        self.plane[self.idx] = rows
+
+    def __array__(self, dtype=None, copy=None):
+        a = self.plane[self.idx]
+        return a if dtype is None else a.astype(dtype)
+
+
 class Q2Block:
     """Views into one 2-bit (layer, head) block of a page (a uint8 array of block_bytes)."""
 
@@ -110,7 +148,7 @@ class Q2Block:
         assert buf.dtype == np.uint8 and buf.size == q2_block_bytes(D)
         self.D = D
         self.k_codes = buf[0:16 * D].reshape(PAGE, D // 4)
-        self.v_codes = buf[16 * D:32 * D].reshape(D, 16)
+        self.v_codes = _VRows(buf[16 * D:32 * D], D)
         self.k_meta = buf[32 * D:32 * D + 512].view(np.float32).reshape(PAGE, 2)
         self.v_meta = buf[32 * D + 512:32 * D + 1024].view(np.float32).reshape(PAGE, 2)
 
@@ -133,7 +171,7 @@ class Q2Block:
         return codes, self.k_meta[:n, 0].copy(), self.k_meta[:n, 1].copy()
 
     def read_v(self, n: int):
-        codes = unpack2_vrow(self.v_codes)[:, :n].T.copy()   # [n][D]
+        codes = unpack2_vrow(np.asarray(self.v_codes))[:, :n].T.copy()   # [n][D]
         return codes, self.v_meta[:n, 0].copy(), self.v_meta[:n, 1].copy()
 
 

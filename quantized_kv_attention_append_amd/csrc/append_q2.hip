@@ -12,10 +12,10 @@
 // order).  A zero min or max is canonicalised to +0.
 //
 // Layout of one (layer, KV head) block of a page: K codes token-major (row t =
-// D/4 bytes, dim j at bit 2*(j%4) of byte j/4), V codes dim-major (row d = 16
-// bytes = four 32-bit words holding the 64 token slots; in word w, slot
-// 16w+q sits at bit 4q for q < 8 and slot 16w+8+q at bit 4q+2), then 64 K
-// metadata rows and 64 V metadata rows.  K rows are read by token for the
+// D/4 bytes, dim j at bit 2*(j%4) of byte j/4), V codes dim-major (four 32-bit
+// words per dim holding the 64 token slots; in word w, slot 16w+q sits at bit
+// 4q for q < 8 and slot 16w+8+q at bit 4q+2; words placed by q2_vword_off),
+// then 64 K metadata rows and 64 V metadata rows.  K rows are read by token for the
 // q.k contraction over dims; V rows by dim for the p.v contraction over
 // tokens, and masking a V word with 0x33333333 yields eight consecutive slots,
 // one per 4-bit nibble, which is the matrix-core operand format the decode
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
         const int d = lane * DPL + k;
-        uint32_t* p = reinterpret_cast<uint32_t*>(blk + q2_vcodes_off(D) + 16 * d + 4 * wave);
+        uint32_t* p = reinterpret_cast<uint32_t*>(blk + q2_vcodes_off(D) + q2_vword_off(D, d, wave));
         uint32_t old = (vmask == 0xFFFFFFFFu) ? 0u : *p;
         *p = (old & ~vmask) | vw[k];
     }
@@ -143,7 +143,8 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(PoolView pv, int fmt,
                 c = (blk[t * (D / 4) + d / 4] >> (2 * (d % 4))) & 3u;
                 meta = *reinterpret_cast<const float2*>(blk + q2_kmeta_off(D) + 8 * t);
             } else {
-                const uint32_t word = *reinterpret_cast<const uint32_t*>(blk + q2_vcodes_off(D) + 16 * d + 4 * (t / 16));
+                const uint32_t word =
+                    *reinterpret_cast<const uint32_t*>(blk + q2_vcodes_off(D) + q2_vword_off(D, d, t / 16));
                 const int q = t & 15;
                 c = (word >> (q < 8 ? 4 * q : 4 * (q - 8) + 2)) & 3u;
                 meta = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * t);

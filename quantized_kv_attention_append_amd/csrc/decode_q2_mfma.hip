@@ -29,8 +29,9 @@
 //
 // One workgroup of four wavefronts per (sequence, KV head, split); wave w
 // takes every fourth pair of pages of the split (128 tokens = one k-block of
-// the instruction), loading the next pair while it computes the current one,
-// and the four waves combine their partial results in LDS.  Token t of the pair sits at
+// the instruction), keeping the next two pairs' loads in flight while it
+// computes the current one, and the four waves combine their partial results
+// in LDS.  Token t of the pair sits at
 // page t/64, slot t%64.  Operand lane layouts of the instruction (fp4: lane
 // group g holds k = 32g..32g+31; fp8: k = 16g..16g+15 and 64+16g..64+16g+15;
 // result: lane l holds column l%16, rows 4(l/16)..+3) let the q.k product
@@ -123,7 +124,7 @@ constexpr float RESCALE_LOG2 = 8.0f;
 template <int D>
 struct Tile {
     uint32_t kc[8][D / 64];  // K code words of this lane's row for the eight q.k token groups
-    uint2 vc[D / 16];        // V code words: 32 token slots of dim 16b + l%16
+    uint4 vc[D / 32];        // V code words: 32 token slots of dims 32c + l%16 and 32c + 16 + l%16
     uint4 meta[2];           // this lane's two 16-byte chunks of the pair's metadata
 };
 
@@ -144,9 +145,9 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, cons
         }
     }
 #pragma unroll
-    for (int b = 0; b < D / 16; ++b)
-        t.vc[b] = *reinterpret_cast<const uint2*>((grp < 2 ? base0 : base1) + q2_vcodes_off(D) + 16 * (16 * b + j) +
-                                                  8 * (grp & 1));
+    for (int c = 0; c < D / 32; ++c)
+        t.vc[c] = *reinterpret_cast<const uint4*>((grp < 2 ? base0 : base1) + q2_vcodes_off(D) +
+                                                  q2_vword_off(D, 32 * c + j, 2 * (grp & 1)));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int ch = l + 64 * h, plane = ch >> 5;
@@ -270,8 +271,10 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, float2 (*meta)[PA
                                 digit_of(wv[m][2], wscale, piece), digit_of(wv[m][3], wscale, piece));
     // ---- p.v ----
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-        st.acc[b] = mma_fp8_fp4(wop, fp4_operand(t.vc[b].x, t.vc[b].y), st.acc[b], 127 - FW);
+    for (int c = 0; c < NB / 2; ++c) {
+        st.acc[2 * c] = mma_fp8_fp4(wop, fp4_operand(t.vc[c].x, t.vc[c].y), st.acc[2 * c], 127 - FW);
+        st.acc[2 * c + 1] = mma_fp8_fp4(wop, fp4_operand(t.vc[c].z, t.vc[c].w), st.acc[2 * c + 1], 127 - FW);
+    }
 }
 
 template <int D>
@@ -346,22 +349,59 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     float* srow = scores ? scores + ((int64_t)e * Hq + g * G + hh) * sstride : nullptr;
     float2(*meta)[PAGE] = meta_s[wave];
 
-    // ---- this wave's page pairs: pr0 + wave, pr0 + wave + 4, ... ----
-    const int pr1 = (pg1 + 1) / 2;
-    int pr = pg0 / 2 + wave;
-    auto base_of = [&](int page) {
-        return pv.pages + (int64_t)bt[page < n_pages ? page : 2 * (page / 2)] * pv.page_bytes + lhoff;
-    };
-    Tile<D> cur, nxt;
-    if (pr < pr1) load_tile<D>(cur, base_of(2 * pr), base_of(2 * pr + 1), l);
-    for (; pr < pr1; pr += 4) {
-        const bool has_next = pr + 4 < pr1;
-        if (has_next) load_tile<D>(nxt, base_of(2 * pr + 8), base_of(2 * pr + 9), l);
-        if ((2 * pr + 2) * PAGE <= ctx)
-            compute_tile<D, true>(cur, meta, l, qop, qc, st, 2 * pr * PAGE, ctx, srow);
-        else
-            compute_tile<D, false>(cur, meta, l, qop, qc, st, 2 * pr * PAGE, ctx, srow);
-        if (has_next) cur = nxt;
+    // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
+    const int pr_first = pg0 / 2 + wave;
+    const int pr_end = (pg1 + 1) / 2;
+    const int T = pr_first < pr_end ? (pr_end - pr_first + 3) / 4 : 0;
+    // the last tile of the sequence may be partly past ctx; it is done on its own
+    const bool last_partial = T > 0 && 2 * (pr_first + 4 * (T - 1)) * PAGE + 2 * PAGE > ctx;
+    const int TF = last_partial ? T - 1 : T;  // full tiles
+    auto tok0_of = [&](int t) { return 2 * (pr_first + 4 * t) * PAGE; };
+
+    // Tiles go in chunks of 64: lane k of pid0/pid1 holds the physical ids of
+    // the two pages of tile c0 + k.  Three tile buffers rotate so that two
+    // tiles are in flight while one is computed; every load is issued
+    // unconditionally (indices clamped to the chunk's last tile, re-read from
+    // cache), so the count of loads in flight is the same on every path.
+    Tile<D> ta, tb, tc;
+    for (int c0 = 0; c0 < TF; c0 += 64) {
+        const int Tc = min(64, TF - c0);
+        int pid0 = 0, pid1 = 0;
+        if (l < Tc) {
+            const int pair = pr_first + 4 * (c0 + l);
+            pid0 = bt[2 * pair];
+            pid1 = bt[2 * pair + 1];
+        }
+        auto load = [&](Tile<D>& tile, int t) {
+            const int tt = min(t, Tc - 1);
+            load_tile<D>(tile, pv.pages + (int64_t)__builtin_amdgcn_readlane(pid0, tt) * pv.page_bytes + lhoff,
+                         pv.pages + (int64_t)__builtin_amdgcn_readlane(pid1, tt) * pv.page_bytes + lhoff, l);
+        };
+        auto run = [&](const Tile<D>& tile, int t) {
+            compute_tile<D, true>(tile, meta, l, qop, qc, st, tok0_of(c0 + t), ctx, srow);
+        };
+        load(ta, 0);
+        load(tb, 1);
+        for (int t = 0; t < Tc; t += 3) {
+            load(tc, t + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            run(ta, t);
+            if (t + 1 >= Tc) break;
+            load(ta, t + 3);
+            __builtin_amdgcn_sched_barrier(0);
+            run(tb, t + 1);
+            if (t + 2 >= Tc) break;
+            load(tb, t + 4);
+            __builtin_amdgcn_sched_barrier(0);
+            run(tc, t + 2);
+        }
+    }
+    if (last_partial) {
+        const int pair = pr_first + 4 * (T - 1);
+        const int p1 = 2 * pair + 1 < n_pages ? 2 * pair + 1 : 2 * pair;
+        load_tile<D>(ta, pv.pages + (int64_t)bt[2 * pair] * pv.page_bytes + lhoff,
+                     pv.pages + (int64_t)bt[p1] * pv.page_bytes + lhoff, l);
+        compute_tile<D, false>(ta, meta, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
     }
 
     // ---- this wave's partial: sum weight digits (lane groups) and lanes' sums ----
@@ -419,7 +459,6 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
             w.ml[2 * row + 1] = lsum;
         }
     }
-    merge_if_last(pv, bd, e, g, splits, ws, out);
 }
 
 hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
@@ -435,7 +474,8 @@ hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, 
     else
         hipLaunchKernelGGL(decode_q2_mfma_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out,
                            scores, sstride);
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }
 
 }  // namespace kvq

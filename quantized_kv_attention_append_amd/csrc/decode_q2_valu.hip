@@ -11,8 +11,8 @@
 // materialising K^ and V^:
 //     q . k^_t = mn_t * sum(q) + scale_t * sum_d q_d c_td
 //     sum_t p_t v^_td = sum_t p_t mn_t + sum_t (p_t scale_t) c_td
-// Partial (m, l, o) go to the workspace; the last workgroup of a (sequence,
-// KV head) to finish merges the splits in fp32 (decode_common.h).
+// Partial (m, l, o) go to the workspace; merge_splits_kernel then merges the
+// splits in fp32.
 #include "decode_common.h"
 
 namespace kvq {
@@ -104,8 +104,9 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
         __syncthreads();
         // p . v over the dim-major V plane, one thread per dim
         if (tid < D) {
-            const uint4 vr = *reinterpret_cast<const uint4*>(blk + q2_vcodes_off(D) + 16 * tid);
-            const uint32_t words[4] = {vr.x, vr.y, vr.z, vr.w};
+            const uint2 v0 = *reinterpret_cast<const uint2*>(blk + q2_vcodes_off(D) + q2_vword_off(D, tid, 0));
+            const uint2 v1 = *reinterpret_cast<const uint2*>(blk + q2_vcodes_off(D) + q2_vword_off(D, tid, 2));
+            const uint32_t words[4] = {v0.x, v0.y, v1.x, v1.y};
             for (int j = 0; j < G; ++j) o[j] *= a_s[j];
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -129,7 +130,6 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
         w.ml[2 * r] = m_s[tid];
         w.ml[2 * r + 1] = l_s[tid];
     }
-    merge_if_last(pv, bd, e, g, splits, ws, out);
 }
 
 hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
@@ -139,7 +139,8 @@ hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc&
         hipLaunchKernelGGL(decode_q2_valu_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
     else
         hipLaunchKernelGGL(decode_q2_valu_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
-    return hipGetLastError();
+    const hipError_t err = hipGetLastError();
+    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }
 
 }  // namespace kvq

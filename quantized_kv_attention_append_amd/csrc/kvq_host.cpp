@@ -75,7 +75,6 @@ struct kv_pool {
     int32_t bt_stride = 0;       // max pages per sequence
     int32_t* d_bt = nullptr;     // [max_seqs][bt_stride]
     uint16_t* d_stage = nullptr; // 8-bit exact-K window
-    int32_t* d_sem = nullptr;    // split-arrival counters
     int device = 0;
     // host metadata
     std::vector<int32_t> owner;      // page -> seq slot or -1
@@ -101,7 +100,6 @@ struct kv_pool {
         v.bt = d_bt;
         v.bt_stride = bt_stride;
         v.stage = d_stage;
-        v.sem = d_sem;
         return v;
     }
 };
@@ -181,8 +179,6 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
     }
     e = hipMalloc((void**)&p->d_bt, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
     if (e == hipSuccess) e = hipMemset(p->d_bt, 0, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMalloc((void**)&p->d_sem, (size_t)KV_MAX_BATCH * geom->n_kv_heads * sizeof(int32_t));
-    if (e == hipSuccess) e = hipMemset(p->d_sem, 0, (size_t)KV_MAX_BATCH * geom->n_kv_heads * sizeof(int32_t));
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e == hipSuccess && fmt == KV_FMT_Q8) {
         size_t sb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * PAGE * geom->head_dim * sizeof(uint16_t);
@@ -210,7 +206,6 @@ kv_status kv_pool_destroy(kv_pool* p) {
     if (p->own_pages && p->d_pages) (void)hipFree(p->d_pages);
     if (p->d_bt) (void)hipFree(p->d_bt);
     if (p->d_stage) (void)hipFree(p->d_stage);
-    if (p->d_sem) (void)hipFree(p->d_sem);
     delete p;
     return KV_OK;
 }

@@ -20,7 +20,6 @@ struct PoolView {
     const int32_t* bt;     // device block tables [max_seqs][bt_stride]
     int32_t bt_stride;
     uint16_t* stage;       // 8-bit pools: exact K window, bf16 [max_seqs][L][Hkv][64][D]
-    int32_t* sem;          // split-arrival counters [KV_MAX_BATCH][Hkv], zero between calls
 };
 
 // Per-call batch description, passed by value as a kernel argument (so it is
@@ -39,6 +38,12 @@ __host__ __device__ constexpr int64_t q2_block_bytes(int D) { return 32 * (int64
 __host__ __device__ constexpr int64_t q2_vcodes_off(int D) { return 16 * (int64_t)D; }
 __host__ __device__ constexpr int64_t q2_kmeta_off(int D) { return 32 * (int64_t)D; }
 __host__ __device__ constexpr int64_t q2_vmeta_off(int D) { return 32 * (int64_t)D + 512; }
+// Offset inside the V plane of word w (token slots 16w..16w+15) of dim d: the
+// plane holds two halves of 32 slots (words 0-1, then 2-3); inside a half the
+// 8 bytes of dims d and d + 16 (d % 32 < 16) are adjacent.
+__host__ __device__ constexpr int64_t q2_vword_off(int D, int d, int w) {
+    return 8 * (int64_t)D * (w >> 1) + 16 * (16 * (d >> 5) + (d & 15)) + 8 * ((d >> 4) & 1) + 4 * (w & 1);
+}
 // Byte offsets inside an 8-bit (layer, head) block.
 __host__ __device__ constexpr int64_t q8_block_bytes(int D) { return 132 * (int64_t)D + 256; }
 __host__ __device__ constexpr int64_t q8_vcodes_off(int D) { return 64 * (int64_t)D; }
@@ -50,8 +55,8 @@ hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, 
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
-// Decode launchers write the fp32 output themselves: the last workgroup of a
-// (sequence, KV head) to finish merges that pair's splits.
+// Decode launchers enqueue the split kernel and then the merge of its
+// partials, which writes the fp32 output.
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,

@@ -75,3 +75,15 @@ def test_v_row_word_layout_matches_loop():
             nibbles_lo = [(word >> (4 * q)) & 0xF & 3 for q in range(8)]
             assert nibbles_lo == list(c[r, 16 * w:16 * w + 8])
     assert np.array_equal(layout.unpack2_vrow(p), c)
+
+
+def test_v_plane_word_offsets_tile_the_plane():
+    for D in (128, 256):
+        offs = sorted(layout.v_word_offset(D, d, w) for d in range(D) for w in range(4))
+        assert offs == list(range(0, 16 * D, 4))
+        for d in range(D):
+            if d % 32 < 16:
+                for half in (0, 1):
+                    a = layout.v_word_offset(D, d, 2 * half)
+                    assert layout.v_word_offset(D, d, 2 * half + 1) == a + 4
+                    assert layout.v_word_offset(D, d + 16, 2 * half) == a + 8  # dims d, d+16 adjacent
