@@ -14,18 +14,31 @@ Prints one JSON line: KV tokens attended per second (lane x layer x token
 triples), the per-launch roofline of the decode kernel against 8 TB/s HBM, and
 the CPU oracle timed on a bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--splits P] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--splits P] [--no-cpu] [--copy-mib M]
+
+The roofline's "traffic" (HBM bytes a decode call really moves, from the
+FETCH_SIZE and WRITE_SIZE counters scaled by a copy of known size) is read
+from the committed counter summary in profiles/ and reported only while the
+decode sources still hash to the version the counters were taken on;
+otherwise it is null.  --copy-mib runs that calibration copy (int32 -> fp32,
+M MiB each way) after the timed region, for the counter passes.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "quantized_kv_attention_append_amd", "csrc")
+# sources of the two kernels of a 2-bit decode call (split kernel + merge)
+DECODE_SOURCES = ("decode_q2_mfma.hip", "merge_splits.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q2_mfma_27b_geometry_traffic.md")
 METRIC = "decode attention: KV tokens attended/s and achieved HBM GB/s (% of peak), 2-bit"
 
 
@@ -37,11 +50,34 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="split-K partitions per (lane, KV head); 0 = library choice")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size for counter passes (0 = none)")
     return ap.parse_args()
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it is absent or was taken on other decode sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            fields = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", "traffic_bytes_per_call:")))
+    except OSError:
+        return None
+    if fields.get("source_sha256", "").strip() != decode_source_hash():
+        log("traffic: counter summary is for other decode sources; reporting null")
+        return None
+    return int(fields["traffic_bytes_per_call"].strip())
 
 
 def oracle_baseline(w, budget_s: float):
@@ -168,6 +204,18 @@ def main():
     log(f"splits={sp} avg decode launch {avg_launch_ms * 1e3:.1f} us, step {ms_per_step:.3f} ms, "
         f"{achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s), wall {wall:.3f} s")
 
+    if args.copy_mib > 0:
+        # calibration for the FETCH_SIZE / WRITE_SIZE counter passes: a plain
+        # elementwise copy that reads and writes copy_mib MiB
+        n = args.copy_mib << 18
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty(n, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: 3 x {args.copy_mib} MiB int32 -> fp32")
+        del src, dst
+
     cpu = None
     if not args.no_cpu:
         cpu = oracle_baseline(w, args.cpu_seconds)
@@ -199,8 +247,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "kernel": "decode_q2 (one launch per layer, merge fused)",
+            "traffic": measured_traffic(),
+            "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then merge_splits_kernel",
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": avg_launch_ms * 1e3,
         },

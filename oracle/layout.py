@@ -12,14 +12,15 @@ pool, section "See it, control it").  Inside a page, the data of one
     [32*D,     32*D+512)  K metadata: 64 x [fp32 scale, fp32 min]
     [32*D+512, 32*D+1024) V metadata: 64 x [fp32 scale, fp32 min]
   K rows pack dims least-significant-bits first: dim j sits in byte j // 4 at
-  bit 2 * (j % 4).  The V codes of a dim are four 32-bit little-endian words,
-  word w holding token slots 16w..16w+15: slot 16w + q (q < 8) at bits
-  4q..4q+1 and slot 16w + 8 + q at bits 4q+2..4q+3 (each 4-bit nibble holds
-  one slot of each half-word), so masking a word with 0x33333333 yields eight
-  slots in order, one per nibble.  Words 0-1 (slots 0-31) of every dim form
-  the first half of the V plane, words 2-3 the second; inside a half the 8
-  bytes of dims d and d + 16 (d % 32 < 16) are adjacent, so the 8-byte pieces
-  of dim d sit at  half * 8D + 16 * (16 * (d // 32) + d % 16) + 8 * ((d // 16) % 2).
+  bit 2 * (j % 4).  The V codes of a dim are four 32-bit little-endian words;
+  token slot s = 16b + 4w + r (b = s // 16, w = (s // 4) % 4, r = s % 4) sits
+  in word w at bits 16 * (r % 2) + 4 * b + 2 * (r // 2).  Masking a word with
+  0x33333333 therefore yields the eight slots with r in {0, 1}, one per 4-bit
+  nibble, and masking it shifted right by two the eight slots with r in {2, 3}.
+  Words 0-1 of every dim form the first half of the V plane, words 2-3 the
+  second; inside a half the 8 bytes of dims d and d + 16 (d % 32 < 16) are
+  adjacent, so the 8-byte pieces of dim d sit at
+  half * 8D + 16 * (16 * (d // 32) + d % 16) + 8 * ((d // 16) % 2).
 
 8-bit block (D dims):
     [0,      64*D)   K codes int8, token-major: row t at t*D
@@ -68,32 +69,30 @@ def pack2(codes) -> np.ndarray:
     return b.astype(np.uint8)
 
 
-def _vslot_field():
-    """2-bit field index (0..15) inside its 32-bit word of each of the word's 16 slots."""
-    return np.array([2 * q for q in range(8)] + [2 * q + 1 for q in range(8)])
+def v_slot_word_bit(slot: int):
+    """(word, bit) of token slot ``slot`` (0..63) in a dim's four V-code words."""
+    b, w, r = slot // 16, (slot // 4) % 4, slot % 4
+    return w, 16 * (r % 2) + 4 * b + 2 * (r // 2)
 
 
 def pack2_vrow(codes) -> np.ndarray:
     """codes uint8 [..., 64] (token slots) -> bytes [..., 16] in the V-row word layout."""
     c = np.asarray(codes, dtype=np.uint8)
     assert c.shape[-1] == 64 and c.max(initial=0) <= 3
-    field = _vslot_field()
     words = np.zeros(c.shape[:-1] + (4,), dtype=np.uint32)
-    for w in range(4):
-        for q in range(16):
-            words[..., w] |= c[..., 16 * w + q].astype(np.uint32) << np.uint32(2 * field[q])
-    return words.view(np.uint8).reshape(c.shape[:-1] + (16,)) if words.flags.c_contiguous else \
-        np.ascontiguousarray(words).view(np.uint8).reshape(c.shape[:-1] + (16,))
+    for s in range(64):
+        w, bit = v_slot_word_bit(s)
+        words[..., w] |= c[..., s].astype(np.uint32) << np.uint32(bit)
+    return np.ascontiguousarray(words).view(np.uint8).reshape(c.shape[:-1] + (16,))
 
 
 def unpack2_vrow(packed) -> np.ndarray:
     p = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
     words = p.view(np.uint32).reshape(p.shape[:-1] + (4,))
-    field = _vslot_field()
     out = np.empty(p.shape[:-1] + (64,), dtype=np.uint8)
-    for w in range(4):
-        for q in range(16):
-            out[..., 16 * w + q] = (words[..., w] >> np.uint32(2 * field[q])) & 3
+    for s in range(64):
+        w, bit = v_slot_word_bit(s)
+        out[..., s] = (words[..., w] >> np.uint32(bit)) & 3
     return out
 
 
@@ -158,9 +157,8 @@ class Q2Block:
 
     def write_v(self, slot: int, codes_row, scale, mn):
         """Set the 2 bits of token ``slot`` in every dim row, leaving other slots untouched."""
-        field = _vslot_field()[slot % 16]
-        bit = 32 * (slot // 16) + 2 * field
-        byte, shift = bit // 8, bit % 8
+        w, bit = v_slot_word_bit(slot)
+        byte, shift = 4 * w + bit // 8, bit % 8
         keep = np.uint8(0xFF ^ (3 << shift))
         col = self.v_codes[:, byte]
         self.v_codes[:, byte] = (col & keep) | (np.asarray(codes_row, np.uint8) << shift)

@@ -13,18 +13,18 @@
 //
 // Layout of one (layer, KV head) block of a page: K codes token-major (row t =
 // D/4 bytes, dim j at bit 2*(j%4) of byte j/4), V codes dim-major (four 32-bit
-// words per dim holding the 64 token slots; in word w, slot 16w+q sits at bit
-// 4q for q < 8 and slot 16w+8+q at bit 4q+2; words placed by q2_vword_off),
-// then 64 K metadata rows and 64 V metadata rows.  K rows are read by token for the
-// q.k contraction over dims; V rows by dim for the p.v contraction over
-// tokens, and masking a V word with 0x33333333 yields eight consecutive slots,
-// one per 4-bit nibble, which is the matrix-core operand format the decode
-// kernel feeds from it.
+// words per dim holding the 64 token slots; slot 16b + 4w + r sits in word w at
+// bit 16(r%2) + 4b + 2(r/2); words placed by q2_vword_off), then 64 K metadata
+// rows and 64 V metadata rows.  K rows are read by token for the q.k
+// contraction over dims; V rows by dim for the p.v contraction over tokens,
+// and masking a V word with 0x33333333 (or its shift right by two) yields
+// eight slots, one per 4-bit nibble, which is the matrix-core operand format
+// the decode kernel feeds from it.
 //
 // Work split: one workgroup of four waves per (sequence, page touched, KV
-// head); wave w owns token slots [16w, 16w+16) of the page, which is exactly
-// one 32-bit word of every dim-major V row, so the V plane is written with one
-// read-modify-write per (dim, word) and no two workgroups share a byte.
+// head); wave w owns the token slots of V word w (slots s with (s/4)%4 == w),
+// so the V plane is written with one read-modify-write per (dim, word) and no
+// two workgroups or waves share a byte.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -71,14 +71,15 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
     uint8_t* blk = pv.pages + (int64_t)phys * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int s0 = max(slot_lo, wave * 16), s1 = min(slot_hi, wave * 16 + 16);
-    if (s0 >= s1) return;
 
     uint32_t vw[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) vw[k] = 0;
     uint32_t vmask = 0;
-    for (int s = s0; s < s1; ++s) {
+    // this wave's slots: 16b + 4 * wave + r, in increasing order
+    for (int i = 0; i < 16; ++i) {
+        const int s = 16 * (i >> 2) + 4 * wave + (i & 3);
+        if (s < slot_lo || s >= slot_hi) continue;
         const int64_t row = (int64_t)bd.row0[e] + (lp * PAGE + s - start);
         const int64_t off = (row * pv.Hkv + head) * D + lane * DPL;
         float xk[DPL], xv[DPL];
@@ -98,8 +99,7 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
             uint32_t other = __shfl_down(bits, 1);
             if ((lane & 1) == 0) krow[lane >> 1] = (uint8_t)(bits | (other << 4));
         }
-        const int q = s & 15;
-        const int sh = q < 8 ? 4 * q : 4 * (q - 8) + 2;
+        const int sh = q2_vslot_bit(s);
 #pragma unroll
         for (int k = 0; k < DPL; ++k) vw[k] |= cv[k] << sh;
         vmask |= 3u << sh;
@@ -108,6 +108,7 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
             *reinterpret_cast<float2*>(blk + q2_vmeta_off(D) + 8 * s) = make_float2(sv, mv);
         }
     }
+    if (vmask == 0) return;
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
         const int d = lane * DPL + k;
@@ -143,10 +144,9 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(PoolView pv, int fmt,
                 c = (blk[t * (D / 4) + d / 4] >> (2 * (d % 4))) & 3u;
                 meta = *reinterpret_cast<const float2*>(blk + q2_kmeta_off(D) + 8 * t);
             } else {
-                const uint32_t word =
-                    *reinterpret_cast<const uint32_t*>(blk + q2_vcodes_off(D) + q2_vword_off(D, d, t / 16));
-                const int q = t & 15;
-                c = (word >> (q < 8 ? 4 * q : 4 * (q - 8) + 2)) & 3u;
+                const uint32_t word = *reinterpret_cast<const uint32_t*>(blk + q2_vcodes_off(D) +
+                                                                         q2_vword_off(D, d, q2_vslot_word(t)));
+                c = (word >> q2_vslot_bit(t)) & 3u;
                 meta = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * t);
             }
             r = __fmaf_rn((float)c, meta.x, meta.y);

@@ -6,21 +6,22 @@
 // sustain at full HBM bandwidth, so both contractions run on
 // v_mfma_scale_f32_16x16x128_f8f6f4.  Its internal sum drops low-order bits
 // of products much smaller than the largest product of a group, but sums
-// small-integer products exactly, so every operand is made of small
-// integers:
+// small-integer products exactly, so every operand is made of small integers
+// and every power of two goes into the instruction's per-row / per-column
+// scale:
 //   * 2-bit codes c become fp4 (e2m1) nibbles whose value is c/2: a 32-bit
 //     word of 16 codes spreads into two words of nibbles with one shift and
 //     two masks (w & 0x33333333, (w >> 2) & 0x33333333);
 //   * the bf16 query of each head becomes a 19-bit fixed-point integer
 //     round(q * 2^E) (exact unless |q| < max|q| / 2^11), written as four
-//     balanced radix-32 digits in -16..16 (exact in e4m3); the 16 columns of
-//     the q.k product are 4 heads x 4 digits, recombined with two row
-//     rotations;
-//   * the softmax weights w_t = p_t * scale_t of a 128-token tile become
-//     19-bit fixed-point integers relative to each head's largest weight in
-//     the tile, also as four balanced digits; the 16 rows of the p.v product
-//     are 4 heads x 4 digits, the instruction's per-row power-of-two scale
-//     undoes the tile scale, and each digit row is weighted once at the end.
+//     balanced radix-32 digits in -16..16 (exact in e4m3); row 4h + i of the
+//     q.k product is digit i of head h, weighted 32^(3-i) 2^-E by its scale;
+//   * the softmax weights w_t = p_t * scale_t become 16-bit fixed-point
+//     integers relative to each head's largest weight in a block of 32
+//     tokens, split into four 4-bit digits.  An e4m3 byte 0..15 is exactly
+//     b * 2^-9, so the digits go into the operand with byte shuffles only;
+//     column 4h + i of the p.v product is digit i of head h, and its scale
+//     for k-block b (32 tokens) weights it 16^i 2^-F(h, b).
 // The dequantization is folded algebraically (q.k^_t = mn_t sum(q) + scale_t
 // q.c_t; p.v^ = sum p_t mn_t + sum (p_t scale_t) c_t), and the online softmax,
 // its rescaling and every running sum are fp32 registers (the two-level
@@ -31,16 +32,19 @@
 // takes every fourth pair of pages of the split (128 tokens = one k-block of
 // the instruction), keeping the next two pairs' loads in flight while it
 // computes the current one, and the four waves combine their partial results
-// in LDS.  Token t of the pair sits at
-// page t/64, slot t%64.  Operand lane layouts of the instruction (fp4: lane
-// group g holds k = 32g..32g+31; fp8: k = 16g..16g+15 and 64+16g..64+16g+15;
-// result: lane l holds column l%16, rows 4(l/16)..+3) let the q.k product
-// deliver each lane exactly the 32 tokens its p.v operand needs:
-//   q.k:  A = K codes (rows = tokens), B = query digits (column 4d + h =
-//         digit d of head h); row i of token group m is token
-//         (m/4)*64 + 16(i/4) + 4(m%4) + i%4.
-//   p.v:  A = weight digits (row 4d + h = digit d of head h),
-//         B = V codes of 16 dims (dim-major rows, so k runs over tokens).
+// in LDS.  Token t of the pair sits at page t/64, slot t%64.  Operand lane
+// layouts of the instruction: fp4 lane group g holds k = 32g..32g+31; fp8
+// lane group g holds k = 16g..16g+15 and 64+16g..64+16g+15; the result lane l
+// holds column l%16, rows 4(l/16)..+3.
+//   q.k (8 per tile): A = query digits (row 4h + i), B = K codes of tokens
+//       16m..16m+15 of the pair (column j = token 16m + j, k = dims), so lane
+//       l ends with the score of token 16m + l%16 for head l/16: every
+//       (token, head) score of the tile is computed once, eight per lane.
+//   p.v (D/16 per tile): A = V codes of 16 dims (k = tokens), B = weight
+//       digits (column 4h + i).  The V words put token
+//       64(g/2) + 16(t%4) + 8(g%2) + 4u + 2x + t/4 at k = 32g + 16u + 8x + t,
+//       and a per-wave LDS transpose moves each lane's digit bytes of its
+//       eight tokens to the lanes whose k-ranges hold those tokens.
 #include "decode_common.h"
 
 namespace kvq {
@@ -53,25 +57,19 @@ namespace {
 constexpr int FMT_FP8 = 0;  // e4m3
 constexpr int FMT_FP4 = 4;  // e2m1
 
-__device__ __forceinline__ v4f mma_fp4_fp8(const v8i& a_fp4, const v8i& b_fp8, v4f c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp4, b_fp8, c, FMT_FP4, FMT_FP8, 0, 127, 0, 127);
-}
-__device__ __forceinline__ v4f mma_fp8_fp4(const v8i& a_fp8, const v8i& b_fp4, v4f c, int scale_a) {
+// q.k: A = query digits (fp8) with per-row scale, B = K codes (fp4)
+__device__ __forceinline__ v4f mma_qk(const v8i& a_fp8, const v8i& b_fp4, v4f c, int scale_a) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp8, b_fp4, c, FMT_FP8, FMT_FP4, 0, scale_a, 0, 127);
+}
+// p.v: A = V codes (fp4), B = weight digits (fp8) with per-column scale
+__device__ __forceinline__ v4f mma_pv(const v8i& a_fp4, const v8i& b_fp8, v4f c, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp4, b_fp8, c, FMT_FP4, FMT_FP8, 0, 127, 0, scale_b);
 }
 
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
-}
-__device__ __forceinline__ float fp8_byte(uint32_t w, int i) {
-    switch (i) {
-        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
-        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
-        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
-        default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
-    }
 }
 
 // 16 two-bit codes -> two words of eight e2m1 nibbles (value = code / 2).
@@ -101,19 +99,48 @@ __device__ __forceinline__ float digit_of(float x, float scale, int d) {
     return (float)(f - 16);
 }
 __device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+__device__ __forceinline__ int exponent_of(float x) { return (int)((__float_as_uint(x) >> 23) & 0xFF) - 127; }
 
-// Sum over the four lanes j, j+4, j+8, j+12 of each 16-lane row.
-__device__ __forceinline__ float row_sum4(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
-    return x;
+// Reductions over the 16 lanes of a DPP row (row_ror by 8, 4, 2, 1).
+template <int CTRL>
+__device__ __forceinline__ float ror(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, ror<0x128>(x));
+    x = fmaxf(x, ror<0x124>(x));
+    x = fmaxf(x, ror<0x122>(x));
+    return fmaxf(x, ror<0x121>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+    x += ror<0x128>(x);
+    x += ror<0x124>(x);
+    x += ror<0x122>(x);
+    return x + ror<0x121>(x);
+}
+// Max over the eight lanes of a half row (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror).
+__device__ __forceinline__ float half_row_max8(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+}
+// Fixed-point exponent F of a block of weights with max wmax: wmax 2^F in
+// [2^15, 2^16), so X = round(w 2^F) fits 16 bits (capped at 2^16 - 1).  F is
+// clamped to [-105, 126] so that the column scale 137 + 4i - F stays a valid
+// power-of-two byte; weights above 2^120 are out of range.
+__device__ __forceinline__ int weight_exp(float wmax) {
+    return wmax > 0.f ? max(min(15 - exponent_of(wmax), 126), -105) : 0;
+}
+// Sum over the four lanes of a quad (quad_perm [1,0,3,2] then [2,3,0,1]).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
 // k index of byte s of an fp8 operand held by lane group grp.
 __device__ __forceinline__ int fp8_k(int grp, int s) { return s < 16 ? 16 * grp + s : 64 + 16 * grp + (s - 16); }
 
 }  // namespace
-
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -123,9 +150,9 @@ constexpr float RESCALE_LOG2 = 8.0f;
 
 template <int D>
 struct Tile {
-    uint32_t kc[8][D / 64];  // K code words of this lane's row for the eight q.k token groups
-    uint4 vc[D / 32];        // V code words: 32 token slots of dims 32c + l%16 and 32c + 16 + l%16
-    uint4 meta[2];           // this lane's two 16-byte chunks of the pair's metadata
+    uint32_t kc[8][D / 64];  // K code words of token 16m + l%16 of the pair, this lane group's D/16 bytes
+    uint4 vc[D / 32];        // V words of dims 32c + l%16 and 32c + 16 + l%16 for this lane group's k-range
+    uint4 meta[2];           // K and V metadata (scale, min) of tokens 2l and 2l + 1 of the pair
 };
 
 template <int D>
@@ -134,8 +161,7 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, cons
     const int j = l & 15, grp = l >> 4;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int slot = 16 * (j >> 2) + 4 * (m & 3) + (j & 3);
-        const uint8_t* src = (m < 4 ? base0 : base1) + slot * (D / 4) + 4 * NW * grp;
+        const uint8_t* src = (m < 4 ? base0 : base1) + (16 * (m & 3) + j) * (D / 4) + 4 * NW * grp;
         if constexpr (NW == 4) {
             const uint4 w = *reinterpret_cast<const uint4*>(src);
             t.kc[m][0] = w.x; t.kc[m][1] = w.y; t.kc[m][2] = w.z; t.kc[m][3] = w.w;
@@ -148,132 +174,158 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, cons
     for (int c = 0; c < D / 32; ++c)
         t.vc[c] = *reinterpret_cast<const uint4*>((grp < 2 ? base0 : base1) + q2_vcodes_off(D) +
                                                   q2_vword_off(D, 32 * c + j, 2 * (grp & 1)));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int ch = l + 64 * h, plane = ch >> 5;
-        t.meta[h] = *reinterpret_cast<const uint4*>(((plane & 1) ? base1 : base0) +
-                                                    (plane < 2 ? q2_kmeta_off(D) : q2_vmeta_off(D)) + (ch & 31) * 16);
-    }
+    const uint8_t* mb = (l < 32 ? base0 : base1) + 16 * (l & 31);
+    t.meta[0] = *reinterpret_cast<const uint4*>(mb + q2_kmeta_off(D));
+    t.meta[1] = *reinterpret_cast<const uint4*>(mb + q2_vmeta_off(D));
 }
 
 template <int D>
 struct WaveState {
-    v4f acc[D / 16];  // p.v sums: block b, register r = head r, lane group = weight digit
-    float m_ref;      // reference max of this lane's head, in units of 1/cB
+    v4f acc[D / 16];  // p.v sums: block b, column 4h + i of lane l%16, dims 16b + 4(l/16) + r
+    float m_ref;      // reference max of head l/16, raw q.k^ units
     float cbm;        // cB * m_ref (log2 units)
-    float l_run;      // this lane's share of sum p
-    float c_run;      // this lane's share of sum p * min_v
+    float l_run;      // this lane's share of sum p (head l/16)
+    float c_run;      // this lane's share of sum p * min_v (head l/16)
 };
 
 struct QConst {
-    float qdig_w;  // 32^(3 - digit) of this lane's q.k column
-    float cAB;     // sum(q) / (2 * 2^-E): min_k's factor in units of the digit sum
-    float cB;      // log2(e) * sm * 2 * 2^-E: digit-sum units -> log2 logits
+    int scale_a;  // q.k row scale of this lane's row (4h + i): 32^(3-i) 2^-E_h * 2 (codes are c/2)
+    float qsum;   // sum_d q_d of head l/16
+    float cB;     // log2(e) * sm: raw q.k^ -> log2 units
 };
 
+// Per-wave LDS: the tile's metadata as {k scale, k min, v scale, v min} per
+// token, and the weight-digit transpose: for head h and digit i, 32 words at
+// wdig_base(h, i); word c (c < 16) holds the digits of tokens 16m + c for
+// m = 0..3, word 16 + c those for m = 4..7.
+struct WaveLds {
+    float4 meta[2 * PAGE];
+    uint32_t wdig[4 * 4 * 32 + 16 * 3];
+};
+__device__ __forceinline__ int wdig_base(int h, int i) { return (4 * h + i) * 32 + 16 * h; }
+
 template <int D, bool FULL>
-__device__ __forceinline__ void compute_tile(const Tile<D>& t, float2 (*meta)[PAGE], int l, const v8i* qop,
+__device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int l, const v8i* qop,
                                              const QConst& qc, WaveState<D>& st, int tok0, int ctx,
                                              float* __restrict__ srow) {
     constexpr int NC = D / 128, NB = D / 16;
-    const int j = l & 15, grp = l >> 4, piece = j >> 2;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int ch = l + 64 * h;
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(&meta[ch >> 5][0]) + (ch & 31) * 16) = t.meta[h];
+    const int j = l & 15, grp = l >> 4;
+    {
+        const uint4 k = t.meta[0], v = t.meta[1];
+        lds.meta[2 * l] = make_float4(__uint_as_float(k.x), __uint_as_float(k.y), __uint_as_float(v.x),
+                                      __uint_as_float(v.y));
+        lds.meta[2 * l + 1] = make_float4(__uint_as_float(k.z), __uint_as_float(k.w), __uint_as_float(v.z),
+                                          __uint_as_float(v.w));
     }
-    // ---- q.k: scores in units of 1/cB ----
-    float s2[8][4];
-    float mt = -INFINITY;
+    // ---- q.k: raw scores q.k^ of tokens 16m + j, head grp ----
+    float s[8];
+    float4 mt[8];
+    float tmax = -INFINITY;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         v4f cq = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) cq = mma_fp4_fp8(fp4_operand(t.kc[m][2 * c], t.kc[m][2 * c + 1]), qop[c], cq);
-        const int pm = m >> 2, slot0 = 16 * grp + 4 * (m & 3);
-        const float4 km0 = *reinterpret_cast<const float4*>(&meta[pm][slot0]);
-        const float4 km1 = *reinterpret_cast<const float4*>(&meta[pm][slot0 + 2]);
-        const float ks[4] = {km0.x, km0.z, km1.x, km1.z};
-        const float kn[4] = {km0.y, km0.w, km1.y, km1.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float s = fmaf(ks[r], row_sum4(cq[r] * qc.qdig_w), kn[r] * qc.cAB);
-            if (!FULL && tok0 + pm * PAGE + slot0 + r >= ctx) s = -INFINITY;
-            s2[m][r] = s;
-            mt = fmaxf(mt, s);
-        }
+        for (int c = 0; c < NC; ++c) cq = mma_qk(qop[c], fp4_operand(t.kc[m][2 * c], t.kc[m][2 * c + 1]), cq, qc.scale_a);
+        mt[m] = lds.meta[16 * m + j];
+        float x = fmaf(mt[m].x, (cq[0] + cq[1]) + (cq[2] + cq[3]), mt[m].y * qc.qsum);
+        if (!FULL && tok0 + 16 * m + j >= ctx) x = -INFINITY;
+        s[m] = x;
+        tmax = fmaxf(tmax, x);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool need = (mt - st.m_ref) * qc.cB > RESCALE_LOG2;
+    tmax = row_max16(tmax);
+    const bool need = (tmax - st.m_ref) * qc.cB > RESCALE_LOG2;
     if (__ballot(need)) {
-        const float m_new = need ? mt : st.m_ref;
+        const float m_new = need ? tmax : st.m_ref;
         const float cbm_new = qc.cB * m_new;
         const float alpha = __builtin_amdgcn_exp2f(st.cbm - cbm_new);
         st.l_run *= alpha;
         st.c_run *= alpha;
-        float al[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) al[r] = __shfl(alpha, (l & ~3) | r);
+        // accumulator columns of lane l belong to head (l%16)/4
+        const float a = __shfl(alpha, 16 * (j >> 2));
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) st.acc[b][r] *= al[r];
+            for (int r = 0; r < 4; ++r) st.acc[b][r] *= a;
         st.m_ref = m_new;
         st.cbm = cbm_new;
     }
     // ---- weights w = p * scale_v ----
-    float wv[8][4];
-    float wmax = 0.f;
+    float w[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int pm = m >> 2, slot0 = 16 * grp + 4 * (m & 3);
-        const float4 vm0 = *reinterpret_cast<const float4*>(&meta[2 + pm][slot0]);
-        const float4 vm1 = *reinterpret_cast<const float4*>(&meta[2 + pm][slot0 + 2]);
-        const float vs[4] = {vm0.x, vm0.z, vm1.x, vm1.z};
-        const float vn[4] = {vm0.y, vm0.w, vm1.y, vm1.w};
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[m], qc.cB, -st.cbm));
+        float x;
+        if (FULL) {
+            x = p * mt[m].z;
+            st.c_run = fmaf(p, mt[m].w, st.c_run);
+        } else {
+            const bool valid = tok0 + 16 * m + j < ctx;
+            x = valid ? p * mt[m].z : 0.f;
+            st.c_run += valid ? p * mt[m].w : 0.f;
+        }
+        st.l_run += p;
+        w[m] = x;
+    }
+    if (srow != nullptr) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s2[m][r], qc.cB, -st.cbm));
-            float w;
-            if (FULL) {
-                w = p * vs[r];
-                st.c_run = fmaf(p, vn[r], st.c_run);
-            } else {
-                const bool valid = tok0 + pm * PAGE + slot0 + r < ctx;
-                w = valid ? p * vs[r] : 0.f;
-                st.c_run += valid ? p * vn[r] : 0.f;
-            }
-            st.l_run += p;
-            wv[m][r] = w;
-            wmax = fmaxf(wmax, w);
+        for (int m = 0; m < 8; ++m) {
+            const int tok = tok0 + 16 * m + j;
+            if (FULL || tok < ctx) srow[tok] = s[m] * (qc.cB * LN2);
         }
     }
-    if (srow != nullptr && piece == 0) {
+    // ---- weight digits: X = round(w 2^F) < 2^16, four 4-bit digits per weight ----
+    // The p.v column scale of lane l covers k-block l/16 (32 tokens): tokens
+    // 16m + c with c in [8 (b % 2), 8 (b % 2) + 8) and m in [4 (b / 2), 4 (b / 2) + 4),
+    // so each lane takes the max of its first and last four weights over its
+    // half row, and F is set per head and 32-token block.
+    const float wlo = half_row_max8(fmaxf(fmaxf(w[0], w[1]), fmaxf(w[2], w[3])));
+    const float whi = half_row_max8(fmaxf(fmaxf(w[4], w[5]), fmaxf(w[6], w[7])));
+    const int FWlo = weight_exp(wlo), FWhi = weight_exp(whi);
+    const float wscale_lo = pow2f(FWlo), wscale_hi = pow2f(FWhi);
+    uint32_t X[8];
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 8; ++m)  // 2^23 + X in the bits of the fused multiply-add, X capped at 2^16 - 1
+        X[m] = min(__float_as_uint(fmaf(w[m], m < 4 ? wscale_lo : wscale_hi, 8388608.0f)), 0x4B00FFFFu);
+    uint32_t P[4];  // X of tokens m = 2k (bytes 0-1) and 2k + 1 (bytes 2-3)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tok = tok0 + (m >> 2) * PAGE + 16 * grp + 4 * (m & 3) + r;
-                if (FULL || tok < ctx) srow[tok] = s2[m][r] * (qc.cB * LN2);
-            }
+    for (int k = 0; k < 4; ++k) P[k] = __builtin_amdgcn_perm(X[2 * k + 1], X[2 * k], 0x05040100u);
+    uint32_t L[4], H[4];  // nibbles 0 and 2 (L), 1 and 3 (H) of each X, one per byte
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        L[k] = P[k] & 0x0F0F0F0Fu;
+        H[k] = (P[k] >> 4) & 0x0F0F0F0Fu;
     }
-    // ---- weight digits, per-head tile scale (lane l's scale byte serves row l%16) ----
-    wmax = fmaxf(wmax, __shfl_xor(wmax, 16));
-    wmax = fmaxf(wmax, __shfl_xor(wmax, 32));
-    const int ew = wmax > 0.f ? (int)((__float_as_uint(wmax) >> 23) & 0xFF) - 127 : 0;
-    const int FW = 18 - ew;  // w * 2^FW < 2^19
-    const float wscale = pow2f(FW);
+    // digit i of tokens m = 0..3 and m = 4..7, one byte per token
+    const uint32_t d0a = __builtin_amdgcn_perm(L[1], L[0], 0x06040200u), d0b = __builtin_amdgcn_perm(L[3], L[2], 0x06040200u);
+    const uint32_t d2a = __builtin_amdgcn_perm(L[1], L[0], 0x07050301u), d2b = __builtin_amdgcn_perm(L[3], L[2], 0x07050301u);
+    const uint32_t d1a = __builtin_amdgcn_perm(H[1], H[0], 0x06040200u), d1b = __builtin_amdgcn_perm(H[3], H[2], 0x06040200u);
+    const uint32_t d3a = __builtin_amdgcn_perm(H[1], H[0], 0x07050301u), d3b = __builtin_amdgcn_perm(H[3], H[2], 0x07050301u);
+    {
+        uint32_t* wd = lds.wdig;
+        wd[wdig_base(grp, 0) + j] = d0a; wd[wdig_base(grp, 0) + 16 + j] = d0b;
+        wd[wdig_base(grp, 1) + j] = d1a; wd[wdig_base(grp, 1) + 16 + j] = d1b;
+        wd[wdig_base(grp, 2) + j] = d2a; wd[wdig_base(grp, 2) + 16 + j] = d2b;
+        wd[wdig_base(grp, 3) + j] = d3a; wd[wdig_base(grp, 3) + 16 + j] = d3b;
+    }
+    // p.v operand of column j = 4h + i: k = 16 grp + s <- word 4 grp + s/4 byte s%4,
+    // k = 64 + 16 grp + s <- word 16 + 4 grp + s/4 byte s%4
     v8i wop;
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-        wop[m] = (int)pack4_fp8(digit_of(wv[m][0], wscale, piece), digit_of(wv[m][1], wscale, piece),
-                                digit_of(wv[m][2], wscale, piece), digit_of(wv[m][3], wscale, piece));
+    {
+        const int base = wdig_base(j >> 2, j & 3) + 4 * grp;
+        const uint4 lo = *reinterpret_cast<const uint4*>(&lds.wdig[base]);
+        const uint4 hi = *reinterpret_cast<const uint4*>(&lds.wdig[base + 16]);
+        wop[0] = (int)lo.x; wop[1] = (int)lo.y; wop[2] = (int)lo.z; wop[3] = (int)lo.w;
+        wop[4] = (int)hi.x; wop[5] = (int)hi.y; wop[6] = (int)hi.z; wop[7] = (int)hi.w;
+    }
+    // column scale of (column j = 4h + i, k-block grp): byte b of digit i is
+    // worth b 2^-9 and the code nibble is c / 2, so 2^(4i - F + 10)
+    const int fw_pair = __shfl((FWlo + 128) | ((FWhi + 128) << 16), 16 * (j >> 2) + 8 * (grp & 1));
+    const int scale_b = 137 + 4 * (j & 3) - (((fw_pair >> (16 * (grp >> 1))) & 0xFFFF) - 128);
     // ---- p.v ----
 #pragma unroll
     for (int c = 0; c < NB / 2; ++c) {
-        st.acc[2 * c] = mma_fp8_fp4(wop, fp4_operand(t.vc[c].x, t.vc[c].y), st.acc[2 * c], 127 - FW);
-        st.acc[2 * c + 1] = mma_fp8_fp4(wop, fp4_operand(t.vc[c].z, t.vc[c].w), st.acc[2 * c + 1], 127 - FW);
+        st.acc[2 * c] = mma_pv(fp4_operand(t.vc[c].x, t.vc[c].y), wop, st.acc[2 * c], scale_b);
+        st.acc[2 * c + 1] = mma_pv(fp4_operand(t.vc[c].z, t.vc[c].w), wop, st.acc[2 * c + 1], scale_b);
     }
 }
 
@@ -294,20 +346,21 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
 
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int j = l & 15, grp = l >> 4;
-    const int hh = j & 3;  // head of this lane's q.k column and p.v row
+    const int hq = j >> 2, iq = j & 3;  // this lane's q.k row: digit iq of head hq
 
-    __shared__ __align__(16) float2 meta_s[4][4][PAGE];  // per wave: K page 0, K page 1, V page 0, V page 1
+    __shared__ __align__(16) WaveLds lds_s[4];
     __shared__ float o_s[4][G][D];
-    __shared__ float ml_s[4][G][2];
+    __shared__ float ml_s[4][G][3];
 
-    // ---- query operand: 19-bit fixed point per head, digit (j >> 2) of head hh ----
-    const uint16_t* qrow = q + ((int64_t)e * Hq + g * G + hh) * D;
+    // ---- query operand: 19-bit fixed point per head, row 4 hq + iq = digit iq of head hq ----
+    const uint16_t* qrow = q + ((int64_t)e * Hq + g * G + hq) * D;
     float qv[NC][32];
     float amax = 0.f, qsum = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int s = 0; s < 32; ++s) {
+            // k of byte s; the K operand puts dim(k) at nibble k % 32 of lane group k / 32
             const int k = fp8_k(grp, s), ga = k >> 5, n = k & 31;
             const int dim = 32 * NC * ga + 32 * c + 16 * (n >> 4) + 2 * (n & 7) + ((n >> 3) & 1);
             const float x = bf16_to_f32(qrow[dim]);
@@ -319,21 +372,19 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     qsum += __shfl_xor(qsum, 16);
     qsum += __shfl_xor(qsum, 32);
-    const int ea = amax > 0.f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 : 0;
-    const int EQ = 18 - ea;  // |q * 2^EQ| < 2^19
+    const int EQ = 18 - (amax > 0.f ? exponent_of(amax) : 0);  // |q * 2^EQ| < 2^19
     const float qscale = pow2f(EQ);
-    const int qdig = j >> 2;
     QConst qc;
-    qc.qdig_w = pow2f(5 * (3 - qdig));
-    qc.cB = LOG2E * sm * pow2f(1 - EQ);  // sum_d q_d c_d = 2 * 2^-EQ * (digit sum)
-    qc.cAB = qsum * pow2f(EQ - 1);
+    qc.scale_a = 127 + 5 * (3 - iq) - EQ + 1;
+    qc.qsum = __shfl(qsum, 4 * grp);  // q.k result lanes hold head l/16
+    qc.cB = LOG2E * sm;
     v8i qop[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int v = 0; v < 8; ++v)
-            qop[c][v] = (int)pack4_fp8(digit_of(qv[c][4 * v], qscale, qdig), digit_of(qv[c][4 * v + 1], qscale, qdig),
-                                       digit_of(qv[c][4 * v + 2], qscale, qdig), digit_of(qv[c][4 * v + 3], qscale, qdig));
+            qop[c][v] = (int)pack4_fp8(digit_of(qv[c][4 * v], qscale, iq), digit_of(qv[c][4 * v + 1], qscale, iq),
+                                       digit_of(qv[c][4 * v + 2], qscale, iq), digit_of(qv[c][4 * v + 3], qscale, iq));
 
     WaveState<D> st;
 #pragma unroll
@@ -346,8 +397,8 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
     const int n_pages = (ctx + PAGE - 1) / PAGE;
-    float* srow = scores ? scores + ((int64_t)e * Hq + g * G + hh) * sstride : nullptr;
-    float2(*meta)[PAGE] = meta_s[wave];
+    float* srow = scores ? scores + ((int64_t)e * Hq + g * G + grp) * sstride : nullptr;
+    WaveLds& lds = lds_s[wave];
 
     // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
     const int pr_first = pg0 / 2 + wave;
@@ -378,7 +429,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
                          pv.pages + (int64_t)__builtin_amdgcn_readlane(pid1, tt) * pv.page_bytes + lhoff, l);
         };
         auto run = [&](const Tile<D>& tile, int t) {
-            compute_tile<D, true>(tile, meta, l, qop, qc, st, tok0_of(c0 + t), ctx, srow);
+            compute_tile<D, true>(tile, lds, l, qop, qc, st, tok0_of(c0 + t), ctx, srow);
         };
         load(ta, 0);
         load(tb, 1);
@@ -401,34 +452,24 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
         const int p1 = 2 * pair + 1 < n_pages ? 2 * pair + 1 : 2 * pair;
         load_tile<D>(ta, pv.pages + (int64_t)bt[2 * pair] * pv.page_bytes + lhoff,
                      pv.pages + (int64_t)bt[p1] * pv.page_bytes + lhoff, l);
-        compute_tile<D, false>(ta, meta, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
+        compute_tile<D, false>(ta, lds, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
     }
 
-    // ---- this wave's partial: sum weight digits (lane groups) and lanes' sums ----
-    float l_run = st.l_run, c_run = st.c_run;
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    c_run += __shfl_xor(c_run, 16);
-    c_run += __shfl_xor(c_run, 32);
-    float cr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) cr[r] = __shfl(c_run, (l & ~3) | r);
+    // ---- this wave's partial: sum the digit columns, and each head's lanes ----
+    const float l_run = row_sum16(st.l_run), c_run = row_sum16(st.c_run);  // head grp
+    if (j == 0) {
+        ml_s[wave][grp][0] = st.cbm;  // log2 units
+        ml_s[wave][grp][1] = l_run;
+        ml_s[wave][grp][2] = c_run;
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        float t[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            // digit row weight 32^(3 - grp), and 2 for the code/2 fp4 values
-            float v = st.acc[b][r] * pow2f(16 - 5 * grp);
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
-            t[r] = v + cr[r];
-        }
-        o_s[wave][grp][16 * b + j] = grp == 0 ? t[0] : grp == 1 ? t[1] : grp == 2 ? t[2] : t[3];
-    }
-    if (l < 4) {
-        ml_s[wave][l][0] = st.cbm;  // log2 units
-        ml_s[wave][l][1] = l_run;
+        float4 o;
+        o.x = quad_sum(st.acc[b][0]);
+        o.y = quad_sum(st.acc[b][1]);
+        o.z = quad_sum(st.acc[b][2]);
+        o.w = quad_sum(st.acc[b][3]);
+        if (iq == 0) *reinterpret_cast<float4*>(&o_s[wave][hq][16 * b + 4 * grp]) = o;
     }
     __syncthreads();
 
@@ -451,7 +492,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
             const int d = l + 64 * k;
             float o = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) o += f[v] * o_s[v][h][d];
+            for (int v = 0; v < 4; ++v) o += f[v] * (o_s[v][h][d] + ml_s[v][h][2]);
             w.o[row * D + d] = o;
         }
         if (l == 0) {

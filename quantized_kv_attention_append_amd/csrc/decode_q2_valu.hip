@@ -109,12 +109,9 @@ __global__ __launch_bounds__(256) void decode_q2_valu_kernel(PoolView pv, int la
             const uint32_t words[4] = {v0.x, v0.y, v1.x, v1.y};
             for (int j = 0; j < G; ++j) o[j] *= a_s[j];
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float c = (float)((words[w] >> (i < 8 ? 4 * i : 4 * (i - 8) + 2)) & 3u);
-                    for (int j = 0; j < G; ++j) o[j] += w_s[j][16 * w + i] * c;
-                }
+            for (int t = 0; t < PAGE; ++t) {
+                const float c = (float)((words[q2_vslot_word(t)] >> q2_vslot_bit(t)) & 3u);
+                for (int j = 0; j < G; ++j) o[j] += w_s[j][t] * c;
             }
         }
         __syncthreads();

@@ -44,6 +44,11 @@ __host__ __device__ constexpr int64_t q2_vmeta_off(int D) { return 32 * (int64_t
 __host__ __device__ constexpr int64_t q2_vword_off(int D, int d, int w) {
     return 8 * (int64_t)D * (w >> 1) + 16 * (16 * (d >> 5) + (d & 15)) + 8 * ((d >> 4) & 1) + 4 * (w & 1);
 }
+// Word (0..3) and bit of token slot s (0..63) among a dim's four V-code words:
+// slot 16b + 4w + r sits in word w at bit 16 (r % 2) + 4b + 2 (r / 2), so the
+// 0x33333333 mask of a word yields its eight slots with r < 2, one per nibble.
+__host__ __device__ constexpr int q2_vslot_word(int s) { return (s >> 2) & 3; }
+__host__ __device__ constexpr int q2_vslot_bit(int s) { return 16 * (s & 1) + 4 * (s >> 4) + 2 * ((s >> 1) & 1); }
 // Byte offsets inside an 8-bit (layer, head) block.
 __host__ __device__ constexpr int64_t q8_block_bytes(int D) { return 132 * (int64_t)D + 256; }
 __host__ __device__ constexpr int64_t q8_vcodes_off(int D) { return 64 * (int64_t)D; }

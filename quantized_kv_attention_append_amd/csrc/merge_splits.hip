@@ -1,25 +1,44 @@
 // Merge of the split-K decode partials: one workgroup per (sequence, query
-// head), one thread per output dim.
+// head), one thread per output dim.  Splits are taken eight at a time with all
+// of a group's loads issued before any is used, so a merge of up to eight
+// splits costs one round trip to memory.
 #include "decode_common.h"
 
 namespace kvq {
 
 __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq, int D, int splits,
                                                            const float* __restrict__ ws, float* __restrict__ out) {
+    constexpr int U = 8;
     const int e = blockIdx.x / Hq;
     const int d = threadIdx.x;
     const int live = live_splits(bd.pos[e], splits);
     const int64_t row = blockIdx.x;  // e * Hq + h
-    const float* ml = ws + (int64_t)bd.n * Hq * splits * D + row * splits * 2;
+    const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + row * splits;
     const float* o = ws + row * splits * D + d;
-    float M = -INFINITY;
-    for (int p = 0; p < live; ++p) M = fmaxf(M, ml[2 * p]);
-    float den = 0.f, acc = 0.f;
-#pragma unroll 4
-    for (int p = 0; p < live; ++p) {
-        const float f = exp2f(ml[2 * p] - M);
-        den += f * ml[2 * p + 1];
-        acc += f * __builtin_nontemporal_load(o + (int64_t)p * D);
+    // running (max, sum, output) over groups of U splits, in base-2 units
+    float M = -INFINITY, den = 0.f, acc = 0.f;
+    for (int p0 = 0; p0 < live; p0 += U) {
+        float2 m[U];
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = p0 + u < live;
+            m[u] = ok ? ml[p0 + u] : make_float2(-INFINITY, 0.f);
+            v[u] = ok ? __builtin_nontemporal_load(o + (int64_t)(p0 + u) * D) : 0.f;
+        }
+        float Mg = M;
+#pragma unroll
+        for (int u = 0; u < U; ++u) Mg = fmaxf(Mg, m[u].x);
+        const float r = exp2f(M - Mg);  // M = -inf on the first group: r = 0
+        den *= r;
+        acc *= r;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float f = exp2f(m[u].x - Mg);  // empty slots: exp2(-inf) = 0
+            den += f * m[u].y;
+            acc += f * v[u];
+        }
+        M = Mg;
     }
     out[row * D + d] = acc / den;
 }

@@ -61,20 +61,25 @@ def test_k_row_layout_positions():
 
 
 def test_v_row_word_layout_matches_loop():
-    """slot 16w+q (q<8) at bits 4q of word w; slot 16w+8+q at bits 4q+2."""
+    """slot 16b + 4w + r sits in word w at bit 16(r % 2) + 4b + 2(r // 2)."""
     rng = np.random.default_rng(23)
     c = rng.integers(0, 4, (7, 64)).astype(np.uint8)
     p = layout.pack2_vrow(c)
     for r in range(7):
         for w in range(4):
             word = 0
-            for q in range(8):
-                word |= int(c[r, 16 * w + q]) << (4 * q)
-                word |= int(c[r, 16 * w + 8 + q]) << (4 * q + 2)
+            for b in range(4):
+                for q in range(4):
+                    word |= int(c[r, 16 * b + 4 * w + q]) << (16 * (q % 2) + 4 * b + 2 * (q // 2))
             assert int.from_bytes(bytes(p[r, 4 * w:4 * w + 4]), "little") == word
-            nibbles_lo = [(word >> (4 * q)) & 0xF & 3 for q in range(8)]
-            assert nibbles_lo == list(c[r, 16 * w:16 * w + 8])
+            # nibble n of the 0x33333333 mask: slot 16 (n % 4) + 4w + n // 4 (r in {0, 1})
+            lo = [(word >> (4 * n)) & 3 for n in range(8)]
+            assert lo == [c[r, 16 * (n % 4) + 4 * w + n // 4] for n in range(8)]
+            hi = [(word >> (4 * n + 2)) & 3 for n in range(8)]
+            assert hi == [c[r, 16 * (n % 4) + 4 * w + 2 + n // 4] for n in range(8)]
     assert np.array_equal(layout.unpack2_vrow(p), c)
+    # every (word, bit) pair is used by exactly one slot
+    assert len({layout.v_slot_word_bit(s) for s in range(64)}) == 64
 
 
 def test_v_plane_word_offsets_tile_the_plane():
