@@ -204,7 +204,7 @@ struct WaveLds {
 };
 __device__ __forceinline__ int wdig_base(int h, int i) { return (4 * h + i) * 32 + 16 * h; }
 
-template <int D, bool FULL>
+template <int D, bool FULL, bool SCORES>
 __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int l, const v8i* qop,
                                              const QConst& qc, WaveState<D>& st, int tok0, int ctx,
                                              float* __restrict__ srow) {
@@ -266,7 +266,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
         st.l_run += p;
         w[m] = x;
     }
-    if (srow != nullptr) {
+    if constexpr (SCORES) {
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int tok = tok0 + 16 * m + j;
@@ -329,7 +329,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
     }
 }
 
-template <int D>
+template <int D, bool SCORES>
 __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                              const uint16_t* __restrict__ q, float sm, int splits,
                                                              float* __restrict__ ws, float* __restrict__ out,
@@ -351,6 +351,49 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     __shared__ __align__(16) WaveLds lds_s[4];
     __shared__ float o_s[4][G][D];
     __shared__ float ml_s[4][G][3];
+
+    const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
+    const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
+    const int n_pages = (ctx + PAGE - 1) / PAGE;
+    float* srow = scores ? scores + ((int64_t)e * Hq + g * G + grp) * sstride : nullptr;
+    WaveLds& lds = lds_s[wave];
+
+    // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
+    const int pr_first = pg0 / 2 + wave;
+    const int pr_end = (pg1 + 1) / 2;
+    const int T = pr_first < pr_end ? (pr_end - pr_first + 3) / 4 : 0;
+    // the last tile of the sequence may be partly past ctx; it is done on its own
+    const bool last_partial = T > 0 && 2 * (pr_first + 4 * (T - 1)) * PAGE + 2 * PAGE > ctx;
+    const int TF = last_partial ? T - 1 : T;  // full tiles
+    auto tok0_of = [&](int t) { return 2 * (pr_first + 4 * t) * PAGE; };
+
+    // Tiles go in chunks of 64: lane k of pid0/pid1 holds the physical ids of
+    // the two pages of tile c0 + k.  Two tile buffers keep one tile in flight
+    // while the other is computed; every load is issued unconditionally
+    // (indices clamped to the chunk's last tile, re-read from cache), and the
+    // loop runs whole two-tile rounds with fixed buffer roles so that no
+    // buffer is ever copied (a copy would wait for its load).
+    Tile<D> ta, tb;
+    int pid0 = 0, pid1 = 0, Tc = 0;
+    auto fetch_ids = [&](int c0) {
+        Tc = min(64, TF - c0);
+        pid0 = pid1 = 0;
+        if (l < Tc) {
+            const int pair = pr_first + 4 * (c0 + l);
+            pid0 = bt[2 * pair];
+            pid1 = bt[2 * pair + 1];
+        }
+    };
+    auto load = [&](Tile<D>& tile, int t) {
+        const int tt = min(t, Tc - 1);
+        load_tile<D>(tile, pv.pages + (int64_t)__builtin_amdgcn_readlane(pid0, tt) * pv.page_bytes + lhoff,
+                     pv.pages + (int64_t)__builtin_amdgcn_readlane(pid1, tt) * pv.page_bytes + lhoff, l);
+    };
+    // the first tile is in flight while the query operand is prepared
+    if (TF > 0) {
+        fetch_ids(0);
+        load(ta, 0);
+    }
 
     // ---- query operand: 19-bit fixed point per head, row 4 hq + iq = digit iq of head hq ----
     const uint16_t* qrow = q + ((int64_t)e * Hq + g * G + hq) * D;
@@ -394,65 +437,32 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     st.l_run = 0.f;
     st.c_run = 0.f;
 
-    const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
-    const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
-    const int n_pages = (ctx + PAGE - 1) / PAGE;
-    float* srow = scores ? scores + ((int64_t)e * Hq + g * G + grp) * sstride : nullptr;
-    WaveLds& lds = lds_s[wave];
-
-    // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
-    const int pr_first = pg0 / 2 + wave;
-    const int pr_end = (pg1 + 1) / 2;
-    const int T = pr_first < pr_end ? (pr_end - pr_first + 3) / 4 : 0;
-    // the last tile of the sequence may be partly past ctx; it is done on its own
-    const bool last_partial = T > 0 && 2 * (pr_first + 4 * (T - 1)) * PAGE + 2 * PAGE > ctx;
-    const int TF = last_partial ? T - 1 : T;  // full tiles
-    auto tok0_of = [&](int t) { return 2 * (pr_first + 4 * t) * PAGE; };
-
-    // Tiles go in chunks of 64: lane k of pid0/pid1 holds the physical ids of
-    // the two pages of tile c0 + k.  Three tile buffers rotate so that two
-    // tiles are in flight while one is computed; every load is issued
-    // unconditionally (indices clamped to the chunk's last tile, re-read from
-    // cache), so the count of loads in flight is the same on every path.
-    Tile<D> ta, tb, tc;
     for (int c0 = 0; c0 < TF; c0 += 64) {
-        const int Tc = min(64, TF - c0);
-        int pid0 = 0, pid1 = 0;
-        if (l < Tc) {
-            const int pair = pr_first + 4 * (c0 + l);
-            pid0 = bt[2 * pair];
-            pid1 = bt[2 * pair + 1];
+        if (c0 > 0) {
+            fetch_ids(c0);
+            load(ta, 0);
         }
-        auto load = [&](Tile<D>& tile, int t) {
-            const int tt = min(t, Tc - 1);
-            load_tile<D>(tile, pv.pages + (int64_t)__builtin_amdgcn_readlane(pid0, tt) * pv.page_bytes + lhoff,
-                         pv.pages + (int64_t)__builtin_amdgcn_readlane(pid1, tt) * pv.page_bytes + lhoff, l);
-        };
         auto run = [&](const Tile<D>& tile, int t) {
-            compute_tile<D, true>(tile, lds, l, qop, qc, st, tok0_of(c0 + t), ctx, srow);
+            compute_tile<D, true, SCORES>(tile, lds, l, qop, qc, st, tok0_of(c0 + t), ctx, srow);
         };
-        load(ta, 0);
-        load(tb, 1);
-        for (int t = 0; t < Tc; t += 3) {
-            load(tc, t + 2);
+        int t = 0;
+        for (; t + 2 <= Tc; t += 2) {
+            load(tb, t + 1);
             __builtin_amdgcn_sched_barrier(0);
             run(ta, t);
-            if (t + 1 >= Tc) break;
-            load(ta, t + 3);
+            load(ta, t + 2);
             __builtin_amdgcn_sched_barrier(0);
             run(tb, t + 1);
-            if (t + 2 >= Tc) break;
-            load(tb, t + 4);
-            __builtin_amdgcn_sched_barrier(0);
-            run(tc, t + 2);
         }
+        // at most one tile left, already loaded into ta
+        if (t < Tc) run(ta, t);
     }
     if (last_partial) {
         const int pair = pr_first + 4 * (T - 1);
         const int p1 = 2 * pair + 1 < n_pages ? 2 * pair + 1 : 2 * pair;
         load_tile<D>(ta, pv.pages + (int64_t)bt[2 * pair] * pv.page_bytes + lhoff,
                      pv.pages + (int64_t)bt[p1] * pv.page_bytes + lhoff, l);
-        compute_tile<D, false>(ta, lds, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
+        compute_tile<D, false, SCORES>(ta, lds, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
     }
 
     // ---- this wave's partial: sum the digit columns, and each head's lanes ----
@@ -509,12 +519,13 @@ hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, 
                             float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
     if (pv.Hq != 4 * pv.Hkv) return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, s);
     dim3 grid(bd.n * pv.Hkv, splits);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
+    };
     if (pv.D == 256)
-        hipLaunchKernelGGL(decode_q2_mfma_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out,
-                           scores, sstride);
+        scores ? go(decode_q2_mfma_kernel<256, true>) : go(decode_q2_mfma_kernel<256, false>);
     else
-        hipLaunchKernelGGL(decode_q2_mfma_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out,
-                           scores, sstride);
+        scores ? go(decode_q2_mfma_kernel<128, true>) : go(decode_q2_mfma_kernel<128, false>);
     const hipError_t err = hipGetLastError();
     return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }
