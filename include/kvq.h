@@ -144,10 +144,13 @@ kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t
  * over the exact rows present in the token's page) and written into slot
  * pos % 64 of page block_table[pos / 64].  No other slot of the pool changes,
  * except that an 8-bit append re-derives the K codes and channel scales of the
- * pages it touches.  The sequences of one call must be distinct.  Errors:
- * KV_ERR_ARG, KV_ERR_BOUND (a position beyond the reserved bound; nothing is
- * written), KV_ERR_UNSUPPORTED (more than KV_MAX_BATCH entries),
- * KV_ERR_DEVICE. */
+ * pages it touches.  8-bit appends are sequential per (sequence, layer):
+ * start_pos must equal the tokens already appended to that layer, because
+ * the exact K rows of the open page are kept only for the tokens appended so
+ * far.  The sequences of one call must be distinct.  Errors: KV_ERR_ARG
+ * (including a non-sequential 8-bit append), KV_ERR_BOUND (a position beyond
+ * the reserved bound; nothing is written), KV_ERR_UNSUPPORTED (more than
+ * KV_MAX_BATCH entries), KV_ERR_DEVICE. */
 kv_status kv_append_quant(kv_pool* pool, int32_t layer, int32_t n, const int32_t* seqs,
                           const int64_t* start_pos, const int32_t* n_new, const uint16_t* d_k,
                           const uint16_t* d_v, kv_stream_t stream);

@@ -1,0 +1,110 @@
+// Quantize-on-append for the 8-bit variant: V per token, K per channel over
+// the tokens present in the open page ("The KV cache and prompt reuse",
+// section "What a sequence is made of": the compressed format keeps a window
+// of exact recent keys; "Half the Cache, Twice the Context", section on
+// per-channel keys and per-token values, symmetric absmax at 127 levels).
+//
+//   V row x (one token, one KV head): s = max|x| / 127 (correctly rounded
+//     fp32), s == 0 -> 1, c_d = clamp(rint(x_d / s), -127, 127).
+//   K channel j of a page: s_j = max over the page's present tokens t of
+//     |k_tj| / 127, c_tj = clamp(rint(k_tj / s_j), -127, 127).
+// The exact bf16 K rows of the open page are kept in a staging page per
+// (sequence, layer, KV head); every append re-derives the codes of all the
+// page's present tokens and its channel scales from them, so a page that
+// reaches 64 tokens holds exactly the per-channel quantization of its 64
+// tokens.
+//
+// Block layout (D dims): K codes int8 token-major [64][D] at 0, V codes int8
+// dim-major [D][64] at 64D, K scales fp32 [D] at 128D, V scales fp32 [64] at
+// 132D.
+//
+// One workgroup of 256 threads per (sequence, page touched, KV head).  The
+// host never launches a page that reads staged rows together with a later
+// page of the same sequence that rewrites them (it splits such an append in
+// two launches), so staging reads and writes never race.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+template <int D>
+__global__ __launch_bounds__(256) void append_q8_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                        const uint16_t* __restrict__ kin,
+                                                        const uint16_t* __restrict__ vin) {
+#pragma clang fp contract(off)
+    constexpr int DPL = D / 64;  // dims per lane in a row-wide wave operation
+    const int x = blockIdx.x, head = blockIdx.y;
+    int e = 0;
+    while (e + 1 < bd.n && bd.work0[e + 1] <= x) ++e;
+    const int start = bd.pos[e], cnt = bd.cnt[e];
+    const int lp = start / PAGE + (x - bd.work0[e]);
+    const int slot_lo = max(start, lp * PAGE) - lp * PAGE;
+    const int slot_hi = min(start + cnt, (lp + 1) * PAGE) - lp * PAGE;
+    const int phys = pv.bt[(int64_t)bd.seq[e] * pv.bt_stride + lp];
+    uint8_t* blk = pv.pages + (int64_t)phys * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
+    uint16_t* stage = pv.stage + ((((int64_t)bd.seq[e] * pv.L + layer) * pv.Hkv + head) * PAGE) * D;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    auto in_row = [&](int s) { return ((int64_t)bd.row0[e] + (lp * PAGE + s - start)) * pv.Hkv + head; };
+
+    // exact K rows of slots [0, slot_hi) as bf16 bits: earlier slots from the
+    // staging page, the new ones from the input
+    __shared__ uint16_t k_s[PAGE][D];
+    for (int i = tid; i < slot_hi * D; i += 256) {
+        const int s = i / D, d = i - s * D;
+        k_s[s][d] = s < slot_lo ? stage[(int64_t)s * D + d] : kin[in_row(s) * D + d];
+    }
+    __syncthreads();
+    // the page stays open: keep its new exact rows for the next append
+    if (slot_hi < PAGE)
+        for (int i = tid; i < (slot_hi - slot_lo) * D; i += 256) {
+            const int s = slot_lo + i / D, d = i % D;
+            stage[(int64_t)s * D + d] = k_s[s][d];
+        }
+
+    // ---- K: per-channel scales and the codes of every present token ----
+    int8_t* kc = reinterpret_cast<int8_t*>(blk);
+    float* ks = reinterpret_cast<float*>(blk + q8_kscale_off(D));
+    for (int d = tid; d < D; d += 256) {
+        float amax = 0.f;
+        for (int s = 0; s < slot_hi; ++s) amax = fmaxf(amax, fabsf(bf16_to_f32(k_s[s][d])));
+        float sc = amax / 127.0f;
+        if (sc == 0.0f) sc = 1.0f;
+        ks[d] = sc;
+        for (int s = 0; s < slot_hi; ++s) {
+            const float c = fminf(fmaxf(rintf(bf16_to_f32(k_s[s][d]) / sc), -127.0f), 127.0f);
+            kc[s * D + d] = (int8_t)c;
+        }
+    }
+
+    // ---- V: per-token scale, codes dim-major; wave w takes slots w, w+4, ... ----
+    int8_t* vc = reinterpret_cast<int8_t*>(blk + q8_vcodes_off(D));
+    float* vs = reinterpret_cast<float*>(blk + q8_vscale_off(D));
+    for (int s = slot_lo + wave; s < slot_hi; s += 4) {
+        float xv[DPL];
+        load_bf16<DPL>(vin + in_row(s) * D + lane * DPL, xv);
+        float amax = 0.f;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) amax = fmaxf(amax, fabsf(xv[k]));
+        amax = wave_max(amax);
+        float sc = amax / 127.0f;
+        if (sc == 0.0f) sc = 1.0f;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            const float c = fminf(fmaxf(rintf(xv[k] / sc), -127.0f), 127.0f);
+            vc[(lane * DPL + k) * PAGE + s] = (int8_t)c;
+        }
+        if (lane == 0) vs[s] = sc;
+    }
+}
+
+hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, int work_items, const uint16_t* k,
+                            const uint16_t* v, hipStream_t s) {
+    dim3 grid(work_items, pv.Hkv);
+    if (pv.D == 256)
+        hipLaunchKernelGGL(append_q8_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+    else
+        hipLaunchKernelGGL(append_q8_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -84,6 +84,7 @@ struct kv_pool {
         bool live = false;
         int64_t bound = 0;     // reserved tokens
         int64_t appended = 0;  // highest position appended + 1, over all layers
+        std::vector<int64_t> layer_appended;  // 8-bit pools: tokens appended per layer (appends are sequential)
         std::vector<int32_t> pages;
     };
     std::vector<Seq> seqs;
@@ -285,6 +286,7 @@ kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, i
     s.live = true;
     s.bound = max_tokens;
     s.appended = 0;
+    s.layer_appended.assign(p->fmt == KV_FMT_Q8 ? (size_t)p->geom.n_layers : 0, 0);
     s.pages = std::move(got);
     *seq = slot;
     return KV_OK;
@@ -358,6 +360,12 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
         if (n_new[i] < 0 || start_pos[i] < 0) return fail(KV_ERR_ARG, "entry %d: negative position or count", i);
         kv_status s = check_seq(p, seqs[i], start_pos[i] + n_new[i], "append");
         if (s != KV_OK) return s;
+        if (p->fmt == KV_FMT_Q8 && start_pos[i] != p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer])
+            return fail(KV_ERR_ARG,
+                        "entry %d: 8-bit appends are sequential per layer (sequence %d layer %d holds %lld tokens, "
+                        "append starts at %lld)",
+                        i, seqs[i], layer, (long long)p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer],
+                        (long long)start_pos[i]);
         for (int j = 0; j < i; ++j)
             if (seqs[j] == seqs[i]) return fail(KV_ERR_ARG, "sequence %d appears twice in one append", seqs[i]);
         bd.seq[i] = seqs[i];
@@ -371,13 +379,45 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
     }
     bd.work0[n] = (int32_t)work;
     if (work == 0) return KV_OK;
-    hipError_t e = p->fmt == KV_FMT_Q2
-                       ? launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream)
-                       : launch_append_q8(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+    hipError_t e = hipSuccess;
+    if (p->fmt == KV_FMT_Q2) {
+        e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+    } else {
+        // An 8-bit append that starts inside a page reads that page's staged
+        // exact K rows; if it also runs past the page, its last page rewrites
+        // the staging rows.  Such appends go in two launches: every entry's
+        // first page, then the rest.
+        bool split = false;
+        for (int i = 0; i < n; ++i)
+            if (bd.pos[i] % PAGE != 0 && bd.pos[i] / PAGE != (bd.pos[i] + bd.cnt[i] - 1) / PAGE) split = true;
+        if (!split) {
+            e = launch_append_q8(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+        } else {
+            BatchDesc b1 = bd, b2 = bd;
+            int64_t w1 = 0, w2 = 0;
+            for (int i = 0; i < n; ++i) {
+                const int first = bd.cnt[i] > 0 ? std::min(bd.cnt[i], PAGE - bd.pos[i] % PAGE) : 0;
+                b1.cnt[i] = first;
+                b1.work0[i] = (int32_t)w1;
+                w1 += first > 0 ? 1 : 0;
+                b2.pos[i] = bd.pos[i] + first;
+                b2.cnt[i] = bd.cnt[i] - first;
+                b2.row0[i] = bd.row0[i] + first;
+                b2.work0[i] = (int32_t)w2;
+                if (b2.cnt[i] > 0) w2 += (b2.pos[i] + b2.cnt[i] - 1) / PAGE - b2.pos[i] / PAGE + 1;
+            }
+            b1.work0[n] = (int32_t)w1;
+            b2.work0[n] = (int32_t)w2;
+            if (w1 > 0) e = launch_append_q8(p->view(), layer, b1, (int)w1, d_k, d_v, (hipStream_t)stream);
+            if (e == hipSuccess && w2 > 0)
+                e = launch_append_q8(p->view(), layer, b2, (int)w2, d_k, d_v, (hipStream_t)stream);
+        }
+    }
     if (e != hipSuccess) return hip_fail(e, "append launch");
     for (int i = 0; i < n; ++i) {
         auto& s = p->seqs[(size_t)seqs[i]];
         s.appended = std::max<int64_t>(s.appended, start_pos[i] + n_new[i]);
+        if (p->fmt == KV_FMT_Q8) s.layer_appended[(size_t)layer] = start_pos[i] + n_new[i];
     }
     return KV_OK;
 }

@@ -1,13 +1,6 @@
 // Entry points whose kernels are not built yet report hipErrorNotSupported.
 #include "kvq_internal.h"
 namespace kvq {
-hipError_t launch_append_q8(const PoolView&, int, const BatchDesc&, int, const uint16_t*, const uint16_t*, hipStream_t) {
-    return hipErrorNotSupported;
-}
-hipError_t launch_decode_q8(const PoolView&, int, const BatchDesc&, const uint16_t*, float, int, float*, float*, float*,
-                            int64_t, hipStream_t) {
-    return hipErrorNotSupported;
-}
 hipError_t launch_prefill_q2(const PoolView&, int, int, int, int, const uint16_t*, float, int, float*, float*,
                              hipStream_t) {
     return hipErrorNotSupported;

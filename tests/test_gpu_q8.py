@@ -1,0 +1,185 @@
+"""GPU parity, 8-bit format: append bit-exact against the oracle's pool image
+(per-token V, per-channel K over the exact rows of the open page), decode
+within tolerance of the fp64 oracle, and the 24-lane, 32-layer workload
+(8 KV heads x 128 dims, 32 query heads, lengths 64 * U[16, 128]) with one more
+token appended per lane after the first decode."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, pool as opool
+from synth import CONFIGS, Workload, c4_lengths, kv_rows, page_permutation, queries
+from tests.gpu_helpers import assert_close, geom_of, make_pool, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+C4 = CONFIGS[4]
+# 2 layers of the 8-bit geometry, 3 lanes
+SMALL8 = Workload(91, "small 8-bit geometry", "q8", 2, 8, 128, 32, 3, 300)
+# a D = 256, group-2 geometry on the 8-bit format
+SMALL8_256 = Workload(92, "small 8-bit D=256 geometry", "q8", 1, 4, 256, 8, 2, 200)
+
+
+def _setup(w, lens, n_pages, salt=0, fill=0xA5):
+    import quantized_kv_attention_append_amd as kvq
+    pool, mem = make_pool(w, n_pages, kvq.FMT_Q8, fill=fill)
+    perm = page_permutation(w, n_pages, salt=salt)
+    bts, seqs, off = [], [], 0
+    for L in lens:
+        npg = -(-L // 64)
+        bts.append(perm[off:off + npg])
+        off += npg
+        seqs.append(pool.reserve(L, pages=bts[-1]))
+    op = opool.OraclePool("q8", w.n_layers, w.n_kv_heads, w.head_dim, n_pages, fill=fill)
+    return pool, mem, op, bts, seqs
+
+
+def _append_chunks(pool, op, layer, seqs, bts, chunks, ks, vs, starts):
+    """chunks: list of [(seq index, n), ...]; each inner list is one batched append."""
+    for chunk in chunks:
+        sq, st, nn, kk, vv = [], [], [], [], []
+        for i, n in chunk:
+            s0 = starts[i]
+            sq.append(seqs[i]); st.append(s0); nn.append(n)
+            kk.append(ks[i][s0:s0 + n]); vv.append(vs[i][s0:s0 + n])
+            op.append(layer, i, bts[i], s0, ks[i][s0:s0 + n].float().numpy(), vs[i][s0:s0 + n].float().numpy())
+            starts[i] += n
+        pool.append(layer, sq, st, nn, torch.cat(kk).cuda(), torch.cat(vv).cuda())
+
+
+def test_append_q8_bit_exact_ragged():
+    need_gpu()
+    w = SMALL8
+    lens = [300, 130, 64]
+    pool, mem, op, bts, seqs = _setup(w, lens, 12)
+    for layer in range(w.n_layers):
+        ks = [kv_rows(w, layer, i, lens[i])[0] for i in range(3)]
+        vs = [kv_rows(w, layer, i, lens[i])[1] for i in range(3)]
+        starts = [0, 0, 0]
+        chunks = [[(0, 37), (1, 1), (2, 64)],   # mid-page end, single token, one full page
+                  [(0, 1)], [(0, 1)],             # decode-style single tokens into the open page
+                  [(0, 150), (1, 70)],            # from mid-page across pages: two launches
+                  [(0, 111), (1, 59)]]            # lane 0 crosses again, lane 1 fills to 130
+        _append_chunks(pool, op, layer, seqs, bts, chunks, ks, vs, starts)
+        assert starts == lens
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(12, -1)
+    diff = np.count_nonzero(got != op.data)
+    say(f"8-bit ragged append: {diff} differing bytes of {got.size}")
+    assert diff == 0
+
+
+def test_append_q8_d256_and_dequant():
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    w = SMALL8_256
+    lens = [200, 65]
+    pool, mem, op, bts, seqs = _setup(w, lens, 6, salt=3)
+    ks = [kv_rows(w, 0, i, lens[i])[0] for i in range(2)]
+    vs = [kv_rows(w, 0, i, lens[i])[1] for i in range(2)]
+    starts = [0, 0]
+    _append_chunks(pool, op, 0, seqs, bts, [[(0, 5), (1, 64)], [(0, 195), (1, 1)]], ks, vs, starts)
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(6, -1)
+    assert np.count_nonzero(got != op.data) == 0
+    # page dequantization equals the oracle's single-product dequantization
+    K, V = op.gather(0, bts[0], 200)
+    for lp in (0, 3):
+        n = min(64, 200 - 64 * lp)
+        for h in (0, 3):
+            gk = pool.dequant_page(int(bts[0][lp]), 0, h, 0).cpu().numpy()[:n]
+            gv = pool.dequant_page(int(bts[0][lp]), 0, h, 1).cpu().numpy()[:n]
+            assert np.array_equal(gk.view(np.uint32), K[64 * lp:64 * lp + n, h].view(np.uint32))
+            assert np.array_equal(gv.view(np.uint32), V[64 * lp:64 * lp + n, h].view(np.uint32))
+    assert kvq.FMT_Q8 == 2
+
+
+def test_append_q8_must_be_sequential():
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    w = SMALL8
+    pool, mem, op, bts, seqs = _setup(w, [128], 4)
+    k, v = kv_rows(w, 0, 0, 128)
+    pool.append(0, [seqs[0]], [0], [10], k[:10].cuda(), v[:10].cuda())
+    before = mem.clone()
+    with pytest.raises(kvq.KvError) as ei:
+        pool.append(0, [seqs[0]], [20], [5], k[20:25].cuda(), v[20:25].cuda())   # gap
+    assert ei.value.name == "KV_ERR_ARG"
+    with pytest.raises(kvq.KvError) as ei:
+        pool.append(1, [seqs[0]], [10], [5], k[10:15].cuda(), v[10:15].cuda())   # layer 1 holds 0 tokens
+    assert ei.value.name == "KV_ERR_ARG"
+    torch.cuda.synchronize()
+    assert torch.equal(mem, before)
+
+
+@pytest.mark.parametrize("w,lens", [(SMALL8, [300, 130, 64]), (SMALL8_256, [200, 65])])
+def test_decode_q8_small(w, lens):
+    need_gpu()
+    n_pages = sum(-(-L // 64) for L in lens) + 2
+    pool, mem, op, bts, seqs = _setup(w, lens, n_pages, salt=11)
+    layer = w.n_layers - 1
+    ks = [kv_rows(w, layer, i, L)[0] for i, L in enumerate(lens)]
+    vs = [kv_rows(w, layer, i, L)[1] for i, L in enumerate(lens)]
+    starts = [0] * len(lens)
+    _append_chunks(pool, op, layer, seqs, bts, [[(i, L) for i, L in enumerate(lens)]], ks, vs, starts)
+    q = queries(w, layer, len(lens))
+    ctxs = [L - 3 for L in lens]   # ragged: the last page is read partly
+    for sp in (1, 2, 0):
+        scores = torch.full((len(lens), w.n_q_heads, max(ctxs)), float("nan"), device="cuda")
+        ws = torch.full((pool.workspace_bytes(0, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = pool.decode(layer, seqs, ctxs, q.cuda(), w.sm_scale, n_splits=sp, ws=ws, scores=scores)
+        torch.cuda.synchronize()
+        for i, c in enumerate(ctxs):
+            K, V = op.gather(layer, bts[i], c)
+            qi = q[i].float().numpy()
+            assert_close(out[i].cpu().numpy(), attention.decode(qi, K, V, w.sm_scale), f"8-bit lane {i} ctx={c} splits={sp}")
+            assert_close(scores[i, :, :c].cpu().numpy(), attention.scores(qi, K, w.sm_scale),
+                         f"8-bit scores lane {i}", rel_l2=1e-5)
+
+
+@pytest.mark.timeout(600)
+def test_c4_workload_decode_then_append():
+    """Full 8-bit workload: populate 32 layers x 24 lanes, decode every layer,
+    append one token per lane, decode again; sampled (layer, lane) pairs against
+    the oracle, both decodes."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    w = C4
+    lens = c4_lengths(w)
+    geom = geom_of(w)
+    _, pb = kvq.token_bytes(geom, kvq.FMT_Q8)
+    n_pages = int(sum(-(-(int(L) + 1) // 64) for L in lens))
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q8, max_seqs=w.lanes, max_seq_tokens=int(lens.max()) + 64)
+    perm = page_permutation(w, n_pages)
+    seqs, off = [], 0
+    for L in lens:
+        npg = -(-(int(L) + 1) // 64)
+        seqs.append(pool.reserve(int(L) + 1, pages=perm[off:off + npg]))
+        off += npg
+    say(f"8-bit workload: {n_pages} pages, {n_pages * pb / 1e9:.2f} GB, lengths {lens.min()}..{lens.max()}")
+    B = w.lanes
+    ws = torch.empty(pool.workspace_bytes(0, B, 0), dtype=torch.uint8, device="cuda")
+    samples = {(0, 0), (13, 7), (31, 23), (31, int(np.argmax(lens)))}
+    for layer in range(w.n_layers):
+        kv = [kv_rows(w, layer, i, int(lens[i]) + 1, device="cuda") for i in range(B)]
+        pool.append(layer, seqs, [0] * B, [int(L) for L in lens],
+                    torch.cat([k[:L] for (k, _), L in zip(kv, lens)]), torch.cat([v[:L] for (_, v), L in zip(kv, lens)]))
+        q = queries(w, layer, B, device="cuda")
+        out1 = pool.decode(layer, seqs, [int(L) for L in lens], q, w.sm_scale, ws=ws).cpu()
+        pool.append(layer, seqs, [int(L) for L in lens], [1] * B,
+                    torch.cat([k[L:L + 1] for (k, _), L in zip(kv, lens)]),
+                    torch.cat([v[L:L + 1] for (_, v), L in zip(kv, lens)]))
+        out2 = pool.decode(layer, seqs, [int(L) + 1 for L in lens], q, w.sm_scale, ws=ws).cpu()
+        for (sl, lane) in samples:
+            if sl != layer:
+                continue
+            k, v = (t.cpu().float().numpy() for t in kv[lane])
+            qi = q[lane].float().cpu().numpy()
+            L = int(lens[lane])
+            K, V = opool.dequantized_rows("q8", k[:L], v[:L])
+            assert_close(out1[lane].numpy(), attention.decode(qi, K, V, w.sm_scale), f"8-bit layer {layer} lane {lane} ctx {L}")
+            K, V = opool.dequantized_rows("q8", k, v)
+            assert_close(out2[lane].numpy(), attention.decode(qi, K, V, w.sm_scale),
+                         f"8-bit layer {layer} lane {lane} ctx {L + 1} after append")
+        del kv
