@@ -159,8 +159,9 @@ enum { KV_OP_DECODE = 0, KV_OP_PREFILL = 1 };
 
 /* Workspace bytes for an attention call: decode with n_rows sequences, or
  * prefill with n_rows chunk queries, and n_splits splits of the context.
- * n_splits = 0 asks for enough bytes for any split count the library picks
- * by itself (decode: up to 256; prefill: 1). */
+ * n_splits = 0 asks for enough bytes for the split count the library picks
+ * by itself (decode: any count up to 256; prefill: the count it picks for
+ * n_rows queries, about one workgroup per compute unit). */
 kv_status kv_workspace_bytes(const kv_pool* pool, int32_t op, int32_t n_rows, int32_t n_splits, int64_t* bytes);
 
 /* Split-count the library picks for a decode batch when n_splits = 0. */
@@ -185,10 +186,17 @@ kv_status kv_attn_decode(kv_pool* pool, int32_t layer, int32_t n, const int32_t*
 
 /* Causal prefill of a chunk of n_q queries of one sequence that sit at
  * positions q_start .. q_start + n_q - 1, after the chunk's own K/V have been
- * appended: query i attends to tokens 0 .. q_start + i, all read from the
- * compressed pool.  d_q: bf16 [n_q][Hq][D]; d_out: fp32 [n_q][Hq][D].  The
- * workspace needs no clearing: every byte read is written first.  Errors as
- * for decode. */
+ * appended ("KV at 9 KB a token", opening section: prefill attention reads
+ * the compressed cache): query i attends to tokens 0 .. q_start + i, all read
+ * from the compressed pool, 2-bit pools only.  Scores are sm_scale x q.k^,
+ * softmax and sums in fp32; both contractions run on bf16 matrix cores with
+ * exact code operands and 16-bit softmax weights.  The keys of each block of
+ * queries are split into n_splits ranges (1..64, 0 = the library's choice)
+ * whose partials go to d_ws and are merged by a second kernel.
+ * d_q: bf16 [n_q][Hq][D]; d_out: fp32 [n_q][Hq][D].  The workspace needs no
+ * clearing: every byte read is written first within the call.  Errors:
+ * KV_ERR_ARG, KV_ERR_BOUND, KV_ERR_FORMAT (an 8-bit pool), KV_ERR_WORKSPACE,
+ * KV_ERR_DEVICE. */
 kv_status kv_attn_prefill(kv_pool* pool, int32_t layer, int32_t seq, int64_t q_start, int32_t n_q,
                           const uint16_t* d_q, float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes,
                           float* d_out, kv_stream_t stream);

@@ -435,7 +435,7 @@ kv_status kv_workspace_bytes(const kv_pool* p, int32_t op, int32_t n_rows, int32
         int sp = n_splits > 0 ? n_splits : 256;
         *bytes = 4 * decode_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
     } else if (op == KV_OP_PREFILL) {
-        int sp = n_splits > 0 ? n_splits : 1;
+        int sp = n_splits > 0 ? n_splits : (n_rows > 0 ? prefill_auto_splits(n_rows, p->geom.n_q_heads, p->geom.n_kv_heads) : 1);
         *bytes = 4 * prefill_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
     } else {
         return fail(KV_ERR_ARG, "unknown op %d", op);
@@ -489,7 +489,7 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
     kv_status st = check_seq(p, seq, q_start + n_q, "prefill");
     if (st != KV_OK) return st;
     if (n_splits < 0 || n_splits > 64) return fail(KV_ERR_ARG, "n_splits %d out of range", n_splits);
-    int sp = n_splits > 0 ? n_splits : 1;
+    int sp = n_splits > 0 ? n_splits : prefill_auto_splits(n_q, p->geom.n_q_heads, p->geom.n_kv_heads);
     int64_t need = 4 * prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim, sp);
     if (!d_ws || ws_bytes < need)
         return fail(KV_ERR_WORKSPACE, "prefill needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);

@@ -68,6 +68,8 @@ hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, 
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_prefill_q2(const PoolView& pv, int layer, int seq, int q_start, int n_q, const uint16_t* q,
                              float sm, int splits, float* ws, float* out, hipStream_t s);
+// Split count a prefill of n_q chunk queries takes when the caller passes 0.
+int prefill_auto_splits(int n_q, int Hq, int Hkv);
 hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,
                                hipStream_t s);
 

@@ -1,0 +1,387 @@
+// Chunked causal prefill over the 2-bit pool: the chunk's queries attend to
+// the prior tokens and to the chunk itself, every key and value read from the
+// compressed pages ("KV at 9 KB a token", opening section: prefill attention
+// reads the compressed cache directly, and every workspace byte a launch reads
+// it wrote first).
+//
+// Query i of the chunk sits at position q_start + i and sees keys
+// 0 .. q_start + i (inclusive).  Scores are sm q.k^ with the dequantization
+// folded algebraically (q.k^_t = min_t sum(q) + scale_t q.c_t); the online
+// softmax and every sum are fp32 (the two-level accumulation of "Half the
+// Cache, Twice the Context", section "The cliff is in the accumulator").
+//
+// Both contractions run on v_mfma_f32_16x16x32_bf16:
+//   * codes 0..3 and the bf16 query are exact bf16 operands, so q.c is exact
+//     up to the fp32 sum;
+//   * the softmax weights w = p scale_v are split into two bf16 terms
+//     (w truncated to bf16, then the truncated residual), 16 significant bits.
+// The score tile is computed transposed, S^T = K~ Q^T (rows = keys, columns =
+// 16 (query, head) rows), so that the lane holding keys 4g..4g+3 and
+// 16+4g..16+4g+3 of a 32-key step already holds the p.v operand
+// O^T = V~ P^T for the k-slots 8g..8g+7: no transpose of P is needed.
+//
+// One workgroup of four waves per (KV head, block of 128 / G queries, split of
+// the keys).  Each wave owns two 16-column blocks of (query, head) rows (128
+// rows per workgroup); every page of 64 keys is converted once per workgroup
+// from the packed codes into bf16 LDS tiles (double-buffered, the next page
+// converted while the current one is multiplied):
+//   K~[key][kappa]  kappa = order of dims in which dim pairs (16u + k,
+//                   16u + k + 8) are adjacent (one 2-bit word -> eight bf16
+//                   pairs with a byte-permute lookup);
+//   V~[dim][key]    natural key order.
+// Partials (m, l, o) of every row go to the workspace; prefill_merge_kernel
+// merges, for each row, the splits whose first key it can see.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int NCB = 2;            // 16-column blocks per wave
+constexpr int ROWS = 4 * NCB * 16;  // (query, head) rows per workgroup
+constexpr int KROW = 16;          // padding of a K~ row, bf16 elements (32 B)
+constexpr int VROW = 8;           // padding of a V~ row, bf16 elements
+
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Two 2-bit codes at bits 0-1 and 16-17 of x -> a dword of two bf16 values
+// (code c -> 0, 1, 2, 3 = 0x0000, 0x3F80, 0x4000, 0x4040), by a byte-permute
+// lookup whose selector bytes are 2c and 2c + 1.
+__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t x) {
+    return __builtin_amdgcn_perm(0x40404000u, 0x3F800000u, x * 0x202u + 0x01000100u);
+}
+// kappa index -> dim: kappa = 16u + 2k + e holds dim 16u + k + 8e
+__device__ __forceinline__ int kappa_dim(int kappa) { return (kappa & ~15) + ((kappa & 1) << 3) + ((kappa & 15) >> 1); }
+// fp32 -> bf16 by truncation, and the truncated residual, packed for two values
+__device__ __forceinline__ void split_hi_lo(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    const float ra = a - __uint_as_float(ua & 0xFFFF0000u), rb = b - __uint_as_float(ub & 0xFFFF0000u);
+    hi = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+    lo = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+}
+
+}  // namespace
+
+template <int D>
+struct PrefillLds {
+    static constexpr int KS = D + KROW;
+    static constexpr int VS = PAGE + VROW;
+    uint16_t k[2][PAGE * KS];  // K~, two buffers
+    uint16_t v[2][D * VS];     // V~, two buffers
+    float4 meta[2][PAGE];      // {k scale, k min, v scale, v min} per key
+};
+
+// Packed codes of one page held by a thread between its load and its conversion.
+template <int D>
+struct PackedPage {
+    static constexpr int NW = D / 64;  // K words and V words per thread
+    uint32_t k[NW];
+    uint32_t v[NW];
+    uint4 meta;  // threads < 64: {k scale, k min, v scale, v min} of key tid
+};
+
+template <int D>
+__device__ __forceinline__ void load_packed(PackedPage<D>& pk, const uint8_t* blk, int tid) {
+    constexpr int NW = PackedPage<D>::NW, KW = D / 16;  // code words per K row
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int item = tid + 256 * i;  // K: (key, word)
+        pk.k[i] = *reinterpret_cast<const uint32_t*>(blk + (item / KW) * (D / 4) + 4 * (item % KW));
+        const int d = item >> 2, w = item & 3;  // V: (dim, word)
+        pk.v[i] = *reinterpret_cast<const uint32_t*>(blk + q2_vcodes_off(D) + q2_vword_off(D, d, w));
+    }
+    if (tid < PAGE) {
+        const float2 km = *reinterpret_cast<const float2*>(blk + q2_kmeta_off(D) + 8 * tid);
+        const float2 vm = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * tid);
+        pk.meta = make_uint4(__float_as_uint(km.x), __float_as_uint(km.y), __float_as_uint(vm.x), __float_as_uint(vm.y));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid) {
+    constexpr int NW = PackedPage<D>::NW, KW = D / 16, KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int item = tid + 256 * i;
+        // K word u of key t: dims 16u..16u+15 -> kappa 16u + 2k + e = dim 16u + k + 8e
+        {
+            const int t = item / KW, u = item % KW;
+            const uint32_t w = pk.k[i];
+            uint32_t o[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = codes_to_bf16x2((w >> (2 * k)) & 0x00030003u);
+            uint4* dst = reinterpret_cast<uint4*>(&L.k[buf][t * KS + 16 * u]);
+            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+        // V word w of dim d: slot 16b + 4w + r at bit 16(r % 2) + 4b + 2(r / 2)
+        {
+            const int d = item >> 2, wi = item & 3;
+            const uint32_t w = pk.v[i];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t lo = codes_to_bf16x2((w >> (4 * b)) & 0x00030003u);      // slots r = 0, 1
+                const uint32_t hi = codes_to_bf16x2((w >> (4 * b + 2)) & 0x00030003u);  // slots r = 2, 3
+                *reinterpret_cast<uint2*>(&L.v[buf][d * VS + 16 * b + 4 * wi]) = make_uint2(lo, hi);
+            }
+        }
+    }
+    if (tid < PAGE) L.meta[buf][tid] = make_float4(__uint_as_float(pk.meta.x), __uint_as_float(pk.meta.y),
+                                                   __uint_as_float(pk.meta.z), __uint_as_float(pk.meta.w));
+}
+
+// Pages [pg0, pg1) of split sp for a block whose last query sits at pos_max.
+__device__ __forceinline__ void prefill_split_range(int pos_max, int splits, int sp, int* pg0, int* pg1) {
+    const int n_pages = pos_max / PAGE + 1;
+    const int per = (n_pages + splits - 1) / splits;
+    *pg0 = min(sp * per, n_pages);
+    *pg1 = min(sp * per + per, n_pages);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer, int seq, int q_start, int n_q,
+                                                         const uint16_t* __restrict__ q, float sm, int splits,
+                                                         float* __restrict__ ws) {
+    constexpr int KSTEPS = D / 32, DB = D / 16;
+    constexpr int KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
+    const int Hkv = pv.Hkv, Hq = pv.Hq, G = Hq / Hkv;
+    const int QB = ROWS / G;  // queries per workgroup
+    const int g = blockIdx.x % Hkv, qb = blockIdx.x / Hkv, sp = blockIdx.y;
+    const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, j = l & 15, grp = l >> 4;
+    const int q_first = qb * QB;
+    const int pos_max = q_start + min(q_first + QB, n_q) - 1;
+    int pg0, pg1;
+    prefill_split_range(pos_max, splits, sp, &pg0, &pg1);
+    if (pg0 >= pg1) return;
+
+    __shared__ __align__(16) PrefillLds<D> L;
+
+    const int32_t* bt = pv.bt + (int64_t)seq * pv.bt_stride;
+    const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
+    auto block_of = [&](int pg) { return pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff; };
+
+    PackedPage<D> pk;
+    load_packed<D>(pk, block_of(pg0), tid);
+
+    // ---- this lane's rows: column j of block cb = (query, head) ----
+    int qi[NCB], pos[NCB];
+    bool live[NCB];
+    float qsum[NCB];
+    bf16x8 qop[NCB][KSTEPS];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int col = 16 * (NCB * wave + cb) + j;
+        qi[cb] = q_first + col / G;
+        live[cb] = qi[cb] < n_q;
+        pos[cb] = q_start + min(qi[cb], n_q - 1);
+        const uint16_t* qrow = q + ((int64_t)min(qi[cb], n_q - 1) * Hq + g * G + col % G) * D;
+        float s = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            // kappa = 32 ks + 8 grp + e; dims of kappa .. kappa + 7: two runs of four
+            const int kap = 32 * ks + 8 * grp, d0 = kappa_dim(kap);
+            const uint2 a = *reinterpret_cast<const uint2*>(qrow + d0);      // dims d0 .. d0+3
+            const uint2 b = *reinterpret_cast<const uint2*>(qrow + d0 + 8);  // dims d0+8 .. d0+11
+            // interleave: kappa order d0, d0+8, d0+1, d0+9, ...
+            const uint4 u = make_uint4(__builtin_amdgcn_perm(b.x, a.x, 0x05040100u),
+                                       __builtin_amdgcn_perm(b.x, a.x, 0x07060302u),
+                                       __builtin_amdgcn_perm(b.y, a.y, 0x05040100u),
+                                       __builtin_amdgcn_perm(b.y, a.y, 0x07060302u));
+            qop[cb][ks] = as_bf16x8(u);
+            s += bf16_to_f32((uint16_t)(a.x & 0xFFFF)) + bf16_to_f32((uint16_t)(a.x >> 16)) +
+                 bf16_to_f32((uint16_t)(a.y & 0xFFFF)) + bf16_to_f32((uint16_t)(a.y >> 16)) +
+                 bf16_to_f32((uint16_t)(b.x & 0xFFFF)) + bf16_to_f32((uint16_t)(b.x >> 16)) +
+                 bf16_to_f32((uint16_t)(b.y & 0xFFFF)) + bf16_to_f32((uint16_t)(b.y >> 16));
+        }
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        qsum[cb] = s;
+    }
+
+    constexpr float LOG2E = 1.4426950408889634f;
+    const float cB = sm * LOG2E;
+    f32x4 acc[NCB][DB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[cb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref[NCB], l_run[NCB], c_run[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        m_ref[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+        c_run[cb] = 0.f;
+    }
+
+    convert_packed<D>(pk, L, 0, tid);
+    __syncthreads();
+    for (int pg = pg0; pg < pg1; ++pg) {
+        const int buf = (pg - pg0) & 1;
+        if (pg + 1 < pg1) load_packed<D>(pk, block_of(pg + 1), tid);
+        const uint16_t* Kt = L.k[buf];
+        const uint16_t* Vt = L.v[buf];
+        // ---- S^T = K~ Q^T: keys 16 kb + 4 grp + r of the page, column j ----
+        f32x4 st[NCB][4];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) st[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[(16 * kb + j) * KS + 32 * ks + 8 * grp]));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) st[cb][kb] = mma(a, qop[cb][ks], st[cb][kb]);
+            }
+        // ---- online softmax per row (column j), weights w = p scale_v ----
+        uint32_t phi[NCB][2][4], plo[NCB][2][4];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            float s[4][4];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 16 * kb + 4 * grp + r;
+                    const float4 mk = L.meta[buf][key];
+                    float x = fmaf(mk.x, st[cb][kb][r], mk.y * qsum[cb]);
+                    if (pg * PAGE + key > pos[cb]) x = -INFINITY;
+                    s[kb][r] = x;
+                    mt = fmaxf(mt, x);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            if ((mt - m_ref[cb]) * cB > 8.0f) {  // lazy rescale: weights stay below 2^8
+                const float alpha = __builtin_amdgcn_exp2f((m_ref[cb] - mt) * cB);
+                l_run[cb] *= alpha;
+                c_run[cb] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha;
+                m_ref[cb] = mt;
+            }
+            const float cbm = m_ref[cb] * cB;
+            float w[4][4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 16 * kb + 4 * grp + r;
+                    const float4 mk = L.meta[buf][key];
+                    const bool valid = pg * PAGE + key <= pos[cb];
+                    const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], cB, -cbm)) : 0.f;
+                    l_run[cb] += p;
+                    c_run[cb] += valid ? p * mk.w : 0.f;
+                    w[kb][r] = valid ? p * mk.z : 0.f;
+                }
+            // p.v operand of 32-key step ks: slots 8 grp .. 8 grp + 7 = keys of blocks 2ks (r) and 2ks + 1 (r)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                split_hi_lo(w[2 * ks][0], w[2 * ks][1], phi[cb][ks][0], plo[cb][ks][0]);
+                split_hi_lo(w[2 * ks][2], w[2 * ks][3], phi[cb][ks][1], plo[cb][ks][1]);
+                split_hi_lo(w[2 * ks + 1][0], w[2 * ks + 1][1], phi[cb][ks][2], plo[cb][ks][2]);
+                split_hi_lo(w[2 * ks + 1][2], w[2 * ks + 1][3], phi[cb][ks][3], plo[cb][ks][3]);
+            }
+        }
+        // ---- O^T += V~ P^T ----
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint16_t* vr = &Vt[(16 * db + j) * VS + 32 * ks + 4 * grp];
+                const uint2 v0 = *reinterpret_cast<const uint2*>(vr);       // keys 32ks + 4grp .. +3
+                const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);  // keys 32ks + 16 + 4grp .. +3
+                const bf16x8 a = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    acc[cb][db] = mma(a, as_bf16x8(make_uint4(phi[cb][ks][0], phi[cb][ks][1], phi[cb][ks][2],
+                                                              phi[cb][ks][3])), acc[cb][db]);
+                    acc[cb][db] = mma(a, as_bf16x8(make_uint4(plo[cb][ks][0], plo[cb][ks][1], plo[cb][ks][2],
+                                                              plo[cb][ks][3])), acc[cb][db]);
+                }
+            }
+        if (pg + 1 < pg1) convert_packed<D>(pk, L, buf ^ 1, tid);
+        __syncthreads();
+    }
+
+    // ---- partials of this split: o^T lanes hold dims 16 db + 4 grp + r of column j ----
+    float* wo = ws;
+    float* wml = ws + (int64_t)n_q * Hq * splits * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const float lsum = l_run[cb] + __shfl_xor(l_run[cb], 16);
+        const float lt = lsum + __shfl_xor(lsum, 32);
+        const float csum = c_run[cb] + __shfl_xor(c_run[cb], 16);
+        const float ct = csum + __shfl_xor(csum, 32);
+        if (!live[cb]) continue;
+        const int col = 16 * (NCB * wave + cb) + j;
+        const int64_t row = ((int64_t)qi[cb] * Hq + g * G + col % G) * splits + sp;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const float4 o = make_float4(acc[cb][db][0] + ct, acc[cb][db][1] + ct, acc[cb][db][2] + ct,
+                                         acc[cb][db][3] + ct);
+            *reinterpret_cast<float4*>(&wo[row * D + 16 * db + 4 * grp]) = o;
+        }
+        if (grp == 0) {
+            wml[2 * row] = m_ref[cb] * cB;  // log2 units
+            wml[2 * row + 1] = lt;
+        }
+    }
+}
+
+// Merge of the prefill partials: one workgroup per (query, head); split p
+// counts for query i when its first page starts at or before i's position.
+__global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q, int Hq, int Hkv, int D, int splits,
+                                                            const float* __restrict__ ws, float* __restrict__ out) {
+    const int row = blockIdx.x;  // i * Hq + h
+    const int i = row / Hq, G = Hq / Hkv;
+    const int d = threadIdx.x;
+    const int QB = ROWS / G, qb = i / QB;
+    const int pos = q_start + i;
+    const int pos_max = q_start + min(qb * QB + QB, n_q) - 1;
+    const int n_pages = pos_max / PAGE + 1, per = (n_pages + splits - 1) / splits;
+    const int live = min(splits, pos / (per * PAGE) + 1);
+    const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)n_q * Hq * splits * D) + (int64_t)row * splits;
+    const float* o = ws + (int64_t)row * splits * D + d;
+    float M = -INFINITY;
+    for (int p = 0; p < live; ++p) M = fmaxf(M, ml[p].x);
+    float den = 0.f, acc = 0.f;
+    for (int p = 0; p < live; ++p) {
+        const float f = exp2f(ml[p].x - M);
+        den += f * ml[p].y;
+        acc += f * o[(int64_t)p * D];
+    }
+    out[(int64_t)row * D + d] = acc / den;
+}
+
+int prefill_auto_splits(int n_q, int Hq, int Hkv) {
+    const int QB = ROWS / (Hq / Hkv);
+    const int blocks = ((n_q + QB - 1) / QB) * Hkv;
+    const int want = (256 + blocks - 1) / blocks;  // about one workgroup per compute unit
+    return want < 1 ? 1 : want > 64 ? 64 : want;
+}
+
+hipError_t launch_prefill_q2(const PoolView& pv, int layer, int seq, int q_start, int n_q, const uint16_t* q,
+                             float sm, int splits, float* ws, float* out, hipStream_t s) {
+    const int G = pv.Hq / pv.Hkv, QB = ROWS / G;
+    dim3 grid(((n_q + QB - 1) / QB) * pv.Hkv, splits);
+    if (pv.D == 256)
+        hipLaunchKernelGGL(prefill_q2_kernel<256>, grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q, sm, splits, ws);
+    else
+        hipLaunchKernelGGL(prefill_q2_kernel<128>, grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q, sm, splits, ws);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3(n_q * pv.Hq), dim3(pv.D), 0, s, q_start, n_q, pv.Hq, pv.Hkv, pv.D,
+                       splits, ws, out);
+    return hipGetLastError();
+}
+
+}  // namespace kvq
