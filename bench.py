@@ -34,6 +34,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "quantized_kv_attention_append_amd", "csrc")
 # sources of the two kernels of a 2-bit decode call (split kernel + merge)
@@ -51,6 +52,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size for counter passes (0 = none)")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
     return ap.parse_args()
 
 
@@ -78,6 +80,63 @@ def measured_traffic():
         log("traffic: counter summary is for other decode sources; reporting null")
         return None
     return int(fields["traffic_bytes_per_call"].strip())
+
+
+def prefill_leg(steps: int, warmup: int):
+    """Chunked prefill over the 2-bit pool: 65,536 prior tokens + a 1,024-token
+    chunk (1 layer, 4 KV heads x 256, 16 query heads), timed with HIP events
+    per call (prefill kernel + its merge).  Useful flops = 4 D Hq sum_i (p0 + i + 1)."""
+    import torch
+
+    import quantized_kv_attention_append_amd as kvq
+    from synth import CONFIGS, kv_rows, page_permutation, queries
+
+    w = CONFIGS[3]
+    prior, n_q = w.ctx, w.chunk
+    total = prior + n_q
+    geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
+    _, pb = kvq.token_bytes(geom, kvq.FMT_Q2)
+    n_pages = total // 64
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q2, max_seqs=1, max_seq_tokens=total)
+    seq = pool.reserve(total, pages=page_permutation(w, n_pages))
+    k, v = kv_rows(w, 0, 0, total, device="cuda")
+    pool.append(0, [seq], [0], [prior], k[:prior], v[:prior])
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    pool.append(0, [seq], [prior], [n_q], k[prior:], v[prior:])
+    e1.record(stream)
+    e1.synchronize()
+    chunk_append_ms = e0.elapsed_time(e1)
+    del k, v
+    q = queries(w, 0, n_q, device="cuda", stream=1)
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_PREFILL, n_q, 0), dtype=torch.uint8, device="cuda")
+    out = torch.empty((n_q, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        pool.prefill(0, seq, prior, q, w.sm_scale, ws=ws, out=out)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        e0.record(stream)
+        pool.prefill(0, seq, prior, q, w.sm_scale, ws=ws, out=out)
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    avg = sum(ms) / len(ms)
+    flops = 4.0 * w.head_dim * w.n_q_heads * sum(prior + i + 1 for i in range(n_q))
+    tflops = flops / (avg * 1e-3) / 1e12
+    log(f"prefill: {avg:.3f} ms per call, {tflops:.0f} TFLOP/s useful ({100 * tflops / MFMA_BF16_TFLOPS:.1f}% of bf16 peak)")
+    return {
+        "workload": "chunked prefill, 2-bit: 65536 prior + 1024 chunk tokens, 1 layer x 4 KV heads x 256 dims, "
+                    "16 query heads",
+        "ms_per_call": avg,
+        "ms_min": min(ms),
+        "useful_flops": flops,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_TFLOPS, "traffic": None,
+                     "kernel": "one kv_attn_prefill call: prefill_q2_kernel<256> then prefill_merge_kernel"},
+        "chunk_append_ms": chunk_append_ms,
+    }
 
 
 def oracle_baseline(w, budget_s: float):
@@ -216,6 +275,8 @@ def main():
         log(f"calibration copy: 3 x {args.copy_mib} MiB int32 -> fp32")
         del src, dst
 
+    prefill = None if args.no_prefill else prefill_leg(max(3, args.steps // 4), 2)
+
     cpu = None
     if not args.no_cpu:
         cpu = oracle_baseline(w, args.cpu_seconds)
@@ -253,6 +314,7 @@ def main():
             "avg_launch_us": avg_launch_ms * 1e3,
         },
         "append": {"rows": append_rows, "ms": app_ms, "gbs": append_bytes / app_ms / 1e6},
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
