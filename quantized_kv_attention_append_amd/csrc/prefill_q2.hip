@@ -31,6 +31,8 @@
 //   V~[dim][key]    natural key order.
 // Partials (m, l, o) of every row go to the workspace; prefill_merge_kernel
 // merges, for each row, the splits whose first key it can see.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -43,7 +45,8 @@ namespace {
 
 constexpr int NCB = 2;            // 16-column blocks per wave
 constexpr int ROWS = 4 * NCB * 16;  // (query, head) rows per workgroup
-constexpr int KROW = 16;          // padding of a K~ row, bf16 elements (32 B)
+constexpr int KROW = 8;           // padding of a K~ row, bf16 elements (16 B: the 16 rows a read group
+                                  // touches start in distinct 16-byte bank slots)
 constexpr int VROW = 8;           // padding of a V~ row, bf16 elements
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
@@ -222,7 +225,10 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
 
     convert_packed<D>(pk, L, 0, tid);
     __syncthreads();
-    for (int pg = pg0; pg < pg1; ++pg) {
+    // pages [pg0, pg_full) are visible to every row of the block (no mask);
+    // the rest reach past the block's first query position
+    const int pg_full = max(pg0, min(pg1, (q_start + q_first + 1) / PAGE));
+    auto page_step = [&](int pg, auto masked_tag) {
         const int buf = (pg - pg0) & 1;
         if (pg + 1 < pg1) load_packed<D>(pk, block_of(pg + 1), tid);
         const uint16_t* Kt = L.k[buf];
@@ -243,52 +249,63 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
             }
         // ---- online softmax per row (column j), weights w = p scale_v ----
         uint32_t phi[NCB][2][4], plo[NCB][2][4];
+        {
+            constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            float s[4][4];
-            float mt = -INFINITY;
+            for (int cb = 0; cb < NCB; ++cb) {
+                float s[4][4];
+                float mt = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 16 * kb + 4 * grp + r;
-                    const float4 mk = L.meta[buf][key];
-                    float x = fmaf(mk.x, st[cb][kb][r], mk.y * qsum[cb]);
-                    if (pg * PAGE + key > pos[cb]) x = -INFINITY;
-                    s[kb][r] = x;
-                    mt = fmaxf(mt, x);
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = 16 * kb + 4 * grp + r;
+                        const float2 km = *reinterpret_cast<const float2*>(&L.meta[buf][key]);
+                        float x = fmaf(km.x, st[cb][kb][r], km.y * qsum[cb]);
+                        if (MASKED && pg * PAGE + key > pos[cb]) x = -INFINITY;
+                        s[kb][r] = x;
+                        mt = fmaxf(mt, x);
+                    }
+                mt = fmaxf(mt, __shfl_xor(mt, 16));
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                if ((mt - m_ref[cb]) * cB > 8.0f) {  // lazy rescale: weights stay below 2^8
+                    const float alpha = __builtin_amdgcn_exp2f((m_ref[cb] - mt) * cB);
+                    l_run[cb] *= alpha;
+                    c_run[cb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha;
+                    m_ref[cb] = mt;
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            if ((mt - m_ref[cb]) * cB > 8.0f) {  // lazy rescale: weights stay below 2^8
-                const float alpha = __builtin_amdgcn_exp2f((m_ref[cb] - mt) * cB);
-                l_run[cb] *= alpha;
-                c_run[cb] *= alpha;
+                const float cbm = m_ref[cb] * cB;
+                float w[4][4];
 #pragma unroll
-                for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha;
-                m_ref[cb] = mt;
-            }
-            const float cbm = m_ref[cb] * cB;
-            float w[4][4];
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+                    for (int r = 0; r < 4; ++r) {
+                        const int key = 16 * kb + 4 * grp + r;
+                        const float2 vm =
+                            *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&L.meta[buf][key]) + 2);
+                        if (MASKED) {  // slots past a row's position (or past the sequence) weigh nothing
+                            const bool valid = pg * PAGE + key <= pos[cb];
+                            const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], cB, -cbm)) : 0.f;
+                            l_run[cb] += p;
+                            c_run[cb] += valid ? p * vm.y : 0.f;
+                            w[kb][r] = valid ? p * vm.x : 0.f;
+                        } else {
+                            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cB, -cbm));
+                            l_run[cb] += p;
+                            c_run[cb] = fmaf(p, vm.y, c_run[cb]);
+                            w[kb][r] = p * vm.x;
+                        }
+                    }
+                // p.v operand of 32-key step ks: slots 8 grp .. 8 grp + 7 = keys of blocks 2ks (r) and 2ks + 1 (r)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 16 * kb + 4 * grp + r;
-                    const float4 mk = L.meta[buf][key];
-                    const bool valid = pg * PAGE + key <= pos[cb];
-                    const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], cB, -cbm)) : 0.f;
-                    l_run[cb] += p;
-                    c_run[cb] += valid ? p * mk.w : 0.f;
-                    w[kb][r] = valid ? p * mk.z : 0.f;
+                for (int ks = 0; ks < 2; ++ks) {
+                    split_hi_lo(w[2 * ks][0], w[2 * ks][1], phi[cb][ks][0], plo[cb][ks][0]);
+                    split_hi_lo(w[2 * ks][2], w[2 * ks][3], phi[cb][ks][1], plo[cb][ks][1]);
+                    split_hi_lo(w[2 * ks + 1][0], w[2 * ks + 1][1], phi[cb][ks][2], plo[cb][ks][2]);
+                    split_hi_lo(w[2 * ks + 1][2], w[2 * ks + 1][3], phi[cb][ks][3], plo[cb][ks][3]);
                 }
-            // p.v operand of 32-key step ks: slots 8 grp .. 8 grp + 7 = keys of blocks 2ks (r) and 2ks + 1 (r)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                split_hi_lo(w[2 * ks][0], w[2 * ks][1], phi[cb][ks][0], plo[cb][ks][0]);
-                split_hi_lo(w[2 * ks][2], w[2 * ks][3], phi[cb][ks][1], plo[cb][ks][1]);
-                split_hi_lo(w[2 * ks + 1][0], w[2 * ks + 1][1], phi[cb][ks][2], plo[cb][ks][2]);
-                split_hi_lo(w[2 * ks + 1][2], w[2 * ks + 1][3], phi[cb][ks][3], plo[cb][ks][3]);
             }
         }
         // ---- O^T += V~ P^T ----
@@ -308,9 +325,13 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
                                                               plo[cb][ks][3])), acc[cb][db]);
                 }
             }
-        if (pg + 1 < pg1) convert_packed<D>(pk, L, buf ^ 1, tid);
+        // the next page's tiles (after the last page this rewrites the idle
+        // buffer with the page already used; nothing reads it)
+        convert_packed<D>(pk, L, buf ^ 1, tid);
         __syncthreads();
-    }
+    };
+    for (int pg = pg0; pg < pg_full; ++pg) page_step(pg, std::false_type{});
+    for (int pg = pg_full; pg < pg1; ++pg) page_step(pg, std::true_type{});
 
     // ---- partials of this split: o^T lanes hold dims 16 db + 4 grp + r of column j ----
     float* wo = ws;
