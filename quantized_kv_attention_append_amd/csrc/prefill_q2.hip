@@ -48,6 +48,7 @@ constexpr int ROWS = 4 * NCB * 16;  // (query, head) rows per workgroup
 constexpr int KROW = 8;           // padding of a K~ row, bf16 elements (16 B: the 16 rows a read group
                                   // touches start in distinct 16-byte bank slots)
 constexpr int VROW = 8;           // padding of a V~ row, bf16 elements
+constexpr int LDS_AHEAD = 3;      // LDS fragments in flight ahead of the matrix-core step using them
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -78,7 +79,7 @@ struct PrefillLds {
     static constexpr int VS = PAGE + VROW;
     uint16_t k[2][PAGE * KS];  // K~, two buffers
     uint16_t v[2][D * VS];     // V~, two buffers
-    float4 meta[2][PAGE];      // {k scale, k min, v scale, v min} per key
+    float4 meta[2][PAGE];      // {k scale, k min - 4 k scale, v scale, v min} per key
 };
 
 // Packed codes of one page held by a thread between its load and its conversion.
@@ -113,13 +114,17 @@ __device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillL
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int item = tid + 256 * i;
-        // K word u of key t: dims 16u..16u+15 -> kappa 16u + 2k + e = dim 16u + k + 8e
+        // K word u of key t: dims 16u..16u+15 -> kappa 16u + 2k + e = dim 16u + k + 8e;
+        // code c is stored as bf16(c + 4) = 0x4080 + 32 c (two bit operations a pair)
         {
             const int t = item / KW, u = item % KW;
             const uint32_t w = pk.k[i];
             uint32_t o[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] = codes_to_bf16x2((w >> (2 * k)) & 0x00030003u);
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t x = (5 - 2 * k) >= 0 ? w << (5 - 2 * k) : w >> (2 * k - 5);
+                o[k] = (x & 0x00600060u) | 0x40804080u;
+            }
             uint4* dst = reinterpret_cast<uint4*>(&L.k[buf][t * KS + 16 * u]);
             dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
             dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
@@ -136,8 +141,12 @@ __device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillL
             }
         }
     }
-    if (tid < PAGE) L.meta[buf][tid] = make_float4(__uint_as_float(pk.meta.x), __uint_as_float(pk.meta.y),
-                                                   __uint_as_float(pk.meta.z), __uint_as_float(pk.meta.w));
+    // the K offset absorbs the +4 of the stored codes: k^ = min + scale c = (min - 4 scale) + scale (c + 4)
+    if (tid < PAGE) {
+        const float ks = __uint_as_float(pk.meta.x);
+        L.meta[buf][tid] = make_float4(ks, __uint_as_float(pk.meta.y) - 4.0f * ks, __uint_as_float(pk.meta.z),
+                                       __uint_as_float(pk.meta.w));
+    }
 }
 
 // Pages [pg0, pg1) of split sp for a block whose last query sits at pos_max.
@@ -228,7 +237,8 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
     // pages [pg0, pg_full) are visible to every row of the block (no mask);
     // the rest reach past the block's first query position
     const int pg_full = max(pg0, min(pg1, (q_start + q_first + 1) / PAGE));
-    auto page_step = [&](int pg, auto masked_tag) {
+    float alpha[NCB];
+    auto page_step = [&](int pg, auto masked_tag) -> bool {
         const int buf = (pg - pg0) & 1;
         if (pg + 1 < pg1) load_packed<D>(pk, block_of(pg + 1), tid);
         const uint16_t* Kt = L.k[buf];
@@ -239,43 +249,56 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) st[cb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // fragments are read LDS_AHEAD steps before their products, so that
+        // the LDS latency hides behind the matrix-core work of the steps between
+        constexpr int NQK = 4 * KSTEPS;
+        auto kfrag = [&](int idx) {
+            const int kb = idx / KSTEPS, ks = idx % KSTEPS;
+            return as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[(16 * kb + j) * KS + 32 * ks + 8 * grp]));
+        };
+        bf16x8 fk[LDS_AHEAD + 1];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int idx = 0; idx < LDS_AHEAD; ++idx) fk[idx] = kfrag(idx);
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(&Kt[(16 * kb + j) * KS + 32 * ks + 8 * grp]));
+        for (int idx = 0; idx < NQK; ++idx) {
+            if (idx + LDS_AHEAD < NQK) fk[(idx + LDS_AHEAD) % (LDS_AHEAD + 1)] = kfrag(idx + LDS_AHEAD);
+            const int kb = idx / KSTEPS, ks = idx % KSTEPS;
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) st[cb][kb] = mma(a, qop[cb][ks], st[cb][kb]);
-            }
-        // ---- online softmax per row (column j), weights w = p scale_v ----
+            for (int cb = 0; cb < NCB; ++cb) st[cb][kb] = mma(fk[idx % (LDS_AHEAD + 1)], qop[cb][ks], st[cb][kb]);
+        }
+        // ---- scores and the page's maximum per row (column j) ----
+        constexpr bool MASKED = decltype(masked_tag)::value;
+        bool need = false;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 16 * kb + 4 * grp + r;
+                    const float2 km = *reinterpret_cast<const float2*>(&L.meta[buf][key]);
+                    float x = fmaf(km.x, st[cb][kb][r], km.y * qsum[cb]);
+                    if (MASKED && pg * PAGE + key > pos[cb]) x = -INFINITY;
+                    st[cb][kb][r] = x;
+                    mt = fmaxf(mt, x);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            // lazy rescale: the reference moves only when a weight would pass 2^8
+            const bool up = (mt - m_ref[cb]) * cB > 8.0f;
+            alpha[cb] = up ? __builtin_amdgcn_exp2f((m_ref[cb] - mt) * cB) : 1.0f;
+            m_ref[cb] = up ? mt : m_ref[cb];
+            need |= up;
+        }
+        // a moved reference rescales the running sums before this page's
+        // weights: the page is given back and retried after the rescale
+        if (__builtin_amdgcn_ballot_w64(need)) return false;
+        // ---- online softmax, weights w = p scale_v ----
         uint32_t phi[NCB][2][4], plo[NCB][2][4];
         {
-            constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                float s[4][4];
-                float mt = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int key = 16 * kb + 4 * grp + r;
-                        const float2 km = *reinterpret_cast<const float2*>(&L.meta[buf][key]);
-                        float x = fmaf(km.x, st[cb][kb][r], km.y * qsum[cb]);
-                        if (MASKED && pg * PAGE + key > pos[cb]) x = -INFINITY;
-                        s[kb][r] = x;
-                        mt = fmaxf(mt, x);
-                    }
-                mt = fmaxf(mt, __shfl_xor(mt, 16));
-                mt = fmaxf(mt, __shfl_xor(mt, 32));
-                if ((mt - m_ref[cb]) * cB > 8.0f) {  // lazy rescale: weights stay below 2^8
-                    const float alpha = __builtin_amdgcn_exp2f((m_ref[cb] - mt) * cB);
-                    l_run[cb] *= alpha;
-                    c_run[cb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha;
-                    m_ref[cb] = mt;
-                }
                 const float cbm = m_ref[cb] * cB;
                 float w[4][4];
 #pragma unroll
@@ -287,12 +310,12 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
                             *reinterpret_cast<const float2*>(reinterpret_cast<const float*>(&L.meta[buf][key]) + 2);
                         if (MASKED) {  // slots past a row's position (or past the sequence) weigh nothing
                             const bool valid = pg * PAGE + key <= pos[cb];
-                            const float p = valid ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], cB, -cbm)) : 0.f;
+                            const float p = valid ? __builtin_amdgcn_exp2f(fmaf(st[cb][kb][r], cB, -cbm)) : 0.f;
                             l_run[cb] += p;
                             c_run[cb] += valid ? p * vm.y : 0.f;
                             w[kb][r] = valid ? p * vm.x : 0.f;
                         } else {
-                            const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], cB, -cbm));
+                            const float p = __builtin_amdgcn_exp2f(fmaf(st[cb][kb][r], cB, -cbm));
                             l_run[cb] += p;
                             c_run[cb] = fmaf(p, vm.y, c_run[cb]);
                             w[kb][r] = p * vm.x;
@@ -309,29 +332,56 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
             }
         }
         // ---- O^T += V~ P^T ----
+        constexpr int NPV = 2 * DB;
+        auto vfrag = [&](int idx) {
+            const int db = idx >> 1, ks = idx & 1;
+            const uint16_t* vr = &Vt[(16 * db + j) * VS + 32 * ks + 4 * grp];
+            const uint2 v0 = *reinterpret_cast<const uint2*>(vr);       // keys 32ks + 4grp .. +3
+            const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);  // keys 32ks + 16 + 4grp .. +3
+            return as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+        };
+        bf16x8 fv[LDS_AHEAD + 1];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int idx = 0; idx < LDS_AHEAD; ++idx) fv[idx] = vfrag(idx);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const uint16_t* vr = &Vt[(16 * db + j) * VS + 32 * ks + 4 * grp];
-                const uint2 v0 = *reinterpret_cast<const uint2*>(vr);       // keys 32ks + 4grp .. +3
-                const uint2 v1 = *reinterpret_cast<const uint2*>(vr + 16);  // keys 32ks + 16 + 4grp .. +3
-                const bf16x8 a = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
+        for (int idx = 0; idx < NPV; ++idx) {
+            if (idx + LDS_AHEAD < NPV) fv[(idx + LDS_AHEAD) % (LDS_AHEAD + 1)] = vfrag(idx + LDS_AHEAD);
+            const int db = idx >> 1, ks = idx & 1;
+            const bf16x8 a = fv[idx % (LDS_AHEAD + 1)];
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    acc[cb][db] = mma(a, as_bf16x8(make_uint4(phi[cb][ks][0], phi[cb][ks][1], phi[cb][ks][2],
-                                                              phi[cb][ks][3])), acc[cb][db]);
-                    acc[cb][db] = mma(a, as_bf16x8(make_uint4(plo[cb][ks][0], plo[cb][ks][1], plo[cb][ks][2],
-                                                              plo[cb][ks][3])), acc[cb][db]);
-                }
+            for (int cb = 0; cb < NCB; ++cb) {
+                acc[cb][db] = mma(a, as_bf16x8(make_uint4(phi[cb][ks][0], phi[cb][ks][1], phi[cb][ks][2],
+                                                          phi[cb][ks][3])), acc[cb][db]);
+                acc[cb][db] = mma(a, as_bf16x8(make_uint4(plo[cb][ks][0], plo[cb][ks][1], plo[cb][ks][2],
+                                                          plo[cb][ks][3])), acc[cb][db]);
             }
+        }
         // the next page's tiles (after the last page this rewrites the idle
         // buffer with the page already used; nothing reads it)
         convert_packed<D>(pk, L, buf ^ 1, tid);
         __syncthreads();
+        return true;
     };
-    for (int pg = pg0; pg < pg_full; ++pg) page_step(pg, std::false_type{});
-    for (int pg = pg_full; pg < pg1; ++pg) page_step(pg, std::true_type{});
+    // A wave that gives a page back rescales and retries it; every wave still
+    // passes the one barrier of each page once.  The retry terminates: after
+    // the rescale the page's maximum equals the reference.
+    int pg = pg0;
+    auto run_pages = [&](int pg_end, auto masked_tag) {
+        while (pg < pg_end) {
+            while (pg < pg_end && page_step(pg, masked_tag)) ++pg;
+            if (pg < pg_end) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    l_run[cb] *= alpha[cb];
+                    c_run[cb] *= alpha[cb];
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) acc[cb][db] *= alpha[cb];
+                }
+            }
+        }
+    };
+    run_pages(pg_full, std::false_type{});
+    run_pages(pg1, std::true_type{});
 
     // ---- partials of this split: o^T lanes hold dims 16 db + 4 grp + r of column j ----
     float* wo = ws;
