@@ -48,7 +48,7 @@ constexpr int ROWS = 4 * NCB * 16;  // (query, head) rows per workgroup
 constexpr int KROW = 8;           // padding of a K~ row, bf16 elements (16 B: the 16 rows a read group
                                   // touches start in distinct 16-byte bank slots)
 constexpr int VROW = 8;           // padding of a V~ row, bf16 elements
-constexpr int LDS_AHEAD = 3;      // LDS fragments in flight ahead of the matrix-core step using them
+constexpr int LDS_AHEAD = 4;      // LDS fragments in flight ahead of the matrix-core step using them
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -108,11 +108,11 @@ __device__ __forceinline__ void load_packed(PackedPage<D>& pk, const uint8_t* bl
     }
 }
 
+// Item i (one K word, one V word) of a thread's share of the page conversion.
 template <int D>
-__device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid) {
-    constexpr int NW = PackedPage<D>::NW, KW = D / 16, KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
+__device__ __forceinline__ void convert_item(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid, int i) {
+    constexpr int KW = D / 16, KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
+    {
         const int item = tid + 256 * i;
         // K word u of key t: dims 16u..16u+15 -> kappa 16u + 2k + e = dim 16u + k + 8e;
         // code c is stored as bf16(c + 4) = 0x4080 + 32 c (two bit operations a pair)
@@ -141,12 +141,24 @@ __device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillL
             }
         }
     }
+}
+
+// The per-key scale and offset of the page.
+template <int D>
+__device__ __forceinline__ void convert_meta(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid) {
     // the K offset absorbs the +4 of the stored codes: k^ = min + scale c = (min - 4 scale) + scale (c + 4)
     if (tid < PAGE) {
         const float ks = __uint_as_float(pk.meta.x);
         L.meta[buf][tid] = make_float4(ks, __uint_as_float(pk.meta.y) - 4.0f * ks, __uint_as_float(pk.meta.z),
                                        __uint_as_float(pk.meta.w));
     }
+}
+
+template <int D>
+__device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid) {
+#pragma unroll
+    for (int i = 0; i < PackedPage<D>::NW; ++i) convert_item<D>(pk, L, buf, tid, i);
+    convert_meta<D>(pk, L, buf, tid);
 }
 
 // Pages [pg0, pg1) of split sp for a block whose last query sits at pos_max.
@@ -356,8 +368,9 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
                                                           plo[cb][ks][3])), acc[cb][db]);
             }
         }
-        // the next page's tiles (after the last page this rewrites the idle
-        // buffer with the page already used; nothing reads it)
+        // the next page's tiles (the idle buffer was last read before the
+        // previous barrier; after the last page this rewrites it with the page
+        // already used, and nothing reads it)
         convert_packed<D>(pk, L, buf ^ 1, tid);
         __syncthreads();
         return true;
