@@ -14,7 +14,7 @@
 //   * codes 0..3 and the bf16 query are exact bf16 operands, so q.c is exact
 //     up to the fp32 sum;
 //   * the softmax weights w = p scale_v are split into two bf16 terms
-//     (w truncated to bf16, then the truncated residual), 16 significant bits.
+//     (w rounded to bf16, then the rounded residual), 17 significant bits.
 // The score tile is computed transposed, S^T = K~ Q^T (rows = keys, columns =
 // 16 (query, head) rows), so that the lane holding keys 4g..4g+3 and
 // 16+4g..16+4g+3 of a 32-key step already holds the p.v operand
@@ -40,6 +40,8 @@ namespace kvq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -63,12 +65,14 @@ __device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t x) {
 }
 // kappa index -> dim: kappa = 16u + 2k + e holds dim 16u + k + 8e
 __device__ __forceinline__ int kappa_dim(int kappa) { return (kappa & ~15) + ((kappa & 1) << 3) + ((kappa & 15) >> 1); }
-// fp32 -> bf16 by truncation, and the truncated residual, packed for two values
+// fp32 -> bf16 rounded to nearest, and the rounded residual, packed for two
+// values: a = hi + lo to 2^-18 relative, with unbiased errors (truncation
+// would bias every weight low, and the bias survives the sum over the keys
+// where the code part and the offset part of the output nearly cancel)
 __device__ __forceinline__ void split_hi_lo(float a, float b, uint32_t& hi, uint32_t& lo) {
-    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-    const float ra = a - __uint_as_float(ua & 0xFFFF0000u), rb = b - __uint_as_float(ub & 0xFFFF0000u);
-    hi = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
-    lo = __builtin_amdgcn_perm(__float_as_uint(rb), __float_as_uint(ra), 0x07060302u);
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+    const float ra = a - __uint_as_float(hi << 16), rb = b - __uint_as_float(hi & 0xFFFF0000u);  // exact
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
 }
 
 }  // namespace
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const float cbm = m_ref[cb] * cB;
-                float w[4][4];
+                float w[4][4], ls = 0.f, cs = 0.f;  // this page's sums, added to the running ones at the end
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -323,16 +327,18 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
                         if (MASKED) {  // slots past a row's position (or past the sequence) weigh nothing
                             const bool valid = pg * PAGE + key <= pos[cb];
                             const float p = valid ? __builtin_amdgcn_exp2f(fmaf(st[cb][kb][r], cB, -cbm)) : 0.f;
-                            l_run[cb] += p;
-                            c_run[cb] += valid ? p * vm.y : 0.f;
+                            ls += p;
+                            cs += valid ? p * vm.y : 0.f;
                             w[kb][r] = valid ? p * vm.x : 0.f;
                         } else {
                             const float p = __builtin_amdgcn_exp2f(fmaf(st[cb][kb][r], cB, -cbm));
-                            l_run[cb] += p;
-                            c_run[cb] = fmaf(p, vm.y, c_run[cb]);
+                            ls += p;
+                            cs = fmaf(p, vm.y, cs);
                             w[kb][r] = p * vm.x;
                         }
                     }
+                l_run[cb] += ls;
+                c_run[cb] += cs;
                 // p.v operand of 32-key step ks: slots 8 grp .. 8 grp + 7 = keys of blocks 2ks (r) and 2ks + 1 (r)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {

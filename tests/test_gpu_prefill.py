@@ -108,7 +108,8 @@ def test_c3_chunked_prefill_full_size():
     assert np.all(np.isfinite(out))
     K, V = opool.dequantized_rows("q2", k.float().cpu().numpy(), v.float().cpu().numpy())
     qn = q.float().cpu().numpy()
-    for i in (0, 1, 63, 64, 500, 1022, 1023):
+    # rows 207 and 707 carry the largest errors of the whole chunk (about 8e-4 on outputs of 10 to 17)
+    for i in (0, 1, 63, 64, 207, 500, 707, 1022, 1023):
         ref = attention.decode(qn[i], K[:prior + i + 1], V[:prior + i + 1], w.sm_scale)
         assert_close(out[i], ref, f"chunk row {i} (ctx {prior + i + 1})")
     say("C3 prefill: sampled rows within tolerance")
