@@ -49,7 +49,8 @@ constexpr int NCB = 2;            // 16-column blocks per wave
 constexpr int ROWS = 4 * NCB * 16;  // (query, head) rows per workgroup
 constexpr int KROW = 8;           // padding of a K~ row, bf16 elements (16 B: the 16 rows a read group
                                   // touches start in distinct 16-byte bank slots)
-constexpr int VROW = 8;           // padding of a V~ row, bf16 elements
+constexpr int VROW = 12;          // padding of a V~ row, bf16 elements (24 B; 0 is 2.5x slower at
+                                  // 256 dims, 4, 8 and 16 are 1 to 20 % slower than 12)
 constexpr int LDS_AHEAD = 4;      // LDS fragments in flight ahead of the matrix-core step using them
 
 __device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, f32x4 c) {
