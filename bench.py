@@ -15,6 +15,12 @@ triples), the per-launch roofline of the decode kernel against 8 TB/s HBM, and
 the CPU oracle timed on a bounded sample of the same work.
 
     python bench.py [--steps K] [--warmup W] [--splits P] [--no-cpu] [--copy-mib M]
+                    [--no-prefill] [--no-extra]
+
+Besides the headline line's decode, the same JSON line holds the chunked
+prefill (65,536 + 1,024 tokens), the 131,072-token split-K decode at 16..128
+splits (cache-warm and after a 1 GiB flush) and the 8-bit 24-lane x 32-layer
+decode, each with its own figures.
 
 The roofline's "traffic" (HBM bytes a decode call really moves, from the
 FETCH_SIZE and WRITE_SIZE counters scaled by a copy of known size) is read
@@ -53,6 +59,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size for counter passes (0 = none)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-context and 8-bit decode legs")
     return ap.parse_args()
 
 
@@ -137,6 +144,138 @@ def prefill_leg(steps: int, warmup: int):
                      "kernel": "one kv_attn_prefill call: prefill_q2_kernel<256> then prefill_merge_kernel"},
         "chunk_append_ms": chunk_append_ms,
     }
+
+
+def _call_ms(fn, reps: int, flush=None):
+    """Average and minimum of HIP-event times of fn() on the current stream;
+    flush() (untimed) runs before each timed call when given."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    return sum(ms) / len(ms), ms[0], ms[len(ms) // 2]
+
+
+def long_context_leg(reps: int):
+    """Split-K decode of one 131,072-token sequence (1 layer, 4 KV heads x 256,
+    16 query heads, 2-bit; a planted key) at 16, 32, 64 and 128 splits: each
+    call timed with HIP events back to back, and again after writing a 1 GiB
+    scratch buffer before every call, so that the 75.5 MB of codes come from
+    HBM rather than the last-level cache."""
+    import torch
+
+    import quantized_kv_attention_append_amd as kvq
+    from synth import CONFIGS, kv_rows, page_permutation, planted_position, queries
+    from synth.workloads import plant_key
+
+    w = CONFIGS[2]
+    ctx = w.ctx
+    geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
+    _, pb = kvq.token_bytes(geom, kvq.FMT_Q2)
+    n_pages = ctx // 64
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q2, max_seqs=1, max_seq_tokens=ctx)
+    seq = pool.reserve(ctx, pages=page_permutation(w, n_pages))
+    k, v = kv_rows(w, 0, 0, ctx, device="cuda")
+    q = queries(w, 0, 1, device="cuda")
+    plant_key(k, q[0], planted_position(w, ctx), w.group)
+    pool.append(0, [seq], [0], [ctx], k, v)
+    del k, v
+    out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    alg = ctx * w.n_kv_heads * 2 * (w.head_dim // 4 + 8) + w.n_q_heads * w.head_dim * (2 + 4)
+    res = []
+    for sp in (16, 32, 64, 128):
+        ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, 1, sp), dtype=torch.uint8, device="cuda")
+        call = lambda: pool.decode(0, [seq], [ctx], q, w.sm_scale, n_splits=sp, ws=ws, out=out)
+        for _ in range(3):
+            call()
+        warm = _call_ms(call, reps)
+        cold = _call_ms(call, reps, flush=lambda: scratch.fill_(sp))
+        res.append({"splits": sp,
+                    "us_mean": warm[0] * 1e3, "us_min": warm[1] * 1e3, "us_median": warm[2] * 1e3,
+                    "gbs_mean": alg / (warm[0] * 1e-3) / 1e9,
+                    "flushed_us_mean": cold[0] * 1e3, "flushed_us_min": cold[1] * 1e3,
+                    "flushed_gbs_mean": alg / (cold[0] * 1e-3) / 1e9})
+        log(f"long context, splits={sp}: {warm[0] * 1e3:.1f} us ({alg / (warm[0] * 1e-3) / 1e9:.0f} GB/s), "
+            f"after a 1 GiB flush {cold[0] * 1e3:.1f} us ({alg / (cold[0] * 1e-3) / 1e9:.0f} GB/s)")
+    del scratch
+    return {"workload": "long split-K decode, 2-bit: 1 lane x 131072 tokens, 1 layer x 4 KV heads x 256 dims, "
+                        "16 query heads, planted key",
+            "bytes_per_call": alg, "per_splits": res}
+
+
+def q8_leg(reps: int):
+    """The 8-bit format: 24 lanes of 64 x U[16, 128] tokens, 32 layers x 8 KV
+    heads x 128 dims, 32 query heads.  Populate every layer (timed, HBM bytes
+    of bf16 rows read and codes written), then decode every layer (one call per
+    layer for all lanes, HIP events); algorithmic bytes 268 per (token, KV
+    head) plus q and out."""
+    import torch
+
+    import quantized_kv_attention_append_amd as kvq
+    from synth import CONFIGS, c4_lengths, kv_rows, page_permutation, queries
+
+    w = CONFIGS[4]
+    lens = [int(x) for x in c4_lengths(w)]
+    geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
+    _, pb = kvq.token_bytes(geom, kvq.FMT_Q8)
+    n_pages = sum(-(-L // 64) for L in lens)
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q8, max_seqs=w.lanes, max_seq_tokens=max(lens))
+    perm = page_permutation(w, n_pages)
+    seqs, off = [], 0
+    for L in lens:
+        npg = -(-L // 64)
+        seqs.append(pool.reserve(L, pages=perm[off:off + npg]))
+        off += npg
+    B = w.lanes
+    stream = torch.cuda.current_stream()
+    app_ms = 0.0
+    for layer in range(w.n_layers):
+        kv = [kv_rows(w, layer, i, lens[i], device="cuda") for i in range(B)]
+        k = torch.cat([a for a, _ in kv])
+        v = torch.cat([b for _, b in kv])
+        del kv
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pool.append(layer, seqs, [0] * B, lens, k, v)
+        e1.record(stream)
+        e1.synchronize()
+        app_ms += e0.elapsed_time(e1)
+        del k, v
+    tokens = sum(lens)
+    qs = [queries(w, layer, B, device="cuda") for layer in range(w.n_layers)]
+    sp = pool.decode_splits(lens)
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, B, sp), dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    calls = []
+    for layer in range(w.n_layers):
+        call = lambda layer=layer: pool.decode(layer, seqs, lens, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=out)
+        call()
+        calls.append(_call_ms(call, reps))
+    avg = sum(c[0] for c in calls) / len(calls)
+    alg = tokens * w.n_kv_heads * 268 + B * w.n_q_heads * w.head_dim * (2 + 4)
+    app_bytes = w.n_layers * tokens * w.n_kv_heads * 2 * (2 * w.head_dim) + w.n_layers * tokens * w.n_kv_heads * (
+        2 * w.head_dim + 8)
+    gbs = alg / (avg * 1e-3) / 1e9
+    log(f"8-bit: populate {w.n_layers} layers x {tokens} tokens in {app_ms:.1f} ms; decode {avg * 1e3:.1f} us a layer "
+        f"call, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), splits={sp}")
+    return {"workload": "8-bit decode, 24 lanes x 64*U[16,128] tokens, 32 layers x 8 KV heads x 128 dims, 32 query heads",
+            "tokens_per_layer": tokens, "pool_bytes": n_pages * pb, "splits": sp,
+            "decode_us_per_layer_call": avg * 1e3, "bytes_per_call": alg,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "one kv_attn_decode call per layer: decode_q8_kernel<128> then merge_splits_kernel"},
+            "kv_tokens_per_s": tokens * w.n_layers / (avg * 1e-3 * w.n_layers),
+            "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
 
 def oracle_baseline(w, budget_s: float):
@@ -276,6 +415,8 @@ def main():
         del src, dst
 
     prefill = None if args.no_prefill else prefill_leg(max(3, args.steps // 4), 2)
+    long_ctx = None if args.no_extra else long_context_leg(10)
+    q8 = None if args.no_extra else q8_leg(5)
 
     cpu = None
     if not args.no_cpu:
@@ -315,6 +456,8 @@ def main():
         },
         "append": {"rows": append_rows, "ms": app_ms, "gbs": append_bytes / app_ms / 1e6},
         "prefill": prefill,
+        "long_context": long_ctx,
+        "q8": q8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -20,6 +20,8 @@
 //   p.v:     thread (d, half) takes dim d over tokens [32 half, 32 half + 32)
 //            (D = 128) or all 64 tokens (D = 256) for every head.
 // Partial (m, l, o) go to the workspace; merge_splits_kernel merges them.
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace kvq {
@@ -200,15 +202,202 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(PoolView pv, int layer, 
     }
 }
 
+// Wave-parallel form for G in {1, 2, 4, 8}: the four waves of a workgroup
+// take every fourth page of the split and run their own online softmax, with
+// no workgroup barrier until the final combine, so that many workgroups per
+// compute unit keep loads in flight while others compute.  Per page, lane t
+// holds token t's K row (D codes) and dims DL*t .. DL*t + DL-1 of V (64
+// tokens each):
+//   scores:  s_j(t) = sum_d (q_jd kscale_d) c_td, the scaled query staged in
+//            the wave's LDS and read as broadcasts;
+//   softmax: wave-wide max and sum per head, weights p_t vscale_t to LDS;
+//   p.v:     o_j,d += sum_t w_j(t) c_dt over the page's 64 tokens.
+template <int D, int G, bool SCORES>
+__global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                             const uint16_t* __restrict__ q, float sm, int splits,
+                                                             float* __restrict__ ws, float* __restrict__ out,
+                                                             float* __restrict__ scores, int64_t sstride) {
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int DL = D / 64;  // V dims of a lane
+    const int Hkv = pv.Hkv, Hq = pv.Hq;
+    const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
+    const int ctx = bd.pos[e];
+    int pg0, pg1;
+    split_range(ctx, splits, sp, &pg0, &pg1);
+    if (pg0 >= pg1) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+    __shared__ __align__(16) float qk_s[4][G][D];    // per wave: query x the page's channel scales; partial o at the end
+    __shared__ __align__(16) float w_s[4][G][PAGE];  // per wave: the page's weights
+    __shared__ float ml_s[4][G][2];
+
+    // this lane's query dims (the ones whose channel scales it loads)
+    float qv[G][DL];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+        for (int i = 0; i < DL; ++i) qv[j][i] = bf16_to_f32(q[((int64_t)e * Hq + g * G + j) * D + DL * lane + i]);
+    float m[G], l[G], o[G][DL];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        m[j] = -INFINITY;
+        l[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DL; ++i) o[j][i] = 0.f;
+    }
+    const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
+    const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
+    const float cs = sm * LOG2E;
+
+    for (int pg = pg0 + wave; pg < pg1; pg += 4) {
+        const uint8_t* blk = pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff;
+        uint4 kc[D / 16];  // K codes of token `lane`
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) kc[i] = reinterpret_cast<const uint4*>(blk + lane * D)[i];
+        uint4 vc[DL][4];  // V codes of dims DL*lane + dd, tokens 0..63
+#pragma unroll
+        for (int dd = 0; dd < DL; ++dd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vc[dd][i] = reinterpret_cast<const uint4*>(blk + q8_vcodes_off(D) + (DL * lane + dd) * PAGE)[i];
+        float ksc[DL];
+#pragma unroll
+        for (int dd = 0; dd < DL; ++dd) ksc[dd] = reinterpret_cast<const float*>(blk + q8_kscale_off(D))[DL * lane + dd];
+        const float vsc = reinterpret_cast<const float*>(blk + q8_vscale_off(D))[lane];
+        const int n_tok = min(PAGE, ctx - pg * PAGE);
+        const bool valid = lane < n_tok;
+
+        // ---- scaled query for this page (the wave's LDS is read in order) ----
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int dd = 0; dd < DL; ++dd) qk_s[wave][j][DL * lane + dd] = qv[j][dd] * ksc[dd];
+
+        // ---- scores of token `lane` ----
+        float s[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) s[j] = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {  // code word c: dims 4c .. 4c + 3
+            const uint4 kw = kc[c >> 2];
+            const uint32_t wd = (c & 3) == 0 ? kw.x : (c & 3) == 1 ? kw.y : (c & 3) == 2 ? kw.z : kw.w;
+            float kf[4];
+            i8x4(wd, kf);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float4 qq = *reinterpret_cast<const float4*>(&qk_s[wave][j][4 * c]);
+                s[j] = fmaf(qq.x, kf[0], s[j]);
+                s[j] = fmaf(qq.y, kf[1], s[j]);
+                s[j] = fmaf(qq.z, kf[2], s[j]);
+                s[j] = fmaf(qq.w, kf[3], s[j]);
+            }
+            // bound the scheduling window: the broadcasts of 16 dims at a time
+            if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- online softmax per head; slots past ctx weigh nothing (their bytes may be anything) ----
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            if constexpr (SCORES)  // a variant of its own: the branch costs the other variant registers
+                if (valid) scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + lane] = sm * s[j];
+            const float x = valid ? s[j] * cs : -INFINITY;
+            const float m_new = fmaxf(m[j], wave_max(x));  // finite: every page of the split holds a token
+            const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
+            const float p = valid ? __builtin_amdgcn_exp2f(x - m_new) : 0.f;
+            l[j] = l[j] * alpha + wave_sum(p);
+            m[j] = m_new;
+            w_s[wave][j][lane] = valid ? p * vsc : 0.f;
+#pragma unroll
+            for (int dd = 0; dd < DL; ++dd) o[j][dd] *= alpha;
+        }
+        // ---- p.v over the page's tokens, four at a time ----
+#pragma unroll
+        for (int t4 = 0; t4 < PAGE / 4; ++t4) {
+            float vf[DL][4];
+#pragma unroll
+            for (int dd = 0; dd < DL; ++dd) {
+                const uint4 vw = vc[dd][t4 >> 2];
+                const uint32_t wd = (t4 & 3) == 0 ? vw.x : (t4 & 3) == 1 ? vw.y : (t4 & 3) == 2 ? vw.z : vw.w;
+                i8x4(wd, vf[dd]);
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float4 ww = *reinterpret_cast<const float4*>(&w_s[wave][j][4 * t4]);
+#pragma unroll
+                for (int dd = 0; dd < DL; ++dd) {
+                    o[j][dd] = fmaf(ww.x, vf[dd][0], o[j][dd]);
+                    o[j][dd] = fmaf(ww.y, vf[dd][1], o[j][dd]);
+                    o[j][dd] = fmaf(ww.z, vf[dd][2], o[j][dd]);
+                    o[j][dd] = fmaf(ww.w, vf[dd][3], o[j][dd]);
+                }
+            }
+            if ((t4 & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- combine the four waves (a wave without pages holds m = -inf, l = 0, o = 0) ----
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+        for (int dd = 0; dd < DL; ++dd) qk_s[wave][j][DL * lane + dd] = o[j][dd];
+        if (lane == 0) {
+            ml_s[wave][j][0] = m[j];
+            ml_s[wave][j][1] = l[j];
+        }
+    }
+    __syncthreads();
+    DecodeWs w(ws, bd.n, Hq, D, splits);
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int j = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_s[v][j][0]);
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float f = __builtin_amdgcn_exp2f(ml_s[v][j][0] - M);  // 0 for a wave without pages
+            acc += f * qk_s[v][j][d];
+            L += f * ml_s[v][j][1];
+        }
+        const int64_t r = ((int64_t)e * Hq + g * G + j) * splits + sp;
+        w.o[r * D + d] = acc;
+        if (d == 0) {
+            w.ml[2 * r] = M;
+            w.ml[2 * r + 1] = L;
+        }
+    }
+}
+
 hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
     dim3 grid(bd.n * pv.Hkv, splits);
-    if (pv.D == 256)
-        hipLaunchKernelGGL(decode_q8_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores,
-                           sstride);
+    const int G = pv.Hq / pv.Hkv;
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
+    };
+    auto wave_form = [&](auto d_tag, auto g_tag) {
+        constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
+        scores ? go(decode_q8_wave_kernel<DD, GG, true>) : go(decode_q8_wave_kernel<DD, GG, false>);
+    };
+    using D128 = std::integral_constant<int, 128>;
+    using D256 = std::integral_constant<int, 256>;
+    if (pv.D == 128 && G == 4)
+        wave_form(D128{}, std::integral_constant<int, 4>{});
+    else if (pv.D == 128 && G == 8)
+        wave_form(D128{}, std::integral_constant<int, 8>{});
+    else if (pv.D == 128 && G == 2)
+        wave_form(D128{}, std::integral_constant<int, 2>{});
+    else if (pv.D == 128 && G == 1)
+        wave_form(D128{}, std::integral_constant<int, 1>{});
+    else if (pv.D == 256 && G == 4)
+        wave_form(D256{}, std::integral_constant<int, 4>{});
+    else if (pv.D == 256 && G == 2)
+        wave_form(D256{}, std::integral_constant<int, 2>{});
+    else if (pv.D == 256 && G == 1)
+        wave_form(D256{}, std::integral_constant<int, 1>{});
+    else if (pv.D == 256)
+        go(decode_q8_kernel<256>);
     else
-        hipLaunchKernelGGL(decode_q8_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores,
-                           sstride);
+        go(decode_q8_kernel<128>);
     const hipError_t err = hipGetLastError();
     return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }
