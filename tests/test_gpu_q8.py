@@ -19,6 +19,12 @@ C4 = CONFIGS[4]
 SMALL8 = Workload(91, "small 8-bit geometry", "q8", 2, 8, 128, 32, 3, 300)
 # a D = 256, group-2 geometry on the 8-bit format
 SMALL8_256 = Workload(92, "small 8-bit D=256 geometry", "q8", 1, 4, 256, 8, 2, 200)
+# the other group sizes of the wave-parallel decode (1, 8; 4 at D = 256) and the
+# one that takes the workgroup-per-page form (8 at D = 256)
+G1 = Workload(94, "8-bit group 1", "q8", 1, 4, 128, 4, 2, 300)
+G8 = Workload(95, "8-bit group 8", "q8", 1, 2, 128, 16, 2, 300)
+G4_256 = Workload(97, "8-bit D=256 group 4", "q8", 1, 2, 256, 8, 2, 200)
+G8_256 = Workload(98, "8-bit D=256 group 8", "q8", 1, 1, 256, 8, 2, 200)
 
 
 def _setup(w, lens, n_pages, salt=0, fill=0xA5):
@@ -113,7 +119,8 @@ def test_append_q8_must_be_sequential():
     assert torch.equal(mem, before)
 
 
-@pytest.mark.parametrize("w,lens", [(SMALL8, [300, 130, 64]), (SMALL8_256, [200, 65])])
+@pytest.mark.parametrize("w,lens", [(SMALL8, [300, 130, 64]), (SMALL8_256, [200, 65]), (G1, [300, 70]),
+                                    (G8, [300, 129]), (G4_256, [200, 65]), (G8_256, [130, 200])])
 def test_decode_q8_small(w, lens):
     need_gpu()
     n_pages = sum(-(-L // 64) for L in lens) + 2
@@ -129,11 +136,14 @@ def test_decode_q8_small(w, lens):
         scores = torch.full((len(lens), w.n_q_heads, max(ctxs)), float("nan"), device="cuda")
         ws = torch.full((pool.workspace_bytes(0, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
         out = pool.decode(layer, seqs, ctxs, q.cuda(), w.sm_scale, n_splits=sp, ws=ws, scores=scores)
+        plain = pool.decode(layer, seqs, ctxs, q.cuda(), w.sm_scale, n_splits=sp, ws=ws)  # the variant without scores
         torch.cuda.synchronize()
         for i, c in enumerate(ctxs):
             K, V = op.gather(layer, bts[i], c)
             qi = q[i].float().numpy()
-            assert_close(out[i].cpu().numpy(), attention.decode(qi, K, V, w.sm_scale), f"8-bit lane {i} ctx={c} splits={sp}")
+            ref = attention.decode(qi, K, V, w.sm_scale)
+            assert_close(out[i].cpu().numpy(), ref, f"8-bit lane {i} ctx={c} splits={sp}")
+            assert_close(plain[i].cpu().numpy(), ref, f"8-bit lane {i} ctx={c} splits={sp}, no scores")
             assert_close(scores[i, :, :c].cpu().numpy(), attention.scores(qi, K, w.sm_scale),
                          f"8-bit scores lane {i}", rel_l2=1e-5)
 
