@@ -147,11 +147,13 @@ def prefill_leg(steps: int, warmup: int):
 
 
 def _call_ms(fn, reps: int, flush=None):
-    """Average and minimum of HIP-event times of fn() on the current stream;
-    flush() (untimed) runs before each timed call when given."""
+    """Average, minimum and median of HIP-event times of fn() on the current
+    stream, the calls enqueued back to back (one synchronisation at the end,
+    so host launch latency does not enter); flush() (untimed) is enqueued
+    before each timed call when given."""
     import torch
     stream = torch.cuda.current_stream()
-    ms = []
+    ev = []
     for _ in range(reps):
         if flush is not None:
             flush()
@@ -159,9 +161,9 @@ def _call_ms(fn, reps: int, flush=None):
         e0.record(stream)
         fn()
         e1.record(stream)
-        e1.synchronize()
-        ms.append(e0.elapsed_time(e1))
-    ms.sort()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     return sum(ms) / len(ms), ms[0], ms[len(ms) // 2]
 
 
@@ -255,13 +257,20 @@ def q8_leg(reps: int):
     qs = [queries(w, layer, B, device="cuda") for layer in range(w.n_layers)]
     sp = pool.decode_splits(lens)
     ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, B, sp), dtype=torch.uint8, device="cuda")
-    out = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
-    calls = []
-    for layer in range(w.n_layers):
-        call = lambda layer=layer: pool.decode(layer, seqs, lens, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=out)
-        call()
-        calls.append(_call_ms(call, reps))
-    avg = sum(c[0] for c in calls) / len(calls)
+    outs = [torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda") for _ in range(w.n_layers)]
+    for layer in range(w.n_layers):  # warm-up
+        pool.decode(layer, seqs, lens, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):  # steps of one call per layer, back to back, an event pair around each call
+        for layer in range(w.n_layers):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pool.decode(layer, seqs, lens, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
+            e1.record(stream)
+            ev.append((e0, e1))
+    torch.cuda.synchronize()
+    avg = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
     alg = tokens * w.n_kv_heads * 268 + B * w.n_q_heads * w.head_dim * (2 + 4)
     app_bytes = w.n_layers * tokens * w.n_kv_heads * 2 * (2 * w.head_dim) + w.n_layers * tokens * w.n_kv_heads * (
         2 * w.head_dim + 8)

@@ -25,10 +25,9 @@ constexpr int MAX_SPLITS = 256;
 // Splits p < live_splits(...) hold at least one page; the rest are empty and
 // leave their partials unwritten (split_range gives every split the same
 // whole number of page pairs, so empty splits only trail).
-__host__ __device__ inline int live_splits(int ctx, int splits) {
+__host__ __device__ inline int live_splits(int ctx, int per) {
     const int n_pages = (ctx + PAGE - 1) / PAGE;
     const int pairs = (n_pages + 1) / 2;
-    const int per = (pairs + splits - 1) / splits;
     return per > 0 ? (pairs + per - 1) / per : 0;
 }
 

@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int ctx = bd.pos[e];
     int pg0, pg1;
-    split_range(ctx, splits, sp, &pg0, &pg1);
+    split_range(ctx, bd.per, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
 
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;

@@ -26,6 +26,8 @@
 
 namespace kvq {
 
+constexpr bool Q8_MATRIX_CORES = true;  // the matrix-core form where it applies (else the wave-parallel VALU form)
+
 namespace {
 
 // four int8 codes of a word -> fp32
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(PoolView pv, int layer, 
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int ctx = bd.pos[e];
     int pg0, pg1;
-    split_range(ctx, splits, sp, &pg0, &pg1);
+    split_range(ctx, bd.per, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int ctx = bd.pos[e];
     int pg0, pg1;
-    split_range(ctx, splits, sp, &pg0, &pg1);
+    split_range(ctx, bd.per, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
@@ -367,6 +369,247 @@ __global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int
     }
 }
 
+// Matrix-core form for G in {1, 2, 4, 8}.  Codes -127..127 are exact in
+// bf16; the query times the page's channel scales enters as two bf16 terms
+// (rounded, then the rounded residual), and so do the weights p_t vscale_t,
+// so both products run on v_mfma_f32_16x16x32_bf16 with a row per (head,
+// term): row 2j + h.  The four waves of a workgroup take every fourth page;
+// per page and wave:
+//   S^T = Q~ K^T for each block of 16 tokens: A = the query rows, B = K codes
+//         (lane l: token 16tb + l%16, 16 consecutive dims, two k-steps), so
+//         lane group g ends with the scores of heads 2g and 2g + 1 for the
+//         lane's token (hi and lo terms in adjacent rows, summed in-lane);
+//   softmax per head over the 64 tokens in the 16 lanes of its group;
+//   O += W~ V for each block of 16 dims: A = the weight rows (through the
+//         wave's LDS), B = V codes (lane l: dim 16db + l%16, 16 consecutive
+//         tokens, two k-steps); lane group g accumulates the rows of heads
+//         2g and 2g + 1, the same heads as its softmax, so the rescale is local.
+// The sum over dims and over tokens is order-free, so each k-step takes the
+// dims (tokens) that one 16-byte load per lane delivers.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+namespace {
+
+__device__ __forceinline__ f32x4_t mma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+}
+// two int8 codes (bytes b, b + 1 of w) -> two bf16, exact
+__device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int b) {
+    const float x = (float)(int8_t)(w >> (8 * b)), y = (float)(int8_t)(w >> (8 * b + 8));
+    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+}
+// eight int8 codes (two words) -> the bf16 operand
+__device__ __forceinline__ uint4 i8x8_bf16(uint32_t w0, uint32_t w1) {
+    return make_uint4(i8x2_bf16(w0, 0), i8x2_bf16(w0, 2), i8x2_bf16(w1, 0), i8x2_bf16(w1, 2));
+}
+// the bf16 term h (0: x rounded; 1: the rounded residual) of two values
+__device__ __forceinline__ uint32_t bf16_term2(float x, float y, int h) {
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x, y}, bf16x2_t));
+    const float rx = x - __uint_as_float(hi << 16), ry = y - __uint_as_float(hi & 0xFFFF0000u);  // exact
+    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){rx, ry}, bf16x2_t));
+    return h ? lo : hi;
+}
+// one value as its bf16 term (low half) and the rounded residual (high half)
+__device__ __forceinline__ uint32_t bf16_hi_lo(float x) {
+    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x, 0.f}, bf16x2_t)) & 0xFFFFu;
+    const float r = x - __uint_as_float(hi << 16);  // exact
+    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){r, 0.f}, bf16x2_t));
+    return hi | (lo << 16);
+}
+__device__ __forceinline__ float row_max16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float row_sum16(float v) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace
+
+template <int D, int G, bool SCORES>
+__global__ __launch_bounds__(256, 2) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                                const uint16_t* __restrict__ q, float sm, int splits,
+                                                                float* __restrict__ ws, float* __restrict__ out,
+                                                                float* __restrict__ scores, int64_t sstride) {
+    static_assert(2 * G <= 16, "two rows per head in a 16-row block");
+    constexpr float LOG2E = 1.4426950408889634f;
+    constexpr int NM = D / 64;   // 16-byte K chunks of a lane's token row (two k-steps each)
+    constexpr int NDB = D / 16;  // 16-dim blocks of the p.v product
+    constexpr int WROW = PAGE + 8;  // padded weight row, bf16 elements
+    const int Hkv = pv.Hkv, Hq = pv.Hq;
+    const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
+    const int ctx = bd.pos[e];
+    int pg0, pg1;
+    split_range(ctx, bd.per, sp, &pg0, &pg1);
+    if (pg0 >= pg1) return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, grp = lane >> 4;
+
+    __shared__ __align__(16) uint16_t w_s[4][16][WROW];  // per wave: weight rows 2j + h over the page's tokens
+    __shared__ __align__(16) float o_s[4][G][D];
+    __shared__ float ml_s[4][G][2];
+
+    // rows 2G.. of the weight operand stay zero
+    for (int i = lane; i < 16 * WROW; i += 64)
+        if (i / WROW >= 2 * G) w_s[wave][i / WROW][i % WROW] = 0;
+
+    // this lane's query row: head col / 2, term col % 2; dims 64m + 16grp + i
+    const int aj = col >> 1, ah = col & 1;
+    const bool arow = col < 2 * G;
+    float qv[NM][16];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            qv[m][i] = arow ? bf16_to_f32(q[((int64_t)e * Hq + g * G + aj) * D + 64 * m + 16 * grp + i]) : 0.f;
+
+    f32x4_t acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};  // heads 2grp, 2grp + 1
+    const float cs = sm * LOG2E;
+    const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
+    const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
+
+    for (int pg = pg0 + wave; pg < pg1; pg += 4) {
+        const uint8_t* blk = pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff;
+        uint4 kraw[4][NM];  // token 16tb + col, dims 64m + 16grp .. +15
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                kraw[tb][m] = *reinterpret_cast<const uint4*>(blk + (16 * tb + col) * D + 64 * m + 16 * grp);
+        uint4 vraw[NDB];  // dim 16db + col, tokens 16grp .. +15
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vraw[db] = *reinterpret_cast<const uint4*>(blk + q8_vcodes_off(D) + (16 * db + col) * PAGE + 16 * grp);
+        float vsc[4];  // scale of token 16tb + col
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) vsc[tb] = reinterpret_cast<const float*>(blk + q8_vscale_off(D))[16 * tb + col];
+        // ---- A: the query row times the channel scales, term ah ----
+        uint4 qa[2 * NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            float x[16];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const float4 k4 =
+                    *reinterpret_cast<const float4*>(blk + q8_kscale_off(D) + 4 * (64 * m + 16 * grp + 4 * c4));
+                x[4 * c4] = qv[m][4 * c4] * k4.x;
+                x[4 * c4 + 1] = qv[m][4 * c4 + 1] * k4.y;
+                x[4 * c4 + 2] = qv[m][4 * c4 + 2] * k4.z;
+                x[4 * c4 + 3] = qv[m][4 * c4 + 3] * k4.w;
+            }
+            qa[2 * m] = make_uint4(bf16_term2(x[0], x[1], ah), bf16_term2(x[2], x[3], ah), bf16_term2(x[4], x[5], ah),
+                                   bf16_term2(x[6], x[7], ah));
+            qa[2 * m + 1] = make_uint4(bf16_term2(x[8], x[9], ah), bf16_term2(x[10], x[11], ah),
+                                       bf16_term2(x[12], x[13], ah), bf16_term2(x[14], x[15], ah));
+        }
+        // ---- S^T: row 4grp + r = (head 2grp + r/2, term r%2), column = token 16tb + col ----
+        f32x4_t st[4];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+            st[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                const uint4 r = kraw[tb][m];
+                st[tb] = mma_bf16(qa[2 * m], i8x8_bf16(r.x, r.y), st[tb]);
+                st[tb] = mma_bf16(qa[2 * m + 1], i8x8_bf16(r.z, r.w), st[tb]);
+            }
+        }
+        // ---- online softmax of heads 2grp, 2grp + 1 over the page's tokens ----
+        const int n_tok = min(PAGE, ctx - pg * PAGE);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int j = 2 * grp + hh;
+            const bool live = j < G;
+            float sv[4], mt = -INFINITY;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                const bool valid = 16 * tb + col < n_tok;
+                const float raw = st[tb][2 * hh] + st[tb][2 * hh + 1];
+                if constexpr (SCORES)
+                    if (live && valid) scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + 16 * tb + col] = sm * raw;
+                sv[tb] = valid && live ? raw * cs : -INFINITY;
+                mt = fmaxf(mt, sv[tb]);
+            }
+            const float m_new = fmaxf(m_run[hh], row_max16(mt));
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[hh] - m_new);
+            float psum = 0.f;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                // slots past ctx weigh nothing (their codes and scales may be any bytes)
+                const float p = sv[tb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb] - m_new);
+                psum += p;
+                const float wgt = p != 0.f ? p * vsc[tb] : 0.f;
+                const uint32_t hl = bf16_hi_lo(wgt);
+                if (live) {
+                    w_s[wave][2 * j][16 * tb + col] = (uint16_t)(hl & 0xFFFF);
+                    w_s[wave][2 * j + 1][16 * tb + col] = (uint16_t)(hl >> 16);
+                }
+            }
+            l_run[hh] = l_run[hh] * alpha + row_sum16(psum);
+            m_run[hh] = m_new;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                acc[db][2 * hh] *= alpha;
+                acc[db][2 * hh + 1] *= alpha;
+            }
+        }
+        // ---- O += W~ V: A = weight row col, tokens 16grp .. +15 (the wave's LDS is read in order) ----
+        const uint4 wa0 = *reinterpret_cast<const uint4*>(&w_s[wave][col][16 * grp]);
+        const uint4 wa1 = *reinterpret_cast<const uint4*>(&w_s[wave][col][16 * grp + 8]);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const uint4 r = vraw[db];
+            acc[db] = mma_bf16(wa0, i8x8_bf16(r.x, r.y), acc[db]);
+            acc[db] = mma_bf16(wa1, i8x8_bf16(r.z, r.w), acc[db]);
+        }
+    }
+
+    // ---- combine the four waves (a wave without pages holds m = -inf, l = 0, o = 0) ----
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int j = 2 * grp + hh;
+        if (j < G) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) o_s[wave][j][16 * db + col] = acc[db][2 * hh] + acc[db][2 * hh + 1];
+            if (col == 0) {
+                ml_s[wave][j][0] = m_run[hh];
+                ml_s[wave][j][1] = l_run[hh];
+            }
+        }
+    }
+    __syncthreads();
+    DecodeWs w(ws, bd.n, Hq, D, splits);
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int j = idx / D, d = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_s[v][j][0]);
+        float accum = 0.f, L = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float f = ml_s[v][j][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml_s[v][j][0] - M);
+            accum += f * o_s[v][j][d];
+            L += f * ml_s[v][j][1];
+        }
+        const int64_t r = ((int64_t)e * Hq + g * G + j) * splits + sp;
+        w.o[r * D + d] = accum;
+        if (d == 0) {
+            w.ml[2 * r] = M;
+            w.ml[2 * r + 1] = L;
+        }
+    }
+}
+
 hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
     dim3 grid(bd.n * pv.Hkv, splits);
@@ -376,7 +619,10 @@ hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, 
     };
     auto wave_form = [&](auto d_tag, auto g_tag) {
         constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
-        scores ? go(decode_q8_wave_kernel<DD, GG, true>) : go(decode_q8_wave_kernel<DD, GG, false>);
+        if constexpr (Q8_MATRIX_CORES && DD == 128)  // at 256 dims its registers spill: the VALU form runs
+            scores ? go(decode_q8_mfma_kernel<DD, GG, true>) : go(decode_q8_mfma_kernel<DD, GG, false>);
+        else
+            scores ? go(decode_q8_wave_kernel<DD, GG, true>) : go(decode_q8_wave_kernel<DD, GG, false>);
     };
     using D128 = std::integral_constant<int, 128>;
     using D256 = std::integral_constant<int, 256>;

@@ -331,17 +331,17 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 // Default split count for a decode batch.  2-bit: about one workgroup per
 // compute unit (256 on MI355X) over all (sequence, KV head) pairs, with at
 // least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
-// about sixteen pages per split of the longest sequence (four per wavefront),
-// since its workgroups are small enough for several to share a compute unit
-// (measured on 24 lanes of 16..124 pages: 8 splits 82 us a layer, 2 splits
-// 215 us, 32 splits 90 us).
+// at least that many workgroups, and splits of about sixteen page pairs of the
+// longest sequence (eight pages per wavefront), since several of its smaller
+// workgroups share a compute unit (measured on 24 lanes of 16..124 pages:
+// 4 splits 67 us a layer, 2 splits 88 us, 8 splits 71 us).
 int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     int64_t max_pages = 1;
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
     const int64_t base = (int64_t)n * p->geom.n_kv_heads;
     const int64_t want = (256 + base - 1) / base;
     if (p->fmt == KV_FMT_Q8)
-        return (int)std::max<int64_t>(1, std::min<int64_t>(256, std::max<int64_t>(want, (max_pages + 15) / 16)));
+        return (int)std::max<int64_t>(1, std::min<int64_t>(256, std::max<int64_t>(want, ((max_pages + 1) / 2 + 15) / 16)));
     const int64_t cap = std::max<int64_t>(1, ((max_pages + 1) / 2) / 8);
     return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
 }
@@ -472,6 +472,7 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
     }
     if (d_scores && scores_stride < max_ctx) return fail(KV_ERR_ARG, "scores_stride %lld < max ctx_len %lld", (long long)scores_stride, (long long)max_ctx);
     int sp = n_splits > 0 ? n_splits : auto_splits(p, n, ctx_len);
+    bd.per = split_pairs_per((int)max_ctx, sp);
     int64_t need = 4 * decode_ws_floats(n, p->geom.n_q_heads, p->geom.head_dim, sp);
     if (!d_ws || ws_bytes < need)
         return fail(KV_ERR_WORKSPACE, "decode needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);

@@ -31,6 +31,7 @@ struct BatchDesc {
     int32_t cnt[KV_MAX_BATCH];        // append: tokens appended
     int32_t row0[KV_MAX_BATCH];       // append: first input row of the entry
     int32_t work0[KV_MAX_BATCH + 1];  // prefix sum of work items per entry
+    int32_t per;                      // decode: page pairs per split, the same for every entry
 };
 
 // Byte offsets inside a 2-bit (layer, head) block of D dims.
@@ -82,12 +83,17 @@ inline int64_t prefill_ws_floats(int n_q, int Hq, int D, int splits) {
     return (int64_t)n_q * Hq * splits * (D + 2);
 }
 
-// Pages of a context of `ctx` tokens handled by split `p` of `splits`, in
-// whole pairs of pages (the decode kernels step two pages at a time).
-__host__ __device__ inline void split_range(int ctx, int splits, int p, int* pg0, int* pg1) {
+// Decode splits: every split of a batch covers `per` whole pairs of pages
+// (the decode kernels step two pages at a time), per = ceil(pairs of the
+// longest context / splits), so a shorter context fills fewer splits and no
+// split holds more work than another.  Pages of a context of `ctx` tokens
+// handled by split `p`:
+__host__ __device__ inline int split_pairs_per(int max_ctx, int splits) {
+    const int pairs = ((max_ctx + PAGE - 1) / PAGE + 1) / 2;
+    return (pairs + splits - 1) / splits;
+}
+__host__ __device__ inline void split_range(int ctx, int per, int p, int* pg0, int* pg1) {
     int n_pages = (ctx + PAGE - 1) / PAGE;
-    int pairs = (n_pages + 1) / 2;
-    int per = (pairs + splits - 1) / splits;
     int a = p * per * 2, b = a + per * 2;
     *pg0 = a < n_pages ? a : n_pages;
     *pg1 = b < n_pages ? b : n_pages;

@@ -11,7 +11,7 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq,
     constexpr int U = 8;
     const int e = blockIdx.x / Hq;
     const int d = threadIdx.x;
-    const int live = live_splits(bd.pos[e], splits);
+    const int live = live_splits(bd.pos[e], bd.per);
     const int64_t row = blockIdx.x;  // e * Hq + h
     const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + row * splits;
     const float* o = ws + row * splits * D + d;
