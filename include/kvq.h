@@ -170,11 +170,13 @@ kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_le
 /* One decode step for n sequences of one layer.  d_q: bf16 [n][Hq][D], one
  * query per sequence; sequence i attends to its tokens 0 .. ctx_len[i]-1
  * (ctx_len >= 1, within the reserved bound).  Scores are sm_scale x q.k^ over
- * the dequantized keys; softmax and all sums are kept in fp32; the context is
- * split into n_splits (1..256, 0 = kv_decode_splits' choice) ranges of
- * whole page pairs (flash-decoding) whose partial results (max, sum,
- * unnormalised output) go to d_ws; a second kernel on the same stream merges
- * them in fp32 (two launches per call).
+ * the dequantized keys; softmax and all sums are kept in fp32; the contexts
+ * are split into ranges of whole page pairs (flash-decoding), all of one size:
+ * ceil(page pairs of the longest context / n_splits), n_splits in 1..256
+ * (0 = kv_decode_splits' choice), so a shorter context fills fewer ranges.
+ * The ranges' partial results (max, sum, unnormalised output) go to d_ws; a
+ * second kernel on the same stream merges them in fp32 (two launches per
+ * call).
  * d_out: fp32 [n][Hq][D].  d_scores: NULL, or fp32 [n][Hq][scores_stride]
  * receiving the raw logits (scores_stride >= max ctx_len).  Every workspace
  * byte read is written first within the call.  Errors: KV_ERR_ARG,
