@@ -45,11 +45,28 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
     hi = wave_max(hi) + 0.0f;
     float sc = (hi - lo) / 3.0f;
     if (sc == 0.0f) sc = 1.0f;
+    // code = clamp(rint(RN(RN(x - mn) / sc)), 0, 3).  Only the rounded integer
+    // is kept, so the quotient is first taken as d * rcp(sc): that is within
+    // 6.6e-7 of the correctly rounded quotient (rcp within one ulp, the product
+    // within half an ulp, the quotient below 3.000001), so unless it lies
+    // within 2e-6 of a half-integer both round to the same code.  The rare
+    // element that does takes the correctly rounded division.
+    const float inv = __builtin_amdgcn_rcpf(sc);
+    bool near = false;
+    float d[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
-        float t = (x[k] - lo) / sc;
-        float r = fminf(fmaxf(rintf(t), 0.0f), 3.0f);
-        c[k] = (uint32_t)r;
+        d[k] = x[k] - lo;
+        const float ta = d[k] * inv;
+        near |= fabsf((ta - floorf(ta)) - 0.5f) < 2e-6f;
+        c[k] = (uint32_t)fminf(fmaxf(rintf(ta), 0.0f), 3.0f);
+    }
+    if (__builtin_amdgcn_ballot_w64(near)) {
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            const float t = d[k] / sc;
+            c[k] = (uint32_t)fminf(fmaxf(rintf(t), 0.0f), 3.0f);
+        }
     }
     scale = sc;
     mn = lo;

@@ -51,6 +51,39 @@ def test_append_q2_tiny_bit_exact():
     assert st["used_pages"] == 4 and st["reserved_pages"] == 4 and st["free_pages"] == 2
 
 
+def test_append_q2_half_step_rows_bit_exact():
+    """Rows whose values sit on half steps of the code grid, x = lo + (k/2) s
+    with s a power of two: every odd k is a tie of the rounding to a code
+    (round half to even), the case where the quotient must be the correctly
+    rounded one."""
+    need_gpu()
+    w = C0
+    n_pages = 3
+    pool, mem = make_pool(w, n_pages, 1)
+    bt = page_permutation(w, n_pages, salt=5)[:2]
+    seq = pool.reserve(128, pages=bt)
+    rng = np.random.default_rng(1234)
+    rows = []
+    for _ in range(2 * 128 * w.n_kv_heads):
+        s = 2.0 ** int(rng.integers(-4, 3))
+        m = int(rng.integers(-40, 40))
+        k = rng.integers(0, 7, size=w.head_dim)
+        k[int(rng.integers(0, w.head_dim))] = 0
+        k[int(rng.integers(0, w.head_dim))] = 6
+        rows.append((m + k) * s / 2)
+    x = torch.tensor(np.array(rows, np.float32)).to(torch.bfloat16)   # exact: |m + k| < 256
+    assert torch.equal(x.float(), torch.tensor(np.array(rows, np.float32)))
+    x = x.view(2, 128, w.n_kv_heads, w.head_dim)
+    k_all, v_all = x[0], x[1]
+    op = opool.OraclePool("q2", 1, w.n_kv_heads, w.head_dim, n_pages)
+    _append_both(pool, op, 0, [seq], [bt], [[(0, 70)], [(0, 58)]], [k_all], [v_all])
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(n_pages, -1)
+    diff = np.count_nonzero(got != op.data)
+    say(f"half-step rows: {diff} differing bytes of {got.size}")
+    assert diff == 0
+
+
 def test_append_q2_batched_ragged_d128_bit_exact():
     need_gpu()
     w = SMALL128
