@@ -24,14 +24,35 @@
 // Work split: one workgroup of four waves per (sequence, page touched, KV
 // head); wave w owns the token slots of V word w (slots s with (s/4)%4 == w),
 // so the V plane is written with one read-modify-write per (dim, word) and no
-// two workgroups or waves share a byte.
+// two workgroups or waves share a byte.  A row is spread over the 16 lanes of
+// a DPP row, so a wave quantizes four rows at once and its min / max
+// reductions stay inside DPP rows.
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 
-// Quantize one row spread over a wavefront, DPL consecutive elements per lane.
-// Returns the lane's codes; scale and mn are the same in every lane.
+// Extreme of a row held by the 16 lanes of a DPP row: butterflies with quad
+// permutes, then rotations by 4 and 8; every lane of the row ends with it.
+template <bool MAX>
+__device__ __forceinline__ float row16_extreme(float v) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+    auto dpp = [](float x, auto ctrl_tag) {
+        constexpr int CTRL = decltype(ctrl_tag)::value;
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+    };
+    v = op(v, dpp(v, std::integral_constant<int, 0xB1>{}));   // quad_perm [1, 0, 3, 2]
+    v = op(v, dpp(v, std::integral_constant<int, 0x4E>{}));   // quad_perm [2, 3, 0, 1]
+    v = op(v, dpp(v, std::integral_constant<int, 0x124>{}));  // row_ror 4
+    v = op(v, dpp(v, std::integral_constant<int, 0x128>{}));  // row_ror 8
+    return v;
+}
+
+// Quantize one row spread over the 16 lanes of a DPP row, DPL consecutive
+// elements per lane.  Returns the lane's codes; scale and mn are the same in
+// every lane of the row.
 template <int DPL>
 __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t (&c)[DPL], float& scale, float& mn) {
 #pragma clang fp contract(off)
@@ -41,8 +62,8 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
         lo = fminf(lo, x[k]);
         hi = fmaxf(hi, x[k]);
     }
-    lo = wave_min(lo) + 0.0f;
-    hi = wave_max(hi) + 0.0f;
+    lo = row16_extreme<false>(lo) + 0.0f;
+    hi = row16_extreme<true>(hi) + 0.0f;
     float sc = (hi - lo) / 3.0f;
     if (sc == 0.0f) sc = 1.0f;
     // code = clamp(rint(RN(RN(x - mn) / sc)), 0, 3).  Only the rounded integer
@@ -58,8 +79,9 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
     for (int k = 0; k < DPL; ++k) {
         d[k] = x[k] - lo;
         const float ta = d[k] * inv;
-        near |= fabsf((ta - floorf(ta)) - 0.5f) < 2e-6f;
-        c[k] = (uint32_t)fminf(fmaxf(rintf(ta), 0.0f), 3.0f);
+        const float ra = rintf(ta);
+        near |= fabsf(ta - ra) > 0.5f - 2e-6f;  // within 2e-6 of a half-integer
+        c[k] = (uint32_t)fminf(fmaxf(ra, 0.0f), 3.0f);
     }
     if (__builtin_amdgcn_ballot_w64(near)) {
 #pragma unroll
@@ -72,11 +94,27 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
     mn = lo;
 }
 
+// N (8 or 16) consecutive bf16 values as fp32, in 16-byte loads
+template <int N>
+__device__ __forceinline__ void load_bf16_rows(const uint16_t* p, float (&x)[N]) {
+    static_assert(N % 8 == 0, "whole 16-byte chunks");
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+        const uint4 w = reinterpret_cast<const uint4*>(p)[i];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[8 * i + 2 * k] = __uint_as_float(u[k] << 16);
+            x[8 * i + 2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, BatchDesc bd,
                                                         const uint16_t* __restrict__ kin,
                                                         const uint16_t* __restrict__ vin) {
-    constexpr int DPL = D / 64;
+    constexpr int DPL = D / 16;  // dims of a lane: a row is spread over 16 lanes
     const int x = blockIdx.x, head = blockIdx.y;
     int e = 0;
     while (e + 1 < bd.n && bd.work0[e + 1] <= x) ++e;
@@ -87,48 +125,65 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
     const int phys = pv.bt[(int64_t)bd.seq[e] * pv.bt_stride + lp];
     uint8_t* blk = pv.pages + (int64_t)phys * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, c = lane & 15;
 
     uint32_t vw[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) vw[k] = 0;
     uint32_t vmask = 0;
-    // this wave's slots: 16b + 4 * wave + r, in increasing order
-    for (int i = 0; i < 16; ++i) {
-        const int s = 16 * (i >> 2) + 4 * wave + (i & 3);
-        if (s < slot_lo || s >= slot_hi) continue;
-        const int64_t row = (int64_t)bd.row0[e] + (lp * PAGE + s - start);
-        const int64_t off = (row * pv.Hkv + head) * D + lane * DPL;
+    // this wave's slots 16b + 4 * wave + r; step b takes the four r at once,
+    // lane group r (16 lanes, DPL dims each) holding slot 16b + 4 * wave + r
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int s0 = 16 * b + 4 * wave;
+        if (s0 + 3 < slot_lo || s0 >= slot_hi) continue;  // none of the four appended
+        const int s = s0 + grp;
+        const bool in = s >= slot_lo && s < slot_hi;
+        const int sl = in ? s : max(s0, slot_lo);  // a slot outside the range re-reads one inside it, unused
+        const int64_t row = (int64_t)bd.row0[e] + (lp * PAGE + sl - start);
+        const int64_t off = (row * pv.Hkv + head) * D + c * DPL;
         float xk[DPL], xv[DPL];
-        load_bf16<DPL>(kin + off, xk);
-        load_bf16<DPL>(vin + off, xv);
+        load_bf16_rows<DPL>(kin + off, xk);
+        load_bf16_rows<DPL>(vin + off, xv);
         uint32_t ck[DPL], cv[DPL];
         float sk, mk, sv, mv;
         q2_quantize_row<DPL>(xk, ck, sk, mk);
         q2_quantize_row<DPL>(xv, cv, sv, mv);
-        uint32_t bits = 0;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) bits |= ck[k] << (2 * k);
-        uint8_t* krow = blk + (int64_t)s * (D / 4);
-        if constexpr (DPL == 4) {
-            krow[lane] = (uint8_t)bits;
-        } else {
-            uint32_t other = __shfl_down(bits, 1);
-            if ((lane & 1) == 0) krow[lane >> 1] = (uint8_t)(bits | (other << 4));
-        }
-        const int sh = q2_vslot_bit(s);
+        for (int r = 0; r < 4; ++r)
+            if (s0 + r >= slot_lo && s0 + r < slot_hi) vmask |= 3u << q2_vslot_bit(s0 + r);
+        if (in) {
+            // K row: dim j at bit 2(j % 4) of byte j / 4, so this lane's DPL dims are
+            // 2 DPL bits at byte DPL / 4 * c
+            uint32_t bits = 0;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) vw[k] |= cv[k] << sh;
-        vmask |= 3u << sh;
-        if (lane == 0) {
-            *reinterpret_cast<float2*>(blk + q2_kmeta_off(D) + 8 * s) = make_float2(sk, mk);
-            *reinterpret_cast<float2*>(blk + q2_vmeta_off(D) + 8 * s) = make_float2(sv, mv);
+            for (int k = 0; k < DPL; ++k) bits |= ck[k] << (2 * k);
+            uint8_t* krow = blk + (int64_t)s * (D / 4);
+            if constexpr (DPL == 16)
+                reinterpret_cast<uint32_t*>(krow)[c] = bits;
+            else
+                reinterpret_cast<uint16_t*>(krow)[c] = (uint16_t)bits;
+            const int sh = q2_vslot_bit(s);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) vw[k] |= cv[k] << sh;
+            if (c == 0) {
+                *reinterpret_cast<float2*>(blk + q2_kmeta_off(D) + 8 * s) = make_float2(sk, mk);
+                *reinterpret_cast<float2*>(blk + q2_vmeta_off(D) + 8 * s) = make_float2(sv, mv);
+            }
         }
     }
     if (vmask == 0) return;
+    // the four lane groups hold disjoint slots of the same dims: OR them, then
+    // the first group writes word `wave` of each of the lane's dims
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {
-        const int d = lane * DPL + k;
+        vw[k] |= __shfl_xor(vw[k], 16);
+        vw[k] |= __shfl_xor(vw[k], 32);
+    }
+    if (grp != 0) return;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+        const int d = c * DPL + k;
         uint32_t* p = reinterpret_cast<uint32_t*>(blk + q2_vcodes_off(D) + q2_vword_off(D, d, wave));
         uint32_t old = (vmask == 0xFFFFFFFFu) ? 0u : *p;
         *p = (old & ~vmask) | vw[k];
