@@ -18,7 +18,9 @@
 // dim-major [D][64] at 64D, K scales fp32 [D] at 128D, V scales fp32 [64] at
 // 132D.
 //
-// One workgroup of 256 threads per (sequence, page touched, KV head).  The
+// One workgroup of 256 threads per (sequence, page touched, KV head); K
+// channels take 256 / D threads each (token ranges whose absmax meet in LDS),
+// V codes are staged dim-major in LDS and written in 4-byte runs of slots.  The
 // host never launches a page that reads staged rows together with a later
 // page of the same sequence that rewrites them (it splits such an append in
 // two launches), so staging reads and writes never race.
@@ -26,6 +28,20 @@
 #include "kvq_internal.h"
 
 namespace kvq {
+
+// clamp(rint(RN(x / s)), -127, 127).  Only the rounded integer is kept, so
+// the quotient is first taken as x * rcp(s): within 2.7e-5 of the correctly
+// rounded quotient (rcp within one ulp, the product within half an ulp, the
+// quotient at most 127.0001 in size), so unless it lies within 1e-4 of a
+// half-integer both round to the same integer; the rare element that does
+// takes the correctly rounded division.
+__device__ __forceinline__ int8_t q8_code(float x, float s, float inv) {
+#pragma clang fp contract(off)
+    const float qa = x * inv;
+    float r = rintf(qa);
+    if (fabsf(qa - r) > 0.5f - 1e-4f) r = rintf(x / s);
+    return (int8_t)fminf(fmaxf(r, -127.0f), 127.0f);
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void append_q8_kernel(PoolView pv, int layer, BatchDesc bd,
@@ -61,23 +77,33 @@ __global__ __launch_bounds__(256) void append_q8_kernel(PoolView pv, int layer, 
             stage[(int64_t)s * D + d] = k_s[s][d];
         }
 
-    // ---- K: per-channel scales and the codes of every present token ----
+    // ---- K: per-channel scales and the codes of every present token; TPD
+    // threads per channel, each a range of tokens ----
+    constexpr int TPD = 256 / D;
+    __shared__ float kamax_s[TPD][D];
+    __shared__ __align__(16) int8_t vq_s[D][PAGE];  // this append's V codes, dim-major
     int8_t* kc = reinterpret_cast<int8_t*>(blk);
     float* ks = reinterpret_cast<float*>(blk + q8_kscale_off(D));
-    for (int d = tid; d < D; d += 256) {
+    {
+        const int d = tid % D, part = tid / D;
+        const int t0 = part * (PAGE / TPD), t1 = min(t0 + PAGE / TPD, slot_hi);
         float amax = 0.f;
-        for (int s = 0; s < slot_hi; ++s) amax = fmaxf(amax, fabsf(bf16_to_f32(k_s[s][d])));
+        for (int s = t0; s < t1; ++s) amax = fmaxf(amax, fabsf(bf16_to_f32(k_s[s][d])));
+        if constexpr (TPD > 1) {
+            kamax_s[part][d] = amax;
+            __syncthreads();
+#pragma unroll
+            for (int p = 0; p < TPD; ++p) amax = fmaxf(amax, kamax_s[p][d]);
+        }
         float sc = amax / 127.0f;
         if (sc == 0.0f) sc = 1.0f;
-        ks[d] = sc;
-        for (int s = 0; s < slot_hi; ++s) {
-            const float c = fminf(fmaxf(rintf(bf16_to_f32(k_s[s][d]) / sc), -127.0f), 127.0f);
-            kc[s * D + d] = (int8_t)c;
-        }
+        if (part == 0) ks[d] = sc;
+        const float inv = __builtin_amdgcn_rcpf(sc);
+        for (int s = t0; s < t1; ++s) kc[s * D + d] = q8_code(bf16_to_f32(k_s[s][d]), sc, inv);
     }
 
-    // ---- V: per-token scale, codes dim-major; wave w takes slots w, w+4, ... ----
-    int8_t* vc = reinterpret_cast<int8_t*>(blk + q8_vcodes_off(D));
+    // ---- V: per-token scale; wave w takes slots slot_lo + w, + 4, ...; codes
+    // go to LDS dim-major, then out in 4-byte runs of slots ----
     float* vs = reinterpret_cast<float*>(blk + q8_vscale_off(D));
     for (int s = slot_lo + wave; s < slot_hi; s += 4) {
         float xv[DPL];
@@ -88,12 +114,23 @@ __global__ __launch_bounds__(256) void append_q8_kernel(PoolView pv, int layer, 
         amax = wave_max(amax);
         float sc = amax / 127.0f;
         if (sc == 0.0f) sc = 1.0f;
+        const float inv = __builtin_amdgcn_rcpf(sc);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) {
-            const float c = fminf(fmaxf(rintf(xv[k] / sc), -127.0f), 127.0f);
-            vc[(lane * DPL + k) * PAGE + s] = (int8_t)c;
-        }
+        for (int k = 0; k < DPL; ++k) vq_s[lane * DPL + k][s] = q8_code(xv[k], sc, inv);
         if (lane == 0) vs[s] = sc;
+    }
+    __syncthreads();
+    uint8_t* vc = blk + q8_vcodes_off(D);
+    for (int i = tid; i < D * (PAGE / 4); i += 256) {
+        const int d = i / (PAGE / 4), s4 = 4 * (i % (PAGE / 4));
+        if (s4 + 3 < slot_lo || s4 >= slot_hi) continue;
+        if (s4 >= slot_lo && s4 + 3 < slot_hi) {
+            *reinterpret_cast<uint32_t*>(vc + d * PAGE + s4) = *reinterpret_cast<const uint32_t*>(&vq_s[d][s4]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (s4 + r >= slot_lo && s4 + r < slot_hi) vc[d * PAGE + s4 + r] = (uint8_t)vq_s[d][s4 + r];
+        }
     }
 }
 

@@ -76,6 +76,34 @@ def test_append_q8_bit_exact_ragged():
     assert diff == 0
 
 
+def test_append_q8_half_step_rows_bit_exact():
+    """Codes on ties: every K channel and every V row holds 127 * 2^e (so the
+    scale is exactly 2^e) and values (k + 1/2) 2^e elsewhere, each a tie of the
+    rounding to an integer code (round half to even)."""
+    need_gpu()
+    w = SMALL8
+    L = 128
+    pool, mem, op, bts, seqs = _setup(w, [L], 3)
+    rng = np.random.default_rng(4321)
+    H, D = w.n_kv_heads, w.head_dim
+    ek = rng.integers(-6, 3, size=(1, H, D)).astype(np.float64)
+    kq = rng.integers(-127, 127, size=(L, H, D)) + 0.5
+    kq[0] = 127.0                                   # token 0: the absmax of every channel
+    ev = rng.integers(-6, 3, size=(L, 1, 1)).astype(np.float64)
+    vq = rng.integers(-127, 127, size=(L, H, D)) + 0.5
+    vq[:, :, 0] = -127.0                            # dim 0: the absmax of every row
+    kf, vf = (kq * 2.0 ** ek).astype(np.float32), (vq * 2.0 ** ev).astype(np.float32)
+    k, v = torch.tensor(kf).to(torch.bfloat16), torch.tensor(vf).to(torch.bfloat16)
+    assert torch.equal(k.float(), torch.tensor(kf)) and torch.equal(v.float(), torch.tensor(vf))
+    starts = [0]
+    _append_chunks(pool, op, 0, seqs, bts, [[(0, 37)], [(0, 1)], [(0, 90)]], [k], [v], starts)
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(3, -1)
+    diff = np.count_nonzero(got != op.data)
+    say(f"8-bit half-step rows: {diff} differing bytes of {got.size}")
+    assert diff == 0
+
+
 def test_append_q8_d256_and_dequant():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
