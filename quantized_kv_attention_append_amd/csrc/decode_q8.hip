@@ -420,15 +420,23 @@ __device__ __forceinline__ uint32_t bf16_hi_lo(float x) {
     const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){r, 0.f}, bf16x2_t));
     return hi | (lo << 16);
 }
+// Max / sum over each 16-lane row with DPP: quad butterflies, then the row
+// rotated by 4 and by 8 (every lane ends with the row's result).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float row_max16(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1, 0, 3, 2]
+    v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+    v = fmaxf(v, dpp_f<0x124>(v));  // row_ror 4
+    return fmaxf(v, dpp_f<0x128>(v));  // row_ror 8
 }
 __device__ __forceinline__ float row_sum16(float v) {
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x124>(v);
+    return v + dpp_f<0x128>(v);
 }
 
 }  // namespace

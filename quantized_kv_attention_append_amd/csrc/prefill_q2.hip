@@ -76,6 +76,15 @@ __device__ __forceinline__ void split_hi_lo(float a, float b, uint32_t& hi, uint
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){ra, rb}, bf16x2));
 }
 
+// Max over the four 16-lane rows of the wave (the value of lanes l, l^16,
+// l^32, l^48), with the row-swapping permutes instead of LDS shuffles.
+__device__ __forceinline__ float max_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 }  // namespace
 
 template <int D>
@@ -300,8 +309,7 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
                     st[cb][kb][r] = x;
                     mt = fmaxf(mt, x);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = max_rows(mt);
             // lazy rescale: the reference moves only when a weight would pass 2^8
             const bool up = (mt - m_ref[cb]) * cB > 8.0f;
             alpha[cb] = up ? __builtin_amdgcn_exp2f((m_ref[cb] - mt) * cB) : 1.0f;
