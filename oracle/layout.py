@@ -28,6 +28,13 @@ pool, section "See it, control it").  Inside a page, the data of one
     [128*D, 132*D)   K scales: fp32 per channel (one set per page)
     [132*D, 132*D+256) V scales: fp32 per token slot
 
+bf16 block (D dims; 512 B per head per token, the BF16 row of the page's
+table, so 65,536 B a token at the 27B geometry):
+    [0,       128*D)  K, bf16 bit patterns, token-major: row t (2D bytes) at 2*D*t
+    [128*D,   256*D)  V, bf16 bit patterns, dim-major:   row d (128 bytes) at 128*d
+  The exact cache the pages compare every compressed format against, kept in
+  the same paged pool so that the same gather reads it.
+
 The arrangement inside a block is not fixed by the pages (they give only the
 bytes per head per token); the byte totals match them exactly.  Pinned by
 closed forms: block sizes reproduce 9,216 B/token at the 27B geometry and the
@@ -50,8 +57,18 @@ def q8_block_bytes(D: int) -> int:
     return 132 * D + 256
 
 
+def bf16_block_bytes(D: int) -> int:
+    return 256 * D
+
+
 def block_bytes(fmt: str, D: int) -> int:
-    return q2_block_bytes(D) if fmt == "q2" else q8_block_bytes(D)
+    if fmt == "q2":
+        return q2_block_bytes(D)
+    if fmt == "q8":
+        return q8_block_bytes(D)
+    if fmt == "bf16":
+        return bf16_block_bytes(D)
+    raise ValueError(fmt)
 
 
 def block_offset(fmt: str, layer: int, head: int, n_kv_heads: int, D: int) -> int:
@@ -189,3 +206,19 @@ class Q8Block:
 
     def read_v(self, n: int):
         return self.v_codes[:, :n].T.copy(), self.v_scale[:n].copy()
+
+
+class Bf16Block:
+    """Views into one bf16 (layer, head) block of a page: bit patterns, no metadata."""
+
+    def __init__(self, buf: np.ndarray, D: int):
+        assert buf.dtype == np.uint8 and buf.size == bf16_block_bytes(D)
+        self.D = D
+        self.k = buf[0:128 * D].view(np.uint16).reshape(PAGE, D)
+        self.v = buf[128 * D:256 * D].view(np.uint16).reshape(D, PAGE)
+
+    def read_k(self, n: int):
+        return self.k[:n].copy()
+
+    def read_v(self, n: int):
+        return self.v[:, :n].T.copy()

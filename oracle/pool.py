@@ -8,7 +8,9 @@ sequence lives in physical page ``bt[i]``; token t sits in slot t % 64 of page
 ``bt[t // 64]``.
 
 append writes each new token's K and V rows quantized into its slot, leaving
-every other slot of the pool untouched.  For the 8-bit variant, K is scaled per
+every other slot of the pool untouched.  The bf16 format stores the rows as
+they come (their bf16 bit patterns): the exact cache the pages measure the
+compressed formats against, read through the same block tables.  For the 8-bit variant, K is scaled per
 channel over the tokens present in the open page; the exact K rows of that page
 are kept aside (the exact window), and each append re-derives the page's K codes
 and scales from the exact rows present, so a full page equals the plain
@@ -23,14 +25,14 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import codec
+from . import bf16, codec
 from .accounting import page_bytes
-from .layout import PAGE, Q2Block, Q8Block, block_bytes, block_offset
+from .layout import PAGE, Bf16Block, Q2Block, Q8Block, block_bytes, block_offset
 
 
 class OraclePool:
     def __init__(self, fmt: str, n_layers: int, n_kv_heads: int, head_dim: int, n_pages: int, fill: int = 0xA5):
-        assert fmt in ("q2", "q8")
+        assert fmt in ("q2", "q8", "bf16")
         self.fmt, self.L, self.H, self.D = fmt, n_layers, n_kv_heads, head_dim
         self.page_bytes = page_bytes(fmt, n_layers, n_kv_heads, head_dim)
         self.data = np.full((n_pages, self.page_bytes), fill, dtype=np.uint8)
@@ -39,7 +41,7 @@ class OraclePool:
     def block(self, page: int, layer: int, head: int):
         off = block_offset(self.fmt, layer, head, self.H, self.D)
         buf = self.data[page, off:off + block_bytes(self.fmt, self.D)]
-        return Q2Block(buf, self.D) if self.fmt == "q2" else Q8Block(buf, self.D)
+        return {"q2": Q2Block, "q8": Q8Block, "bf16": Bf16Block}[self.fmt](buf, self.D)
 
     # ------------------------------------------------------------ append --
     def append(self, layer: int, seq: int, bt, start: int, k_rows, v_rows):
@@ -50,6 +52,16 @@ class OraclePool:
         if n == 0:
             return
         assert k.shape == (n, self.H, self.D) and v.shape == k.shape
+        if self.fmt == "bf16":
+            kb, vb = bf16.f32_to_bits(k), bf16.f32_to_bits(v)
+            for i in range(n):
+                pos = start + i
+                page, slot = int(bt[pos // PAGE]), pos % PAGE
+                for h in range(self.H):
+                    blk = self.block(page, layer, h)
+                    blk.k[slot] = kb[i, h]
+                    blk.v[:, slot] = vb[i, h]
+            return
         if self.fmt == "q2":
             ck, sk, mk = codec.q2_quantize(k)
             cv, sv, mv = codec.q2_quantize(v)
@@ -102,7 +114,10 @@ class OraclePool:
             page = int(bt[lp])
             for h in range(self.H):
                 blk = self.block(page, layer, h)
-                if self.fmt == "q2":
+                if self.fmt == "bf16":
+                    K[lp * PAGE:lp * PAGE + n, h] = bf16.bits_to_f32(blk.read_k(n))
+                    V[lp * PAGE:lp * PAGE + n, h] = bf16.bits_to_f32(blk.read_v(n))
+                elif self.fmt == "q2":
                     c, s, m = blk.read_k(n)
                     K[lp * PAGE:lp * PAGE + n, h] = codec.q2_dequantize(c, s, m)
                     c, s, m = blk.read_v(n)
@@ -123,6 +138,9 @@ def dequantized_rows(fmt: str, k_rows, v_rows):
     """
     k = np.asarray(k_rows, np.float32)
     v = np.asarray(v_rows, np.float32)
+    if fmt == "bf16":
+        bf16.f32_to_bits(k), bf16.f32_to_bits(v)  # the rows must be bf16 numbers
+        return k.copy(), v.copy()
     if fmt == "q2":
         K = codec.q2_dequantize(*codec.q2_quantize(k))
         V = codec.q2_dequantize(*codec.q2_quantize(v))

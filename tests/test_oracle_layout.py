@@ -31,6 +31,9 @@ def test_block_sizes_match_token_bytes():
         assert L * H * layout.q2_block_bytes(D) == accounting.page_bytes("q2", L, H, D)
     assert 32 * 8 * layout.q8_block_bytes(128) == accounting.page_bytes("q8", 32, 8, 128)
     assert layout.q2_block_bytes(256) == 2 * 64 * 72  # K and V rows of 64 tokens
+    for L, H, D in ((16, 4, 256), (32, 8, 128)):
+        assert L * H * layout.bf16_block_bytes(D) == accounting.page_bytes("bf16", L, H, D)
+    assert layout.bf16_block_bytes(256) == 2 * 64 * 512  # the page's 512 B per head per token
 
 
 def test_v_plane_write_touches_only_its_slot():

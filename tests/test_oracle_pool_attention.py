@@ -17,7 +17,7 @@ def _c0_rows(n=256):
     return w, k.float().numpy(), v.float().numpy()
 
 
-@pytest.mark.parametrize("fmt", ["q2", "q8"])
+@pytest.mark.parametrize("fmt", ["q2", "q8", "bf16"])
 def test_append_gather_is_permutation_invariant(fmt):
     w, k, v = _c0_rows()
     D = 128 if fmt == "q8" else 256
@@ -35,6 +35,35 @@ def test_append_gather_is_permutation_invariant(fmt):
         assert np.array_equal(a, b)
     K, V = pool.dequantized_rows(fmt, k, v)
     assert np.array_equal(outs[0][0], K) and np.array_equal(outs[0][1], V)
+
+
+def test_bf16_pool_stores_rows_as_given_at_their_byte_offsets():
+    # the exact format: the gather returns the appended rows bit for bit, and
+    # the bytes sit where the block layout puts them (K row t at 2 D t, V
+    # element (d, t) at 128 D + 2 (64 d + t)), read back here by hand
+    w, k, v = _c0_rows(100)
+    D, H = 256, 4
+    p = pool.OraclePool("bf16", 2, H, D, 5, fill=0x5A)
+    bt = np.array([3, 0], np.int32)
+    p.append(1, 0, bt, 0, k[:70], v[:70])
+    p.append(1, 0, bt, 70, k[70:], v[70:])
+    K, V = p.gather(1, bt, 100)
+    assert np.array_equal(K, k) and np.array_equal(V, v)
+    for page in (1, 2, 4):
+        assert np.all(p.data[page] == 0x5A)
+    kbits = k.view(np.uint32) >> 16
+    vbits = v.view(np.uint32) >> 16
+    for t, h, d in ((0, 0, 0), (63, 3, 255), (64, 1, 7), (99, 2, 128), (37, 0, 200)):
+        page, slot = int(bt[t // 64]), t % 64
+        base = (1 * H + h) * layout.bf16_block_bytes(D)   # layer 1
+        ko = base + 2 * D * slot + 2 * d
+        vo = base + 128 * D + 2 * (64 * d + slot)
+        assert int(p.data[page, ko]) | int(p.data[page, ko + 1]) << 8 == kbits[t, h, d]
+        assert int(p.data[page, vo]) | int(p.data[page, vo + 1]) << 8 == vbits[t, h, d]
+    # layer 0 of the used pages was never written
+    assert np.all(p.data[3, :H * layout.bf16_block_bytes(D)] == 0x5A)
+    with pytest.raises(AssertionError):   # rows off the bf16 grid are refused
+        p.append(1, 0, bt, 0, k[:1] * np.float32(1.0001), v[:1])
 
 
 def test_append_leaves_other_slots_and_pages_alone():
