@@ -61,7 +61,14 @@ typedef enum {
     KV_FMT_Q2 = 1,
     /* int8 codes: K scaled per channel over the tokens of its 64-token page,
      * V scaled per token (fp32 scales, symmetric, codes in [-127, 127]). */
-    KV_FMT_Q8 = 2
+    KV_FMT_Q8 = 2,
+    /* the rows as given, bf16: 512 B per head per token at D = 256, the BF16
+     * row of "KV at 9 KB a token" (section "How it works", table).  It is the
+     * exact cache that the compressed format is priced against (same page,
+     * sections "The numbers": the decode price of hq against BF16, and "See
+     * it, control it": the format is hq-e8-2b or bf16), in the same paged
+     * pool and through the same calls. */
+    KV_FMT_BF16 = 3
 } kv_format;
 
 typedef enum {
@@ -94,7 +101,8 @@ typedef struct {
 } kv_pool_stats_t;
 
 /* Bytes one token costs in a format, and the bytes of one 64-token page.
- * 2-bit: 2 x L x Hkv x (D/4 + 8).  8-bit: L x Hkv x (2D + 4 + 4D/64). */
+ * 2-bit: 2 x L x Hkv x (D/4 + 8).  8-bit: L x Hkv x (2D + 4 + 4D/64).
+ * bf16: 4 x L x Hkv x D. */
 kv_status kv_token_bytes(const kv_geom* geom, kv_format fmt, int64_t* token_bytes, int64_t* page_bytes);
 
 /* Byte budget that holds `tokens` tokens in whole pages (the pool size can be
@@ -141,7 +149,8 @@ kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t
  * sequence seqs[i]; same for d_v.  Each token's K and V rows are quantized in
  * fp32 (2-bit: min, scale = (max - min) / 3 correctly rounded, codes
  * rint((x - min) / scale) clamped to 0..3; 8-bit: V per token; K per channel
- * over the exact rows present in the token's page) and written into slot
+ * over the exact rows present in the token's page; bf16: stored as given) and
+ * written into slot
  * pos % 64 of page block_table[pos / 64].  No other slot of the pool changes,
  * except that an 8-bit append re-derives the K codes and channel scales of the
  * pages it touches.  8-bit appends are sequential per (sequence, layer):
@@ -190,7 +199,7 @@ kv_status kv_attn_decode(kv_pool* pool, int32_t layer, int32_t n, const int32_t*
  * positions q_start .. q_start + n_q - 1, after the chunk's own K/V have been
  * appended ("KV at 9 KB a token", opening section: prefill attention reads
  * the compressed cache): query i attends to tokens 0 .. q_start + i, all read
- * from the compressed pool, 2-bit pools only.  Scores are sm_scale x q.k^,
+ * from the pool, 2-bit and bf16 pools.  Scores are sm_scale x q.k^,
  * softmax and sums in fp32; both contractions run on bf16 matrix cores with
  * exact code operands and 16-bit softmax weights.  The keys of each block of
  * queries are split into n_splits ranges (1..64, 0 = the library's choice)

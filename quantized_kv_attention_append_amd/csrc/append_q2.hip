@@ -222,6 +222,9 @@ __global__ __launch_bounds__(256) void dequant_page_kernel(PoolView pv, int fmt,
                 meta = *reinterpret_cast<const float2*>(blk + q2_vmeta_off(D) + 8 * t);
             }
             r = __fmaf_rn((float)c, meta.x, meta.y);
+        } else if (fmt == KV_FMT_BF16) {
+            const uint16_t* vals = reinterpret_cast<const uint16_t*>(blk);
+            r = bf16_to_f32(kv == 0 ? vals[t * D + d] : vals[64 * D + PAGE * d + t]);
         } else {
             if (kv == 0) {
                 int8_t c = (int8_t)blk[t * D + d];

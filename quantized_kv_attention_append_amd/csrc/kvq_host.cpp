@@ -43,7 +43,8 @@ kv_status hip_fail(hipError_t e, const char* what) {
 
 kv_status check_geom(const kv_geom* g, kv_format fmt) {
     if (!g) return fail(KV_ERR_ARG, "geometry is NULL");
-    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8) return fail(KV_ERR_FORMAT, "unknown format %d", (int)fmt);
+    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8 && fmt != KV_FMT_BF16)
+        return fail(KV_ERR_FORMAT, "unknown format %d", (int)fmt);
     if (g->n_layers <= 0 || g->n_kv_heads <= 0 || g->n_q_heads <= 0 || g->head_dim <= 0)
         return fail(KV_ERR_ARG, "geometry fields must be positive");
     if (g->head_dim != 128 && g->head_dim != 256)
@@ -56,7 +57,10 @@ kv_status check_geom(const kv_geom* g, kv_format fmt) {
     return KV_OK;
 }
 
-int64_t block_bytes_of(kv_format fmt, int D) { return fmt == KV_FMT_Q2 ? q2_block_bytes(D) : q8_block_bytes(D); }
+int64_t block_bytes_of(kv_format fmt, int D) {
+    return fmt == KV_FMT_Q2 ? q2_block_bytes(D) : fmt == KV_FMT_Q8 ? q8_block_bytes(D) : bf16_block_bytes(D);
+}
+const char* fmt_name(kv_format fmt) { return fmt == KV_FMT_Q2 ? "q2" : fmt == KV_FMT_Q8 ? "q8" : "bf16"; }
 
 int64_t token_bytes_of(const kv_geom* g, kv_format fmt) {
     return (int64_t)g->n_layers * g->n_kv_heads * block_bytes_of(fmt, g->head_dim) / PAGE;
@@ -196,7 +200,7 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
     p->free_count = n_pages;
     p->seqs.resize((size_t)max_seqs);
     fprintf(stderr, "kvq: pool %s kv_pool_pages=%lld kv_pool_tokens=%lld kv_page_bytes=%lld token_bytes=%lld\n",
-            fmt == KV_FMT_Q2 ? "q2" : "q8", (long long)n_pages, (long long)(n_pages * PAGE), (long long)pb,
+            fmt_name(fmt), (long long)n_pages, (long long)(n_pages * PAGE), (long long)pb,
             (long long)tb);
     *out = p;
     return KV_OK;
@@ -340,7 +344,7 @@ int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
     const int64_t base = (int64_t)n * p->geom.n_kv_heads;
     const int64_t want = (256 + base - 1) / base;
-    if (p->fmt == KV_FMT_Q8)
+    if (p->fmt != KV_FMT_Q2)
         return (int)std::max<int64_t>(1, std::min<int64_t>(256, std::max<int64_t>(want, ((max_pages + 1) / 2 + 15) / 16)));
     const int64_t cap = std::max<int64_t>(1, ((max_pages + 1) / 2) / 8);
     return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
@@ -388,6 +392,8 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
     hipError_t e = hipSuccess;
     if (p->fmt == KV_FMT_Q2) {
         e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+    } else if (p->fmt == KV_FMT_BF16) {
+        e = launch_append_bf16(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
     } else {
         // An 8-bit append that starts inside a page reads that page's staged
         // exact K rows; if it also runs past the page, its last page rewrites
@@ -478,9 +484,11 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
         return fail(KV_ERR_WORKSPACE, "decode needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
     hipStream_t s = (hipStream_t)stream;
     PoolView pv = p->view();
-    hipError_t e = p->fmt == KV_FMT_Q2
-                       ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
-                       : launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s);
+    hipError_t e =
+        p->fmt == KV_FMT_Q2   ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
+        : p->fmt == KV_FMT_Q8 ? launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
+                              : launch_decode_bf16(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores,
+                                                   scores_stride, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return KV_OK;
 }
@@ -489,7 +497,7 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
                           float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes, float* d_out,
                           kv_stream_t stream) {
     if (!p) return fail(KV_ERR_ARG, "pool is NULL");
-    if (p->fmt != KV_FMT_Q2) return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit format only");
+    if (p->fmt == KV_FMT_Q8) return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit and bf16 formats only");
     if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
     if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
     if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
@@ -500,8 +508,8 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
     int64_t need = 4 * prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim, sp);
     if (!d_ws || ws_bytes < need)
         return fail(KV_ERR_WORKSPACE, "prefill needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
-    hipError_t e = launch_prefill_q2(p->view(), layer, seq, (int)q_start, n_q, d_q, sm_scale, sp, (float*)d_ws, d_out,
-                                     (hipStream_t)stream);
+    hipError_t e = launch_prefill(p->view(), (int)p->fmt, layer, seq, (int)q_start, n_q, d_q, sm_scale, sp,
+                                  (float*)d_ws, d_out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return KV_OK;
 }

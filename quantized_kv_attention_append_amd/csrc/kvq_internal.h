@@ -56,19 +56,27 @@ __host__ __device__ constexpr int64_t q8_vcodes_off(int D) { return 64 * (int64_
 __host__ __device__ constexpr int64_t q8_kscale_off(int D) { return 128 * (int64_t)D; }
 __host__ __device__ constexpr int64_t q8_vscale_off(int D) { return 132 * (int64_t)D; }
 
+// Byte offsets inside a bf16 (layer, head) block: K [64][D] then V [D][64].
+__host__ __device__ constexpr int64_t bf16_block_bytes(int D) { return 256 * (int64_t)D; }
+
 // Launchers (defined in the .hip files).  Each returns the launch status.
 hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
+hipError_t launch_append_bf16(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
+                              const uint16_t* k, const uint16_t* v, hipStream_t s);
 // Decode launchers enqueue the split kernel and then the merge of its
 // partials, which writes the fp32 output.
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
-hipError_t launch_prefill_q2(const PoolView& pv, int layer, int seq, int q_start, int n_q, const uint16_t* q,
-                             float sm, int splits, float* ws, float* out, hipStream_t s);
+hipError_t launch_decode_bf16(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
+                              int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
+// Prefill over a 2-bit or bf16 pool (fmt).
+hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
+                          float sm, int splits, float* ws, float* out, hipStream_t s);
 // Split count a prefill of n_q chunk queries takes when the caller passes 0.
 int prefill_auto_splits(int n_q, int Hq, int Hkv);
 hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,

@@ -1,8 +1,8 @@
-// Chunked causal prefill over the 2-bit pool: the chunk's queries attend to
-// the prior tokens and to the chunk itself, every key and value read from the
-// compressed pages ("KV at 9 KB a token", opening section: prefill attention
-// reads the compressed cache directly, and every workspace byte a launch reads
-// it wrote first).
+// Chunked causal prefill over the 2-bit pool (and, through the same kernel,
+// the bf16 pool): the chunk's queries attend to the prior tokens and to the
+// chunk itself, every key and value read from the compressed pages ("KV at 9
+// KB a token", opening section: prefill attention reads the compressed cache
+// directly, and every workspace byte a launch reads it wrote first).
 //
 // Query i of the chunk sits at position q_start + i and sees keys
 // 0 .. q_start + i (inclusive).  Scores are sm q.k^ with the dequantization
@@ -31,6 +31,10 @@
 //   V~[dim][key]    natural key order.
 // Partials (m, l, o) of every row go to the workspace; prefill_merge_kernel
 // merges, for each row, the splits whose first key it can see.
+//
+// A bf16 pool fills the same tiles with the stored values (K dims interleaved
+// into kappa order by byte permutes, V copied) and unit metadata (scale 1,
+// offset 0), so that the rest of the kernel is the same code.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -97,17 +101,42 @@ struct PrefillLds {
 };
 
 // Packed codes of one page held by a thread between its load and its conversion.
-template <int D>
+template <int D, int FMT>
 struct PackedPage {
     static constexpr int NW = D / 64;  // K words and V words per thread
     uint32_t k[NW];
     uint32_t v[NW];
     uint4 meta;  // threads < 64: {k scale, k min, v scale, v min} of key tid
 };
+// bf16 pool: the page's values as stored, 16-byte pieces
+template <int D>
+struct PackedPage<D, KV_FMT_BF16> {
+    static constexpr int NK = D / 64;  // K items (key, 16 dims: two pieces) per thread
+    static constexpr int NV = D / 32;  // V pieces (dim, 8 keys) per thread
+    uint4 k[2 * NK];
+    uint4 v[NV];
+};
 
 template <int D>
-__device__ __forceinline__ void load_packed(PackedPage<D>& pk, const uint8_t* blk, int tid) {
-    constexpr int NW = PackedPage<D>::NW, KW = D / 16;  // code words per K row
+__device__ __forceinline__ void load_packed(PackedPage<D, KV_FMT_BF16>& pk, const uint8_t* blk, int tid) {
+    constexpr int NK = PackedPage<D, KV_FMT_BF16>::NK, NV = PackedPage<D, KV_FMT_BF16>::NV;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int item = tid + 256 * i, t = item / (D / 16), u = item % (D / 16);
+        const uint4* src = reinterpret_cast<const uint4*>(blk + 2 * (t * D + 16 * u));
+        pk.k[2 * i] = src[0];
+        pk.k[2 * i + 1] = src[1];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int item = tid + 256 * i;  // dim item / 8, keys 8 (item % 8) ..
+        pk.v[i] = *reinterpret_cast<const uint4*>(blk + 128 * D + 16 * item);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_packed(PackedPage<D, KV_FMT_Q2>& pk, const uint8_t* blk, int tid) {
+    constexpr int NW = PackedPage<D, KV_FMT_Q2>::NW, KW = D / 16;  // code words per K row
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const int item = tid + 256 * i;  // K: (key, word)
@@ -124,7 +153,8 @@ __device__ __forceinline__ void load_packed(PackedPage<D>& pk, const uint8_t* bl
 
 // Item i (one K word, one V word) of a thread's share of the page conversion.
 template <int D>
-__device__ __forceinline__ void convert_item(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid, int i) {
+__device__ __forceinline__ void convert_item(const PackedPage<D, KV_FMT_Q2>& pk, PrefillLds<D>& L, int buf, int tid,
+                                             int i) {
     constexpr int KW = D / 16, KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
     {
         const int item = tid + 256 * i;
@@ -159,7 +189,7 @@ __device__ __forceinline__ void convert_item(const PackedPage<D>& pk, PrefillLds
 
 // The per-key scale and offset of the page.
 template <int D>
-__device__ __forceinline__ void convert_meta(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid) {
+__device__ __forceinline__ void convert_meta(const PackedPage<D, KV_FMT_Q2>& pk, PrefillLds<D>& L, int buf, int tid) {
     // the K offset absorbs the +4 of the stored codes: k^ = min + scale c = (min - 4 scale) + scale (c + 4)
     if (tid < PAGE) {
         const float ks = __uint_as_float(pk.meta.x);
@@ -169,10 +199,53 @@ __device__ __forceinline__ void convert_meta(const PackedPage<D>& pk, PrefillLds
 }
 
 template <int D>
-__device__ __forceinline__ void convert_packed(const PackedPage<D>& pk, PrefillLds<D>& L, int buf, int tid) {
+__device__ __forceinline__ void convert_packed(const PackedPage<D, KV_FMT_Q2>& pk, PrefillLds<D>& L, int buf, int tid,
+                                               int /*n_valid: codes are finite in any slot*/) {
 #pragma unroll
-    for (int i = 0; i < PackedPage<D>::NW; ++i) convert_item<D>(pk, L, buf, tid, i);
+    for (int i = 0; i < PackedPage<D, KV_FMT_Q2>::NW; ++i) convert_item<D>(pk, L, buf, tid, i);
     convert_meta<D>(pk, L, buf, tid);
+}
+
+// bf16 pool: K dims 16u + k and 16u + k + 8 made adjacent (kappa order), V
+// copied; unit scales and zero offsets.  Slots from n_valid on were never
+// written and may hold NaN patterns: they become zeros (a zero weight times a
+// NaN value would still poison the p.v sum).
+template <int D>
+__device__ __forceinline__ void convert_packed(const PackedPage<D, KV_FMT_BF16>& pk, PrefillLds<D>& L, int buf,
+                                               int tid, int n_valid) {
+    constexpr int NK = PackedPage<D, KV_FMT_BF16>::NK, NV = PackedPage<D, KV_FMT_BF16>::NV;
+    constexpr int KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int item = tid + 256 * i, t = item / (D / 16), u = item % (D / 16);
+        const uint4 a = pk.k[2 * i], b = pk.k[2 * i + 1];  // dims 16u .. +7, 16u + 8 .. +15
+        const uint32_t keep = t < n_valid ? 0xFFFFFFFFu : 0u;
+        const uint32_t aa[4] = {a.x & keep, a.y & keep, a.z & keep, a.w & keep};
+        const uint32_t bb[4] = {b.x & keep, b.y & keep, b.z & keep, b.w & keep};
+        uint32_t o[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            o[2 * k] = __builtin_amdgcn_perm(bb[k], aa[k], 0x05040100u);      // dims 16u + 2k, 16u + 2k + 8
+            o[2 * k + 1] = __builtin_amdgcn_perm(bb[k], aa[k], 0x07060302u);  // dims 16u + 2k + 1, 16u + 2k + 9
+        }
+        uint4* dst = reinterpret_cast<uint4*>(&L.k[buf][t * KS + 16 * u]);
+        dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int item = tid + 256 * i, d = item >> 3, p = item & 7;
+        uint32_t w[4] = {pk.v[i].x, pk.v[i].y, pk.v[i].z, pk.v[i].w};
+        if (8 * p + 8 > n_valid) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w[k] &= (8 * p + 2 * k < n_valid ? 0xFFFFu : 0u) | (8 * p + 2 * k + 1 < n_valid ? 0xFFFF0000u : 0u);
+        }
+        uint2* dst = reinterpret_cast<uint2*>(&L.v[buf][d * VS + 8 * p]);
+        dst[0] = make_uint2(w[0], w[1]);
+        dst[1] = make_uint2(w[2], w[3]);
+    }
+    if (tid < PAGE) L.meta[buf][tid] = make_float4(1.f, 0.f, 1.f, 0.f);
 }
 
 // Pages [pg0, pg1) of split sp for a block whose last query sits at pos_max.
@@ -183,10 +256,10 @@ __device__ __forceinline__ void prefill_split_range(int pos_max, int splits, int
     *pg1 = min(sp * per + per, n_pages);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer, int seq, int q_start, int n_q,
-                                                         const uint16_t* __restrict__ q, float sm, int splits,
-                                                         float* __restrict__ ws) {
+template <int D, int FMT>
+__global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, int seq, int q_start, int n_q,
+                                                      const uint16_t* __restrict__ q, float sm, int splits,
+                                                      float* __restrict__ ws) {
     constexpr int KSTEPS = D / 32, DB = D / 16;
     constexpr int KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
     const int Hkv = pv.Hkv, Hq = pv.Hq, G = Hq / Hkv;
@@ -205,7 +278,7 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
     auto block_of = [&](int pg) { return pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff; };
 
-    PackedPage<D> pk;
+    PackedPage<D, FMT> pk;
     load_packed<D>(pk, block_of(pg0), tid);
 
     // ---- this lane's rows: column j of block cb = (query, head) ----
@@ -258,7 +331,8 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
         c_run[cb] = 0.f;
     }
 
-    convert_packed<D>(pk, L, 0, tid);
+    const int key_end = q_start + n_q;  // keys at and past it were never appended
+    convert_packed<D>(pk, L, 0, tid, key_end - pg0 * PAGE);
     __syncthreads();
     // pages [pg0, pg_full) are visible to every row of the block (no mask);
     // the rest reach past the block's first query position
@@ -386,7 +460,7 @@ __global__ __launch_bounds__(256) void prefill_q2_kernel(PoolView pv, int layer,
         // the next page's tiles (the idle buffer was last read before the
         // previous barrier; after the last page this rewrites it with the page
         // already used, and nothing reads it)
-        convert_packed<D>(pk, L, buf ^ 1, tid);
+        convert_packed<D>(pk, L, buf ^ 1, tid, key_end - (pg + 1) * PAGE);
         __syncthreads();
         return true;
     };
@@ -468,14 +542,24 @@ int prefill_auto_splits(int n_q, int Hq, int Hkv) {
     return want < 1 ? 1 : want > 64 ? 64 : want;
 }
 
-hipError_t launch_prefill_q2(const PoolView& pv, int layer, int seq, int q_start, int n_q, const uint16_t* q,
-                             float sm, int splits, float* ws, float* out, hipStream_t s) {
+hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
+                          float sm, int splits, float* ws, float* out, hipStream_t s) {
     const int G = pv.Hq / pv.Hkv, QB = ROWS / G;
     dim3 grid(((n_q + QB - 1) / QB) * pv.Hkv, splits);
-    if (pv.D == 256)
-        hipLaunchKernelGGL(prefill_q2_kernel<256>, grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q, sm, splits, ws);
-    else
-        hipLaunchKernelGGL(prefill_q2_kernel<128>, grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q, sm, splits, ws);
+    if (fmt == KV_FMT_BF16) {
+        if (pv.D == 256)
+            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_BF16>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
+                               q, sm, splits, ws);
+        else
+            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_BF16>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
+                               q, sm, splits, ws);
+    } else if (pv.D == 256) {
+        hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q,
+                           sm, splits, ws);
+    } else {
+        hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q,
+                           sm, splits, ws);
+    }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(n_q * pv.Hq), dim3(pv.D), 0, s, q_start, n_q, pv.Hq, pv.Hkv, pv.D,
