@@ -141,7 +141,7 @@ def prefill_leg(steps: int, warmup: int):
         "useful_flops": flops,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_TFLOPS, "traffic": None,
-                     "kernel": "one kv_attn_prefill call: prefill_q2_kernel<256> then prefill_merge_kernel"},
+                     "kernel": "one kv_attn_prefill call: prefill_kernel<256, 1> then prefill_merge_kernel"},
         "chunk_append_ms": chunk_append_ms,
     }
 
@@ -282,9 +282,121 @@ def q8_leg(reps: int):
             "decode_us_per_layer_call": avg * 1e3, "bytes_per_call": alg,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "one kv_attn_decode call per layer: decode_q8_kernel<128> then merge_splits_kernel"},
+                         "kernel": "one kv_attn_decode call per layer: decode_q8_mfma_kernel<128, 4> then merge_splits_kernel"},
             "kv_tokens_per_s": tokens * w.n_layers / (avg * 1e-3 * w.n_layers),
             "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
+
+
+def bf16_leg(reps: int):
+    """The exact bf16 cache of the same 27B-geometry batch (16 layers x 4 KV
+    heads x 256 dims, 8 lanes x 40,960 tokens: 21.47 GB, the pages' 20.0 GiB),
+    through the same calls: populate, then the 16-layer decode step (each call
+    timed with HIP events, and the step replayed as a HIP graph), and the
+    65,536 + 1,024 chunked prefill over a bf16 pool."""
+    import torch
+
+    import quantized_kv_attention_append_amd as kvq
+    from synth import CONFIGS, kv_rows, page_permutation, queries
+
+    w = CONFIGS[1]
+    L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
+    geom = (L, H, D, Hq)
+    tb, pb = kvq.token_bytes(geom, kvq.FMT_BF16)
+    ppl = ctx // 64
+    n_pages = B * ppl
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_BF16, max_seqs=B, max_seq_tokens=ctx)
+    perm = page_permutation(w, n_pages)
+    seqs = [pool.reserve(ctx, pages=perm[i * ppl:(i + 1) * ppl]) for i in range(B)]
+    stream = torch.cuda.current_stream()
+    app_ms = 0.0
+    for layer in range(L):
+        kv = [kv_rows(w, layer, lane, ctx, device="cuda") for lane in range(B)]
+        k = torch.cat([a for a, _ in kv])
+        v = torch.cat([b for _, b in kv])
+        del kv
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pool.append(layer, seqs, [0] * B, [ctx] * B, k, v)
+        e1.record(stream)
+        e1.synchronize()
+        app_ms += e0.elapsed_time(e1)
+        del k, v
+    app_bytes = 2 * B * ctx * tb   # every row of every layer read once and written once (tb covers all layers)
+    qs = [queries(w, layer, B, device="cuda") for layer in range(L)]
+    sp = pool.decode_splits([ctx] * B)
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, B, sp), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device="cuda") for _ in range(L)]
+
+    def step():
+        for layer in range(L):
+            pool.decode(layer, seqs, [ctx] * B, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
+
+    step()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        for layer in range(L):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pool.decode(layer, seqs, [ctx] * B, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
+            e1.record(stream)
+            ev.append((e0, e1))
+    torch.cuda.synchronize()
+    avg_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    eager_outs = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    g1.record(stream)
+    g1.synchronize()
+    graph_ms = g0.elapsed_time(g1) / reps
+    same = all(torch.equal(a, b) for a, b in zip(outs, eager_outs))
+    del g
+    alg = B * ppl * H * 64 * (4 * D) + B * Hq * D * (2 + 4)   # K and V rows, q in, fp32 out
+    gbs = alg / (avg_ms * 1e-3) / 1e9
+    log(f"bf16: populate {app_ms:.1f} ms ({app_bytes / app_ms / 1e6:.0f} GB/s); decode {avg_ms * 1e3:.1f} us a call, "
+        f"{gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), splits={sp}; graph step {graph_ms:.3f} ms "
+        f"(identical to eager: {same})")
+    del pool, ws, outs, qs, eager_outs
+    torch.cuda.empty_cache()
+
+    # ---- chunked prefill over a bf16 pool: 65,536 prior + 1,024 chunk ----
+    w3 = CONFIGS[3]
+    prior, n_q = w3.ctx, w3.chunk
+    total = prior + n_q
+    geom3 = (w3.n_layers, w3.n_kv_heads, w3.head_dim, w3.n_q_heads)
+    _, pb3 = kvq.token_bytes(geom3, kvq.FMT_BF16)
+    n3 = total // 64
+    pool3 = kvq.Pool(n3 * pb3, geom3, kvq.FMT_BF16, max_seqs=1, max_seq_tokens=total)
+    seq3 = pool3.reserve(total, pages=page_permutation(w3, n3))
+    k, v = kv_rows(w3, 0, 0, total, device="cuda")
+    pool3.append(0, [seq3], [0], [total], k, v)
+    del k, v
+    q = queries(w3, 0, n_q, device="cuda", stream=1)
+    ws3 = torch.empty(pool3.workspace_bytes(kvq.OP_PREFILL, n_q, 0), dtype=torch.uint8, device="cuda")
+    out3 = torch.empty((n_q, w3.n_q_heads, w3.head_dim), dtype=torch.float32, device="cuda")
+    pf = _call_ms(lambda: pool3.prefill(0, seq3, prior, q, w3.sm_scale, ws=ws3, out=out3), reps)
+    flops = 4.0 * w3.head_dim * w3.n_q_heads * sum(prior + i + 1 for i in range(n_q))
+    pf_tflops = flops / (pf[0] * 1e-3) / 1e12
+    log(f"bf16 prefill: {pf[0]:.3f} ms per call, {pf_tflops:.0f} TFLOP/s useful")
+    return {"workload": "27B-geometry batched decode, bf16: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
+                        "8 lanes x 40960 tokens", "pool_bytes": n_pages * pb, "splits": sp,
+            "decode_us_per_call": avg_ms * 1e3, "bytes_per_call": alg,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then "
+                                   "merge_splits_kernel"},
+            "graph_ms_per_step": graph_ms, "graph_identical_to_eager": same,
+            "kv_tokens_per_s": B * L * ctx / (graph_ms * 1e-3),
+            "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6,
+            "prefill_ms_per_call": pf[0], "prefill_ms_min": pf[1], "prefill_useful_tflops": pf_tflops}
 
 
 def oracle_baseline(w, budget_s: float):
@@ -457,6 +569,14 @@ def main():
     prefill = None if args.no_prefill else prefill_leg(max(3, args.steps // 4), 2)
     long_ctx = None if args.no_extra else long_context_leg(10)
     q8 = None if args.no_extra else q8_leg(5)
+    bf16 = None if args.no_extra else bf16_leg(5)
+    if bf16 is not None:
+        # the pages' A/B: decode price of the 2-bit cache against the exact one, same batch and calls
+        bf16["q2_step_speedup"] = bf16["graph_ms_per_step"] / ms_per_step
+        if prefill is not None:
+            bf16["q2_prefill_time_ratio"] = prefill["ms_per_call"] / bf16["prefill_ms_per_call"]
+        log(f"2-bit against bf16: decode step {bf16['q2_step_speedup']:.2f}x faster"
+            + (f", prefill {bf16['q2_prefill_time_ratio']:.2f}x the bf16 time" if prefill is not None else ""))
 
     cpu = None
     if not args.no_cpu:
@@ -501,6 +621,7 @@ def main():
         "prefill": prefill,
         "long_context": long_ctx,
         "q8": q8,
+        "bf16": bf16,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

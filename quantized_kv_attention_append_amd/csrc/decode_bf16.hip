@@ -62,12 +62,17 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 }  // namespace
 
-template <int D, int G, bool SCORES>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(PoolView pv, int layer, BatchDesc bd,
+// TB: 16-token blocks a wave takes per step (4: a whole page, loads of
+// 64 KB a wave at D = 256; 2: half a page, few enough registers for two
+// waves per SIMD).
+template <int D, int G, bool SCORES, int TB>
+__global__ __launch_bounds__(256, TB == 2 ? 2 : 1) void decode_bf16_kernel(PoolView pv, int layer, BatchDesc bd,
                                                           const uint16_t* __restrict__ q, float sm, int splits,
                                                           float* __restrict__ ws, float* __restrict__ scores,
                                                           int64_t sstride) {
     static_assert(2 * G <= 16, "two rows per head in a 16-row block");
+    static_assert(TB == 2 || TB == 4, "half or whole pages");
+    constexpr int KS = TB / 2;  // 32-token k-steps of the p.v product per step
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int NM = D / 64;      // 64-dim slices of a K row (two k-steps each)
     constexpr int NDB = D / 16;     // 16-dim blocks of the p.v product
@@ -111,45 +116,51 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(PoolView pv, int layer
     const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
 
+    // a wave takes every fourth page of the split; with half pages, both halves of it in turn
     for (int pg = pg0 + wave; pg < pg1; pg += 4) {
+      for (int hf = 0; hf < 4 / TB; ++hf) {
+        const int t0 = 16 * TB * hf;                        // first token slot of the step
+        const int n_tok = min(PAGE, ctx - pg * PAGE) - t0;  // valid tokens from t0 on
+        if (n_tok <= 0) break;                              // the second half of a short last page
         const uint8_t* blk = pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff;
-        uint4 kraw[4][2 * NM];  // token 16tb + col, dims 64m + 16grp + 8h .. +7
+        uint4 kraw[TB][2 * NM];  // token t0 + 16tb + col, dims 64m + 16grp + 8h .. +7
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
             for (int m = 0; m < NM; ++m)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    kraw[tb][2 * m + h] =
-                        *reinterpret_cast<const uint4*>(blk + 2 * ((16 * tb + col) * D + 64 * m + 16 * grp + 8 * h));
-        uint4 vraw[NDB][2];  // dim 16db + col, tokens 16grp + 8h .. +7
+                    kraw[tb][2 * m + h] = *reinterpret_cast<const uint4*>(
+                        blk + 2 * ((t0 + 16 * tb + col) * D + 64 * m + 16 * grp + 8 * h));
+        uint4 vraw[NDB][KS];  // dim 16db + col, tokens t0 + 8 KS grp + 8h .. +7
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                vraw[db][h] = *reinterpret_cast<const uint4*>(blk + 128 * D + 2 * ((16 * db + col) * PAGE + 16 * grp + 8 * h));
+            for (int h = 0; h < KS; ++h)
+                vraw[db][h] = *reinterpret_cast<const uint4*>(
+                    blk + 128 * D + 2 * ((16 * db + col) * PAGE + t0 + 8 * KS * grp + 8 * h));
 
-        // ---- S^T: row 4grp + r (head 2grp + r/2 when r is even), column = token 16tb + col ----
-        f32x4_t st[4];
+        // ---- S^T: row 4grp + r (head 2grp + r/2 when r is even), column = token t0 + 16tb + col ----
+        f32x4_t st[TB];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int tb = 0; tb < TB; ++tb) {
             st[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < 2 * NM; ++k) st[tb] = mma_bf16(qa[k], kraw[tb][k], st[tb]);
         }
         // ---- online softmax of heads 2grp, 2grp + 1 over the page's tokens ----
-        const int n_tok = min(PAGE, ctx - pg * PAGE);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int j = 2 * grp + hh;
             const bool live = j < G;
-            float sv[4], mt = -INFINITY;
+            float sv[TB], mt = -INFINITY;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
+            for (int tb = 0; tb < TB; ++tb) {
                 const bool valid = 16 * tb + col < n_tok;
                 const float raw = st[tb][2 * hh];
                 if constexpr (SCORES)
-                    if (live && valid) scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + 16 * tb + col] = sm * raw;
+                    if (live && valid)
+                        scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + t0 + 16 * tb + col] = sm * raw;
                 sv[tb] = valid && live ? raw * cs : -INFINITY;
                 mt = fmaxf(mt, sv[tb]);
             }
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(PoolView pv, int layer
             const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[hh] - m_new);
             float psum = 0.f;
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
+            for (int tb = 0; tb < TB; ++tb) {
                 // slots past ctx weigh nothing (their bytes may be anything, NaN included)
                 const float p = sv[tb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb] - m_new);
                 psum += p;
@@ -175,31 +186,32 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(PoolView pv, int layer
                 acc[db][2 * hh + 1] *= alpha;
             }
         }
-        // ---- O += W~ V: A = weight row col, tokens 16grp .. +15 (the wave's LDS is read in order) ----
-        const uint4 wa0 = *reinterpret_cast<const uint4*>(&w_s[wave][col][16 * grp]);
-        const uint4 wa1 = *reinterpret_cast<const uint4*>(&w_s[wave][col][16 * grp + 8]);
+        // ---- O += W~ V: A = weight row col, tokens 8 KS grp .. +8 KS - 1 of the step (the wave's LDS is read in order) ----
+        uint4 wa[KS];
+#pragma unroll
+        for (int h = 0; h < KS; ++h) wa[h] = *reinterpret_cast<const uint4*>(&w_s[wave][col][8 * KS * grp + 8 * h]);
         // a slot past ctx has weight 0, but 0 x NaN would still poison the
         // sum: the V bytes of such slots are replaced by zeros
-        if (n_tok < PAGE) {
+        if (n_tok < 16 * TB) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int t0 = 16 * grp + 8 * h;
+            for (int h = 0; h < KS; ++h) {
+                const int tv = 8 * KS * grp + 8 * h;
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     uint32_t* w = reinterpret_cast<uint32_t*>(&vraw[db][h]);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const uint32_t keep = (t0 + 2 * i < n_tok ? 0xFFFFu : 0u) | (t0 + 2 * i + 1 < n_tok ? 0xFFFF0000u : 0u);
+                        const uint32_t keep = (tv + 2 * i < n_tok ? 0xFFFFu : 0u) | (tv + 2 * i + 1 < n_tok ? 0xFFFF0000u : 0u);
                         w[i] &= keep;
                     }
                 }
             }
         }
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            acc[db] = mma_bf16(wa0, vraw[db][0], acc[db]);
-            acc[db] = mma_bf16(wa1, vraw[db][1], acc[db]);
-        }
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int h = 0; h < KS; ++h) acc[db] = mma_bf16(wa[h], vraw[db][h], acc[db]);
+      }
     }
 
     // ---- combine the four waves (a wave without pages holds m = -inf, l = 0, o = 0) ----
@@ -238,6 +250,8 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(PoolView pv, int layer
     }
 }
 
+constexpr int BF16_STEP_BLOCKS = 4;  // whole pages per step (see decode_bf16_kernel)
+
 hipError_t launch_decode_bf16(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                               int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
     dim3 grid(bd.n * pv.Hkv, splits);
@@ -245,10 +259,10 @@ hipError_t launch_decode_bf16(const PoolView& pv, int layer, const BatchDesc& bd
     auto go = [&](auto d_tag, auto g_tag) {
         constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
         if (scores)
-            hipLaunchKernelGGL((decode_bf16_kernel<DD, GG, true>), grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits,
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, GG, true, BF16_STEP_BLOCKS>), grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits,
                                ws, scores, sstride);
         else
-            hipLaunchKernelGGL((decode_bf16_kernel<DD, GG, false>), grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits,
+            hipLaunchKernelGGL((decode_bf16_kernel<DD, GG, false, BF16_STEP_BLOCKS>), grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits,
                                ws, scores, sstride);
     };
     auto by_group = [&](auto d_tag) {

@@ -332,7 +332,7 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
     return KV_OK;
 }
 
-// Default split count for a decode batch.  2-bit: about one workgroup per
+// Default split count for a decode batch.  2-bit and bf16: about one workgroup per
 // compute unit (256 on MI355X) over all (sequence, KV head) pairs, with at
 // least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
 // at least that many workgroups, and splits of about sixteen page pairs of the
@@ -344,7 +344,7 @@ int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
     const int64_t base = (int64_t)n * p->geom.n_kv_heads;
     const int64_t want = (256 + base - 1) / base;
-    if (p->fmt != KV_FMT_Q2)
+    if (p->fmt == KV_FMT_Q8)
         return (int)std::max<int64_t>(1, std::min<int64_t>(256, std::max<int64_t>(want, ((max_pages + 1) / 2 + 15) / 16)));
     const int64_t cap = std::max<int64_t>(1, ((max_pages + 1) / 2) / 8);
     return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
