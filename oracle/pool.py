@@ -16,9 +16,22 @@ are kept aside (the exact window), and each append re-derives the page's K codes
 and scales from the exact rows present, so a full page equals the plain
 per-channel quantization of its 64 tokens.
 
+The 2-bit format with an exact window ("q2w") keeps, besides the 2-bit pages,
+the exact rows of the last page a (sequence, layer) has appended to: the
+"window of exact recent keys that the compressed KV format keeps" of "The KV
+cache and prompt reuse" (What a sequence is made of), read here as one page.
+With A tokens appended, every reader sees tokens 64 * floor((A - 1) / 64) ..
+A - 1 exact and every earlier token through the 2-bit codec; the pages
+themselves hold exactly what a plain 2-bit pool holds.  Appends are then
+sequential per (sequence, layer), since only the last page's rows are kept.
+
 Pins: append-then-gather returns exactly the codec's dequantized rows for any
 block table (permutation invariance) and slots outside the appended range keep
-their fill bytes (tests/test_oracle_pool.py).
+their fill bytes (tests/test_oracle_pool_attention.py); the window format's
+body equals a plain 2-bit pool byte for byte, its last page reads back as the
+appended rows, a sequence within one page attends exactly as a loop over the
+input rows does, and the window moves when a new page opens
+(tests/test_oracle_window.py).
 """
 
 from __future__ import annotations
@@ -32,16 +45,19 @@ from .layout import PAGE, Bf16Block, Q2Block, Q8Block, block_bytes, block_offset
 
 class OraclePool:
     def __init__(self, fmt: str, n_layers: int, n_kv_heads: int, head_dim: int, n_pages: int, fill: int = 0xA5):
-        assert fmt in ("q2", "q8", "bf16")
+        assert fmt in ("q2", "q8", "bf16", "q2w")
         self.fmt, self.L, self.H, self.D = fmt, n_layers, n_kv_heads, head_dim
-        self.page_bytes = page_bytes(fmt, n_layers, n_kv_heads, head_dim)
+        self.page_fmt = "q2" if fmt == "q2w" else fmt  # the window format's pages are 2-bit pages
+        self.page_bytes = page_bytes(self.page_fmt, n_layers, n_kv_heads, head_dim)
         self.data = np.full((n_pages, self.page_bytes), fill, dtype=np.uint8)
         self._exact_k = {}  # (seq, layer) -> fp32 [64][H][D] exact K rows of the open page (8-bit only)
+        # q2w: (seq, layer) -> (tokens appended A, exact K and V fp32 [64][H][D] of page (A - 1) // 64)
+        self._window = {}
 
     def block(self, page: int, layer: int, head: int):
-        off = block_offset(self.fmt, layer, head, self.H, self.D)
-        buf = self.data[page, off:off + block_bytes(self.fmt, self.D)]
-        return {"q2": Q2Block, "q8": Q8Block, "bf16": Bf16Block}[self.fmt](buf, self.D)
+        off = block_offset(self.page_fmt, layer, head, self.H, self.D)
+        buf = self.data[page, off:off + block_bytes(self.page_fmt, self.D)]
+        return {"q2": Q2Block, "q8": Q8Block, "bf16": Bf16Block}[self.page_fmt](buf, self.D)
 
     # ------------------------------------------------------------ append --
     def append(self, layer: int, seq: int, bt, start: int, k_rows, v_rows):
@@ -62,7 +78,9 @@ class OraclePool:
                     blk.k[slot] = kb[i, h]
                     blk.v[:, slot] = vb[i, h]
             return
-        if self.fmt == "q2":
+        if self.fmt == "q2w":
+            self._append_window(layer, seq, start, k, v)
+        if self.page_fmt == "q2":
             ck, sk, mk = codec.q2_quantize(k)
             cv, sv, mv = codec.q2_quantize(v)
             for i in range(n):
@@ -104,9 +122,46 @@ class OraclePool:
             self._exact_k[key] = exact
             pos = page_end
 
+    def _append_window(self, layer: int, seq: int, start: int, k, v):
+        """Keep the exact rows of the last page this append reaches."""
+        bf16.f32_to_bits(k), bf16.f32_to_bits(v)  # the rows must be bf16 numbers
+        appended, wk, wv = self._window.get((seq, layer), (0, None, None))
+        if start != appended:
+            raise ValueError(f"window appends are sequential: {appended} tokens held, append starts at {start}")
+        end = start + k.shape[0]
+        last = (end - 1) // PAGE
+        if appended == 0 or (appended - 1) // PAGE != last:
+            wk = np.zeros((PAGE, self.H, self.D), np.float32)
+            wv = np.zeros_like(wk)
+        lo = max(start, last * PAGE)
+        wk[lo - last * PAGE:end - last * PAGE] = k[lo - start:]
+        wv[lo - last * PAGE:end - last * PAGE] = v[lo - start:]
+        self._window[(seq, layer)] = (end, wk, wv)
+
+    def window_start(self, layer: int, seq: int) -> int:
+        """First position read exactly (q2w): 64 * floor((A - 1) / 64) with A tokens appended."""
+        appended = self._window[(seq, layer)][0]
+        return PAGE * ((appended - 1) // PAGE)
+
     # ------------------------------------------------------------ gather --
-    def gather(self, layer: int, bt, ctx_len: int):
-        """Dequantized K^ and V^ [ctx_len][H][D] (fp32) read through the block table."""
+    def gather(self, layer: int, bt, ctx_len: int, seq: int = None):
+        """Dequantized K^ and V^ [ctx_len][H][D] (fp32) read through the block table.
+
+        The window format also needs the sequence: its tokens from the window
+        start up to ctx_len (at most the tokens appended) are the exact rows."""
+        if self.fmt == "q2w":
+            appended, wk, wv = self._window[(seq, layer)]
+            if ctx_len > appended:
+                raise ValueError(f"ctx_len {ctx_len} beyond the {appended} tokens appended")
+            K, V = self._gather_pages(layer, bt, ctx_len)
+            w0 = self.window_start(layer, seq)
+            if ctx_len > w0:
+                K[w0:ctx_len] = wk[:ctx_len - w0]
+                V[w0:ctx_len] = wv[:ctx_len - w0]
+            return K, V
+        return self._gather_pages(layer, bt, ctx_len)
+
+    def _gather_pages(self, layer: int, bt, ctx_len: int):
         K = np.empty((ctx_len, self.H, self.D), np.float32)
         V = np.empty_like(K)
         for lp in range(-(-ctx_len // PAGE)):
@@ -117,7 +172,7 @@ class OraclePool:
                 if self.fmt == "bf16":
                     K[lp * PAGE:lp * PAGE + n, h] = bf16.bits_to_f32(blk.read_k(n))
                     V[lp * PAGE:lp * PAGE + n, h] = bf16.bits_to_f32(blk.read_v(n))
-                elif self.fmt == "q2":
+                elif self.page_fmt == "q2":
                     c, s, m = blk.read_k(n)
                     K[lp * PAGE:lp * PAGE + n, h] = codec.q2_dequantize(c, s, m)
                     c, s, m = blk.read_v(n)
@@ -141,9 +196,14 @@ def dequantized_rows(fmt: str, k_rows, v_rows):
     if fmt == "bf16":
         bf16.f32_to_bits(k), bf16.f32_to_bits(v)  # the rows must be bf16 numbers
         return k.copy(), v.copy()
-    if fmt == "q2":
+    if fmt in ("q2", "q2w"):
         K = codec.q2_dequantize(*codec.q2_quantize(k))
         V = codec.q2_dequantize(*codec.q2_quantize(v))
+        if fmt == "q2w":  # the last page holds the exact rows
+            bf16.f32_to_bits(k), bf16.f32_to_bits(v)
+            w0 = PAGE * ((k.shape[0] - 1) // PAGE)
+            K[w0:] = k[w0:]
+            V[w0:] = v[w0:]
         return K, V
     cv, sv = codec.q8_quantize_v(v)
     V = codec.q8_dequantize(cv, sv[..., None])
