@@ -68,7 +68,19 @@ typedef enum {
      * sections "The numbers": the decode price of hq against BF16, and "See
      * it, control it": the format is hq-e8-2b or bf16), in the same paged
      * pool and through the same calls. */
-    KV_FMT_BF16 = 3
+    KV_FMT_BF16 = 3,
+    /* KV_FMT_Q2 pages plus the window of exact recent keys that "The KV
+     * cache and prompt reuse" (section "What a sequence is made of") has the
+     * compressed format keep, read as one page: for each (sequence, layer, KV
+     * head) the bf16 K and V rows of the last page appended to.  With A
+     * tokens of a (sequence, layer) appended, decode and prefill read tokens
+     * 64 * floor((A - 1) / 64) .. A - 1 exact and every earlier token from
+     * the 2-bit pages, which hold exactly what a KV_FMT_Q2 pool holds.  The
+     * pages cost what 2-bit pages cost; the exact rows take 256 x D bytes per
+     * (sequence slot, layer, KV head) outside the page budget (2 MiB a slot
+     * at 16 x 4 x 256).  Appends are sequential per (sequence, layer), and
+     * attention reads at most the tokens appended. */
+    KV_FMT_Q2_WINDOW = 4
 } kv_format;
 
 typedef enum {
@@ -112,8 +124,9 @@ kv_status kv_pool_bytes_for_tokens(const kv_geom* geom, kv_format fmt, int64_t t
 /* Create a pool of floor(bytes / page_bytes) pages.  d_mem: NULL to let the
  * library allocate device memory (freed by kv_pool_destroy), or caller-owned
  * device memory of at least pages x page_bytes bytes.  max_seqs and
- * max_seq_tokens size the device block tables (and, for KV_FMT_Q8, the
- * per-sequence exact-key window of one page per layer and head).  Prints one
+ * max_seq_tokens size the device block tables (and, for KV_FMT_Q8 and
+ * KV_FMT_Q2_WINDOW, the per-sequence exact window of one page per layer and
+ * head).  Prints one
  * line with the page and token counts to stderr.  Errors: KV_ERR_ARG,
  * KV_ERR_UNSUPPORTED (geometry), KV_ERR_NO_SPACE (budget below one page),
  * KV_ERR_DEVICE. */
@@ -156,8 +169,10 @@ kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t
  * pages it touches.  8-bit appends are sequential per (sequence, layer):
  * start_pos must equal the tokens already appended to that layer, because
  * the exact K rows of the open page are kept only for the tokens appended so
- * far.  The sequences of one call must be distinct.  Errors: KV_ERR_ARG
- * (including a non-sequential 8-bit append), KV_ERR_BOUND (a position beyond
+ * far; the same holds for KV_FMT_Q2_WINDOW, whose append also copies the
+ * rows of the last page it reaches into the sequence's exact window.  The
+ * sequences of one call must be distinct.  Errors: KV_ERR_ARG (including a
+ * non-sequential 8-bit or window append), KV_ERR_BOUND (a position beyond
  * the reserved bound; nothing is written), KV_ERR_UNSUPPORTED (more than
  * KV_MAX_BATCH entries), KV_ERR_DEVICE. */
 kv_status kv_append_quant(kv_pool* pool, int32_t layer, int32_t n, const int32_t* seqs,
@@ -170,7 +185,8 @@ enum { KV_OP_DECODE = 0, KV_OP_PREFILL = 1 };
  * prefill with n_rows chunk queries, and n_splits splits of the context.
  * n_splits = 0 asks for enough bytes for the split count the library picks
  * by itself (decode: any count up to 256; prefill: the count it picks for
- * n_rows queries, about one workgroup per compute unit). */
+ * n_rows queries, about one workgroup per compute unit).  A KV_FMT_Q2_WINDOW
+ * prefill needs one more split's worth for the window's partials. */
 kv_status kv_workspace_bytes(const kv_pool* pool, int32_t op, int32_t n_rows, int32_t n_splits, int64_t* bytes);
 
 /* Split-count the library picks for a decode batch when n_splits = 0. */
@@ -186,6 +202,9 @@ kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_le
  * The ranges' partial results (max, sum, unnormalised output) go to d_ws; a
  * second kernel on the same stream merges them in fp32 (two launches per
  * call).
+ * KV_FMT_Q2_WINDOW: the ranges cover the tokens before the window; the merge
+ * kernel also attends to the window's exact rows (ctx_len at most the tokens
+ * appended to the layer, else KV_ERR_BOUND).
  * d_out: fp32 [n][Hq][D].  d_scores: NULL, or fp32 [n][Hq][scores_stride]
  * receiving the raw logits (scores_stride >= max ctx_len).  Every workspace
  * byte read is written first within the call.  Errors: KV_ERR_ARG,
@@ -199,7 +218,10 @@ kv_status kv_attn_decode(kv_pool* pool, int32_t layer, int32_t n, const int32_t*
  * positions q_start .. q_start + n_q - 1, after the chunk's own K/V have been
  * appended ("KV at 9 KB a token", opening section: prefill attention reads
  * the compressed cache): query i attends to tokens 0 .. q_start + i, all read
- * from the pool, 2-bit and bf16 pools.  Scores are sm_scale x q.k^,
+ * from the pool, 2-bit, bf16 and 2-bit window pools (the window's keys come
+ * exact from its bf16 rows, through a third kernel whose partials the merge
+ * adds; the chunk must lie within the tokens appended).  Scores are
+ * sm_scale x q.k^,
  * softmax and sums in fp32; both contractions run on bf16 matrix cores with
  * exact code operands and 16-bit softmax weights.  The keys of each block of
  * queries are split into n_splits ranges (1..64, 0 = the library's choice)

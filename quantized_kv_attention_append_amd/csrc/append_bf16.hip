@@ -10,13 +10,17 @@
 // 16-byte pieces where all eight slots of a piece are appended.
 //
 // One workgroup of 256 threads per (sequence, page touched, KV head); only
-// the slots of the appended range are written.
+// the slots of the appended range are written.  The same kernel fills the
+// exact window of a 2-bit window pool: the block of the last page an append
+// reaches goes to the (sequence, layer, head) window block instead of the
+// page ("The KV cache and prompt reuse", section "What a sequence is made
+// of": the window of exact recent keys).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
 namespace kvq {
 
-template <int D>
+template <int D, bool WINDOW>
 __global__ __launch_bounds__(256) void append_bf16_kernel(PoolView pv, int layer, BatchDesc bd,
                                                           const uint16_t* __restrict__ kin,
                                                           const uint16_t* __restrict__ vin) {
@@ -29,8 +33,13 @@ __global__ __launch_bounds__(256) void append_bf16_kernel(PoolView pv, int layer
     const int lp = start / PAGE + (x - bd.work0[e]);
     const int slot_lo = max(start, lp * PAGE) - lp * PAGE;
     const int slot_hi = min(start + cnt, (lp + 1) * PAGE) - lp * PAGE;
-    const int phys = pv.bt[(int64_t)bd.seq[e] * pv.bt_stride + lp];
-    uint8_t* blk = pv.pages + (int64_t)phys * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
+    uint8_t* blk;
+    if constexpr (WINDOW) {
+        blk = window_block(pv, bd.seq[e], layer, head);
+    } else {
+        const int phys = pv.bt[(int64_t)bd.seq[e] * pv.bt_stride + lp];
+        blk = pv.pages + (int64_t)phys * pv.page_bytes + ((int64_t)layer * pv.Hkv + head) * pv.block_bytes;
+    }
     const int64_t row_of_slot0 = (int64_t)bd.row0[e] + (lp * PAGE - start);  // input row of slot 0 (may be < 0)
 
     __shared__ __align__(16) uint16_t vt[D * VS];
@@ -73,9 +82,19 @@ hipError_t launch_append_bf16(const PoolView& pv, int layer, const BatchDesc& bd
                               const uint16_t* v, hipStream_t s) {
     dim3 grid(work_items, pv.Hkv);
     if (pv.D == 256)
-        hipLaunchKernelGGL(append_bf16_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+        hipLaunchKernelGGL((append_bf16_kernel<256, false>), grid, dim3(256), 0, s, pv, layer, bd, k, v);
     else
-        hipLaunchKernelGGL(append_bf16_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+        hipLaunchKernelGGL((append_bf16_kernel<128, false>), grid, dim3(256), 0, s, pv, layer, bd, k, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_window(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* k,
+                                const uint16_t* v, hipStream_t s) {
+    dim3 grid(bd.n, pv.Hkv);
+    if (pv.D == 256)
+        hipLaunchKernelGGL((append_bf16_kernel<256, true>), grid, dim3(256), 0, s, pv, layer, bd, k, v);
+    else
+        hipLaunchKernelGGL((append_bf16_kernel<128, true>), grid, dim3(256), 0, s, pv, layer, bd, k, v);
     return hipGetLastError();
 }
 

@@ -515,18 +515,24 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
 hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                                  int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 
-hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
-                            float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
-    if (pv.Hq != 4 * pv.Hkv) return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, s);
+hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
+                                     int splits, float* ws, float* scores, int64_t sstride, hipStream_t s) {
+    if (pv.Hq != 4 * pv.Hkv)
+        return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, nullptr, scores, sstride, s);
     dim3 grid(bd.n * pv.Hkv, splits);
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, nullptr, scores, sstride);
     };
     if (pv.D == 256)
         scores ? go(decode_q2_mfma_kernel<256, true>) : go(decode_q2_mfma_kernel<256, false>);
     else
         scores ? go(decode_q2_mfma_kernel<128, true>) : go(decode_q2_mfma_kernel<128, false>);
-    const hipError_t err = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
+                            float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
+    const hipError_t err = launch_decode_q2_partials(pv, layer, bd, q, sm, splits, ws, scores, sstride, s);
     return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }
 

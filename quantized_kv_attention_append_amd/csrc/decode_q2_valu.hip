@@ -136,8 +136,7 @@ hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc&
         hipLaunchKernelGGL(decode_q2_valu_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
     else
         hipLaunchKernelGGL(decode_q2_valu_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
-    const hipError_t err = hipGetLastError();
-    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
+    return hipGetLastError();
 }
 
 }  // namespace kvq

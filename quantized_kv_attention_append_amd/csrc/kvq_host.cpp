@@ -43,7 +43,7 @@ kv_status hip_fail(hipError_t e, const char* what) {
 
 kv_status check_geom(const kv_geom* g, kv_format fmt) {
     if (!g) return fail(KV_ERR_ARG, "geometry is NULL");
-    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8 && fmt != KV_FMT_BF16)
+    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8 && fmt != KV_FMT_BF16 && fmt != KV_FMT_Q2_WINDOW)
         return fail(KV_ERR_FORMAT, "unknown format %d", (int)fmt);
     if (g->n_layers <= 0 || g->n_kv_heads <= 0 || g->n_q_heads <= 0 || g->head_dim <= 0)
         return fail(KV_ERR_ARG, "geometry fields must be positive");
@@ -57,10 +57,18 @@ kv_status check_geom(const kv_geom* g, kv_format fmt) {
     return KV_OK;
 }
 
+// The pages of a window pool are 2-bit pages.
+kv_format page_format(kv_format fmt) { return fmt == KV_FMT_Q2_WINDOW ? KV_FMT_Q2 : fmt; }
 int64_t block_bytes_of(kv_format fmt, int D) {
+    fmt = page_format(fmt);
     return fmt == KV_FMT_Q2 ? q2_block_bytes(D) : fmt == KV_FMT_Q8 ? q8_block_bytes(D) : bf16_block_bytes(D);
 }
-const char* fmt_name(kv_format fmt) { return fmt == KV_FMT_Q2 ? "q2" : fmt == KV_FMT_Q8 ? "q8" : "bf16"; }
+const char* fmt_name(kv_format fmt) {
+    return fmt == KV_FMT_Q2 ? "q2" : fmt == KV_FMT_Q8 ? "q8" : fmt == KV_FMT_BF16 ? "bf16" : "q2-window";
+}
+// Formats whose appends are sequential per (sequence, layer): the exact rows
+// of the open page are kept only for the tokens appended so far.
+bool sequential_appends(kv_format fmt) { return fmt == KV_FMT_Q8 || fmt == KV_FMT_Q2_WINDOW; }
 
 int64_t token_bytes_of(const kv_geom* g, kv_format fmt) {
     return (int64_t)g->n_layers * g->n_kv_heads * block_bytes_of(fmt, g->head_dim) / PAGE;
@@ -79,6 +87,7 @@ struct kv_pool {
     int32_t bt_stride = 0;       // max pages per sequence
     int32_t* d_bt = nullptr;     // [max_seqs][bt_stride]
     uint16_t* d_stage = nullptr; // 8-bit exact-K window
+    uint8_t* d_win = nullptr;    // 2-bit window pools: exact rows of the last page, per (seq, layer, head)
     int device = 0;
     // host metadata
     std::vector<int32_t> owner;      // page -> seq slot or -1
@@ -88,7 +97,7 @@ struct kv_pool {
         bool live = false;
         int64_t bound = 0;     // reserved tokens
         int64_t appended = 0;  // highest position appended + 1, over all layers
-        std::vector<int64_t> layer_appended;  // 8-bit pools: tokens appended per layer (appends are sequential)
+        std::vector<int64_t> layer_appended;  // 8-bit and window pools: tokens appended per layer (sequential)
         std::vector<int32_t> pages;
     };
     std::vector<Seq> seqs;
@@ -105,6 +114,7 @@ struct kv_pool {
         v.bt = d_bt;
         v.bt_stride = bt_stride;
         v.stage = d_stage;
+        v.win = d_win;
         return v;
     }
 };
@@ -189,6 +199,10 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
         size_t sb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * PAGE * geom->head_dim * sizeof(uint16_t);
         e = hipMalloc((void**)&p->d_stage, sb);
     }
+    if (e == hipSuccess && fmt == KV_FMT_Q2_WINDOW) {
+        size_t wb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * 256 * (size_t)geom->head_dim;
+        e = hipMalloc((void**)&p->d_win, wb);
+    }
     if (e != hipSuccess) {
         kv_status r = hip_fail(e, "hipMalloc(block tables / window)");
         kv_pool_destroy(p);
@@ -211,6 +225,7 @@ kv_status kv_pool_destroy(kv_pool* p) {
     if (p->own_pages && p->d_pages) (void)hipFree(p->d_pages);
     if (p->d_bt) (void)hipFree(p->d_bt);
     if (p->d_stage) (void)hipFree(p->d_stage);
+    if (p->d_win) (void)hipFree(p->d_win);
     delete p;
     return KV_OK;
 }
@@ -290,7 +305,7 @@ kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, i
     s.live = true;
     s.bound = max_tokens;
     s.appended = 0;
-    s.layer_appended.assign(p->fmt == KV_FMT_Q8 ? (size_t)p->geom.n_layers : 0, 0);
+    s.layer_appended.assign(sequential_appends(p->fmt) ? (size_t)p->geom.n_layers : 0, 0);
     s.pages = std::move(got);
     *seq = slot;
     return KV_OK;
@@ -370,11 +385,12 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
         if (n_new[i] < 0 || start_pos[i] < 0) return fail(KV_ERR_ARG, "entry %d: negative position or count", i);
         kv_status s = check_seq(p, seqs[i], start_pos[i] + n_new[i], "append");
         if (s != KV_OK) return s;
-        if (p->fmt == KV_FMT_Q8 && start_pos[i] != p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer])
+        if (sequential_appends(p->fmt) && start_pos[i] != p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer])
             return fail(KV_ERR_ARG,
-                        "entry %d: 8-bit appends are sequential per layer (sequence %d layer %d holds %lld tokens, "
+                        "entry %d: %s appends are sequential per layer (sequence %d layer %d holds %lld tokens, "
                         "append starts at %lld)",
-                        i, seqs[i], layer, (long long)p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer],
+                        i, fmt_name(p->fmt), seqs[i], layer,
+                        (long long)p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer],
                         (long long)start_pos[i]);
         for (int j = 0; j < i; ++j)
             if (seqs[j] == seqs[i]) return fail(KV_ERR_ARG, "sequence %d appears twice in one append", seqs[i]);
@@ -392,6 +408,26 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
     hipError_t e = hipSuccess;
     if (p->fmt == KV_FMT_Q2) {
         e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+    } else if (p->fmt == KV_FMT_Q2_WINDOW) {
+        // every row to the 2-bit pages, and the rows of the last page each
+        // entry reaches to its window block
+        e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+        BatchDesc wd = bd;
+        int m = 0;
+        for (int i = 0; i < n; ++i) {
+            if (bd.cnt[i] == 0) continue;
+            const int end = bd.pos[i] + bd.cnt[i];
+            const int lo = std::max(bd.pos[i], PAGE * ((end - 1) / PAGE));
+            wd.seq[m] = bd.seq[i];
+            wd.pos[m] = lo;
+            wd.cnt[m] = end - lo;
+            wd.row0[m] = bd.row0[i] + (lo - bd.pos[i]);
+            wd.work0[m] = m;
+            ++m;
+        }
+        wd.n = m;
+        wd.work0[m] = m;
+        if (e == hipSuccess && m > 0) e = launch_append_window(p->view(), layer, wd, d_k, d_v, (hipStream_t)stream);
     } else if (p->fmt == KV_FMT_BF16) {
         e = launch_append_bf16(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
     } else {
@@ -429,7 +465,7 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
     for (int i = 0; i < n; ++i) {
         auto& s = p->seqs[(size_t)seqs[i]];
         s.appended = std::max<int64_t>(s.appended, start_pos[i] + n_new[i]);
-        if (p->fmt == KV_FMT_Q8) s.layer_appended[(size_t)layer] = start_pos[i] + n_new[i];
+        if (sequential_appends(p->fmt)) s.layer_appended[(size_t)layer] = start_pos[i] + n_new[i];
     }
     return KV_OK;
 }
@@ -448,6 +484,7 @@ kv_status kv_workspace_bytes(const kv_pool* p, int32_t op, int32_t n_rows, int32
         *bytes = 4 * decode_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
     } else if (op == KV_OP_PREFILL) {
         int sp = n_splits > 0 ? n_splits : (n_rows > 0 ? prefill_auto_splits(n_rows, p->geom.n_q_heads, p->geom.n_kv_heads) : 1);
+        if (p->fmt == KV_FMT_Q2_WINDOW) ++sp;  // the window's partials
         *bytes = 4 * prefill_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
     } else {
         return fail(KV_ERR_ARG, "unknown op %d", op);
@@ -467,23 +504,46 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
     BatchDesc bd;
     memset(&bd, 0, sizeof bd);
     bd.n = n;
-    int64_t max_ctx = 0;
+    const bool window = p->fmt == KV_FMT_Q2_WINDOW;
+    int64_t max_ctx = 0, max_paged = 0;
+    int64_t paged[KV_MAX_BATCH];  // tokens read from the pages
     for (int i = 0; i < n; ++i) {
         if (ctx_len[i] <= 0) return fail(KV_ERR_ARG, "entry %d: ctx_len must be >= 1", i);
         kv_status s = check_seq(p, seqs[i], ctx_len[i], "decode");
         if (s != KV_OK) return s;
         bd.seq[i] = seqs[i];
-        bd.pos[i] = (int32_t)ctx_len[i];
+        paged[i] = ctx_len[i];
+        if (window) {
+            // tokens 64 floor((A - 1) / 64) .. A - 1 are read from the window block
+            const int64_t A = p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer];
+            if (ctx_len[i] > A)
+                return fail(KV_ERR_BOUND, "decode: entry %d: ctx_len %lld beyond the %lld tokens appended to layer %d",
+                            i, (long long)ctx_len[i], (long long)A, layer);
+            paged[i] = std::min<int64_t>(ctx_len[i], PAGE * ((A - 1) / PAGE));
+            bd.cnt[i] = (int32_t)(ctx_len[i] - paged[i]);
+        }
+        bd.pos[i] = (int32_t)paged[i];
         max_ctx = std::max(max_ctx, ctx_len[i]);
+        max_paged = std::max(max_paged, paged[i]);
     }
     if (d_scores && scores_stride < max_ctx) return fail(KV_ERR_ARG, "scores_stride %lld < max ctx_len %lld", (long long)scores_stride, (long long)max_ctx);
-    int sp = n_splits > 0 ? n_splits : auto_splits(p, n, ctx_len);
-    bd.per = split_pairs_per((int)max_ctx, sp);
+    int sp = n_splits > 0 ? n_splits : auto_splits(p, n, paged);
+    bd.per = split_pairs_per((int)max_paged, sp);
     int64_t need = 4 * decode_ws_floats(n, p->geom.n_q_heads, p->geom.head_dim, sp);
     if (!d_ws || ws_bytes < need)
         return fail(KV_ERR_WORKSPACE, "decode needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
     hipStream_t s = (hipStream_t)stream;
     PoolView pv = p->view();
+    if (window) {
+        hipError_t e = hipSuccess;
+        if (max_paged > 0)
+            e = launch_decode_q2_partials(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_scores, scores_stride, s);
+        if (e == hipSuccess)
+            e = launch_decode_window_merge(pv, layer, bd, d_q, sm_scale, sp, (const float*)d_ws, d_out, d_scores,
+                                           scores_stride, s);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+        return KV_OK;
+    }
     hipError_t e =
         p->fmt == KV_FMT_Q2   ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
         : p->fmt == KV_FMT_Q8 ? launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
@@ -497,19 +557,29 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
                           float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes, float* d_out,
                           kv_stream_t stream) {
     if (!p) return fail(KV_ERR_ARG, "pool is NULL");
-    if (p->fmt == KV_FMT_Q8) return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit and bf16 formats only");
+    if (p->fmt == KV_FMT_Q8)
+        return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit, bf16 and 2-bit window formats only");
     if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
     if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
     if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
     kv_status st = check_seq(p, seq, q_start + n_q, "prefill");
     if (st != KV_OK) return st;
     if (n_splits < 0 || n_splits > 64) return fail(KV_ERR_ARG, "n_splits %d out of range", n_splits);
+    int w0 = 0;
+    if (p->fmt == KV_FMT_Q2_WINDOW) {
+        const int64_t A = p->seqs[(size_t)seq].layer_appended[(size_t)layer];
+        if (q_start + n_q > A)
+            return fail(KV_ERR_BOUND, "prefill: chunk ends at %lld, beyond the %lld tokens appended to layer %d",
+                        (long long)(q_start + n_q), (long long)A, layer);
+        w0 = (int)(PAGE * ((A - 1) / PAGE));
+    }
     int sp = n_splits > 0 ? n_splits : prefill_auto_splits(n_q, p->geom.n_q_heads, p->geom.n_kv_heads);
-    int64_t need = 4 * prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim, sp);
+    int64_t need = 4 * prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim,
+                                         sp + (p->fmt == KV_FMT_Q2_WINDOW ? 1 : 0));
     if (!d_ws || ws_bytes < need)
         return fail(KV_ERR_WORKSPACE, "prefill needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
     hipError_t e = launch_prefill(p->view(), (int)p->fmt, layer, seq, (int)q_start, n_q, d_q, sm_scale, sp,
-                                  (float*)d_ws, d_out, (hipStream_t)stream);
+                                  (float*)d_ws, d_out, w0, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
     return KV_OK;
 }
@@ -521,7 +591,7 @@ kv_status kv_dequant_page(const kv_pool* p, int32_t page, int32_t layer, int32_t
     if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
     if (head < 0 || head >= p->geom.n_kv_heads) return fail(KV_ERR_ARG, "head %d out of range", head);
     if (kv != 0 && kv != 1) return fail(KV_ERR_ARG, "kv must be 0 (K) or 1 (V)");
-    hipError_t e = launch_dequant_page(p->view(), (int)p->fmt, page, layer, head, kv, d_out, (hipStream_t)stream);
+    hipError_t e = launch_dequant_page(p->view(), (int)page_format(p->fmt), page, layer, head, kv, d_out, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "dequant launch");
     return KV_OK;
 }

@@ -20,7 +20,13 @@ struct PoolView {
     const int32_t* bt;     // device block tables [max_seqs][bt_stride]
     int32_t bt_stride;
     uint16_t* stage;       // 8-bit pools: exact K window, bf16 [max_seqs][L][Hkv][64][D]
+    uint8_t* win;          // 2-bit window pools: one bf16 block (K [64][D], V [D][64]) per (seq, layer, head)
 };
+
+// The window block of (seq, layer, head) in a 2-bit window pool.
+__host__ __device__ inline uint8_t* window_block(const PoolView& pv, int seq, int layer, int head) {
+    return pv.win + (((int64_t)seq * pv.L + layer) * pv.Hkv + head) * (256 * (int64_t)pv.D);
+}
 
 // Per-call batch description, passed by value as a kernel argument (so it is
 // captured with the launch and needs no device copy).
@@ -32,6 +38,8 @@ struct BatchDesc {
     int32_t row0[KV_MAX_BATCH];       // append: first input row of the entry
     int32_t work0[KV_MAX_BATCH + 1];  // prefix sum of work items per entry
     int32_t per;                      // decode: page pairs per split, the same for every entry
+    // 2-bit window pools, decode: pos = tokens read from the pages, cnt = the
+    // window tokens after them (read from the window block, slots 0 .. cnt-1)
 };
 
 // Byte offsets inside a 2-bit (layer, head) block of D dims.
@@ -66,17 +74,31 @@ hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, 
                             const uint16_t* k, const uint16_t* v, hipStream_t s);
 hipError_t launch_append_bf16(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
                               const uint16_t* k, const uint16_t* v, hipStream_t s);
+// The same copy into the window blocks of a 2-bit window pool: every entry of
+// bd covers slots of one page only (one work item per entry).
+hipError_t launch_append_window(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* k,
+                                const uint16_t* v, hipStream_t s);
 // Decode launchers enqueue the split kernel and then the merge of its
 // partials, which writes the fp32 output.
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
+// The 2-bit split kernel alone (partials to ws, no merge).
+hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
+                                     int splits, float* ws, float* scores, int64_t sstride, hipStream_t s);
+// 2-bit window pools: merge of the split partials together with the exact
+// window tokens of every entry (bd.pos pages-read tokens, bd.cnt window tokens).
+hipError_t launch_decode_window_merge(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q,
+                                      float sm, int splits, const float* ws, float* out, float* scores,
+                                      int64_t sstride, hipStream_t s);
 hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_decode_bf16(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                               int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
-// Prefill over a 2-bit or bf16 pool (fmt).
+// Prefill over a 2-bit, bf16 or 2-bit window pool (fmt).  Window pools: keys
+// from w0 = 64 * floor((A - 1) / 64) on come from the window block, and the
+// window's partials sit after the splits' in ws (one more split's worth).
 hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
-                          float sm, int splits, float* ws, float* out, hipStream_t s);
+                          float sm, int splits, float* ws, float* out, int w0, hipStream_t s);
 // Split count a prefill of n_q chunk queries takes when the caller passes 0.
 int prefill_auto_splits(int n_q, int Hq, int Hkv);
 hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,

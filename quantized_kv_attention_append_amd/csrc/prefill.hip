@@ -35,6 +35,7 @@
 // A bf16 pool fills the same tiles with the stored values (K dims interleaved
 // into kappa order by byte permutes, V copied) and unit metadata (scale 1,
 // offset 0), so that the rest of the kernel is the same code.
+#include <climits>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -248,9 +249,11 @@ __device__ __forceinline__ void convert_packed(const PackedPage<D, KV_FMT_BF16>&
     if (tid < PAGE) L.meta[buf][tid] = make_float4(1.f, 0.f, 1.f, 0.f);
 }
 
-// Pages [pg0, pg1) of split sp for a block whose last query sits at pos_max.
-__device__ __forceinline__ void prefill_split_range(int pos_max, int splits, int sp, int* pg0, int* pg1) {
-    const int n_pages = pos_max / PAGE + 1;
+// Pages [pg0, pg1) of split sp for a block whose last query sits at pos_max;
+// only pages below kpl are read from the pool (a window pool's window page
+// and later are not).
+__device__ __forceinline__ void prefill_split_range(int pos_max, int splits, int sp, int kpl, int* pg0, int* pg1) {
+    const int n_pages = min(pos_max / PAGE + 1, kpl);
     const int per = (n_pages + splits - 1) / splits;
     *pg0 = min(sp * per, n_pages);
     *pg1 = min(sp * per + per, n_pages);
@@ -259,7 +262,7 @@ __device__ __forceinline__ void prefill_split_range(int pos_max, int splits, int
 template <int D, int FMT>
 __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, int seq, int q_start, int n_q,
                                                       const uint16_t* __restrict__ q, float sm, int splits,
-                                                      float* __restrict__ ws) {
+                                                      int kpl, float* __restrict__ ws) {
     constexpr int KSTEPS = D / 32, DB = D / 16;
     constexpr int KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
     const int Hkv = pv.Hkv, Hq = pv.Hq, G = Hq / Hkv;
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, in
     const int q_first = qb * QB;
     const int pos_max = q_start + min(q_first + QB, n_q) - 1;
     int pg0, pg1;
-    prefill_split_range(pos_max, splits, sp, &pg0, &pg1);
+    prefill_split_range(pos_max, splits, sp, kpl, &pg0, &pg1);
     if (pg0 >= pg1) return;
 
     __shared__ __align__(16) PrefillLds<D> L;
@@ -511,22 +514,41 @@ __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, in
 }
 
 // Merge of the prefill partials: one workgroup per (query, head); split p
-// counts for query i when its first page starts at or before i's position.
+// counts for query i when its first page starts at or before i's position and
+// holds a page below kpl.  A window pool's window partials (win: outputs
+// [n_q][Hq][D], then (max, sum) pairs) count for every row.
 __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q, int Hq, int Hkv, int D, int splits,
-                                                            const float* __restrict__ ws, float* __restrict__ out) {
+                                                            int kpl, const float* __restrict__ ws,
+                                                            const float* __restrict__ win, float* __restrict__ out) {
     const int row = blockIdx.x;  // i * Hq + h
     const int i = row / Hq, G = Hq / Hkv;
     const int d = threadIdx.x;
     const int QB = ROWS / G, qb = i / QB;
     const int pos = q_start + i;
     const int pos_max = q_start + min(qb * QB + QB, n_q) - 1;
-    const int n_pages = pos_max / PAGE + 1, per = (n_pages + splits - 1) / splits;
-    const int live = min(splits, pos / (per * PAGE) + 1);
+    const int n_pages = min(pos_max / PAGE + 1, kpl);
+    int live = 0;
+    if (n_pages > 0) {
+        const int per = (n_pages + splits - 1) / splits;
+        live = min(min(splits, pos / (per * PAGE) + 1), (n_pages + per - 1) / per);
+    }
     const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)n_q * Hq * splits * D) + (int64_t)row * splits;
     const float* o = ws + (int64_t)row * splits * D + d;
-    float M = -INFINITY;
+    float M = -INFINITY, wm = -INFINITY, wl = 0.f, wo = 0.f;
+    if (win) {
+        const float2 w = reinterpret_cast<const float2*>(win + (int64_t)n_q * Hq * D)[row];
+        wm = w.x;
+        wl = w.y;
+        wo = win[(int64_t)row * D + d];
+        M = wm;
+    }
     for (int p = 0; p < live; ++p) M = fmaxf(M, ml[p].x);
     float den = 0.f, acc = 0.f;
+    if (wl > 0.f) {
+        const float f = exp2f(wm - M);
+        den = f * wl;
+        acc = f * wo;
+    }
     for (int p = 0; p < live; ++p) {
         const float f = exp2f(ml[p].x - M);
         den += f * ml[p].y;
@@ -542,28 +564,40 @@ int prefill_auto_splits(int n_q, int Hq, int Hkv) {
     return want < 1 ? 1 : want > 64 ? 64 : want;
 }
 
+hipError_t launch_prefill_window(const PoolView& pv, int layer, int seq, int q_start, int n_q, int w0,
+                                 const uint16_t* q, float sm, float* wo, float* wml, hipStream_t s);
+
 hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
-                          float sm, int splits, float* ws, float* out, hipStream_t s) {
+                          float sm, int splits, float* ws, float* out, int w0, hipStream_t s) {
     const int G = pv.Hq / pv.Hkv, QB = ROWS / G;
+    const bool window = fmt == KV_FMT_Q2_WINDOW;
+    const int kpl = window ? w0 / PAGE : INT_MAX;
     dim3 grid(((n_q + QB - 1) / QB) * pv.Hkv, splits);
     if (fmt == KV_FMT_BF16) {
         if (pv.D == 256)
             hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_BF16>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
-                               q, sm, splits, ws);
+                               q, sm, splits, kpl, ws);
         else
             hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_BF16>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
-                               q, sm, splits, ws);
-    } else if (pv.D == 256) {
-        hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q,
-                           sm, splits, ws);
-    } else {
-        hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q, q,
-                           sm, splits, ws);
+                               q, sm, splits, kpl, ws);
+    } else if (kpl > 0) {
+        if (pv.D == 256)
+            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
+                               q, sm, splits, kpl, ws);
+        else
+            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
+                               q, sm, splits, kpl, ws);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    float* win = nullptr;
+    if (window) {
+        win = ws + prefill_ws_floats(n_q, pv.Hq, pv.D, splits);
+        err = launch_prefill_window(pv, layer, seq, q_start, n_q, w0, q, sm, win, win + (int64_t)n_q * pv.Hq * pv.D, s);
+        if (err != hipSuccess) return err;
+    }
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(n_q * pv.Hq), dim3(pv.D), 0, s, q_start, n_q, pv.Hq, pv.Hkv, pv.D,
-                       splits, ws, out);
+                       splits, kpl, ws, win, out);
     return hipGetLastError();
 }
 

@@ -36,6 +36,8 @@ def test_token_bytes_from_the_library():
     assert kvq.token_bytes((32, 8, 128, 32), kvq.FMT_Q8) == (68608, 4390912)
     # bf16: the 65,536 B a token of the 27B geometry, against 9,216 for 2-bit
     assert kvq.token_bytes((16, 4, 256, 16), kvq.FMT_BF16) == (65536, 64 * 65536)
+    # the exact window lives outside the pages: window pools cost 2-bit pages
+    assert kvq.token_bytes((16, 4, 256, 16), kvq.FMT_Q2_WINDOW) == (9216, 589824)
     assert kvq.pool_bytes_for_tokens((16, 4, 256, 16), kvq.FMT_Q2, 8 * 40960) == 3_019_898_880
     assert kvq.pool_bytes_for_tokens((1, 4, 256, 16), kvq.FMT_Q2, 65) == 2 * 36864
 
@@ -45,7 +47,7 @@ def test_token_bytes_from_the_library():
     ((16, 4, 256, 6), 1, "KV_ERR_UNSUPPORTED"),    # Hq not a multiple of Hkv
     ((16, 4, 256, 64), 1, "KV_ERR_UNSUPPORTED"),   # group 16
     ((0, 4, 256, 16), 1, "KV_ERR_ARG"),
-    ((16, 4, 256, 16), 4, "KV_ERR_FORMAT"),       # no format 4
+    ((16, 4, 256, 16), 5, "KV_ERR_FORMAT"),       # no format 5
 ])
 def test_bad_geometry_is_refused(geom, fmt, status):
     import quantized_kv_attention_append_amd as kvq
