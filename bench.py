@@ -287,24 +287,30 @@ def q8_leg(reps: int):
             "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
 
-def bf16_leg(reps: int):
+def bf16_leg(reps: int, window: bool = False):
     """The exact bf16 cache of the same 27B-geometry batch (16 layers x 4 KV
     heads x 256 dims, 8 lanes x 40,960 tokens: 21.47 GB, the pages' 20.0 GiB),
     through the same calls: populate, then the 16-layer decode step (each call
     timed with HIP events, and the step replayed as a HIP graph), and the
-    65,536 + 1,024 chunked prefill over a bf16 pool."""
+    65,536 + 1,024 chunked prefill over a bf16 pool.
+
+    window=True runs the same legs over 2-bit pools with the exact window of
+    the last page: each lane's last 64 tokens are read as bf16 rows, the rest
+    as 2-bit rows (the pool's pages are the 2-bit 3.02 GB)."""
     import torch
 
     import quantized_kv_attention_append_amd as kvq
     from synth import CONFIGS, kv_rows, page_permutation, queries
 
+    fmt = kvq.FMT_Q2_WINDOW if window else kvq.FMT_BF16
+    name = "2-bit window" if window else "bf16"
     w = CONFIGS[1]
     L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
     geom = (L, H, D, Hq)
-    tb, pb = kvq.token_bytes(geom, kvq.FMT_BF16)
+    tb, pb = kvq.token_bytes(geom, fmt)
     ppl = ctx // 64
     n_pages = B * ppl
-    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_BF16, max_seqs=B, max_seq_tokens=ctx)
+    pool = kvq.Pool(n_pages * pb, geom, fmt, max_seqs=B, max_seq_tokens=ctx)
     perm = page_permutation(w, n_pages)
     seqs = [pool.reserve(ctx, pages=perm[i * ppl:(i + 1) * ppl]) for i in range(B)]
     stream = torch.cuda.current_stream()
@@ -321,7 +327,8 @@ def bf16_leg(reps: int):
         e1.synchronize()
         app_ms += e0.elapsed_time(e1)
         del k, v
-    app_bytes = 2 * B * ctx * tb   # every row of every layer read once and written once (tb covers all layers)
+    # every row of every layer read once (bf16) and written once (tb covers all layers)
+    app_bytes = B * ctx * (L * H * 4 * D + tb)
     qs = [queries(w, layer, B, device="cuda") for layer in range(L)]
     sp = pool.decode_splits([ctx] * B)
     ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, B, sp), dtype=torch.uint8, device="cuda")
@@ -359,9 +366,12 @@ def bf16_leg(reps: int):
     graph_ms = g0.elapsed_time(g1) / reps
     same = all(torch.equal(a, b) for a, b in zip(outs, eager_outs))
     del g
-    alg = B * ppl * H * 64 * (4 * D) + B * Hq * D * (2 + 4)   # K and V rows, q in, fp32 out
+    if window:   # 2-bit K and V rows before the window, bf16 rows in it, q in, fp32 out
+        alg = B * H * ((ctx - 64) * 2 * (D // 4 + 8) + 64 * 4 * D) + B * Hq * D * (2 + 4)
+    else:        # bf16 K and V rows, q in, fp32 out
+        alg = B * ppl * H * 64 * (4 * D) + B * Hq * D * (2 + 4)
     gbs = alg / (avg_ms * 1e-3) / 1e9
-    log(f"bf16: populate {app_ms:.1f} ms ({app_bytes / app_ms / 1e6:.0f} GB/s); decode {avg_ms * 1e3:.1f} us a call, "
+    log(f"{name}: populate {app_ms:.1f} ms ({app_bytes / app_ms / 1e6:.0f} GB/s); decode {avg_ms * 1e3:.1f} us a call, "
         f"{gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), splits={sp}; graph step {graph_ms:.3f} ms "
         f"(identical to eager: {same})")
     del pool, ws, outs, qs, eager_outs
@@ -372,12 +382,13 @@ def bf16_leg(reps: int):
     prior, n_q = w3.ctx, w3.chunk
     total = prior + n_q
     geom3 = (w3.n_layers, w3.n_kv_heads, w3.head_dim, w3.n_q_heads)
-    _, pb3 = kvq.token_bytes(geom3, kvq.FMT_BF16)
+    _, pb3 = kvq.token_bytes(geom3, fmt)
     n3 = total // 64
-    pool3 = kvq.Pool(n3 * pb3, geom3, kvq.FMT_BF16, max_seqs=1, max_seq_tokens=total)
+    pool3 = kvq.Pool(n3 * pb3, geom3, fmt, max_seqs=1, max_seq_tokens=total)
     seq3 = pool3.reserve(total, pages=page_permutation(w3, n3))
     k, v = kv_rows(w3, 0, 0, total, device="cuda")
-    pool3.append(0, [seq3], [0], [total], k, v)
+    pool3.append(0, [seq3], [0], [prior], k[:prior], v[:prior])
+    pool3.append(0, [seq3], [prior], [n_q], k[prior:], v[prior:])
     del k, v
     q = queries(w3, 0, n_q, device="cuda", stream=1)
     ws3 = torch.empty(pool3.workspace_bytes(kvq.OP_PREFILL, n_q, 0), dtype=torch.uint8, device="cuda")
@@ -385,14 +396,14 @@ def bf16_leg(reps: int):
     pf = _call_ms(lambda: pool3.prefill(0, seq3, prior, q, w3.sm_scale, ws=ws3, out=out3), reps)
     flops = 4.0 * w3.head_dim * w3.n_q_heads * sum(prior + i + 1 for i in range(n_q))
     pf_tflops = flops / (pf[0] * 1e-3) / 1e12
-    log(f"bf16 prefill: {pf[0]:.3f} ms per call, {pf_tflops:.0f} TFLOP/s useful")
-    return {"workload": "27B-geometry batched decode, bf16: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
+    log(f"{name} prefill: {pf[0]:.3f} ms per call, {pf_tflops:.0f} TFLOP/s useful")
+    kernel = ("one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then decode_window_merge_kernel<256>"
+              if window else "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then merge_splits_kernel")
+    return {"workload": f"27B-geometry batched decode, {name}: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
                         "8 lanes x 40960 tokens", "pool_bytes": n_pages * pb, "splits": sp,
             "decode_us_per_call": avg_ms * 1e3, "bytes_per_call": alg,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then "
-                                   "merge_splits_kernel"},
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": kernel},
             "graph_ms_per_step": graph_ms, "graph_identical_to_eager": same,
             "kv_tokens_per_s": B * L * ctx / (graph_ms * 1e-3),
             "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6,
@@ -578,6 +589,15 @@ def main():
         log(f"2-bit against bf16: decode step {bf16['q2_step_speedup']:.2f}x faster"
             + (f", prefill {bf16['q2_prefill_time_ratio']:.2f}x the bf16 time" if prefill is not None else ""))
 
+    win = None if args.no_extra else bf16_leg(5, window=True)
+    if win is not None:
+        # the price of reading each lane's last page exact, same batch and calls
+        win["step_time_vs_q2"] = win["graph_ms_per_step"] / ms_per_step
+        if prefill is not None:
+            win["prefill_time_vs_q2"] = win["prefill_ms_per_call"] / prefill["ms_per_call"]
+        log(f"2-bit window against 2-bit: decode step {win['step_time_vs_q2']:.3f}x the time"
+            + (f", prefill {win['prefill_time_vs_q2']:.3f}x" if prefill is not None else ""))
+
     cpu = None
     if not args.no_cpu:
         cpu = oracle_baseline(w, args.cpu_seconds)
@@ -622,6 +642,7 @@ def main():
         "long_context": long_ctx,
         "q8": q8,
         "bf16": bf16,
+        "q2_window": win,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

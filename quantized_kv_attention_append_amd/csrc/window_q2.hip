@@ -20,24 +20,31 @@ namespace {
 constexpr float WIN_LOG2E = 1.4426950408889634f;
 }
 
-// One workgroup of D threads per (sequence, query head); thread d owns dim d.
+// One workgroup of D threads (D / 64 waves) per (sequence, query head);
+// thread d owns dim d.  Every global load that does not depend on the scores
+// (the query, this dim's V row of the window, the first U split partials) is
+// issued first; then wave w takes dims [64w, 64w + 64) of every window key
+// (lane t: key t), wave 0 adds the D / 64 parts and forms the weights, and
+// each thread sums its dim over the keys with four partial sums.
 template <int D>
 __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                   const uint16_t* __restrict__ q, float sm, int splits,
                                                                   const float* __restrict__ ws, float* __restrict__ out,
                                                                   float* __restrict__ scores, int64_t sstride) {
     constexpr int U = 8;
+    constexpr int NWAVE = D / 64;
     const int row = blockIdx.x;  // e * Hq + h
     const int Hq = pv.Hq, e = row / Hq, h = row % Hq, g = h / (Hq / pv.Hkv);
-    const int d = threadIdx.x;
+    const int d = threadIdx.x, wave = d >> 6, lane = d & 63;
     const int c = bd.pos[e], nw = bd.cnt[e];  // tokens from the pages, then window slots 0 .. nw-1
     const int live = live_splits(c, bd.per);
     const uint8_t* blk = window_block(pv, bd.seq[e], layer, g);
 
     __shared__ float qs[D];
-    __shared__ float sc[PAGE];
+    __shared__ float part[NWAVE][PAGE];
+    __shared__ float pw[PAGE];
+    __shared__ float wml[2];
 
-    // loads that do not depend on the scores: the query, this dim's V row
     qs[d] = bf16_to_f32(q[(int64_t)row * D + d]);
     uint4 vrow[PAGE / 8];
     {
@@ -45,60 +52,91 @@ __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, i
 #pragma unroll
         for (int k = 0; k < PAGE / 8; ++k) vrow[k] = vp[k];
     }
-    __syncthreads();
-
-    // ---- scores of the window slots: lane t of the first wave takes slot t ----
-    if (d < PAGE) {
-        float s = -INFINITY;
-        if (d < nw) {
-            const uint4* kp = reinterpret_cast<const uint4*>(blk + 2 * (int64_t)D * d);
-            float dot = 0.f;
-#pragma unroll 8
-            for (int k = 0; k < D / 8; ++k) {
-                const uint4 w = kp[k];
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + (int64_t)row * splits;
+    const float* o = ws + (int64_t)row * splits * D + d;
+    float2 m0[U];
+    float v0[U];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    dot = fmaf(qs[8 * k + 2 * i], bf16lo(u[i]), dot);
-                    dot = fmaf(qs[8 * k + 2 * i + 1], bf16hi(u[i]), dot);
-                }
-            }
-            if (scores) scores[(int64_t)row * sstride + c + d] = dot * sm;
-            s = dot * (sm * WIN_LOG2E);
-        }
-        sc[d] = s;
+    for (int u = 0; u < U; ++u) {
+        const bool ok = u < live;
+        m0[u] = ok ? ml[u] : make_float2(-INFINITY, 0.f);
+        v0[u] = ok ? o[(int64_t)u * D] : 0.f;
     }
     __syncthreads();
 
-    // ---- the window's partial: M_w, l_w, o_w[d] ----
-    float M = -INFINITY;
-    for (int t = 0; t < nw; ++t) M = fmaxf(M, sc[t]);
-    float den = 0.f, acc = 0.f;
+    // ---- partial dot products: wave w, dims 64w .. 64w + 63, lane t = window slot t ----
+    if (lane < nw) {
+        const uint4* kp = reinterpret_cast<const uint4*>(blk + 2 * ((int64_t)D * lane + 64 * wave));
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < PAGE / 8; ++k) {
-        const uint32_t u[4] = {vrow[k].x, vrow[k].y, vrow[k].z, vrow[k].w};
+        for (int k = 0; k < 8; ++k) {
+            const uint4 w = kp[k];
+            const uint32_t uw[4] = {w.x, w.y, w.z, w.w};
+            const float* qq = &qs[64 * wave + 8 * k];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int t = 8 * k + i;
-            if (t < nw) {
-                const float p = exp2f(sc[t] - M);
-                den += p;
-                acc = fmaf(p, (i & 1) ? bf16hi(u[i >> 1]) : bf16lo(u[i >> 1]), acc);
+            for (int i = 0; i < 4; ++i) {
+                a[i] = fmaf(qq[2 * i], bf16lo(uw[i]), a[i]);
+                a[i] = fmaf(qq[2 * i + 1], bf16hi(uw[i]), a[i]);
             }
         }
+        part[wave][lane] = (a[0] + a[1]) + (a[2] + a[3]);
+    }
+    __syncthreads();
+
+    // ---- weights of the window keys (wave 0) ----
+    if (wave == 0) {
+        float s = -INFINITY, p = 0.f;
+        if (lane < nw) {
+            float dot = 0.f;
+#pragma unroll
+            for (int w = 0; w < NWAVE; ++w) dot += part[w][lane];
+            if (scores) scores[(int64_t)row * sstride + c + lane] = dot * sm;
+            s = dot * (sm * WIN_LOG2E);
+        }
+        const float M = wave_max(s);
+        if (lane < nw) p = exp2f(s - M);
+        const float l = wave_sum(p);
+        pw[lane] = p;
+        if (lane == 0) {
+            wml[0] = M;
+            wml[1] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- the window's partial for dim d: o_w = sum_t p_t v[d][t] ----
+    float M = wml[0], den = wml[1];  // M = -inf and den = 0 when the window is empty
+    float acc;
+    {
+        float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < PAGE / 8; ++k) {
+            const uint32_t uw[4] = {vrow[k].x, vrow[k].y, vrow[k].z, vrow[k].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int t = 8 * k + i;
+                const float x = (i & 1) ? bf16hi(uw[i >> 1]) : bf16lo(uw[i >> 1]);
+                // slots past the window hold stale rows: select, never multiply by a zero weight
+                a[i & 3] = t < nw ? fmaf(pw[t], x, a[i & 3]) : a[i & 3];
+            }
+        }
+        acc = (a[0] + a[1]) + (a[2] + a[3]);
     }
 
     // ---- merge with the split partials (running max over groups of U splits) ----
-    const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + (int64_t)row * splits;
-    const float* o = ws + (int64_t)row * splits * D + d;
     for (int p0 = 0; p0 < live; p0 += U) {
         float2 m[U];
         float v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool ok = p0 + u < live;
-            m[u] = ok ? ml[p0 + u] : make_float2(-INFINITY, 0.f);
-            v[u] = ok ? o[(int64_t)(p0 + u) * D] : 0.f;
+            if (p0 == 0) {
+                m[u] = m0[u];
+                v[u] = v0[u];
+            } else {
+                const bool ok = p0 + u < live;
+                m[u] = ok ? ml[p0 + u] : make_float2(-INFINITY, 0.f);
+                v[u] = ok ? o[(int64_t)(p0 + u) * D] : 0.f;
+            }
         }
         float Mg = M;
 #pragma unroll
@@ -186,13 +224,14 @@ __global__ __launch_bounds__(256) void prefill_window_kernel(PoolView pv, int la
         if (nvis > 0) {
             const uint32_t* kr = &Kl[l * KW];
             const uint32_t* qr = &Ql[r * QW];
-            float dot = 0.f;
+            float a[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
             for (int i = 0; i < QW; ++i) {
                 const uint32_t kk = kr[i], qq = qr[i];
-                dot = fmaf(bf16lo(qq), bf16lo(kk), dot);
-                dot = fmaf(bf16hi(qq), bf16hi(kk), dot);
+                a[2 * (i & 1)] = fmaf(bf16lo(qq), bf16lo(kk), a[2 * (i & 1)]);
+                a[2 * (i & 1) + 1] = fmaf(bf16hi(qq), bf16hi(kk), a[2 * (i & 1) + 1]);
             }
+            const float dot = (a[0] + a[1]) + (a[2] + a[3]);
             const float s = l < nvis ? dot * cB : -INFINITY;
             M = wave_max(s);
             const float p = l < nvis ? exp2f(s - M) : 0.f;
