@@ -389,14 +389,31 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
         load_tile<D>(tile, pv.pages + (int64_t)__builtin_amdgcn_readlane(pid0, tt) * pv.page_bytes + lhoff,
                      pv.pages + (int64_t)__builtin_amdgcn_readlane(pid1, tt) * pv.page_bytes + lhoff, l);
     };
-    // the first tile is in flight while the query operand is prepared
+    // The query rows of the group's G heads (contiguous, G D bf16) are loaded
+    // first, in 16-byte pieces, so that preparing the query operand waits for
+    // them only while the first tile is still in flight; they pass through
+    // this wave's metadata area of LDS, unused until the first tile.
+    constexpr int QPIECES = G * D * 2 / 16 / 64;  // 16-byte pieces per lane
+    static_assert(G * D * 2 <= sizeof(WaveLds::meta), "query rows fit the metadata area");
+    uint4 qraw[QPIECES];
+    {
+        const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((int64_t)e * Hq + g * G) * D);
+#pragma unroll
+        for (int i = 0; i < QPIECES; ++i) qraw[i] = qsrc[l + 64 * i];
+    }
     if (TF > 0) {
         fetch_ids(0);
         load(ta, 0);
     }
+    {
+        uint4* qdst = reinterpret_cast<uint4*>(lds.meta);
+#pragma unroll
+        for (int i = 0; i < QPIECES; ++i) qdst[l + 64 * i] = qraw[i];
+    }
+    __syncthreads();
 
     // ---- query operand: 19-bit fixed point per head, row 4 hq + iq = digit iq of head hq ----
-    const uint16_t* qrow = q + ((int64_t)e * Hq + g * G + hq) * D;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(lds.meta) + hq * D;
     float qv[NC][32];
     float amax = 0.f, qsum = 0.f;
 #pragma unroll
