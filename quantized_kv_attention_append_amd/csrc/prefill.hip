@@ -516,7 +516,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, in
 // Merge of the prefill partials: one workgroup per (query, head); split p
 // counts for query i when its first page starts at or before i's position and
 // holds a page below kpl.  A window pool's window partials (win: outputs
-// [n_q][Hq][D], then (max, sum) pairs) count for every row.
+// [n_q][Hq][D], then (max, sum) pairs; the window starts at key 64 kpl) count
+// for the rows whose position reaches the window, the only rows written.
 __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q, int Hq, int Hkv, int D, int splits,
                                                             int kpl, const float* __restrict__ ws,
                                                             const float* __restrict__ win, float* __restrict__ out) {
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q
     const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)n_q * Hq * splits * D) + (int64_t)row * splits;
     const float* o = ws + (int64_t)row * splits * D + d;
     float M = -INFINITY, wm = -INFINITY, wl = 0.f, wo = 0.f;
-    if (win) {
+    if (win && pos >= kpl * PAGE) {
         const float2 w = reinterpret_cast<const float2*>(win + (int64_t)n_q * Hq * D)[row];
         wm = w.x;
         wl = w.y;
