@@ -16,6 +16,11 @@ are kept aside (the exact window), and each append re-derives the page's K codes
 and scales from the exact rows present, so a full page equals the plain
 per-channel quantization of its 64 tokens.
 
+A fork gives a new sequence the first n tokens of another: the whole pages
+of that prefix are shared (both block tables name them), the page it only
+partly fills is copied whole into a page of the child's, with the exact rows
+kept for it.
+
 The 2-bit format with an exact window ("q2w") keeps, besides the 2-bit pages,
 the exact rows of the last page a (sequence, layer) has appended to: the
 "window of exact recent keys that the compressed KV format keeps" of "The KV
@@ -142,6 +147,39 @@ class OraclePool:
         """First position read exactly (q2w): 64 * floor((A - 1) / 64) with A tokens appended."""
         appended = self._window[(seq, layer)][0]
         return PAGE * ((appended - 1) // PAGE)
+
+    # -------------------------------------------------------------- fork --
+    def fork(self, parent: int, parent_bt, child: int, child_bt, n: int):
+        """A child sequence that starts with the parent's first n tokens.
+
+        Its whole pages (logical pages below n // 64) are the parent's pages,
+        shared: child_bt must name the same physical pages there.  A page the
+        prefix only partly fills is copied whole into the child's own page
+        (copy on write), so the child can append into it; the tokens the copy
+        holds past n are never read by the child before it overwrites them.
+        The exact rows kept for the open page (8-bit K window, 2-bit window)
+        are copied with it, as the child's, with n tokens appended.  Follows
+        "The KV cache and prompt reuse" (What a sequence is made of: a lane is
+        charged for the pages it holds; full pages of a shared prefix are
+        reused, the page being written is not)."""
+        full = n // PAGE
+        if list(map(int, child_bt[:full])) != list(map(int, parent_bt[:full])):
+            raise ValueError("the child's whole prefix pages must be the parent's pages")
+        if n % PAGE:
+            src, dst = int(parent_bt[full]), int(child_bt[full])
+            if src == dst:
+                raise ValueError("the partly filled page must be copied, not shared")
+            self.data[dst] = self.data[src]
+        for layer in range(self.L):
+            if self.fmt == "q2w":
+                appended, wk, wv = self._window[(parent, layer)]
+                if (n - 1) // PAGE != (appended - 1) // PAGE or n > appended:
+                    raise ValueError("a window fork must end in the parent's last page")
+                self._window[(child, layer)] = (n, wk.copy(), wv.copy())
+            elif self.fmt == "q8" and n % PAGE:
+                if (parent, layer) not in self._exact_k:
+                    raise ValueError("the parent's open page was not appended")
+                self._exact_k[(child, layer)] = self._exact_k[(parent, layer)].copy()
 
     # ------------------------------------------------------------ gather --
     def gather(self, layer: int, bt, ctx_len: int, seq: int = None):
