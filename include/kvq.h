@@ -77,7 +77,7 @@ typedef enum {
      * 64 * floor((A - 1) / 64) .. A - 1 exact and every earlier token from
      * the 2-bit pages, which hold exactly what a KV_FMT_Q2 pool holds.  The
      * pages cost what 2-bit pages cost; the exact rows take 256 x D bytes per
-     * (sequence slot, layer, KV head) outside the page budget (2 MiB a slot
+     * (sequence slot, layer, KV head) outside the page budget (4 MiB a slot
      * at 16 x 4 x 256).  Appends are sequential per (sequence, layer), and
      * attention reads at most the tokens appended. */
     KV_FMT_Q2_WINDOW = 4
@@ -104,8 +104,8 @@ typedef struct {
 typedef struct {
     int64_t pages;          /* pages the byte budget bought */
     int64_t free_pages;     /* pages not reserved by any sequence */
-    int64_t reserved_pages; /* pages reserved by live sequences */
-    int64_t used_pages;     /* reserved pages that hold at least one appended token */
+    int64_t reserved_pages; /* pages reserved by live sequences (a shared page counts once) */
+    int64_t used_pages;     /* reserved pages that hold at least one appended token (shared: once) */
     int64_t page_bytes;     /* 64 x token_bytes */
     int64_t token_bytes;    /* e.g. 9,216 for 2-bit at 16 x 4 x 256 */
     int64_t tokens;         /* pages x 64 */
@@ -150,7 +150,29 @@ kv_status kv_pool_device_ptr(const kv_pool* pool, void** d_pages, int64_t* bytes
  * sequence slot), KV_ERR_DEVICE. */
 kv_status kv_seq_reserve(kv_pool* pool, int64_t max_tokens, const int32_t* pages, int32_t* seq);
 
-/* Return a sequence's pages to the free list. */
+/* Prefix sharing ("The KV cache and prompt reuse", section "What a sequence
+ * is made of": a lane is charged for the pages it holds, and the full pages of
+ * a shared prefix are held once).  Admit a new sequence with a bound of
+ * max_tokens whose first n_tokens tokens are those of sequence `parent`:
+ *  - the parent's pages that n_tokens fills completely (logical pages below
+ *    n_tokens / 64) are shared: both block tables name them, each page counts
+ *    its holders, and neither sequence may append into a page held twice;
+ *  - the page n_tokens fills only partly is copied whole, on `stream`, into a
+ *    fresh page of the child's (copy on write), with the exact rows the
+ *    format keeps for it (8-bit pools: the open page's exact K rows; 2-bit
+ *    window pools: every layer's window block);
+ *  - the rest of the child's bound takes fresh pages.
+ * The child starts with n_tokens appended in every layer.  Requirements:
+ * 1 <= n_tokens <= max_tokens, n_tokens at most the tokens appended to the
+ * parent; 8-bit pools: n_tokens equals the tokens appended to every layer of
+ * the parent; 2-bit window pools: n_tokens lies in the last page appended to
+ * in every layer.  Errors: KV_ERR_ARG, KV_ERR_BOUND (max_tokens above the
+ * pool's max_seq_tokens), KV_ERR_NO_SPACE, KV_ERR_DEVICE. */
+kv_status kv_seq_fork(kv_pool* pool, int32_t parent, int64_t n_tokens, int64_t max_tokens, kv_stream_t stream,
+                      int32_t* child);
+
+/* Release a sequence: each of its pages loses a holder, and a page with no
+ * holder left returns to the free list. */
 kv_status kv_seq_release(kv_pool* pool, int32_t seq);
 
 /* Host copy of a sequence's block table: writes up to cap page ids. */
@@ -170,7 +192,8 @@ kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t
  * start_pos must equal the tokens already appended to that layer, because
  * the exact K rows of the open page are kept only for the tokens appended so
  * far; the same holds for KV_FMT_Q2_WINDOW, whose append also copies the
- * rows of the last page it reaches into the sequence's exact window.  The
+ * rows of the last page it reaches into the sequence's exact window.  No
+ * append may write into a page that two sequences hold (kv_seq_fork).  The
  * sequences of one call must be distinct.  Errors: KV_ERR_ARG (including a
  * non-sequential 8-bit or window append), KV_ERR_BOUND (a position beyond
  * the reserved bound; nothing is written), KV_ERR_UNSUPPORTED (more than

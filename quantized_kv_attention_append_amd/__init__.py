@@ -123,6 +123,13 @@ class Pool:
         check(lib.kv_seq_reserve(self._h, int(max_tokens), arr, C.byref(seq)))
         return seq.value
 
+    def fork(self, parent: int, n_tokens: int, max_tokens: int, stream=None) -> int:
+        """A new sequence whose first n_tokens are the parent's: whole pages
+        shared, the partly filled page copied; returns its id."""
+        seq = C.c_int32()
+        check(lib.kv_seq_fork(self._h, int(parent), int(n_tokens), int(max_tokens), _stream(stream), C.byref(seq)))
+        return seq.value
+
     def release(self, seq: int):
         check(lib.kv_seq_release(self._h, int(seq)))
 

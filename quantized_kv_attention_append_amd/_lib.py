@@ -51,6 +51,7 @@ SIGNATURES = {
     "kv_pool_stats": [_P, C.POINTER(PoolStats)],
     "kv_pool_device_ptr": [_P, C.POINTER(_P), _PI64],
     "kv_seq_reserve": [_P, _I64, _PI32, _PI32],
+    "kv_seq_fork": [_P, _I32, _I64, _I64, _P, _PI32],
     "kv_seq_release": [_P, _I32],
     "kv_seq_pages": [_P, _I32, _PI32, _I32, _PI32],
     "kv_append_quant": [_P, _I32, _I32, _PI32, _PI64, _PI32, _P, _P, _P],

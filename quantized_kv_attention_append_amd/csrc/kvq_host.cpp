@@ -90,7 +90,7 @@ struct kv_pool {
     uint8_t* d_win = nullptr;    // 2-bit window pools: exact rows of the last page, per (seq, layer, head)
     int device = 0;
     // host metadata
-    std::vector<int32_t> owner;      // page -> seq slot or -1
+    std::vector<int32_t> refs;       // page -> sequences holding it (0: free)
     std::vector<int32_t> free_stack; // may hold pages reserved explicitly since (skipped lazily)
     int64_t free_count = 0;
     struct Seq {
@@ -208,7 +208,7 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
         kv_pool_destroy(p);
         return r;
     }
-    p->owner.assign((size_t)n_pages, -1);
+    p->refs.assign((size_t)n_pages, 0);
     p->free_stack.resize((size_t)n_pages);
     for (int64_t i = 0; i < n_pages; ++i) p->free_stack[(size_t)i] = (int32_t)(n_pages - 1 - i);
     p->free_count = n_pages;
@@ -232,16 +232,18 @@ kv_status kv_pool_destroy(kv_pool* p) {
 
 kv_status kv_pool_stats(const kv_pool* p, kv_pool_stats_t* o) {
     if (!p || !o) return fail(KV_ERR_ARG, "NULL argument");
-    int64_t reserved = 0, used = 0, n = 0;
+    int64_t used = 0, n = 0;
+    std::vector<char> seen((size_t)p->n_pages, 0);  // a shared page counts once
     for (const auto& s : p->seqs) {
         if (!s.live) continue;
         ++n;
-        reserved += (int64_t)s.pages.size();
-        used += (s.appended + PAGE - 1) / PAGE;
+        const int64_t held = (s.appended + PAGE - 1) / PAGE;
+        for (int64_t i = 0; i < held && i < (int64_t)s.pages.size(); ++i)
+            if (!seen[(size_t)s.pages[(size_t)i]]++) ++used;
     }
     o->pages = p->n_pages;
     o->free_pages = p->free_count;
-    o->reserved_pages = reserved;
+    o->reserved_pages = p->n_pages - p->free_count;
     o->used_pages = used;
     o->page_bytes = p->page_bytes;
     o->token_bytes = p->token_bytes;
@@ -282,14 +284,14 @@ kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, i
             int32_t pg = sorted[(size_t)i];
             if (pg < 0 || pg >= p->n_pages) return fail(KV_ERR_ARG, "page id %d out of range", pg);
             if (i > 0 && sorted[(size_t)i - 1] == pg) return fail(KV_ERR_ARG, "page id %d listed twice", pg);
-            if (p->owner[(size_t)pg] != -1) return fail(KV_ERR_NO_SPACE, "page %d is already reserved", pg);
+            if (p->refs[(size_t)pg] != 0) return fail(KV_ERR_NO_SPACE, "page %d is already reserved", pg);
         }
         got.assign(pages, pages + need);
     } else {
         while ((int64_t)got.size() < need) {
             int32_t pg = p->free_stack.back();
             p->free_stack.pop_back();
-            if (p->owner[(size_t)pg] == -1) got.push_back(pg);
+            if (p->refs[(size_t)pg] == 0) got.push_back(pg);
         }
     }
     hipError_t e = hipMemcpy(p->d_bt + (size_t)slot * p->bt_stride, got.data(), got.size() * sizeof(int32_t),
@@ -299,7 +301,7 @@ kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, i
             for (int32_t pg : got) p->free_stack.push_back(pg);
         return hip_fail(e, "hipMemcpy(block table)");
     }
-    for (int32_t pg : got) p->owner[(size_t)pg] = slot;
+    for (int32_t pg : got) p->refs[(size_t)pg] = 1;
     p->free_count -= need;
     auto& s = p->seqs[(size_t)slot];
     s.live = true;
@@ -311,15 +313,92 @@ kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, i
     return KV_OK;
 }
 
+kv_status kv_seq_fork(kv_pool* p, int32_t parent, int64_t n, int64_t max_tokens, kv_stream_t stream, int32_t* child) {
+    if (!p || !child) return fail(KV_ERR_ARG, "NULL argument");
+    if (parent < 0 || parent >= p->max_seqs || !p->seqs[(size_t)parent].live)
+        return fail(KV_ERR_ARG, "fork: sequence %d is not live", parent);
+    const auto& ps = p->seqs[(size_t)parent];
+    if (n < 1 || n > max_tokens) return fail(KV_ERR_ARG, "fork: need 1 <= n_tokens (%lld) <= max_tokens (%lld)",
+                                             (long long)n, (long long)max_tokens);
+    const int64_t need_total = (max_tokens + PAGE - 1) / PAGE;
+    if (need_total > p->bt_stride)
+        return fail(KV_ERR_BOUND, "fork: bound of %lld tokens exceeds the pool's max_seq_tokens (%d pages)",
+                    (long long)max_tokens, p->bt_stride);
+    if (n > ps.appended)
+        return fail(KV_ERR_ARG, "fork: n_tokens %lld beyond the %lld tokens appended to sequence %d", (long long)n,
+                    (long long)ps.appended, parent);
+    for (int layer = 0; layer < (int)ps.layer_appended.size(); ++layer) {
+        const int64_t A = ps.layer_appended[(size_t)layer];
+        if (p->fmt == KV_FMT_Q8 && A != n)
+            return fail(KV_ERR_ARG, "fork: an 8-bit fork takes all %lld tokens of layer %d, not %lld", (long long)A,
+                        layer, (long long)n);
+        if (p->fmt == KV_FMT_Q2_WINDOW && (n > A || (n - 1) / PAGE != (A - 1) / PAGE))
+            return fail(KV_ERR_ARG, "fork: a window fork ends in the last page of layer %d (%lld tokens appended)",
+                        layer, (long long)A);
+    }
+    const int64_t full = n / PAGE;            // pages shared
+    const bool copy = n % PAGE != 0;          // the partly filled page is copied
+    const int64_t fresh = need_total - full;  // pages the child takes
+    int32_t slot = -1;
+    for (int32_t i = 0; i < p->max_seqs; ++i)
+        if (!p->seqs[(size_t)i].live) {
+            slot = i;
+            break;
+        }
+    if (slot < 0) return fail(KV_ERR_NO_SPACE, "all %d sequence slots are live", p->max_seqs);
+    if (fresh > p->free_count)
+        return fail(KV_ERR_NO_SPACE, "fork needs %lld pages, %lld free", (long long)fresh, (long long)p->free_count);
+    std::vector<int32_t> pages(ps.pages.begin(), ps.pages.begin() + full);
+    std::vector<int32_t> got;
+    while ((int64_t)got.size() < fresh) {
+        const int32_t pg = p->free_stack.back();
+        p->free_stack.pop_back();
+        if (p->refs[(size_t)pg] == 0) got.push_back(pg);
+    }
+    pages.insert(pages.end(), got.begin(), got.end());
+    hipError_t e = hipMemcpy(p->d_bt + (size_t)slot * p->bt_stride, pages.data(), pages.size() * sizeof(int32_t),
+                             hipMemcpyHostToDevice);
+    CopyRange r[3];
+    int nr = 0;
+    if (copy)
+        r[nr++] = {p->d_pages + (int64_t)ps.pages[(size_t)full] * p->page_bytes,
+                   p->d_pages + (int64_t)got[0] * p->page_bytes, p->page_bytes};
+    const int64_t per_seq_blocks = (int64_t)p->geom.n_layers * p->geom.n_kv_heads;
+    if (p->fmt == KV_FMT_Q8 && copy) {
+        const int64_t b = per_seq_blocks * PAGE * p->geom.head_dim * (int64_t)sizeof(uint16_t);
+        r[nr++] = {(uint8_t*)p->d_stage + parent * b, (uint8_t*)p->d_stage + slot * b, b};
+    }
+    if (p->fmt == KV_FMT_Q2_WINDOW) {
+        const int64_t b = per_seq_blocks * 256 * (int64_t)p->geom.head_dim;
+        r[nr++] = {p->d_win + parent * b, p->d_win + slot * b, b};
+    }
+    if (e == hipSuccess && nr > 0) e = launch_copy_ranges(r, nr, (hipStream_t)stream);
+    if (e != hipSuccess) {
+        for (int32_t pg : got) p->free_stack.push_back(pg);
+        return hip_fail(e, "fork");
+    }
+    for (int64_t i = 0; i < full; ++i) ++p->refs[(size_t)pages[(size_t)i]];
+    for (int32_t pg : got) p->refs[(size_t)pg] = 1;
+    p->free_count -= fresh;
+    auto& cs = p->seqs[(size_t)slot];
+    cs.live = true;
+    cs.bound = max_tokens;
+    cs.appended = n;
+    cs.layer_appended.assign(ps.layer_appended.size(), n);
+    cs.pages = std::move(pages);
+    *child = slot;
+    return KV_OK;
+}
+
 kv_status kv_seq_release(kv_pool* p, int32_t seq) {
     if (!p) return fail(KV_ERR_ARG, "pool is NULL");
     if (seq < 0 || seq >= p->max_seqs || !p->seqs[(size_t)seq].live) return fail(KV_ERR_ARG, "sequence %d is not live", seq);
     auto& s = p->seqs[(size_t)seq];
-    for (int32_t pg : s.pages) {
-        p->owner[(size_t)pg] = -1;
-        p->free_stack.push_back(pg);
-    }
-    p->free_count += (int64_t)s.pages.size();
+    for (int32_t pg : s.pages)
+        if (--p->refs[(size_t)pg] == 0) {
+            p->free_stack.push_back(pg);
+            ++p->free_count;
+        }
     s = kv_pool::Seq();
     return KV_OK;
 }
@@ -394,6 +473,13 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
                         (long long)start_pos[i]);
         for (int j = 0; j < i; ++j)
             if (seqs[j] == seqs[i]) return fail(KV_ERR_ARG, "sequence %d appears twice in one append", seqs[i]);
+        if (n_new[i] > 0) {
+            const auto& sq = p->seqs[(size_t)seqs[i]];
+            for (int64_t lp = start_pos[i] / PAGE; lp <= (start_pos[i] + n_new[i] - 1) / PAGE; ++lp)
+                if (p->refs[(size_t)sq.pages[(size_t)lp]] > 1)
+                    return fail(KV_ERR_ARG, "entry %d: logical page %lld of sequence %d is shared with another sequence",
+                                i, (long long)lp, seqs[i]);
+        }
         bd.seq[i] = seqs[i];
         bd.pos[i] = (int32_t)start_pos[i];
         bd.cnt[i] = n_new[i];

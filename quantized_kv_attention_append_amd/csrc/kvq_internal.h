@@ -101,6 +101,13 @@ hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q
                           float sm, int splits, float* ws, float* out, int w0, hipStream_t s);
 // Split count a prefill of n_q chunk queries takes when the caller passes 0.
 int prefill_auto_splits(int n_q, int Hq, int Hkv);
+// Device-to-device copies of byte ranges (multiples of 16 bytes, 16-byte aligned).
+struct CopyRange {
+    const uint8_t* src;
+    uint8_t* dst;
+    int64_t bytes;
+};
+hipError_t launch_copy_ranges(const CopyRange* r, int n, hipStream_t s);
 hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,
                                hipStream_t s);
 
