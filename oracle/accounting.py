@@ -38,7 +38,7 @@ def token_bytes(fmt: str, layers: int, kv_heads: int, head_dim: int) -> int:
     """Page bytes per token.  The 2-bit format with an exact window ("q2w") has
     the 2-bit pages; its exact rows are one page per (sequence, layer, head)
     outside the page budget."""
-    if fmt in ("q2", "q2w"):
+    if fmt in ("q2", "q2w", "q2r"):
         return q2_token_bytes(layers, kv_heads, head_dim)
     if fmt == "q8":
         return q8_token_bytes(layers, kv_heads, head_dim)

@@ -55,6 +55,44 @@ def q2_quantize(x):
     return c, scale, mn
 
 
+def hadamard_rows(x):
+    """Unnormalised Walsh-Hadamard transform of rows x[..., D] (D a power of
+    two) in emulated fp32: stages h = 1, 2, 4, .., D/2, each replacing the pair
+    (x_i, x_{i+h}) (i with bit h clear) by (x_i + x_{i+h}, x_i - x_{i+h}), one
+    rounding per operation.  The result is H x with H the Sylvester-ordered
+    Hadamard matrix (entries +-1, H H = D I), up to the fp32 roundings of the
+    butterflies, which every implementation that takes the same stages in the
+    same order reproduces bit for bit.  The rotated 2-bit variant quantizes
+    H k and H v instead of k and v ("Half the Cache, Twice the Context",
+    closing notes: the axis and rotation choices matter at 2 bits)."""
+    y = np.array(x, dtype=F32, copy=True)
+    D = y.shape[-1]
+    assert D & (D - 1) == 0
+    lead = y.shape[:-1]
+    h = 1
+    while h < D:
+        v = y.reshape(*lead, D // (2 * h), 2, h)
+        a, b = v[..., 0, :], v[..., 1, :]
+        y = np.stack([np.add(a, b, dtype=F32), np.subtract(a, b, dtype=F32)], axis=-2).reshape(*lead, D)
+        h *= 2
+    return y
+
+
+def unrotate_rows(xr):
+    """Back to the original basis, in fp64: x = H x_r / D (H symmetric, H H = D I)."""
+    xr = np.asarray(xr, dtype=np.float64)
+    D = xr.shape[-1]
+    y = xr.copy()
+    lead = y.shape[:-1]
+    h = 1
+    while h < D:
+        v = y.reshape(*lead, D // (2 * h), 2, h)
+        a, b = v[..., 0, :], v[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(*lead, D)
+        h *= 2
+    return y / D
+
+
 def _fma_f32(a64, b64, c64):
     """fl32(a*b + c) with a single rounding, for a*b exact in fp64.
 

@@ -16,6 +16,11 @@ are kept aside (the exact window), and each append re-derives the page's K codes
 and scales from the exact rows present, so a full page equals the plain
 per-channel quantization of its 64 tokens.
 
+The rotated 2-bit variant ("q2r") stores the 2-bit rows of H k and H v (H the
+unnormalised Walsh-Hadamard matrix, applied in fp32 butterflies); its gather
+returns H x^_r / D in fp64, the dequantized rows back in the original basis,
+so attention over it is the plain attention of the other formats.
+
 A fork gives a new sequence the first n tokens of another: the whole pages
 of that prefix are shared (both block tables name them), the page it only
 partly fills is copied whole into a page of the child's, with the exact rows
@@ -50,9 +55,10 @@ from .layout import PAGE, Bf16Block, Q2Block, Q8Block, block_bytes, block_offset
 
 class OraclePool:
     def __init__(self, fmt: str, n_layers: int, n_kv_heads: int, head_dim: int, n_pages: int, fill: int = 0xA5):
-        assert fmt in ("q2", "q8", "bf16", "q2w")
+        assert fmt in ("q2", "q8", "bf16", "q2w", "q2r")
         self.fmt, self.L, self.H, self.D = fmt, n_layers, n_kv_heads, head_dim
-        self.page_fmt = "q2" if fmt == "q2w" else fmt  # the window format's pages are 2-bit pages
+        # the window and rotated formats' pages are 2-bit pages
+        self.page_fmt = "q2" if fmt in ("q2w", "q2r") else fmt
         self.page_bytes = page_bytes(self.page_fmt, n_layers, n_kv_heads, head_dim)
         self.data = np.full((n_pages, self.page_bytes), fill, dtype=np.uint8)
         self._exact_k = {}  # (seq, layer) -> fp32 [64][H][D] exact K rows of the open page (8-bit only)
@@ -85,6 +91,9 @@ class OraclePool:
             return
         if self.fmt == "q2w":
             self._append_window(layer, seq, start, k, v)
+        if self.fmt == "q2r":   # the rotated variant stores the 2-bit codes of H k and H v
+            bf16.f32_to_bits(k), bf16.f32_to_bits(v)
+            k, v = codec.hadamard_rows(k), codec.hadamard_rows(v)
         if self.page_fmt == "q2":
             ck, sk, mk = codec.q2_quantize(k)
             cv, sv, mv = codec.q2_quantize(v)
@@ -187,6 +196,9 @@ class OraclePool:
 
         The window format also needs the sequence: its tokens from the window
         start up to ctx_len (at most the tokens appended) are the exact rows."""
+        if self.fmt == "q2r":   # dequantized rotated rows, back in the original basis (fp64)
+            K, V = self._gather_pages(layer, bt, ctx_len)
+            return codec.unrotate_rows(K), codec.unrotate_rows(V)
         if self.fmt == "q2w":
             appended, wk, wv = self._window[(seq, layer)]
             if ctx_len > appended:
@@ -234,6 +246,11 @@ def dequantized_rows(fmt: str, k_rows, v_rows):
     if fmt == "bf16":
         bf16.f32_to_bits(k), bf16.f32_to_bits(v)  # the rows must be bf16 numbers
         return k.copy(), v.copy()
+    if fmt == "q2r":
+        bf16.f32_to_bits(k), bf16.f32_to_bits(v)
+        K = codec.unrotate_rows(codec.q2_dequantize(*codec.q2_quantize(codec.hadamard_rows(k))))
+        V = codec.unrotate_rows(codec.q2_dequantize(*codec.q2_quantize(codec.hadamard_rows(v))))
+        return K, V
     if fmt in ("q2", "q2w"):
         K = codec.q2_dequantize(*codec.q2_quantize(k))
         V = codec.q2_dequantize(*codec.q2_quantize(v))
