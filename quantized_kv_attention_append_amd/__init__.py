@@ -16,10 +16,10 @@ import torch
 
 from ._lib import Geom, KvError, PoolStats, check, lib
 
-__all__ = ["Geom", "KvError", "Pool", "FMT_Q2", "FMT_Q8", "FMT_BF16", "FMT_Q2_WINDOW", "OP_DECODE", "OP_PREFILL", "token_bytes",
+__all__ = ["Geom", "KvError", "Pool", "FMT_Q2", "FMT_Q8", "FMT_BF16", "FMT_Q2_WINDOW", "FMT_Q2_ROT", "OP_DECODE", "OP_PREFILL", "token_bytes",
            "pool_bytes_for_tokens", "lib"]
 
-FMT_Q2, FMT_Q8, FMT_BF16, FMT_Q2_WINDOW = 1, 2, 3, 4
+FMT_Q2, FMT_Q8, FMT_BF16, FMT_Q2_WINDOW, FMT_Q2_ROT = 1, 2, 3, 4, 5
 OP_DECODE, OP_PREFILL = 0, 1
 PAGE = 64
 MAX_BATCH = 128

@@ -110,7 +110,35 @@ __device__ __forceinline__ void load_bf16_rows(const uint16_t* p, float (&x)[N])
     }
 }
 
-template <int D>
+// Unnormalised Walsh-Hadamard transform of a row spread over the 16 lanes of a
+// DPP row (lane c holds dims c DPL .. c DPL + DPL - 1), for the rotated
+// variant: stages h = 1, 2, .., D/2 in that order, each replacing (x_i,
+// x_{i+h}) by (x_i + x_{i+h}, x_i - x_{i+h}) with one fp32 rounding; stages
+// h < DPL stay inside the lane, the others pair lane c with lane c ^ (h / DPL).
+template <int DPL>
+__device__ __forceinline__ void hadamard_row16(float (&x)[DPL], int c) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int h = 1; h < DPL; h *= 2)
+#pragma unroll
+        for (int i = 0; i < DPL; ++i)
+            if (!(i & h)) {
+                const float a = x[i], b = x[i + h];
+                x[i] = a + b;
+                x[i + h] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < 16; m *= 2) {
+        const bool upper = (c & m) != 0;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+            const float o = __shfl_xor(x[i], m);
+            x[i] = upper ? o - x[i] : x[i] + o;
+        }
+    }
+}
+
+template <int D, bool ROT>
 __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, BatchDesc bd,
                                                         const uint16_t* __restrict__ kin,
                                                         const uint16_t* __restrict__ vin) {
@@ -145,6 +173,10 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
         float xk[DPL], xv[DPL];
         load_bf16_rows<DPL>(kin + off, xk);
         load_bf16_rows<DPL>(vin + off, xv);
+        if constexpr (ROT) {  // the rotated variant quantizes H k and H v
+            hadamard_row16<DPL>(xk, c);
+            hadamard_row16<DPL>(xv, c);
+        }
         uint32_t ck[DPL], cv[DPL];
         float sk, mk, sv, mv;
         q2_quantize_row<DPL>(xk, ck, sk, mk);
@@ -191,12 +223,13 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
 }
 
 hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, int work_items, const uint16_t* k,
-                            const uint16_t* v, hipStream_t s) {
+                            const uint16_t* v, hipStream_t s, bool rot) {
     dim3 grid(work_items, pv.Hkv);
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, k, v); };
     if (pv.D == 256)
-        hipLaunchKernelGGL(append_q2_kernel<256>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+        rot ? go(append_q2_kernel<256, true>) : go(append_q2_kernel<256, false>);
     else
-        hipLaunchKernelGGL(append_q2_kernel<128>, grid, dim3(256), 0, s, pv, layer, bd, k, v);
+        rot ? go(append_q2_kernel<128, true>) : go(append_q2_kernel<128, false>);
     return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ struct DecodeWs {
         : o(ws), ml(ws + (int64_t)n * Hq * splits * D) {}
 };
 
-hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s);
+// rot: the outputs of the Hadamard-rotated variant are rotated back, H o / D.
+hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s,
+                               bool rot = false);
 
 }  // namespace kvq

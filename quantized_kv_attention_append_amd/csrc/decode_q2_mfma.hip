@@ -329,7 +329,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
     }
 }
 
-template <int D, bool SCORES>
+template <int D, bool SCORES, bool ROT>
 __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                              const uint16_t* __restrict__ q, float sm, int splits,
                                                              float* __restrict__ ws, float* __restrict__ out,
@@ -405,15 +405,50 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
         fetch_ids(0);
         load(ta, 0);
     }
-    {
+    // The rotated variant scores H q against the codes of H k (the launcher
+    // passes sm / D): the rows are widened to fp32 over this wave's whole LDS
+    // area and transformed there, stages h = 1 .. D/2 as on append.
+    static_assert(!ROT || sizeof(WaveLds) >= G * D * sizeof(float), "fp32 query rows fit the wave's LDS area");
+    if constexpr (ROT) {
+        float* qf = reinterpret_cast<float*>(&lds);
+#pragma unroll
+        for (int i = 0; i < QPIECES; ++i) {
+            const uint32_t u[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                qf[8 * (l + 64 * i) + 2 * k] = bf16lo(u[k]);
+                qf[8 * (l + 64 * i) + 2 * k + 1] = bf16hi(u[k]);
+            }
+        }
+        __syncthreads();
+        for (int h = 1; h < D; h *= 2) {  // additions only: nothing to contract
+            float a[G * D / 128], b[G * D / 128];
+            int ia[G * D / 128];
+#pragma unroll
+            for (int k = 0; k < G * D / 128; ++k) {  // pair p = l + 64 k of the G D / 2 pairs
+                const int pr = l + 64 * k, row = pr / (D / 2), jj = pr % (D / 2);
+                ia[k] = row * D + (jj / h) * 2 * h + jj % h;
+                a[k] = qf[ia[k]];
+                b[k] = qf[ia[k] + h];
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < G * D / 128; ++k) {
+                qf[ia[k]] = a[k] + b[k];
+                qf[ia[k] + h] = a[k] - b[k];
+            }
+            __syncthreads();
+        }
+    } else {
         uint4* qdst = reinterpret_cast<uint4*>(lds.meta);
 #pragma unroll
         for (int i = 0; i < QPIECES; ++i) qdst[l + 64 * i] = qraw[i];
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- query operand: 19-bit fixed point per head, row 4 hq + iq = digit iq of head hq ----
     const uint16_t* qrow = reinterpret_cast<const uint16_t*>(lds.meta) + hq * D;
+    const float* qrow_f = reinterpret_cast<const float*>(&lds) + hq * D;
     float qv[NC][32];
     float amax = 0.f, qsum = 0.f;
 #pragma unroll
@@ -423,7 +458,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
             // k of byte s; the K operand puts dim(k) at nibble k % 32 of lane group k / 32
             const int k = fp8_k(grp, s), ga = k >> 5, n = k & 31;
             const int dim = 32 * NC * ga + 32 * c + 16 * (n >> 4) + 2 * (n & 7) + ((n >> 3) & 1);
-            const float x = bf16_to_f32(qrow[dim]);
+            const float x = ROT ? qrow_f[dim] : bf16_to_f32(qrow[dim]);
             qv[c][s] = x;
             amax = fmaxf(amax, fabsf(x));
             qsum += x;
@@ -533,24 +568,34 @@ hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc&
                                  int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 
 hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
-                                     int splits, float* ws, float* scores, int64_t sstride, hipStream_t s) {
-    if (pv.Hq != 4 * pv.Hkv)
+                                     int splits, float* ws, float* scores, int64_t sstride, hipStream_t s, bool rot) {
+    if (pv.Hq != 4 * pv.Hkv) {
+        if (rot) return hipErrorInvalidValue;  // the rotated variant runs on the group-4 kernel only
         return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, nullptr, scores, sstride, s);
+    }
     dim3 grid(bd.n * pv.Hkv, splits);
+    const float smk = rot ? sm / (float)pv.D : sm;  // H q . H k = D q . k
     auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, nullptr, scores, sstride);
+        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, nullptr, scores, sstride);
     };
-    if (pv.D == 256)
-        scores ? go(decode_q2_mfma_kernel<256, true>) : go(decode_q2_mfma_kernel<256, false>);
-    else
-        scores ? go(decode_q2_mfma_kernel<128, true>) : go(decode_q2_mfma_kernel<128, false>);
+    if (pv.D == 256) {
+        if (rot)
+            scores ? go(decode_q2_mfma_kernel<256, true, true>) : go(decode_q2_mfma_kernel<256, false, true>);
+        else
+            scores ? go(decode_q2_mfma_kernel<256, true, false>) : go(decode_q2_mfma_kernel<256, false, false>);
+    } else {
+        if (rot)
+            scores ? go(decode_q2_mfma_kernel<128, true, true>) : go(decode_q2_mfma_kernel<128, false, true>);
+        else
+            scores ? go(decode_q2_mfma_kernel<128, true, false>) : go(decode_q2_mfma_kernel<128, false, false>);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
-                            float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
-    const hipError_t err = launch_decode_q2_partials(pv, layer, bd, q, sm, splits, ws, scores, sstride, s);
-    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
+                            float* ws, float* out, float* scores, int64_t sstride, hipStream_t s, bool rot) {
+    const hipError_t err = launch_decode_q2_partials(pv, layer, bd, q, sm, splits, ws, scores, sstride, s, rot);
+    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s, rot);
 }
 
 }  // namespace kvq

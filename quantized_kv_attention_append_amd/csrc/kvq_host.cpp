@@ -43,7 +43,7 @@ kv_status hip_fail(hipError_t e, const char* what) {
 
 kv_status check_geom(const kv_geom* g, kv_format fmt) {
     if (!g) return fail(KV_ERR_ARG, "geometry is NULL");
-    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8 && fmt != KV_FMT_BF16 && fmt != KV_FMT_Q2_WINDOW)
+    if (fmt != KV_FMT_Q2 && fmt != KV_FMT_Q8 && fmt != KV_FMT_BF16 && fmt != KV_FMT_Q2_WINDOW && fmt != KV_FMT_Q2_ROT)
         return fail(KV_ERR_FORMAT, "unknown format %d", (int)fmt);
     if (g->n_layers <= 0 || g->n_kv_heads <= 0 || g->n_q_heads <= 0 || g->head_dim <= 0)
         return fail(KV_ERR_ARG, "geometry fields must be positive");
@@ -54,17 +54,20 @@ kv_status check_geom(const kv_geom* g, kv_format fmt) {
                     g->n_kv_heads);
     int G = g->n_q_heads / g->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(KV_ERR_UNSUPPORTED, "GQA group %d (supported: 1, 2, 4, 8)", G);
+    if (fmt == KV_FMT_Q2_ROT && G != 4)
+        return fail(KV_ERR_UNSUPPORTED, "the rotated 2-bit format needs GQA group 4 (got %d)", G);
     return KV_OK;
 }
 
-// The pages of a window pool are 2-bit pages.
-kv_format page_format(kv_format fmt) { return fmt == KV_FMT_Q2_WINDOW ? KV_FMT_Q2 : fmt; }
+// The pages of window and rotated pools are 2-bit pages.
+kv_format page_format(kv_format fmt) { return fmt == KV_FMT_Q2_WINDOW || fmt == KV_FMT_Q2_ROT ? KV_FMT_Q2 : fmt; }
 int64_t block_bytes_of(kv_format fmt, int D) {
     fmt = page_format(fmt);
     return fmt == KV_FMT_Q2 ? q2_block_bytes(D) : fmt == KV_FMT_Q8 ? q8_block_bytes(D) : bf16_block_bytes(D);
 }
 const char* fmt_name(kv_format fmt) {
-    return fmt == KV_FMT_Q2 ? "q2" : fmt == KV_FMT_Q8 ? "q8" : fmt == KV_FMT_BF16 ? "bf16" : "q2-window";
+    return fmt == KV_FMT_Q2 ? "q2" : fmt == KV_FMT_Q8 ? "q8" : fmt == KV_FMT_BF16 ? "bf16"
+         : fmt == KV_FMT_Q2_WINDOW ? "q2-window" : "q2-rotated";
 }
 // Formats whose appends are sequential per (sequence, layer): the exact rows
 // of the open page are kept only for the tokens appended so far.
@@ -492,8 +495,8 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
     bd.work0[n] = (int32_t)work;
     if (work == 0) return KV_OK;
     hipError_t e = hipSuccess;
-    if (p->fmt == KV_FMT_Q2) {
-        e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream);
+    if (p->fmt == KV_FMT_Q2 || p->fmt == KV_FMT_Q2_ROT) {
+        e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream, p->fmt == KV_FMT_Q2_ROT);
     } else if (p->fmt == KV_FMT_Q2_WINDOW) {
         // every row to the 2-bit pages, and the rows of the last page each
         // entry reaches to its window block
@@ -631,7 +634,9 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
         return KV_OK;
     }
     hipError_t e =
-        p->fmt == KV_FMT_Q2   ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
+        p->fmt == KV_FMT_Q2 || p->fmt == KV_FMT_Q2_ROT
+            ? launch_decode_q2(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s,
+                               p->fmt == KV_FMT_Q2_ROT)
         : p->fmt == KV_FMT_Q8 ? launch_decode_q8(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores, scores_stride, s)
                               : launch_decode_bf16(pv, layer, bd, d_q, sm_scale, sp, (float*)d_ws, d_out, d_scores,
                                                    scores_stride, s);
@@ -643,7 +648,7 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
                           float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes, float* d_out,
                           kv_stream_t stream) {
     if (!p) return fail(KV_ERR_ARG, "pool is NULL");
-    if (p->fmt == KV_FMT_Q8)
+    if (p->fmt == KV_FMT_Q8 || p->fmt == KV_FMT_Q2_ROT)
         return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit, bf16 and 2-bit window formats only");
     if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
     if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");

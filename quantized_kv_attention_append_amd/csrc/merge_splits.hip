@@ -1,11 +1,13 @@
 // Merge of the split-K decode partials: one workgroup per (sequence, query
-// head), one thread per output dim.  Splits are taken eight at a time with all
-// of a group's loads issued before any is used, so a merge of up to eight
-// splits costs one round trip to memory.
+// head), one thread per output dim.  Splits are taken eight at a time with
+// all of a group's loads issued before any is used, so a merge of up to eight
+// splits costs one round trip to memory.  For the Hadamard-rotated 2-bit
+// variant the merged output is rotated back to the original basis.
 #include "decode_common.h"
 
 namespace kvq {
 
+template <bool ROT>
 __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq, int D, int splits,
                                                            const float* __restrict__ ws, float* __restrict__ out) {
     constexpr int U = 8;
@@ -40,11 +42,30 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq,
         }
         M = Mg;
     }
-    out[row * D + d] = acc / den;
+    float res = acc / den;
+    if constexpr (ROT) {
+        // the rotated variant's output is H o / D: butterflies over the D
+        // threads of the row, stages h = 1 .. D/2, then the exact 1/D
+        __shared__ float r[256];
+        r[d] = res;
+        __syncthreads();
+        for (int h = 1; h < D; h *= 2) {  // additions only: nothing to contract
+            const float mine = r[d], other = r[d ^ h];
+            __syncthreads();
+            r[d] = (d & h) ? other - mine : mine + other;
+            __syncthreads();
+        }
+        res = r[d] * (1.0f / (float)D);
+    }
+    out[row * D + d] = res;
 }
 
-hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s) {
-    hipLaunchKernelGGL(merge_splits_kernel, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
+hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s,
+                               bool rot) {
+    if (rot)
+        hipLaunchKernelGGL(merge_splits_kernel<true>, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
+    else
+        hipLaunchKernelGGL(merge_splits_kernel<false>, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
     return hipGetLastError();
 }
 

@@ -1,0 +1,159 @@
+"""GPU parity, the Hadamard-rotated 2-bit variant: pages bit-exact against
+the oracle's image (the rows are rotated in fp32 butterflies before the 2-bit
+codec, so the codes are a pure function of the bf16 inputs), decode within
+tolerance of the fp64 oracle that reads the rows back in the original basis,
+raw scores against the oracle's, and the refusals the format documents."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, pool as opool
+from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+C0 = CONFIGS[0]
+# 2 layers x 2 KV heads x 128 dims, 8 query heads (group 4)
+SMALL128 = Workload(91, "rotated, D=128", "q2r", 2, 2, 128, 8, 3, 300)
+NAN_FILL = 0xFF
+
+
+def _fmt():
+    import quantized_kv_attention_append_amd as kvq
+    return kvq.FMT_Q2_ROT
+
+
+def test_rotated_append_bit_exact_d256():
+    need_gpu()
+    n_pages = 6
+    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(C0, n_pages)[:4]
+    seq = pool.reserve(256, pages=bt)
+    k, v = kv_rows(C0, 0, 0, 256)
+    op = opool.OraclePool("q2r", 1, 4, 256, n_pages, fill=NAN_FILL)
+    start = 0
+    for n in (100, 1, 27, 64, 64):
+        pool.append(0, [seq], [start], [n], k[start:start + n].cuda(), v[start:start + n].cuda())
+        op.append(0, 0, bt, start, k[start:start + n].float().numpy(), v[start:start + n].float().numpy())
+        start += n
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(n_pages, -1)
+    diff = np.count_nonzero(got != op.data)
+    say(f"rotated append D=256: {diff} differing bytes of {got.size}")
+    assert diff == 0
+
+
+def test_rotated_append_batched_d128_bit_exact():
+    need_gpu()
+    w = SMALL128
+    n_pages = 20
+    pool, mem = make_pool(w, n_pages, _fmt(), fill=NAN_FILL)
+    perm = page_permutation(w, n_pages)
+    lens = [300, 65, 130]
+    bts, seqs, off = [], [], 0
+    for L in lens:
+        npg = -(-L // 64)
+        bts.append(perm[off:off + npg]); off += npg
+        seqs.append(pool.reserve(L, pages=bts[-1]))
+    op = opool.OraclePool("q2r", 2, 2, 128, n_pages, fill=NAN_FILL)
+    for layer in range(2):
+        rows = [kv_rows(w, layer, i, lens[i]) for i in range(3)]
+        ks = torch.cat([r[0] for r in rows])
+        vs = torch.cat([r[1] for r in rows])
+        pool.append(layer, seqs, [0, 0, 0], lens, ks.cuda(), vs.cuda())
+        for i in range(3):
+            op.append(layer, i, bts[i], 0, rows[i][0].float().numpy(), rows[i][1].float().numpy())
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(n_pages, -1)
+    diff = np.count_nonzero(got != op.data)
+    say(f"rotated batched append D=128: {diff} differing bytes of {got.size}")
+    assert diff == 0
+
+
+@pytest.mark.parametrize("ctx", [1, 63, 65, 200, 1000])
+def test_rotated_decode_ragged(ctx):
+    need_gpu()
+    n_pages = -(-ctx // 64) + 2
+    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(C0, n_pages, salt=ctx)[:-2]
+    seq = pool.reserve(ctx, pages=bt)
+    k, v = kv_rows(C0, 0, 0, ctx)
+    pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
+    q = queries(C0, 0, 1, stream=ctx)
+    K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
+    qn = q[0].float().numpy()
+    ref = attention.decode(qn, K, V, C0.sm_scale)
+    ref_s = attention.scores(qn, K, C0.sm_scale)
+    for sp in (1, 3, 0):
+        scores = torch.full((1, C0.n_q_heads, ctx), float("nan"), device="cuda")
+        ws = torch.full((pool.workspace_bytes(0, 1, sp),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = pool.decode(0, [seq], [ctx], q.cuda(), C0.sm_scale, n_splits=sp, ws=ws, scores=scores)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy()[0], ref, f"rotated decode ctx={ctx} splits={sp}")
+        # raw scores: a check of this build's own, beside the output tolerance.
+        # The rotated score is sm / D (H q) . x^_r: the query passes through
+        # eight fp32 butterfly stages and its fixed-point digits are taken at
+        # the rotated row's larger magnitude, so the bar is 5e-5 here against
+        # 1e-5 for the plain 2-bit scores (1.8e-5 measured at ctx = 200).
+        s = scores.cpu().numpy()[0].astype(np.float64)
+        rel = np.linalg.norm(s - ref_s) / np.linalg.norm(ref_s)
+        assert rel <= 5e-5, f"rotated scores ctx={ctx} splits={sp}: rel L2 {rel:.2e}"
+
+
+def test_rotated_decode_batch_d128():
+    need_gpu()
+    w = SMALL128
+    lens = [300, 65, 130]
+    n_pages = sum(-(-L // 64) for L in lens)
+    pool, mem = make_pool(w, n_pages, _fmt(), fill=NAN_FILL)
+    perm = page_permutation(w, n_pages)
+    seqs, off, refs = [], 0, []
+    q = queries(w, 1, len(lens))
+    for i, L in enumerate(lens):
+        npg = -(-L // 64)
+        seqs.append(pool.reserve(L, pages=perm[off:off + npg])); off += npg
+        k, v = kv_rows(w, 1, i, L)
+        pool.append(1, [seqs[-1]], [0], [L], k.cuda(), v.cuda())
+        K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
+        refs.append(attention.decode(q[i].float().numpy(), K, V, w.sm_scale))
+    for sp in (1, 2, 0):
+        out = pool.decode(1, seqs, lens, q.cuda(), w.sm_scale, n_splits=sp)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), np.stack(refs), f"rotated batch D=128 splits={sp}")
+
+
+def test_rotated_lowers_the_decode_error_against_the_exact_rows():
+    """Against attention over the exact bf16 rows, the rotated pool's decode
+    error on the outlier-bearing synthetic rows is below the plain 2-bit
+    pool's (the quality reason for the variant), measured on the GPU output."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    ctx = 1024
+    errs = {}
+    k, v = kv_rows(C0, 0, 0, ctx)
+    q = queries(C0, 0, 1, stream=5)
+    exact = attention.decode(q[0].float().numpy(), k.float().numpy(), v.float().numpy(), C0.sm_scale)
+    for name, fmt in (("q2", kvq.FMT_Q2), ("q2r", kvq.FMT_Q2_ROT)):
+        pool, _ = make_pool(C0, ctx // 64, fmt)
+        seq = pool.reserve(ctx)
+        pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
+        out = pool.decode(0, [seq], [ctx], q.cuda(), C0.sm_scale)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()[0].astype(np.float64)
+        errs[name] = np.linalg.norm(o - exact) / np.linalg.norm(exact)
+    say(f"decode rel L2 against exact rows: 2-bit {errs['q2']:.3e}, rotated {errs['q2r']:.3e}")
+    assert errs["q2r"] < errs["q2"]
+
+
+def test_rotated_refusals():
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    pool, _ = make_pool(C0, 4, _fmt())
+    seq = pool.reserve(128)
+    k, v = kv_rows(C0, 0, 0, 128)
+    pool.append(0, [seq], [0], [128], k.cuda(), v.cuda())
+    with pytest.raises(kvq.KvError) as ei:
+        pool.prefill(0, seq, 64, queries(C0, 0, 64, stream=1).cuda(), C0.sm_scale)
+    assert ei.value.name == "KV_ERR_FORMAT"
