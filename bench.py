@@ -287,7 +287,7 @@ def q8_leg(reps: int):
             "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
 
-def bf16_leg(reps: int, window: bool = False):
+def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     """The exact bf16 cache of the same 27B-geometry batch (16 layers x 4 KV
     heads x 256 dims, 8 lanes x 40,960 tokens: 21.47 GB, the pages' 20.0 GiB),
     through the same calls: populate, then the 16-layer decode step (each call
@@ -296,14 +296,16 @@ def bf16_leg(reps: int, window: bool = False):
 
     window=True runs the same legs over 2-bit pools with the exact window of
     the last page: each lane's last 64 tokens are read as bf16 rows, the rest
-    as 2-bit rows (the pool's pages are the 2-bit 3.02 GB)."""
+    as 2-bit rows (the pool's pages are the 2-bit 3.02 GB).  rotated=True runs
+    the decode legs over the Hadamard-rotated 2-bit pool (same pages; no
+    prefill for that format)."""
     import torch
 
     import quantized_kv_attention_append_amd as kvq
     from synth import CONFIGS, kv_rows, page_permutation, queries
 
-    fmt = kvq.FMT_Q2_WINDOW if window else kvq.FMT_BF16
-    name = "2-bit window" if window else "bf16"
+    fmt = kvq.FMT_Q2_WINDOW if window else kvq.FMT_Q2_ROT if rotated else kvq.FMT_BF16
+    name = "2-bit window" if window else "2-bit rotated" if rotated else "bf16"
     w = CONFIGS[1]
     L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
     geom = (L, H, D, Hq)
@@ -368,6 +370,8 @@ def bf16_leg(reps: int, window: bool = False):
     del g
     if window:   # 2-bit K and V rows before the window, bf16 rows in it, q in, fp32 out
         alg = B * H * ((ctx - 64) * 2 * (D // 4 + 8) + 64 * 4 * D) + B * Hq * D * (2 + 4)
+    elif rotated:  # 2-bit K and V rows, q in, fp32 out
+        alg = B * H * ctx * 2 * (D // 4 + 8) + B * Hq * D * (2 + 4)
     else:        # bf16 K and V rows, q in, fp32 out
         alg = B * ppl * H * 64 * (4 * D) + B * Hq * D * (2 + 4)
     gbs = alg / (avg_ms * 1e-3) / 1e9
@@ -376,6 +380,17 @@ def bf16_leg(reps: int, window: bool = False):
         f"(identical to eager: {same})")
     del pool, ws, outs, qs, eager_outs
     torch.cuda.empty_cache()
+    if rotated:
+        return {"workload": f"27B-geometry batched decode, {name}: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
+                            "8 lanes x 40960 tokens", "pool_bytes": n_pages * pb, "splits": sp,
+                "decode_us_per_call": avg_ms * 1e3, "bytes_per_call": alg,
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                             "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256, false, true> "
+                                       "then merge_splits_kernel<true>"},
+                "graph_ms_per_step": graph_ms, "graph_identical_to_eager": same,
+                "kv_tokens_per_s": B * L * ctx / (graph_ms * 1e-3),
+                "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
     # ---- chunked prefill over a bf16 pool: 65,536 prior + 1,024 chunk ----
     w3 = CONFIGS[3]
@@ -598,6 +613,14 @@ def main():
         log(f"2-bit window against 2-bit: decode step {win['step_time_vs_q2']:.3f}x the time"
             + (f", prefill {win['prefill_time_vs_q2']:.3f}x" if prefill is not None else ""))
 
+    rot = None if args.no_extra else bf16_leg(5, rotated=True)
+    if rot is not None:
+        # the price of the rotation: query and output transforms, butterflies on append
+        rot["step_time_vs_q2"] = rot["graph_ms_per_step"] / ms_per_step
+        rot["populate_time_vs_q2"] = rot["populate_ms"] / app_ms
+        log(f"2-bit rotated against 2-bit: decode step {rot['step_time_vs_q2']:.3f}x the time, "
+            f"populate {rot['populate_time_vs_q2']:.3f}x")
+
     cpu = None
     if not args.no_cpu:
         cpu = oracle_baseline(w, args.cpu_seconds)
@@ -643,6 +666,7 @@ def main():
         "q8": q8,
         "bf16": bf16,
         "q2_window": win,
+        "q2_rotated": rot,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
