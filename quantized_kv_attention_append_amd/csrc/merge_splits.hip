@@ -1,16 +1,15 @@
 // Merge of the split-K decode partials: one workgroup per (sequence, query
-// head), one thread per output dim.  Splits are taken eight at a time with
-// all of a group's loads issued before any is used, so a merge of up to eight
-// splits costs one round trip to memory.  For the Hadamard-rotated 2-bit
+// head), one thread per output dim.  Splits are taken U at a time (8, or 32
+// when there are more than 8) with all of a group's loads issued before any
+// is used, so a merge costs one round trip to memory per U splits.  For the Hadamard-rotated 2-bit
 // variant the merged output is rotated back to the original basis.
 #include "decode_common.h"
 
 namespace kvq {
 
-template <bool ROT>
+template <bool ROT, int U>
 __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq, int D, int splits,
                                                            const float* __restrict__ ws, float* __restrict__ out) {
-    constexpr int U = 8;
     const int e = blockIdx.x / Hq;
     const int d = threadIdx.x;
     const int live = live_splits(bd.pos[e], bd.per);
@@ -62,10 +61,13 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq,
 
 hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s,
                                bool rot) {
-    if (rot)
-        hipLaunchKernelGGL(merge_splits_kernel<true>, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
+    };
+    if (splits > 8)
+        rot ? go(merge_splits_kernel<true, 32>) : go(merge_splits_kernel<false, 32>);
     else
-        hipLaunchKernelGGL(merge_splits_kernel<false>, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
+        rot ? go(merge_splits_kernel<true, 8>) : go(merge_splits_kernel<false, 8>);
     return hipGetLastError();
 }
 
