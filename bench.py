@@ -297,7 +297,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     window=True runs the same legs over 2-bit pools with the exact window of
     the last page: each lane's last 64 tokens are read as bf16 rows, the rest
     as 2-bit rows (the pool's pages are the 2-bit 3.02 GB).  rotated=True runs
-    the decode legs over the Hadamard-rotated 2-bit pool (same pages; no
+    the decode legs over the 2-bit pool of Hadamard-rotated K rows (same pages; no
     prefill for that format)."""
     import torch
 
@@ -387,7 +387,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                              "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256, false, true> "
-                                       "then merge_splits_kernel<true>"},
+                                       "then merge_splits_kernel"},
                 "graph_ms_per_step": graph_ms, "graph_identical_to_eager": same,
                 "kv_tokens_per_s": B * L * ctx / (graph_ms * 1e-3),
                 "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
@@ -615,7 +615,7 @@ def main():
 
     rot = None if args.no_extra else bf16_leg(5, rotated=True)
     if rot is not None:
-        # the price of the rotation: query and output transforms, butterflies on append
+        # the price of the rotation: the query transform, butterflies on the K rows of append
         rot["step_time_vs_q2"] = rot["graph_ms_per_step"] / ms_per_step
         rot["populate_time_vs_q2"] = rot["populate_ms"] / app_ms
         log(f"2-bit rotated against 2-bit: decode step {rot['step_time_vs_q2']:.3f}x the time, "

@@ -81,17 +81,18 @@ typedef enum {
      * at 16 x 4 x 256).  Appends are sequential per (sequence, layer), and
      * attention reads at most the tokens appended. */
     KV_FMT_Q2_WINDOW = 4,
-    /* KV_FMT_Q2 pages holding the 2-bit rows of H k and H v, with H the
+    /* KV_FMT_Q2 pages holding the 2-bit rows of H k, with H the
      * unnormalised Walsh-Hadamard matrix (Sylvester order, entries +-1,
      * H H = D I), applied in fp32 butterflies, stages h = 1, 2, .., D/2, each
-     * replacing (x_i, x_{i+h}) by (x_i + x_{i+h}, x_i - x_{i+h}): the rotation
-     * choice at 2 bits that "Half the Cache, Twice the Context" names in its
-     * closing notes, which spreads channel outliers over the row before the
-     * per-token range is taken.  Decode rotates the query the same way and
-     * scores with sm_scale / D; the merge returns H o / D, so outputs are in
-     * the original basis.  Needs GQA group 4 (KV_ERR_UNSUPPORTED otherwise);
-     * prefill is not implemented for it (KV_ERR_FORMAT); kv_dequant_page
-     * returns the rotated rows. */
+     * replacing (x_i, x_{i+h}) by (x_i + x_{i+h}, x_i - x_{i+h}), and V rows
+     * as KV_FMT_Q2 holds them: the rotation choice at 2 bits that "Half the
+     * Cache, Twice the Context" names in its closing notes, applied where its
+     * outliers are channels (K), which the rotation spreads over the row
+     * before the per-token range is taken.  Decode rotates the query the same
+     * way and scores with sm_scale / D (H q . H k = D q . k).  Needs GQA
+     * group 4 (KV_ERR_UNSUPPORTED otherwise); prefill is not implemented for
+     * it (KV_ERR_FORMAT); kv_dequant_page returns K rows in the rotated
+     * basis. */
     KV_FMT_Q2_ROT = 5
 } kv_format;
 

@@ -63,8 +63,8 @@ def hadamard_rows(x):
     Hadamard matrix (entries +-1, H H = D I), up to the fp32 roundings of the
     butterflies, which every implementation that takes the same stages in the
     same order reproduces bit for bit.  The rotated 2-bit variant quantizes
-    H k and H v instead of k and v ("Half the Cache, Twice the Context",
-    closing notes: the axis and rotation choices matter at 2 bits)."""
+    H k instead of k ("Half the Cache, Twice the Context", closing notes: the
+    axis and rotation choices matter at 2 bits)."""
     y = np.array(x, dtype=F32, copy=True)
     D = y.shape[-1]
     assert D & (D - 1) == 0

@@ -16,10 +16,15 @@ are kept aside (the exact window), and each append re-derives the page's K codes
 and scales from the exact rows present, so a full page equals the plain
 per-channel quantization of its 64 tokens.
 
-The rotated 2-bit variant ("q2r") stores the 2-bit rows of H k and H v (H the
-unnormalised Walsh-Hadamard matrix, applied in fp32 butterflies); its gather
-returns H x^_r / D in fp64, the dequantized rows back in the original basis,
-so attention over it is the plain attention of the other formats.
+The rotated 2-bit variant ("q2r") stores the 2-bit rows of H k (H the
+unnormalised Walsh-Hadamard matrix, applied in fp32 butterflies) and V as the
+2-bit format does; its gather returns H k^_r / D in fp64, the dequantized K
+rows back in the original basis, so attention over it is the plain attention
+of the other formats.  Only K is rotated: its outliers are channels, which the
+rotation spreads over the row, while V's are whole tokens, which a per-token
+range already absorbs ("Half the Cache, Twice the Context", section "What the
+cache loses when you round it": persistent key-channel outliers, value-token
+outliers).
 
 A fork gives a new sequence the first n tokens of another: the whole pages
 of that prefix are shared (both block tables name them), the page it only
@@ -91,9 +96,9 @@ class OraclePool:
             return
         if self.fmt == "q2w":
             self._append_window(layer, seq, start, k, v)
-        if self.fmt == "q2r":   # the rotated variant stores the 2-bit codes of H k and H v
-            bf16.f32_to_bits(k), bf16.f32_to_bits(v)
-            k, v = codec.hadamard_rows(k), codec.hadamard_rows(v)
+        if self.fmt == "q2r":   # the rotated variant stores the 2-bit codes of H k (V as in 2-bit)
+            bf16.f32_to_bits(k)
+            k = codec.hadamard_rows(k)
         if self.page_fmt == "q2":
             ck, sk, mk = codec.q2_quantize(k)
             cv, sv, mv = codec.q2_quantize(v)
@@ -196,9 +201,9 @@ class OraclePool:
 
         The window format also needs the sequence: its tokens from the window
         start up to ctx_len (at most the tokens appended) are the exact rows."""
-        if self.fmt == "q2r":   # dequantized rotated rows, back in the original basis (fp64)
+        if self.fmt == "q2r":   # dequantized rotated K rows, back in the original basis (fp64)
             K, V = self._gather_pages(layer, bt, ctx_len)
-            return codec.unrotate_rows(K), codec.unrotate_rows(V)
+            return codec.unrotate_rows(K), V
         if self.fmt == "q2w":
             appended, wk, wv = self._window[(seq, layer)]
             if ctx_len > appended:
@@ -249,7 +254,7 @@ def dequantized_rows(fmt: str, k_rows, v_rows):
     if fmt == "q2r":
         bf16.f32_to_bits(k), bf16.f32_to_bits(v)
         K = codec.unrotate_rows(codec.q2_dequantize(*codec.q2_quantize(codec.hadamard_rows(k))))
-        V = codec.unrotate_rows(codec.q2_dequantize(*codec.q2_quantize(codec.hadamard_rows(v))))
+        V = codec.q2_dequantize(*codec.q2_quantize(v))
         return K, V
     if fmt in ("q2", "q2w"):
         K = codec.q2_dequantize(*codec.q2_quantize(k))

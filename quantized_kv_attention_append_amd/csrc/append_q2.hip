@@ -173,10 +173,7 @@ __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, 
         float xk[DPL], xv[DPL];
         load_bf16_rows<DPL>(kin + off, xk);
         load_bf16_rows<DPL>(vin + off, xv);
-        if constexpr (ROT) {  // the rotated variant quantizes H k and H v
-            hadamard_row16<DPL>(xk, c);
-            hadamard_row16<DPL>(xv, c);
-        }
+        if constexpr (ROT) hadamard_row16<DPL>(xk, c);  // the rotated variant quantizes H k (V as given)
         uint32_t ck[DPL], cv[DPL];
         float sk, mk, sv, mv;
         q2_quantize_row<DPL>(xk, ck, sk, mk);

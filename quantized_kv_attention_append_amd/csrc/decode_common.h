@@ -38,8 +38,6 @@ struct DecodeWs {
         : o(ws), ml(ws + (int64_t)n * Hq * splits * D) {}
 };
 
-// rot: the outputs of the Hadamard-rotated variant are rotated back, H o / D.
-hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s,
-                               bool rot = false);
+hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s);
 
 }  // namespace kvq

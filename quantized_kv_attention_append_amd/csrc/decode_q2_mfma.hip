@@ -595,7 +595,7 @@ hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchD
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
                             float* ws, float* out, float* scores, int64_t sstride, hipStream_t s, bool rot) {
     const hipError_t err = launch_decode_q2_partials(pv, layer, bd, q, sm, splits, ws, scores, sstride, s, rot);
-    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s, rot);
+    return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }
 
 }  // namespace kvq

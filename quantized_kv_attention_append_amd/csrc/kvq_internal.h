@@ -68,7 +68,7 @@ __host__ __device__ constexpr int64_t q8_vscale_off(int D) { return 132 * (int64
 __host__ __device__ constexpr int64_t bf16_block_bytes(int D) { return 256 * (int64_t)D; }
 
 // Launchers (defined in the .hip files).  Each returns the launch status.
-// rot: the Hadamard-rotated variant (rows transformed before quantization)
+// rot: the Hadamard-rotated variant (K rows transformed before quantization)
 hipError_t launch_append_q2(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
                             const uint16_t* k, const uint16_t* v, hipStream_t s, bool rot = false);
 hipError_t launch_append_q8(const PoolView& pv, int layer, const BatchDesc& bd, int work_items,
@@ -82,7 +82,7 @@ hipError_t launch_append_window(const PoolView& pv, int layer, const BatchDesc& 
 // Decode launchers enqueue the split kernel and then the merge of its
 // partials, which writes the fp32 output.
 // rot: the Hadamard-rotated variant (group 4 only): the split kernel rotates
-// the query and scores with sm / D, the merge rotates the output back.
+// the query and scores with sm / D against the rotated K rows.
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s,
                             bool rot = false);

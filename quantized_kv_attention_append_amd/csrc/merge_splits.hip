@@ -1,13 +1,12 @@
 // Merge of the split-K decode partials: one workgroup per (sequence, query
 // head), one thread per output dim.  Splits are taken U at a time (8, or 32
 // when there are more than 8) with all of a group's loads issued before any
-// is used, so a merge costs one round trip to memory per U splits.  For the Hadamard-rotated 2-bit
-// variant the merged output is rotated back to the original basis.
+// is used, so a merge costs one round trip to memory per U splits.
 #include "decode_common.h"
 
 namespace kvq {
 
-template <bool ROT, int U>
+template <int U>
 __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq, int D, int splits,
                                                            const float* __restrict__ ws, float* __restrict__ out) {
     const int e = blockIdx.x / Hq;
@@ -41,33 +40,17 @@ __global__ __launch_bounds__(256) void merge_splits_kernel(BatchDesc bd, int Hq,
         }
         M = Mg;
     }
-    float res = acc / den;
-    if constexpr (ROT) {
-        // the rotated variant's output is H o / D: butterflies over the D
-        // threads of the row, stages h = 1 .. D/2, then the exact 1/D
-        __shared__ float r[256];
-        r[d] = res;
-        __syncthreads();
-        for (int h = 1; h < D; h *= 2) {  // additions only: nothing to contract
-            const float mine = r[d], other = r[d ^ h];
-            __syncthreads();
-            r[d] = (d & h) ? other - mine : mine + other;
-            __syncthreads();
-        }
-        res = r[d] * (1.0f / (float)D);
-    }
-    out[row * D + d] = res;
+    out[row * D + d] = acc / den;
 }
 
-hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s,
-                               bool rot) {
+hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s) {
     auto go = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, dim3(bd.n * Hq), dim3(D), 0, s, bd, Hq, D, splits, ws, out);
     };
     if (splits > 8)
-        rot ? go(merge_splits_kernel<true, 32>) : go(merge_splits_kernel<false, 32>);
+        go(merge_splits_kernel<32>);
     else
-        rot ? go(merge_splits_kernel<true, 8>) : go(merge_splits_kernel<false, 8>);
+        go(merge_splits_kernel<8>);
     return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 pytestmark = pytest.mark.gpu
 
 NAN_FILL = 0xFF
-FMTS = {"q2": 1, "q8": 2, "bf16": 3, "q2w": 4}
+FMTS = {"q2": 1, "q8": 2, "bf16": 3, "q2w": 4, "q2r": 5}
 
 
 def _w(fmt):
@@ -31,7 +31,7 @@ def _append(pool, op, w, seq, oseq, bt, k, v, start, end):
         op.append(layer, oseq, bt, start, k[layer][start:end].float().numpy(), v[layer][start:end].float().numpy())
 
 
-@pytest.mark.parametrize("fmt", ["q2", "q8", "bf16", "q2w"])
+@pytest.mark.parametrize("fmt", ["q2", "q8", "bf16", "q2w", "q2r"])
 @pytest.mark.parametrize("n", [150, 128])
 def test_fork_then_both_continue(fmt, n):
     need_gpu()

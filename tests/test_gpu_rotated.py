@@ -1,8 +1,9 @@
 """GPU parity, the Hadamard-rotated 2-bit variant: pages bit-exact against
-the oracle's image (the rows are rotated in fp32 butterflies before the 2-bit
-codec, so the codes are a pure function of the bf16 inputs), decode within
-tolerance of the fp64 oracle that reads the rows back in the original basis,
-raw scores against the oracle's, and the refusals the format documents."""
+the oracle's image (K rows are rotated in fp32 butterflies before the 2-bit
+codec, so the codes are a pure function of the bf16 inputs; V rows are the
+2-bit format's), decode within tolerance of the fp64 oracle that reads K back
+in the original basis, raw scores against the oracle's, and the refusals the
+format documents."""
 
 import numpy as np
 import pytest

@@ -17,7 +17,7 @@ import pytest
 from oracle import pool
 from synth import CONFIGS, kv_rows
 
-FORMATS = ["q2", "q8", "bf16", "q2w"]
+FORMATS = ["q2", "q8", "bf16", "q2w", "q2r"]
 
 
 def _rows(n, lane=0):

@@ -1,13 +1,14 @@
 """Oracle pins: the Hadamard-rotated 2-bit variant.
 
-The rotated variant quantizes H k and H v (H the unnormalised Sylvester
-Walsh-Hadamard matrix) and reads back H x^_r / D.  Pinned by:
+The rotated variant quantizes H k (H the unnormalised Sylvester
+Walsh-Hadamard matrix) and reads back H k^_r / D; V is the 2-bit format's.
+Pinned by:
   * the fp32 butterfly transform equals the product with scipy's Hadamard
     matrix exactly on small-integer rows (every fp32 operation exact) and to
     fp32 rounding on bf16 rows; the inverse undoes it;
-  * the error bound the rotation keeps: ||x^ - x||_2 <= scale_r / 2 per row,
+  * the error bound the rotation keeps: ||k^ - k||_2 <= scale_r / 2 per row,
     because H / sqrt(D) is orthogonal and every rotated element is within
-    scale_r / 2 of its code;
+    scale_r / 2 of its code; V reads back as the plain 2-bit codec's rows;
   * scores over the read-back rows equal (H q) . x^_r / D, the identity the
     decode kernel uses;
   * on rows with the channel outliers of "Half the Cache, Twice the Context"
@@ -52,10 +53,9 @@ def test_rotated_error_bound_and_score_identity():
     p.append(0, 0, bt, 120, k[120:], v[120:])
     K, V = p.gather(0, bt, 200)
     _, sk, _ = codec.q2_quantize(codec.hadamard_rows(k))
-    _, sv, _ = codec.q2_quantize(codec.hadamard_rows(v))
     ek = np.linalg.norm(K - k.astype(np.float64), axis=-1)
-    ev = np.linalg.norm(V - v.astype(np.float64), axis=-1)
-    assert np.all(ek <= 0.5 * sk * (1 + 1e-5)) and np.all(ev <= 0.5 * sv * (1 + 1e-5))
+    assert np.all(ek <= 0.5 * sk * (1 + 1e-5))
+    assert np.array_equal(V, codec.q2_dequantize(*codec.q2_quantize(v)))
     # scores in the original basis equal (H q) . x^_r / D over the raw rotated rows
     Kr = p._gather_pages(0, bt, 200)[0].astype(np.float64)
     q = queries(w, 0, 1)[0].float().numpy().astype(np.float64)
