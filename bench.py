@@ -96,9 +96,9 @@ def prefill_leg(steps: int, warmup: int):
     import torch
 
     import quantized_kv_attention_append_amd as kvq
-    from synth import CONFIGS, kv_rows, page_permutation, queries
+    from synth import WORKLOADS, kv_rows, page_permutation, queries
 
-    w = CONFIGS[3]
+    w = WORKLOADS["prefill"]
     prior, n_q = w.ctx, w.chunk
     total = prior + n_q
     geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
@@ -176,10 +176,10 @@ def long_context_leg(reps: int):
     import torch
 
     import quantized_kv_attention_append_amd as kvq
-    from synth import CONFIGS, kv_rows, page_permutation, planted_position, queries
+    from synth import WORKLOADS, kv_rows, page_permutation, planted_position, queries
     from synth.workloads import plant_key
 
-    w = CONFIGS[2]
+    w = WORKLOADS["long"]
     ctx = w.ctx
     geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
     _, pb = kvq.token_bytes(geom, kvq.FMT_Q2)
@@ -224,10 +224,10 @@ def q8_leg(reps: int):
     import torch
 
     import quantized_kv_attention_append_amd as kvq
-    from synth import CONFIGS, c4_lengths, kv_rows, page_permutation, queries
+    from synth import WORKLOADS, q8_batch_lengths, kv_rows, page_permutation, queries
 
-    w = CONFIGS[4]
-    lens = [int(x) for x in c4_lengths(w)]
+    w = WORKLOADS["q8"]
+    lens = [int(x) for x in q8_batch_lengths(w)]
     geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
     _, pb = kvq.token_bytes(geom, kvq.FMT_Q8)
     n_pages = sum(-(-L // 64) for L in lens)
@@ -302,11 +302,11 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     import torch
 
     import quantized_kv_attention_append_amd as kvq
-    from synth import CONFIGS, kv_rows, page_permutation, queries
+    from synth import WORKLOADS, kv_rows, page_permutation, queries
 
     fmt = kvq.FMT_Q2_WINDOW if window else kvq.FMT_Q2_ROT if rotated else kvq.FMT_BF16
     name = "2-bit window" if window else "2-bit rotated" if rotated else "bf16"
-    w = CONFIGS[1]
+    w = WORKLOADS["27b"]
     L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
     geom = (L, H, D, Hq)
     tb, pb = kvq.token_bytes(geom, fmt)
@@ -393,7 +393,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
                 "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
     # ---- chunked prefill over a bf16 pool: 65,536 prior + 1,024 chunk ----
-    w3 = CONFIGS[3]
+    w3 = WORKLOADS["prefill"]
     prior, n_q = w3.ctx, w3.chunk
     total = prior + n_q
     geom3 = (w3.n_layers, w3.n_kv_heads, w3.head_dim, w3.n_q_heads)
@@ -476,9 +476,9 @@ def main():
     import torch
 
     import quantized_kv_attention_append_amd as kvq
-    from synth import CONFIGS, kv_rows, page_permutation, queries
+    from synth import WORKLOADS, kv_rows, page_permutation, queries
 
-    w = CONFIGS[1]
+    w = WORKLOADS["27b"]
     L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
     geom = (L, H, D, Hq)
     tb, pb = kvq.token_bytes(geom, kvq.FMT_Q2)

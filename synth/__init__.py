@@ -10,13 +10,13 @@ oracle and the HIP path can both consume its output without sharing code.
 """
 
 from .workloads import (  # noqa: F401
-    CONFIGS,
+    WORKLOADS,
     Workload,
     seed_for,
     kv_rows,
     queries,
     page_permutation,
-    c4_lengths,
+    q8_batch_lengths,
     planted_position,
     bf16_bits_to_f32,
     f32_to_bf16_bits,

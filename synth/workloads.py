@@ -33,8 +33,8 @@ class Workload:
     head_dim: int
     n_q_heads: int
     lanes: int
-    ctx: int            # context tokens per lane (C4: upper bound; lengths are drawn)
-    chunk: int = 0      # prefill chunk (C3)
+    ctx: int            # context tokens per lane (the 8-bit batch: upper bound; lengths are drawn)
+    chunk: int = 0      # prefill chunk
 
     @property
     def group(self) -> int:
@@ -45,12 +45,14 @@ class Workload:
         return 1.0 / float(np.sqrt(self.head_dim))
 
 
-CONFIGS = {
-    0: Workload(0, "tiny decode, 1 layer, 1 lane x 256 tokens, 2-bit", "q2", 1, 4, 256, 16, 1, 256),
-    1: Workload(1, "27B geometry decode, 16 layers, 8 lanes x 40960 tokens, 2-bit", "q2", 16, 4, 256, 16, 8, 40960),
-    2: Workload(2, "long split-K decode, 1 layer, 1 lane x 131072 tokens, 2-bit", "q2", 1, 4, 256, 16, 1, 131072),
-    3: Workload(3, "chunked prefill, 1 layer, 65536 prior + 1024 chunk, 2-bit", "q2", 1, 4, 256, 16, 1, 65536, 1024),
-    4: Workload(4, "8-bit decode + append, 32 layers x 8 KV heads x 128, 24 lanes", "q8", 32, 8, 128, 32, 24, 8192),
+# The five workloads; the first field numbers each one's seed stream.
+WORKLOADS = {
+    "tiny": Workload(0, "tiny decode, 1 layer, 1 lane x 256 tokens, 2-bit", "q2", 1, 4, 256, 16, 1, 256),
+    "27b": Workload(1, "27B geometry decode, 16 layers, 8 lanes x 40960 tokens, 2-bit", "q2", 16, 4, 256, 16, 8, 40960),
+    "long": Workload(2, "long split-K decode, 1 layer, 1 lane x 131072 tokens, 2-bit", "q2", 1, 4, 256, 16, 1, 131072),
+    "prefill": Workload(3, "chunked prefill, 1 layer, 65536 prior + 1024 chunk, 2-bit", "q2", 1, 4, 256, 16, 1, 65536,
+                        1024),
+    "q8": Workload(4, "8-bit decode + append, 32 layers x 8 KV heads x 128, 24 lanes", "q8", 32, 8, 128, 32, 24, 8192),
 }
 
 
@@ -104,7 +106,7 @@ def page_permutation(w: Workload, n_pages: int, salt: int = 0) -> np.ndarray:
     return rng.permutation(n_pages).astype(np.int32)
 
 
-def c4_lengths(w: Workload) -> np.ndarray:
+def q8_batch_lengths(w: Workload) -> np.ndarray:
     """Context lengths for the 8-bit workload: 64 * UniformInt[16, 128] per lane."""
     rng = np.random.default_rng(seed_for(w.cfg, 0, 0, T_LEN))
     return (PAGE * rng.integers(16, 129, size=w.lanes)).astype(np.int64)

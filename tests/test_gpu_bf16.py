@@ -10,13 +10,13 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-C0 = CONFIGS[0]
-C1 = CONFIGS[1]
+TINY = WORKLOADS["tiny"]
+GEOM27B = WORKLOADS["27b"]
 # 2 layers x 2 KV heads x 128 dims, 8 query heads (group 4)
 SMALL128 = Workload(90, "small D=128 geometry", "bf16", 2, 2, 128, 8, 3, 300)
 # group 8 and group 1 at 128 dims, group 2 at 256
@@ -35,10 +35,10 @@ def _fmt():
 def test_append_bf16_ragged_chunks_bit_exact():
     need_gpu()
     n_pages = 6
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
-    bt = page_permutation(C0, n_pages)[:4]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages)[:4]
     seq = pool.reserve(256, pages=bt)
-    k, v = kv_rows(C0, 0, 0, 256)
+    k, v = kv_rows(TINY, 0, 0, 256)
     op = opool.OraclePool("bf16", 1, 4, 256, n_pages, fill=NAN_FILL)
     start = 0
     for n in (100, 1, 27, 64, 64):   # ragged chunks, some crossing page ends
@@ -89,10 +89,10 @@ def test_append_bf16_batched_d128_bit_exact():
 def test_dequant_page_bf16_returns_rows():
     need_gpu()
     n_pages = 6
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=0)
-    bt = page_permutation(C0, n_pages)[:4]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=0)
+    bt = page_permutation(TINY, n_pages)[:4]
     seq = pool.reserve(256, pages=bt)
-    k, v = kv_rows(C0, 0, 0, 256)
+    k, v = kv_rows(TINY, 0, 0, 256)
     pool.append(0, [seq], [0], [256], k.cuda(), v.cuda())
     K, V = k.float().numpy(), v.float().numpy()
     for lp in range(4):
@@ -126,7 +126,7 @@ def _decode_case(w, ctx, splits_list, layer=0):
 @pytest.mark.parametrize("ctx", [1, 63, 65, 256, 1000])
 def test_decode_bf16_ragged_lengths(ctx):
     need_gpu()
-    _decode_case(C0, ctx, [1, 3, 0])
+    _decode_case(TINY, ctx, [1, 3, 0])
 
 
 @pytest.mark.parametrize("w", [G8_128, G1_128, G2_256], ids=lambda w: w.name)
@@ -179,12 +179,12 @@ def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):
 
 def test_prefill_bf16_d256():
     need_gpu()
-    _prefill_case(C0, 0, 100, 45, [1, 2, 0])
+    _prefill_case(TINY, 0, 100, 45, [1, 2, 0])
 
 
 def test_prefill_bf16_chunk_from_zero_d256():
     need_gpu()
-    _prefill_case(C0, 0, 0, 77, [1, 2])
+    _prefill_case(TINY, 0, 0, 77, [1, 2])
 
 
 def test_prefill_bf16_d128_group4():
@@ -199,21 +199,21 @@ def test_decode_bf16_27b_geometry_layer_sampled_lanes():
     split count the library picks; lanes 0 and 7 against the oracle."""
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    w = Workload(C1.cfg, C1.name, "bf16", 1, C1.n_kv_heads, C1.head_dim, C1.n_q_heads, C1.lanes, C1.ctx)
+    w = Workload(GEOM27B.cfg, GEOM27B.name, "bf16", 1, GEOM27B.n_kv_heads, GEOM27B.head_dim, GEOM27B.n_q_heads, GEOM27B.lanes, GEOM27B.ctx)
     B, ctx = w.lanes, w.ctx
     ppl = ctx // 64
     n_pages = B * ppl
     pool, mem = make_pool(w, n_pages, kvq.FMT_BF16, fill=NAN_FILL, max_seqs=B, max_seq_tokens=ctx)
-    perm = page_permutation(C1, n_pages)
+    perm = page_permutation(GEOM27B, n_pages)
     seqs = [pool.reserve(ctx, pages=perm[i * ppl:(i + 1) * ppl]) for i in range(B)]
     rows = []
     for lane in range(B):
-        k, v = kv_rows(C1, 3, lane, ctx, device="cuda")   # the rows of layer 3 of the 27B batch
+        k, v = kv_rows(GEOM27B, 3, lane, ctx, device="cuda")   # the rows of layer 3 of the 27B batch
         pool.append(0, [seqs[lane]], [0], [ctx], k, v)
         if lane in (0, B - 1):
             rows.append((lane, k.float().cpu().numpy(), v.float().cpu().numpy()))
         del k, v
-    q = queries(C1, 3, B, device="cuda")
+    q = queries(GEOM27B, 3, B, device="cuda")
     out = pool.decode(0, seqs, [ctx] * B, q, w.sm_scale).cpu().numpy()
     assert np.all(np.isfinite(out))
     qn = q.float().cpu().numpy()

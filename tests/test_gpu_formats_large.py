@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,7 @@ def test_27b_geometry_layers_sampled(name):
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
     fmt = {"q2w": kvq.FMT_Q2_WINDOW, "q2r": kvq.FMT_Q2_ROT}[name]
-    w = CONFIGS[1]
+    w = WORKLOADS["27b"]
     L, B, ctx = w.n_layers, w.lanes, w.ctx
     geom = (L, w.n_kv_heads, w.head_dim, w.n_q_heads)
     ppl = ctx // 64

@@ -9,13 +9,13 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-C0 = CONFIGS[0]
-C3 = CONFIGS[3]
+TINY = WORKLOADS["tiny"]
+PREFILL = WORKLOADS["prefill"]
 SMALL128 = Workload(90, "small D=128 geometry", "q2", 2, 2, 128, 8, 3, 300)
 
 
@@ -45,12 +45,12 @@ def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):
 
 def test_prefill_small_d256_splits():
     need_gpu()
-    _prefill_case(C0, 0, 100, 45, [1, 2, 3, 0])
+    _prefill_case(TINY, 0, 100, 45, [1, 2, 3, 0])
 
 
 def test_prefill_small_d256_chunk_from_zero():
     need_gpu()
-    _prefill_case(C0, 0, 0, 77, [1, 2])
+    _prefill_case(TINY, 0, 0, 77, [1, 2])
 
 
 def test_prefill_d128_group4():
@@ -60,8 +60,8 @@ def test_prefill_d128_group4():
 
 def test_prefill_last_row_equals_decode():
     need_gpu()
-    pool, seq, q, outs = _prefill_case(C0, 0, 192, 33, [2], salt=4)
-    dec = pool.decode(0, [seq], [192 + 33], q[-1:].cuda(), C0.sm_scale, n_splits=1).cpu()
+    pool, seq, q, outs = _prefill_case(TINY, 0, 192, 33, [2], salt=4)
+    dec = pool.decode(0, [seq], [192 + 33], q[-1:].cuda(), TINY.sm_scale, n_splits=1).cpu()
     # two independent GPU paths, each within ~1e-4 of the oracle: compared at the same bar
     assert_close(outs[0][-1].numpy(), dec[0].numpy().astype(np.float64), "last prefill row vs decode")
 
@@ -69,14 +69,14 @@ def test_prefill_last_row_equals_decode():
 def test_prefill_refuses_bad_calls():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    pool, mem = make_pool(C0, 4, kvq.FMT_Q2)
+    pool, mem = make_pool(TINY, 4, kvq.FMT_Q2)
     seq = pool.reserve(128)
-    q = queries(C0, 0, 10).cuda()
+    q = queries(TINY, 0, 10).cuda()
     with pytest.raises(kvq.KvError) as ei:
-        pool.prefill(0, seq, 0, q, C0.sm_scale, n_splits=2, ws=torch.empty(64, dtype=torch.uint8, device="cuda"))
+        pool.prefill(0, seq, 0, q, TINY.sm_scale, n_splits=2, ws=torch.empty(64, dtype=torch.uint8, device="cuda"))
     assert ei.value.name == "KV_ERR_WORKSPACE"
     with pytest.raises(kvq.KvError) as ei:
-        pool.prefill(0, seq, 120, q, C0.sm_scale)   # 130 > bound of 128
+        pool.prefill(0, seq, 120, q, TINY.sm_scale)   # 130 > bound of 128
     assert ei.value.name == "KV_ERR_BOUND"
     w8 = Workload(93, "8-bit", "q8", 1, 4, 128, 16, 1, 64)
     p8, _ = make_pool(w8, 2, kvq.FMT_Q8)
@@ -93,7 +93,7 @@ def test_c3_chunked_prefill_full_size():
     decode at each row's own length (equal to its prefill row)."""
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    w = C3
+    w = PREFILL
     prior, n_q = w.ctx, w.chunk
     total = prior + n_q
     n_pages = total // 64
@@ -112,4 +112,4 @@ def test_c3_chunked_prefill_full_size():
     for i in (0, 1, 63, 64, 207, 500, 707, 1022, 1023):
         ref = attention.decode(qn[i], K[:prior + i + 1], V[:prior + i + 1], w.sm_scale)
         assert_close(out[i], ref, f"chunk row {i} (ctx {prior + i + 1})")
-    say("C3 prefill: sampled rows within tolerance")
+    say("PREFILL prefill: sampled rows within tolerance")

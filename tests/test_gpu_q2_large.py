@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from oracle import attention, codec
-from synth import CONFIGS, kv_rows, page_permutation, planted_position, queries
+from synth import WORKLOADS, kv_rows, page_permutation, planted_position, queries
 from synth.workloads import plant_key
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
@@ -31,7 +31,7 @@ def _oracle_rows(k, v):
 @pytest.mark.timeout(600)
 def test_long_split_k_decode_planted_key():
     need_gpu()
-    w = CONFIGS[2]
+    w = WORKLOADS["long"]
     ctx = w.ctx
     say("long decode: drawing inputs")
     k, v = kv_rows(w, 0, 0, ctx)
@@ -79,7 +79,7 @@ def test_long_split_k_decode_planted_key():
 def test_27b_geometry_batched_decode_sampled():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    w = CONFIGS[1]
+    w = WORKLOADS["27b"]
     L, B, ctx = w.n_layers, w.lanes, w.ctx
     ppl = ctx // 64
     n_pages = B * ppl

@@ -8,12 +8,12 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-C0 = CONFIGS[0]
+TINY = WORKLOADS["tiny"]
 # a second geometry: 2 layers x 2 KV heads x 128 dims, 8 query heads
 SMALL128 = Workload(90, "small D=128 geometry", "q2", 2, 2, 128, 8, 3, 300)
 
@@ -35,11 +35,11 @@ def _append_both(pool, op, layer, seq_ids, bts, chunks, k_all, v_all):
 def test_append_q2_tiny_bit_exact():
     need_gpu()
     n_pages = 6
-    pool, mem = make_pool(C0, n_pages, 1)
-    bt = page_permutation(C0, n_pages)[:4]
+    pool, mem = make_pool(TINY, n_pages, 1)
+    bt = page_permutation(TINY, n_pages)[:4]
     seq = pool.reserve(256, pages=bt)
     assert pool.pages(seq) == list(bt)
-    k, v = kv_rows(C0, 0, 0, 256)
+    k, v = kv_rows(TINY, 0, 0, 256)
     op = opool.OraclePool("q2", 1, 4, 256, n_pages)
     _append_both(pool, op, 0, [seq], [bt], [[(0, 100)], [(0, 1)], [(0, 27)], [(0, 64)], [(0, 64)]], [k], [v])
     torch.cuda.synchronize()
@@ -57,7 +57,7 @@ def test_append_q2_half_step_rows_bit_exact():
     (round half to even), the case where the quotient must be the correctly
     rounded one."""
     need_gpu()
-    w = C0
+    w = TINY
     n_pages = 3
     pool, mem = make_pool(w, n_pages, 1)
     bt = page_permutation(w, n_pages, salt=5)[:2]
@@ -113,10 +113,10 @@ def test_append_q2_batched_ragged_d128_bit_exact():
 def test_dequant_page_bit_exact():
     need_gpu()
     n_pages = 6
-    pool, mem = make_pool(C0, n_pages, 1, fill=0)
-    bt = page_permutation(C0, n_pages)[:4]
+    pool, mem = make_pool(TINY, n_pages, 1, fill=0)
+    bt = page_permutation(TINY, n_pages)[:4]
     seq = pool.reserve(256, pages=bt)
-    k, v = kv_rows(C0, 0, 0, 256)
+    k, v = kv_rows(TINY, 0, 0, 256)
     pool.append(0, [seq], [0], [256], k.cuda(), v.cuda())
     K, V = opool.dequantized_rows("q2", k.float().numpy(), v.float().numpy())
     for lp in range(4):
@@ -152,18 +152,18 @@ def _decode_case(w, ctx, splits_list, layer=0):
 
 def test_decode_q2_tiny():
     need_gpu()
-    _decode_case(C0, 256, [1, 2, 3, 0])
+    _decode_case(TINY, 256, [1, 2, 3, 0])
 
 
 @pytest.mark.parametrize("ctx", [1, 63, 65, 200, 1000])
 def test_decode_q2_ragged_lengths(ctx):
     need_gpu()
-    _decode_case(C0, ctx, [1, 4])
+    _decode_case(TINY, ctx, [1, 4])
 
 
 def test_decode_q2_block_table_permutation_invariance():
     need_gpu()
-    w, ctx = C0, 256
+    w, ctx = TINY, 256
     k, v = kv_rows(w, 0, 0, ctx)
     q = queries(w, 0, 1).cuda()
     outs = []
@@ -202,9 +202,9 @@ def test_decode_q2_batch_of_lanes_d128():
 def test_errors_refused_before_any_write():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    pool, mem = make_pool(C0, 4, 1)
+    pool, mem = make_pool(TINY, 4, 1)
     seq = pool.reserve(100)
-    k, v = kv_rows(C0, 0, 0, 101)
+    k, v = kv_rows(TINY, 0, 0, 101)
     before = mem.clone()
     with pytest.raises(kvq.KvError) as ei:
         pool.append(0, [seq], [0], [101], k.cuda(), v.cuda())   # beyond the 100-token bound
@@ -212,7 +212,7 @@ def test_errors_refused_before_any_write():
     with pytest.raises(kvq.KvError) as ei:
         pool.reserve(64 * 3)                                     # only 2 pages left
     assert ei.value.name == "KV_ERR_NO_SPACE"
-    q = queries(C0, 0, 1).cuda()
+    q = queries(TINY, 0, 1).cuda()
     with pytest.raises(kvq.KvError) as ei:
         pool.decode(0, [seq], [50], q, 0.0625, n_splits=1, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert ei.value.name == "KV_ERR_WORKSPACE"

@@ -9,12 +9,12 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, c4_lengths, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, q8_batch_lengths, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, geom_of, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-C4 = CONFIGS[4]
+Q8B = WORKLOADS["q8"]
 # 2 layers of the 8-bit geometry, 3 lanes
 SMALL8 = Workload(91, "small 8-bit geometry", "q8", 2, 8, 128, 32, 3, 300)
 # a D = 256, group-2 geometry on the 8-bit format
@@ -177,14 +177,14 @@ def test_decode_q8_small(w, lens):
 
 
 @pytest.mark.timeout(600)
-def test_c4_workload_decode_then_append():
+def test_q8_batch_decode_then_append():
     """Full 8-bit workload: populate 32 layers x 24 lanes, decode every layer,
     append one token per lane, decode again; sampled (layer, lane) pairs against
     the oracle, both decodes."""
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    w = C4
-    lens = c4_lengths(w)
+    w = Q8B
+    lens = q8_batch_lengths(w)
     geom = geom_of(w)
     _, pb = kvq.token_bytes(geom, kvq.FMT_Q8)
     n_pages = int(sum(-(-(int(L) + 1) // 64) for L in lens))

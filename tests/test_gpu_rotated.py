@@ -10,12 +10,12 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-C0 = CONFIGS[0]
+TINY = WORKLOADS["tiny"]
 # 2 layers x 2 KV heads x 128 dims, 8 query heads (group 4)
 SMALL128 = Workload(91, "rotated, D=128", "q2r", 2, 2, 128, 8, 3, 300)
 NAN_FILL = 0xFF
@@ -29,10 +29,10 @@ def _fmt():
 def test_rotated_append_bit_exact_d256():
     need_gpu()
     n_pages = 6
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
-    bt = page_permutation(C0, n_pages)[:4]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages)[:4]
     seq = pool.reserve(256, pages=bt)
-    k, v = kv_rows(C0, 0, 0, 256)
+    k, v = kv_rows(TINY, 0, 0, 256)
     op = opool.OraclePool("q2r", 1, 4, 256, n_pages, fill=NAN_FILL)
     start = 0
     for n in (100, 1, 27, 64, 64):
@@ -77,23 +77,23 @@ def test_rotated_append_batched_d128_bit_exact():
 def test_rotated_decode_ragged(ctx):
     need_gpu()
     n_pages = -(-ctx // 64) + 2
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
-    bt = page_permutation(C0, n_pages, salt=ctx)[:-2]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages, salt=ctx)[:-2]
     seq = pool.reserve(ctx, pages=bt)
-    k, v = kv_rows(C0, 0, 0, ctx)
+    k, v = kv_rows(TINY, 0, 0, ctx)
     pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
-    q = queries(C0, 0, 1, stream=ctx)
+    q = queries(TINY, 0, 1, stream=ctx)
     K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
     qn = q[0].float().numpy()
-    ref = attention.decode(qn, K, V, C0.sm_scale)
-    ref_s = attention.scores(qn, K, C0.sm_scale)
+    ref = attention.decode(qn, K, V, TINY.sm_scale)
+    ref_s = attention.scores(qn, K, TINY.sm_scale)
     for sp in (1, 3, 0):
-        scores = torch.full((1, C0.n_q_heads, ctx), float("nan"), device="cuda")
+        scores = torch.full((1, TINY.n_q_heads, ctx), float("nan"), device="cuda")
         ws = torch.full((pool.workspace_bytes(0, 1, sp),), 0xFF, dtype=torch.uint8, device="cuda")
-        out = pool.decode(0, [seq], [ctx], q.cuda(), C0.sm_scale, n_splits=sp, ws=ws, scores=scores)
+        out = pool.decode(0, [seq], [ctx], q.cuda(), TINY.sm_scale, n_splits=sp, ws=ws, scores=scores)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy()[0], ref, f"rotated decode ctx={ctx} splits={sp}")
-        # raw scores: a check of this build's own, beside the output tolerance.
+        # raw scores: a check of the library's own, beside the output tolerance.
         # The rotated score is sm / D (H q) . x^_r: the query passes through
         # eight fp32 butterfly stages and its fixed-point digits are taken at
         # the rotated row's larger magnitude, so the bar is 5e-5 here against
@@ -133,14 +133,14 @@ def test_rotated_lowers_the_decode_error_against_the_exact_rows():
     import quantized_kv_attention_append_amd as kvq
     ctx = 1024
     errs = {}
-    k, v = kv_rows(C0, 0, 0, ctx)
-    q = queries(C0, 0, 1, stream=5)
-    exact = attention.decode(q[0].float().numpy(), k.float().numpy(), v.float().numpy(), C0.sm_scale)
+    k, v = kv_rows(TINY, 0, 0, ctx)
+    q = queries(TINY, 0, 1, stream=5)
+    exact = attention.decode(q[0].float().numpy(), k.float().numpy(), v.float().numpy(), TINY.sm_scale)
     for name, fmt in (("q2", kvq.FMT_Q2), ("q2r", kvq.FMT_Q2_ROT)):
-        pool, _ = make_pool(C0, ctx // 64, fmt)
+        pool, _ = make_pool(TINY, ctx // 64, fmt)
         seq = pool.reserve(ctx)
         pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
-        out = pool.decode(0, [seq], [ctx], q.cuda(), C0.sm_scale)
+        out = pool.decode(0, [seq], [ctx], q.cuda(), TINY.sm_scale)
         torch.cuda.synchronize()
         o = out.cpu().numpy()[0].astype(np.float64)
         errs[name] = np.linalg.norm(o - exact) / np.linalg.norm(exact)
@@ -151,10 +151,10 @@ def test_rotated_lowers_the_decode_error_against_the_exact_rows():
 def test_rotated_refusals():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    pool, _ = make_pool(C0, 4, _fmt())
+    pool, _ = make_pool(TINY, 4, _fmt())
     seq = pool.reserve(128)
-    k, v = kv_rows(C0, 0, 0, 128)
+    k, v = kv_rows(TINY, 0, 0, 128)
     pool.append(0, [seq], [0], [128], k.cuda(), v.cuda())
     with pytest.raises(kvq.KvError) as ei:
-        pool.prefill(0, seq, 64, queries(C0, 0, 64, stream=1).cuda(), C0.sm_scale)
+        pool.prefill(0, seq, 64, queries(TINY, 0, 64, stream=1).cuda(), TINY.sm_scale)
     assert ei.value.name == "KV_ERR_FORMAT"

@@ -9,13 +9,13 @@ import pytest
 import torch
 
 from oracle import attention, pool as opool
-from synth import CONFIGS, Workload, kv_rows, page_permutation, queries
+from synth import WORKLOADS, Workload, kv_rows, page_permutation, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
-C0 = CONFIGS[0]
-C3 = CONFIGS[3]
+TINY = WORKLOADS["tiny"]
+PREFILL = WORKLOADS["prefill"]
 # group 2 at 128 dims (the vector-ALU split kernel), 2 layers
 G2_128 = Workload(97, "group 2, D=128, window", "q2w", 2, 2, 128, 4, 3, 400)
 NAN_FILL = 0xFF
@@ -37,10 +37,10 @@ def _append_both(pool, op, layer, seq, oseq, bt, k, v, pieces, start=0):
 def test_window_append_pages_bit_exact():
     need_gpu()
     n_pages = 6
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
-    bt = page_permutation(C0, n_pages)[:4]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages)[:4]
     seq = pool.reserve(256, pages=bt)
-    k, v = kv_rows(C0, 0, 0, 256)
+    k, v = kv_rows(TINY, 0, 0, 256)
     op = opool.OraclePool("q2w", 1, 4, 256, n_pages, fill=NAN_FILL)
     _append_both(pool, op, 0, seq, 0, bt, k, v, (100, 1, 27, 64, 64))
     torch.cuda.synchronize()
@@ -73,17 +73,17 @@ def test_window_decode_ragged(pieces):
     need_gpu()
     total = sum(pieces)
     n_pages = -(-total // 64) + 2
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
-    bt = page_permutation(C0, n_pages, salt=total)[:-2]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages, salt=total)[:-2]
     seq = pool.reserve(total, pages=bt)
-    k, v = kv_rows(C0, 0, 0, total)
+    k, v = kv_rows(TINY, 0, 0, total)
     op = opool.OraclePool("q2w", 1, 4, 256, n_pages, fill=NAN_FILL)
     _append_both(pool, op, 0, seq, 0, bt, k, v, pieces)
     w0 = op.window_start(0, 0)
     # the whole context, one token short, the window start and a context before it
     ctxs = sorted({c for c in (total, total - 1, w0, w0 - 5) if c >= 1})
     for ctx in ctxs:
-        _decode_check(pool, op, C0, 0, seq, 0, bt, ctx, [1, 3, 0], f"window pieces={pieces}")
+        _decode_check(pool, op, TINY, 0, seq, 0, bt, ctx, [1, 3, 0], f"window pieces={pieces}")
 
 
 def test_window_decode_batched_group2_d128():
@@ -138,17 +138,17 @@ def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):
 
 def test_window_prefill_small():
     need_gpu()
-    _prefill_case(C0, 0, 100, 45, [1, 2, 3, 0])
+    _prefill_case(TINY, 0, 100, 45, [1, 2, 3, 0])
 
 
 def test_window_prefill_all_in_window():
     need_gpu()
-    _prefill_case(C0, 0, 0, 50, [1, 2])     # every key is a window key: no page is read
+    _prefill_case(TINY, 0, 0, 50, [1, 2])     # every key is a window key: no page is read
 
 
 def test_window_prefill_chunk_from_zero_two_pages():
     need_gpu()
-    _prefill_case(C0, 0, 0, 130, [1, 2, 0])
+    _prefill_case(TINY, 0, 0, 130, [1, 2, 0])
 
 
 def test_window_prefill_group2_d128():
@@ -162,7 +162,7 @@ def test_window_prefill_full_chunk_sampled():
     against the oracle."""
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    w = C3
+    w = PREFILL
     prior, n_q = w.ctx, w.chunk
     total = prior + n_q
     n_pages = total // 64
@@ -186,27 +186,27 @@ def test_window_refusals_before_any_byte_moves():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
     n_pages = 4
-    pool, mem = make_pool(C0, n_pages, _fmt(), fill=NAN_FILL)
-    bt = page_permutation(C0, n_pages)[:3]
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages)[:3]
     seq = pool.reserve(192, pages=bt)
-    k, v = kv_rows(C0, 0, 0, 192)
+    k, v = kv_rows(TINY, 0, 0, 192)
     pool.append(0, [seq], [0], [100], k[:100].cuda(), v[:100].cuda())
     torch.cuda.synchronize()
     before = mem.cpu().clone()
     with pytest.raises(kvq.KvError) as ei:      # appends are sequential per layer
         pool.append(0, [seq], [101], [10], k[101:111].cuda(), v[101:111].cuda())
     assert ei.value.name == "KV_ERR_ARG"
-    q = queries(C0, 0, 1)
+    q = queries(TINY, 0, 1)
     with pytest.raises(kvq.KvError) as ei:      # decode past the appended tokens
-        pool.decode(0, [seq], [101], q.cuda(), C0.sm_scale)
+        pool.decode(0, [seq], [101], q.cuda(), TINY.sm_scale)
     assert ei.value.name == "KV_ERR_BOUND"
-    qc = queries(C0, 0, 10, stream=1)
+    qc = queries(TINY, 0, 10, stream=1)
     with pytest.raises(kvq.KvError) as ei:      # prefill chunk past the appended tokens
-        pool.prefill(0, seq, 95, qc.cuda(), C0.sm_scale)
+        pool.prefill(0, seq, 95, qc.cuda(), TINY.sm_scale)
     assert ei.value.name == "KV_ERR_BOUND"
     ws = torch.empty((pool.workspace_bytes(kvq.OP_PREFILL, 5, 1) - 4,), dtype=torch.uint8, device="cuda")
     with pytest.raises(kvq.KvError) as ei:      # the window's partials need their room
-        pool.prefill(0, seq, 95, qc[:5].cuda(), C0.sm_scale, n_splits=1, ws=ws)
+        pool.prefill(0, seq, 95, qc[:5].cuda(), TINY.sm_scale, n_splits=1, ws=ws)
     assert ei.value.name == "KV_ERR_WORKSPACE"
     torch.cuda.synchronize()
     assert torch.equal(mem.cpu(), before)

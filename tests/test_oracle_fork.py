@@ -15,13 +15,13 @@ import numpy as np
 import pytest
 
 from oracle import pool
-from synth import CONFIGS, kv_rows
+from synth import WORKLOADS, kv_rows
 
 FORMATS = ["q2", "q8", "bf16", "q2w", "q2r"]
 
 
 def _rows(n, lane=0):
-    w = CONFIGS[0]
+    w = WORKLOADS["tiny"]
     k, v = kv_rows(w, 0, lane, n)
     return k.float().numpy(), v.float().numpy()
 

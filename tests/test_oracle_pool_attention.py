@@ -6,13 +6,13 @@ import numpy as np
 import pytest
 
 from oracle import attention, codec, layout, pool
-from synth import CONFIGS, kv_rows, page_permutation, queries
+from synth import WORKLOADS, kv_rows, page_permutation, queries
 
 F32 = np.float32
 
 
 def _c0_rows(n=256):
-    w = CONFIGS[0]
+    w = WORKLOADS["tiny"]
     k, v = kv_rows(w, 0, 0, n)
     return w, k.float().numpy(), v.float().numpy()
 

@@ -20,11 +20,11 @@ import numpy as np
 import pytest
 
 from oracle import attention, codec, pool
-from synth import CONFIGS, kv_rows, queries
+from synth import WORKLOADS, kv_rows, queries
 
 
 def _rows(n):
-    w = CONFIGS[0]
+    w = WORKLOADS["tiny"]
     k, v = kv_rows(w, 0, 0, n)
     return w, k.float().numpy(), v.float().numpy()
 
