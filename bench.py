@@ -437,7 +437,10 @@ def oracle_baseline(w, budget_s: float):
 
     ctx = w.ctx
     done_tokens, spent, units = 0, 0.0, []
-    for layer, lane in ((0, 0), (1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (6, 6), (7, 7)):
+    # (layer, lane) units in an order that spreads the sample over layers and
+    # lanes, until the budget of oracle time is spent
+    order = [(layer, (layer + s) % w.lanes) for s in range(w.lanes) for layer in range(w.n_layers)]
+    for layer, lane in order:
         k, v = kv_rows(w, layer, lane, ctx, device="cuda")
         kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
         del k, v
