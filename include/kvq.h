@@ -89,10 +89,9 @@ typedef enum {
      * Cache, Twice the Context" names in its closing notes, applied where its
      * outliers are channels (K), which the rotation spreads over the row
      * before the per-token range is taken.  Decode rotates the query the same
-     * way and scores with sm_scale / D (H q . H k = D q . k).  Needs GQA
-     * group 4 (KV_ERR_UNSUPPORTED otherwise); prefill is not implemented for
-     * it (KV_ERR_FORMAT); kv_dequant_page returns K rows in the rotated
-     * basis. */
+     * way and scores with sm_scale / D (H q . H k = D q . k).  Prefill is
+     * not implemented for it (KV_ERR_FORMAT); kv_dequant_page returns K rows
+     * in the rotated basis. */
     KV_FMT_Q2_ROT = 5
 } kv_format;
 

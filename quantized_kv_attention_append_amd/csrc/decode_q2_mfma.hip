@@ -1,5 +1,7 @@
 // Split-K decode attention over the 2-bit pool on the gfx950 matrix cores
-// (GQA group 4, head_dim 128 or 256).
+// (head_dim 128 or 256; four query heads of a KV head's group a launch, so
+// groups 1 and 2 leave rows of the products empty and group 8 takes two
+// launches).
 //
 // At group 4 and 256 dims a decode step does 2 x 4 x 256 multiply-adds for
 // every 144 bytes of K and V rows it reads, more than the vector ALUs can
@@ -266,7 +268,7 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
         st.l_run += p;
         w[m] = x;
     }
-    if constexpr (SCORES) {
+    if (SCORES && srow) {  // lanes of a head past the group's end hold no score row
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const int tok = tok0 + 16 * m + j;
@@ -333,12 +335,17 @@ template <int D, bool SCORES, bool ROT>
 __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                              const uint16_t* __restrict__ q, float sm, int splits,
                                                              float* __restrict__ ws, float* __restrict__ out,
-                                                             float* __restrict__ scores, int64_t sstride) {
+                                                             float* __restrict__ scores, int64_t sstride, int h0,
+                                                             int nh) {
+    // The kernel takes four query heads of a KV head's group at a time: heads
+    // h0 .. h0 + nh - 1 (nh <= 4; rows of the missing heads are zero queries
+    // whose results are dropped).
     constexpr int G = 4;
     constexpr int NC = D / 128;  // k-chunks of the q.k product
     constexpr int NB = D / 16;   // 16-dim blocks of the p.v product
-    const int Hkv = pv.Hkv, Hq = pv.Hq;
+    const int Hkv = pv.Hkv, Hq = pv.Hq, Gq = Hq / Hkv;  // Gq: the pool's GQA group
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
+    const int64_t head0 = (int64_t)e * Hq + (int64_t)g * Gq + h0;  // first query row of this launch
     const int ctx = bd.pos[e];
     int pg0, pg1;
     split_range(ctx, bd.per, sp, &pg0, &pg1);
@@ -355,7 +362,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
     const int n_pages = (ctx + PAGE - 1) / PAGE;
-    float* srow = scores ? scores + ((int64_t)e * Hq + g * G + grp) * sstride : nullptr;
+    float* srow = scores && grp < nh ? scores + (head0 + grp) * sstride : nullptr;
     WaveLds& lds = lds_s[wave];
 
     // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
@@ -397,9 +404,12 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     static_assert(G * D * 2 <= sizeof(WaveLds::meta), "query rows fit the metadata area");
     uint4 qraw[QPIECES];
     {
-        const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((int64_t)e * Hq + g * G) * D);
+        const uint4* qsrc = reinterpret_cast<const uint4*>(q + head0 * D);
 #pragma unroll
-        for (int i = 0; i < QPIECES; ++i) qraw[i] = qsrc[l + 64 * i];
+        for (int i = 0; i < QPIECES; ++i) {  // piece p holds bf16 8p .. 8p + 7 of the four rows
+            const int p = l + 64 * i;
+            qraw[i] = 8 * p < nh * D ? qsrc[p] : make_uint4(0u, 0u, 0u, 0u);
+        }
     }
     if (TF > 0) {
         fetch_ids(0);
@@ -548,48 +558,49 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
             f[v] = __builtin_amdgcn_exp2f(ml_s[v][h][0] - M);
             lsum += f[v] * ml_s[v][h][1];
         }
-        const int64_t row = ((int64_t)e * Hq + g * G + h) * splits + sp;
+        const int64_t row = (head0 + h) * splits + sp;
 #pragma unroll
         for (int k = 0; k < D / 64; ++k) {
             const int d = l + 64 * k;
             float o = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) o += f[v] * (o_s[v][h][d] + ml_s[v][h][2]);
-            w.o[row * D + d] = o;
+            if (h < nh) w.o[row * D + d] = o;
         }
-        if (l == 0) {
+        if (l == 0 && h < nh) {
             w.ml[2 * row] = M;
             w.ml[2 * row + 1] = lsum;
         }
     }
 }
 
-hipError_t launch_decode_q2_valu(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
-                                 int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
-
 hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                                      int splits, float* ws, float* scores, int64_t sstride, hipStream_t s, bool rot) {
-    if (pv.Hq != 4 * pv.Hkv) {
-        if (rot) return hipErrorInvalidValue;  // the rotated variant runs on the group-4 kernel only
-        return launch_decode_q2_valu(pv, layer, bd, q, sm, splits, ws, nullptr, scores, sstride, s);
-    }
     dim3 grid(bd.n * pv.Hkv, splits);
     const float smk = rot ? sm / (float)pv.D : sm;  // H q . H k = D q . k
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, nullptr, scores, sstride);
-    };
-    if (pv.D == 256) {
-        if (rot)
-            scores ? go(decode_q2_mfma_kernel<256, true, true>) : go(decode_q2_mfma_kernel<256, false, true>);
-        else
-            scores ? go(decode_q2_mfma_kernel<256, true, false>) : go(decode_q2_mfma_kernel<256, false, false>);
-    } else {
-        if (rot)
-            scores ? go(decode_q2_mfma_kernel<128, true, true>) : go(decode_q2_mfma_kernel<128, false, true>);
-        else
-            scores ? go(decode_q2_mfma_kernel<128, true, false>) : go(decode_q2_mfma_kernel<128, false, false>);
+    const int Gq = pv.Hq / pv.Hkv;
+    // groups of up to four query heads per launch: one launch for G <= 4, two for G = 8
+    for (int h0 = 0; h0 < Gq; h0 += 4) {
+        const int nh = Gq - h0 < 4 ? Gq - h0 : 4;
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, nullptr, scores,
+                               sstride, h0, nh);
+        };
+        if (pv.D == 256) {
+            if (rot)
+                scores ? go(decode_q2_mfma_kernel<256, true, true>) : go(decode_q2_mfma_kernel<256, false, true>);
+            else
+                scores ? go(decode_q2_mfma_kernel<256, true, false>) : go(decode_q2_mfma_kernel<256, false, false>);
+        } else {
+            if (rot)
+                scores ? go(decode_q2_mfma_kernel<128, true, true>) : go(decode_q2_mfma_kernel<128, false, true>);
+            else
+                scores ? go(decode_q2_mfma_kernel<128, true, false>) : go(decode_q2_mfma_kernel<128, false, false>);
+        }
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,

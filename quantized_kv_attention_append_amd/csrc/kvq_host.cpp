@@ -54,8 +54,6 @@ kv_status check_geom(const kv_geom* g, kv_format fmt) {
                     g->n_kv_heads);
     int G = g->n_q_heads / g->n_kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8) return fail(KV_ERR_UNSUPPORTED, "GQA group %d (supported: 1, 2, 4, 8)", G);
-    if (fmt == KV_FMT_Q2_ROT && G != 4)
-        return fail(KV_ERR_UNSUPPORTED, "the rotated 2-bit format needs GQA group 4 (got %d)", G);
     return KV_OK;
 }
 

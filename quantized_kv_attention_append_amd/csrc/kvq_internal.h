@@ -81,8 +81,8 @@ hipError_t launch_append_window(const PoolView& pv, int layer, const BatchDesc& 
                                 const uint16_t* v, hipStream_t s);
 // Decode launchers enqueue the split kernel and then the merge of its
 // partials, which writes the fp32 output.
-// rot: the Hadamard-rotated variant (group 4 only): the split kernel rotates
-// the query and scores with sm / D against the rotated K rows.
+// rot: the Hadamard-rotated variant: the split kernel rotates the query and
+// scores with sm / D against the rotated K rows.
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s,
                             bool rot = false);

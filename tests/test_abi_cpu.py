@@ -48,7 +48,6 @@ def test_token_bytes_from_the_library():
     ((16, 4, 256, 64), 1, "KV_ERR_UNSUPPORTED"),   # group 16
     ((0, 4, 256, 16), 1, "KV_ERR_ARG"),
     ((16, 4, 256, 16), 6, "KV_ERR_FORMAT"),       # no format 6
-    ((16, 4, 256, 32), 5, "KV_ERR_UNSUPPORTED"),  # the rotated format needs group 4
 ])
 def test_bad_geometry_is_refused(geom, fmt, status):
     import quantized_kv_attention_append_amd as kvq

@@ -218,3 +218,40 @@ def test_errors_refused_before_any_write():
     assert ei.value.name == "KV_ERR_WORKSPACE"
     torch.cuda.synchronize()
     assert torch.equal(mem, before)
+
+
+# GQA groups other than 4 run the same matrix-core kernel four query heads at
+# a time (group 8 in two launches; groups 1 and 2 with empty rows)
+GROUPS = [
+    Workload(93, "group 1, D=128", "q2", 1, 4, 128, 4, 2, 300),
+    Workload(93, "group 2, D=256", "q2", 1, 2, 256, 4, 2, 300),
+    Workload(93, "group 8, D=128", "q2", 1, 2, 128, 16, 2, 300),
+    Workload(93, "group 8, D=256", "q2", 1, 1, 256, 8, 2, 300),
+]
+
+
+@pytest.mark.parametrize("w", GROUPS, ids=lambda w: w.name)
+def test_decode_q2_other_groups(w):
+    need_gpu()
+    lens = [300, 97]
+    n_pages = sum(-(-n // 64) for n in lens)
+    pool, mem = make_pool(w, n_pages, 1)
+    seqs, refs, refs_s = [], [], []
+    q = queries(w, 0, len(lens))
+    for i, n in enumerate(lens):
+        seqs.append(pool.reserve(n))
+        k, v = kv_rows(w, 0, i, n)
+        pool.append(0, [seqs[-1]], [0], [n], k.cuda(), v.cuda())
+        K, V = opool.dequantized_rows("q2", k.float().numpy(), v.float().numpy())
+        refs.append(attention.decode(q[i].float().numpy(), K, V, w.sm_scale))
+        refs_s.append(attention.scores(q[i].float().numpy(), K, w.sm_scale))
+    for sp in (1, 3):
+        scores = torch.full((len(lens), w.n_q_heads, max(lens)), float("nan"), device="cuda")
+        ws = torch.full((pool.workspace_bytes(0, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = pool.decode(0, seqs, lens, q.cuda(), w.sm_scale, n_splits=sp, ws=ws, scores=scores)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), np.stack(refs), f"{w.name} splits={sp}")
+        sc = scores.cpu().numpy().astype(np.float64)
+        for i, n in enumerate(lens):
+            rel = np.linalg.norm(sc[i, :, :n] - refs_s[i]) / np.linalg.norm(refs_s[i])
+            assert rel <= 1e-5, f"{w.name} lane {i}: scores rel L2 {rel:.2e}"

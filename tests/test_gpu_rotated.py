@@ -158,3 +158,24 @@ def test_rotated_refusals():
     with pytest.raises(kvq.KvError) as ei:
         pool.prefill(0, seq, 64, queries(TINY, 0, 64, stream=1).cuda(), TINY.sm_scale)
     assert ei.value.name == "KV_ERR_FORMAT"
+
+
+@pytest.mark.parametrize("w", [Workload(94, "rotated, group 8, D=128", "q2r", 1, 2, 128, 16, 2, 300),
+                               Workload(94, "rotated, group 1, D=256", "q2r", 1, 4, 256, 4, 2, 300)],
+                         ids=lambda w: w.name)
+def test_rotated_decode_other_groups(w):
+    need_gpu()
+    lens = [300, 97]
+    n_pages = sum(-(-n // 64) for n in lens)
+    pool, mem = make_pool(w, n_pages, _fmt())
+    seqs, refs = [], []
+    q = queries(w, 0, len(lens))
+    for i, n in enumerate(lens):
+        seqs.append(pool.reserve(n))
+        k, v = kv_rows(w, 0, i, n)
+        pool.append(0, [seqs[-1]], [0], [n], k.cuda(), v.cuda())
+        K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
+        refs.append(attention.decode(q[i].float().numpy(), K, V, w.sm_scale))
+    out = pool.decode(0, seqs, lens, q.cuda(), w.sm_scale, n_splits=2)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), np.stack(refs), w.name)
