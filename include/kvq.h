@@ -206,7 +206,8 @@ kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t
  * far; the same holds for KV_FMT_Q2_WINDOW, whose append also copies the
  * rows of the last page it reaches into the sequence's exact window.  No
  * append may write into a page that two sequences hold (kv_seq_fork).  The
- * sequences of one call must be distinct.  Errors: KV_ERR_ARG (including a
+ * sequences of one call must be distinct; d_k and d_v may be NULL when no
+ * entry appends a token.  Errors: KV_ERR_ARG (including a
  * non-sequential 8-bit or window append), KV_ERR_BOUND (a position beyond
  * the reserved bound; nothing is written), KV_ERR_UNSUPPORTED (more than
  * KV_MAX_BATCH entries), KV_ERR_DEVICE. */

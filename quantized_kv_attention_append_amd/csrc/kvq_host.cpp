@@ -455,7 +455,7 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
     if (n < 0) return fail(KV_ERR_ARG, "negative batch size");
     if (n == 0) return KV_OK;
     if (n > KV_MAX_BATCH) return fail(KV_ERR_UNSUPPORTED, "batch of %d exceeds KV_MAX_BATCH (%d)", n, KV_MAX_BATCH);
-    if (!seqs || !start_pos || !n_new || !d_k || !d_v) return fail(KV_ERR_ARG, "NULL argument");
+    if (!seqs || !start_pos || !n_new) return fail(KV_ERR_ARG, "NULL argument");
     if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
     BatchDesc bd;
     memset(&bd, 0, sizeof bd);
@@ -491,7 +491,8 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
         if (rows >= ((int64_t)1 << 31)) return fail(KV_ERR_UNSUPPORTED, "more than 2^31 rows in one append");
     }
     bd.work0[n] = (int32_t)work;
-    if (work == 0) return KV_OK;
+    if (work == 0) return KV_OK;  // no token to append: the row pointers are not read
+    if (!d_k || !d_v) return fail(KV_ERR_ARG, "NULL k or v rows");
     hipError_t e = hipSuccess;
     if (p->fmt == KV_FMT_Q2 || p->fmt == KV_FMT_Q2_ROT) {
         e = launch_append_q2(p->view(), layer, bd, (int)work, d_k, d_v, (hipStream_t)stream, p->fmt == KV_FMT_Q2_ROT);

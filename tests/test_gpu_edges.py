@@ -1,0 +1,68 @@
+"""GPU parity at the library's size limits and on empty inputs, 2-bit pools:
+a batch of KV_MAX_BATCH (128) sequences of ragged lengths appended in one
+call (entries with no tokens among them) and decoded in one call, at the
+library's split count and at the maximum of 256 splits; one entry more is
+refused; an append of no tokens changes no byte."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, pool as opool
+from synth import Workload, kv_rows, queries
+from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+# 1 layer x 2 KV heads x 128 dims, 8 query heads (group 4)
+W = Workload(95, "edges, D=128", "q2", 1, 2, 128, 8, 128, 300)
+
+
+def test_max_batch_ragged_and_max_splits():
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    B = 128
+    rng = np.random.default_rng(11)
+    lens = [int(x) for x in rng.integers(1, 300, size=B)]
+    n_pages = sum(-(-n // 64) for n in lens)
+    pool, mem = make_pool(W, n_pages, kvq.FMT_Q2, fill=0xFF, max_seqs=B)
+    seqs = [pool.reserve(n) for n in lens]
+    rows = [kv_rows(W, 0, i, n) for i, n in enumerate(lens)]
+    # first call: every entry, some with no tokens (their first part is empty)
+    first = [0 if i % 7 == 0 else min(n, 40) for i, n in enumerate(lens)]
+    pool.append(0, seqs, [0] * B, first, torch.cat([rows[i][0][:first[i]] for i in range(B)]).cuda(),
+                torch.cat([rows[i][1][:first[i]] for i in range(B)]).cuda())
+    rest = [n - f for n, f in zip(lens, first)]
+    pool.append(0, seqs, first, rest, torch.cat([rows[i][0][first[i]:] for i in range(B)]).cuda(),
+                torch.cat([rows[i][1][first[i]:] for i in range(B)]).cuda())
+    q = queries(W, 0, B)
+    refs = []
+    for i in range(B):
+        K, V = opool.dequantized_rows("q2", rows[i][0].float().numpy(), rows[i][1].float().numpy())
+        refs.append(attention.decode(q[i].float().numpy(), K, V, W.sm_scale))
+    refs = np.stack(refs)
+    for sp in (0, 256):
+        ws = torch.full((pool.workspace_bytes(kvq.OP_DECODE, B, sp),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = pool.decode(0, seqs, lens, q.cuda(), W.sm_scale, n_splits=sp, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), refs, f"128 ragged lanes, splits={sp or pool.decode_splits(lens)}")
+    with pytest.raises(kvq.KvError) as ei:
+        pool.decode(0, seqs + [seqs[0]], lens + [lens[0]], torch.cat([q, q[:1]]).cuda(), W.sm_scale)
+    assert ei.value.name == "KV_ERR_UNSUPPORTED"
+
+
+def test_empty_append_changes_nothing():
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    pool, mem = make_pool(W, 4, kvq.FMT_Q2, fill=0x5A)
+    seq = pool.reserve(200)
+    k, v = kv_rows(W, 0, 0, 100)
+    pool.append(0, [seq], [0], [100], k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    before = mem.cpu().clone()
+    empty = torch.empty((0, W.n_kv_heads, W.head_dim), dtype=torch.bfloat16, device="cuda")
+    pool.append(0, [seq], [100], [0], empty, empty)
+    pool.append(0, [seq], [37], [0], empty, empty)
+    torch.cuda.synchronize()
+    assert torch.equal(mem.cpu(), before)
+    say("empty appends: no byte changed")
