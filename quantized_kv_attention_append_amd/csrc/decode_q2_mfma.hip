@@ -47,6 +47,8 @@
 //       64(g/2) + 16(t%4) + 8(g%2) + 4u + 2x + t/4 at k = 32g + 16u + 8x + t,
 //       and a per-wave LDS transpose moves each lane's digit bytes of its
 //       eight tokens to the lanes whose k-ranges hold those tokens.
+#include <type_traits>
+
 #include "decode_common.h"
 
 namespace kvq {
@@ -331,20 +333,26 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
     }
 }
 
-template <int D, bool SCORES, bool ROT>
-__global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
-                                                             const uint16_t* __restrict__ q, float sm, int splits,
-                                                             float* __restrict__ ws, float* __restrict__ out,
-                                                             float* __restrict__ scores, int64_t sstride, int h0,
-                                                             int nh) {
+template <int D, bool SCORES, bool ROT, bool GENERAL>
+__device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int layer, const BatchDesc& bd,
+                                                    const uint16_t* __restrict__ q, float sm, int splits,
+                                                    float* __restrict__ ws, float* __restrict__ scores,
+                                                    int64_t sstride, int h0, int nh) {
     // The kernel takes four query heads of a KV head's group at a time: heads
-    // h0 .. h0 + nh - 1 (nh <= 4; rows of the missing heads are zero queries
-    // whose results are dropped).
+    // h0 .. h0 + nh - 1.  Without GENERAL the group is exactly these four
+    // (group 4, h0 = 0, nh = 4, all known when compiling); with it the group
+    // size is the pool's, and when nh < 4 the rows of the missing heads are
+    // zero queries whose results are dropped.
     constexpr int G = 4;
     constexpr int NC = D / 128;  // k-chunks of the q.k product
     constexpr int NB = D / 16;   // 16-dim blocks of the p.v product
-    const int Hkv = pv.Hkv, Hq = pv.Hq, Gq = Hq / Hkv;  // Gq: the pool's GQA group
+    const int Hkv = pv.Hkv, Hq = pv.Hq;
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
+    const int Gq = GENERAL ? Hq / Hkv : G;  // the pool's GQA group
+    if constexpr (!GENERAL) {
+        h0 = 0;
+        nh = G;
+    }
     const int64_t head0 = (int64_t)e * Hq + (int64_t)g * Gq + h0;  // first query row of this launch
     const int ctx = bd.pos[e];
     int pg0, pg1;
@@ -362,7 +370,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
     const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
     const int n_pages = (ctx + PAGE - 1) / PAGE;
-    float* srow = scores && grp < nh ? scores + (head0 + grp) * sstride : nullptr;
+    float* srow = scores && (!GENERAL || grp < nh) ? scores + (head0 + grp) * sstride : nullptr;
     WaveLds& lds = lds_s[wave];
 
     // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
@@ -408,7 +416,7 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
 #pragma unroll
         for (int i = 0; i < QPIECES; ++i) {  // piece p holds bf16 8p .. 8p + 7 of the four rows
             const int p = l + 64 * i;
-            qraw[i] = 8 * p < nh * D ? qsrc[p] : make_uint4(0u, 0u, 0u, 0u);
+            qraw[i] = !GENERAL || 8 * p < nh * D ? qsrc[p] : make_uint4(0u, 0u, 0u, 0u);
         }
     }
     if (TF > 0) {
@@ -565,13 +573,32 @@ __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int la
             float o = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) o += f[v] * (o_s[v][h][d] + ml_s[v][h][2]);
-            if (h < nh) w.o[row * D + d] = o;
+            if (!GENERAL || h < nh) w.o[row * D + d] = o;
         }
-        if (l == 0 && h < nh) {
+        if (l == 0 && (!GENERAL || h < nh)) {
             w.ml[2 * row] = M;
             w.ml[2 * row + 1] = lsum;
         }
     }
+}
+
+// Group 4: the four heads of each KV head's group in one launch.
+template <int D, bool SCORES, bool ROT>
+__global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                             const uint16_t* __restrict__ q, float sm, int splits,
+                                                             float* __restrict__ ws, float* __restrict__ scores,
+                                                             int64_t sstride) {
+    decode_q2_mfma_body<D, SCORES, ROT, false>(pv, layer, bd, q, sm, splits, ws, scores, sstride, 0, 4);
+}
+
+// Other groups: heads h0 .. h0 + nh - 1 of each KV head's group.
+template <int D, bool SCORES, bool ROT>
+__global__ __launch_bounds__(256) void decode_q2_mfma_group_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                                   const uint16_t* __restrict__ q, float sm,
+                                                                   int splits, float* __restrict__ ws,
+                                                                   float* __restrict__ scores, int64_t sstride,
+                                                                   int h0, int nh) {
+    decode_q2_mfma_body<D, SCORES, ROT, true>(pv, layer, bd, q, sm, splits, ws, scores, sstride, h0, nh);
 }
 
 hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
@@ -579,24 +606,39 @@ hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchD
     dim3 grid(bd.n * pv.Hkv, splits);
     const float smk = rot ? sm / (float)pv.D : sm;  // H q . H k = D q . k
     const int Gq = pv.Hq / pv.Hkv;
-    // groups of up to four query heads per launch: one launch for G <= 4, two for G = 8
+    using D128 = std::integral_constant<int, 128>;
+    using D256 = std::integral_constant<int, 256>;
+    if (Gq == 4) {
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, scores, sstride);
+        };
+        auto pick = [&](auto d_tag) {
+            constexpr int DD = decltype(d_tag)::value;
+            if (rot)
+                scores ? go(decode_q2_mfma_kernel<DD, true, true>) : go(decode_q2_mfma_kernel<DD, false, true>);
+            else
+                scores ? go(decode_q2_mfma_kernel<DD, true, false>) : go(decode_q2_mfma_kernel<DD, false, false>);
+        };
+        pv.D == 256 ? pick(D256{}) : pick(D128{});
+        return hipGetLastError();
+    }
+    // other groups: up to four query heads per launch (two launches for group 8)
     for (int h0 = 0; h0 < Gq; h0 += 4) {
         const int nh = Gq - h0 < 4 ? Gq - h0 : 4;
         auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, nullptr, scores,
-                               sstride, h0, nh);
+            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, scores, sstride, h0,
+                               nh);
         };
-        if (pv.D == 256) {
+        auto pick = [&](auto d_tag) {
+            constexpr int DD = decltype(d_tag)::value;
             if (rot)
-                scores ? go(decode_q2_mfma_kernel<256, true, true>) : go(decode_q2_mfma_kernel<256, false, true>);
+                scores ? go(decode_q2_mfma_group_kernel<DD, true, true>)
+                       : go(decode_q2_mfma_group_kernel<DD, false, true>);
             else
-                scores ? go(decode_q2_mfma_kernel<256, true, false>) : go(decode_q2_mfma_kernel<256, false, false>);
-        } else {
-            if (rot)
-                scores ? go(decode_q2_mfma_kernel<128, true, true>) : go(decode_q2_mfma_kernel<128, false, true>);
-            else
-                scores ? go(decode_q2_mfma_kernel<128, true, false>) : go(decode_q2_mfma_kernel<128, false, false>);
-        }
+                scores ? go(decode_q2_mfma_group_kernel<DD, true, false>)
+                       : go(decode_q2_mfma_group_kernel<DD, false, false>);
+        };
+        pv.D == 256 ? pick(D256{}) : pick(D128{});
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
