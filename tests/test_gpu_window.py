@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 TINY = WORKLOADS["tiny"]
 PREFILL = WORKLOADS["prefill"]
-# group 2 at 128 dims (the vector-ALU split kernel), 2 layers
+# group 2 at 128 dims (the matrix-core split kernel with two empty query rows), 2 layers
 G2_128 = Workload(97, "group 2, D=128, window", "q2w", 2, 2, 128, 4, 3, 400)
 NAN_FILL = 0xFF
 
