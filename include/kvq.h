@@ -35,8 +35,12 @@
  *    (reservations, block tables) is updated synchronously.
  *  - A kv_pool is not thread-safe: calls on one pool must not overlap.
  *  - Token positions and lengths are < 2^31; head_dim is 128 or 256; the GQA
- *    group G = n_q_heads / n_kv_heads must be 1, 2, 4 or 8.
+ *    group G = n_q_heads / n_kv_heads must be 1, 2, 4 or 8; n_layers is at
+ *    most KV_MAX_LAYERS and n_kv_heads at most KV_MAX_KV_HEADS
+ *    (KV_ERR_UNSUPPORTED otherwise).
  *  - A batch holds at most KV_MAX_BATCH sequences per call.
+ *  - No C++ exception leaves the library: a failed host allocation returns
+ *    KV_ERR_DEVICE, like a failed HIP call, with the pool unchanged.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -50,6 +54,8 @@ extern "C" {
 
 #define KV_PAGE_TOKENS 64
 #define KV_MAX_BATCH 128
+#define KV_MAX_LAYERS 1024
+#define KV_MAX_KV_HEADS 256
 
 typedef void* kv_stream_t; /* hipStream_t */
 typedef struct kv_pool kv_pool;
@@ -103,7 +109,7 @@ typedef enum {
     KV_ERR_FORMAT = -4,      /* operation does not match the pool's format */
     KV_ERR_UNSUPPORTED = -5, /* geometry / batch size this library does not implement */
     KV_ERR_WORKSPACE = -6,   /* workspace null or smaller than kv_workspace_bytes() */
-    KV_ERR_DEVICE = -7       /* a HIP runtime call failed */
+    KV_ERR_DEVICE = -7       /* a HIP runtime call (or a host allocation) failed */
 } kv_status;
 
 typedef struct {

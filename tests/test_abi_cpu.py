@@ -48,6 +48,8 @@ def test_token_bytes_from_the_library():
     ((16, 4, 256, 64), 1, "KV_ERR_UNSUPPORTED"),   # group 16
     ((0, 4, 256, 16), 1, "KV_ERR_ARG"),
     ((16, 4, 256, 16), 6, "KV_ERR_FORMAT"),       # no format 6
+    ((1025, 4, 256, 16), 1, "KV_ERR_UNSUPPORTED"),  # above KV_MAX_LAYERS
+    ((16, 257, 256, 257), 1, "KV_ERR_UNSUPPORTED"),  # above KV_MAX_KV_HEADS
 ])
 def test_bad_geometry_is_refused(geom, fmt, status):
     import quantized_kv_attention_append_amd as kvq
@@ -55,3 +57,16 @@ def test_bad_geometry_is_refused(geom, fmt, status):
         kvq.token_bytes(geom, fmt)
     assert ei.value.name == status
     assert status in str(ei.value)
+
+
+def test_limits_and_byte_count_overflow():
+    """The largest geometry the header allows still gives a byte count, and a
+    token count whose bytes overflow int64 is refused instead of wrapping."""
+    import quantized_kv_attention_append_amd as kvq
+    tb, pb = kvq.token_bytes((1024, 256, 256, 2048), kvq.FMT_BF16)
+    assert tb == 1024 * 256 * 2 * 256 * 2 and pb == 64 * tb
+    assert kvq.pool_bytes_for_tokens((1024, 256, 256, 2048), kvq.FMT_BF16, 64) == pb
+    with pytest.raises(kvq.KvError) as ei:
+        kvq.pool_bytes_for_tokens((16, 4, 256, 16), kvq.FMT_Q2, 2 ** 62)
+    assert ei.value.name == "KV_ERR_ARG"
+    assert kvq.pool_bytes_for_tokens((16, 4, 256, 16), kvq.FMT_Q2, 2 ** 40) == 2 ** 40 * 9216

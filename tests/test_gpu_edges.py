@@ -66,3 +66,50 @@ def test_empty_append_changes_nothing():
     torch.cuda.synchronize()
     assert torch.equal(mem.cpu(), before)
     say("empty appends: no byte changed")
+
+
+def test_free_list_after_explicit_reservations():
+    """Pages reserved by explicit id, released, then taken from the free list
+    (also through a fork) come back once each: a sequence that takes the whole
+    pool holds every page exactly once, and its tokens decode as the oracle's
+    over the same block table (two logical pages on one physical page would
+    overwrite each other)."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    n_pages = 8
+    pool, mem = make_pool(W, n_pages, kvq.FMT_Q2, fill=0xFF)
+    for _ in range(3):   # explicit reservations and releases, the last page of the stack included
+        a = pool.reserve(128, pages=[0, 3])
+        b = pool.reserve(64, pages=[7])
+        pool.release(a)
+        pool.release(b)
+    k, v = kv_rows(W, 0, 0, 150)
+    parent = pool.reserve(150, pages=[0, 1, 2])
+    pool.append(0, [parent], [0], [150], k.cuda(), v.cuda())
+    child = pool.fork(parent, 150, 300)          # shares pages 0, 1; copies page 2 into a free-list page
+    assert len(set(pool.pages(child))) == 5
+    pool.release(parent)
+    pool.release(child)
+    assert pool.stats()["free_pages"] == n_pages
+    total = 64 * n_pages
+    seq = pool.reserve(total)
+    bt = np.array(pool.pages(seq), np.int32)
+    say(f"whole-pool reservation after explicit ones: pages {list(bt)}")
+    assert sorted(bt.tolist()) == list(range(n_pages)), "every page exactly once"
+    assert pool.stats()["free_pages"] == 0
+    with pytest.raises(kvq.KvError) as ei:
+        pool.reserve(1)
+    assert ei.value.name == "KV_ERR_NO_SPACE"
+    k, v = kv_rows(W, 0, 1, total)
+    pool.append(0, [seq], [0], [total], k.cuda(), v.cuda())
+    op = opool.OraclePool("q2", 1, W.n_kv_heads, W.head_dim, n_pages, fill=0xFF)
+    op.append(0, 0, bt, 0, k.float().numpy(), v.float().numpy())
+    torch.cuda.synchronize()
+    got = mem.cpu().numpy().reshape(n_pages, -1)
+    assert np.count_nonzero(got != op.data) == 0
+    q = queries(W, 0, 1)
+    K, V = op.gather(0, bt, total)
+    ref = attention.decode(q[0].float().numpy(), K, V, W.sm_scale)
+    out = pool.decode(0, [seq], [total], q.cuda(), W.sm_scale)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy()[0], ref, "whole pool after explicit reservations")
