@@ -536,6 +536,8 @@ kv_status kv_append_quant(kv_pool* p, int32_t layer, int32_t n, const int32_t* s
         int64_t rows = 0, work = 0;
         for (int i = 0; i < n; ++i) {
             if (n_new[i] < 0 || start_pos[i] < 0) return fail(KV_ERR_ARG, "entry %d: negative position or count", i);
+            if (start_pos[i] > INT32_MAX)
+                return fail(KV_ERR_BOUND, "entry %d: position %lld is not below 2^31", i, (long long)start_pos[i]);
             kv_status s = check_seq(p, seqs[i], start_pos[i] + n_new[i], "append");
             if (s != KV_OK) return s;
             if (sequential_appends(p->fmt) && start_pos[i] != p->seqs[(size_t)seqs[i]].layer_appended[(size_t)layer])
@@ -731,6 +733,7 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
         if (p->fmt == KV_FMT_Q8 || p->fmt == KV_FMT_Q2_ROT)
             return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit, bf16 and 2-bit window formats only");
         if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
+        if (q_start > INT32_MAX) return fail(KV_ERR_BOUND, "q_start %lld is not below 2^31", (long long)q_start);
         if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
         if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
         kv_status st = check_seq(p, seq, q_start + n_q, "prefill");

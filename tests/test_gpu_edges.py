@@ -113,3 +113,24 @@ def test_free_list_after_explicit_reservations():
     out = pool.decode(0, [seq], [total], q.cuda(), W.sm_scale)
     torch.cuda.synchronize()
     assert_close(out.cpu().numpy()[0], ref, "whole pool after explicit reservations")
+
+
+def test_positions_beyond_2_31_refused():
+    """Positions whose end would overflow are refused as out of bound before
+    any byte moves."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    pool, mem = make_pool(W, 2, kvq.FMT_Q2, fill=0x5A)
+    seq = pool.reserve(100)
+    k, v = kv_rows(W, 0, 0, 4)
+    torch.cuda.synchronize()
+    before = mem.cpu().clone()
+    for pos in (2 ** 31, 2 ** 63 - 2):
+        with pytest.raises(kvq.KvError) as ei:
+            pool.append(0, [seq], [pos], [4], k.cuda(), v.cuda())
+        assert ei.value.name == "KV_ERR_BOUND"
+        with pytest.raises(kvq.KvError) as ei:
+            pool.prefill(0, seq, pos, queries(W, 0, 4).cuda(), W.sm_scale)
+        assert ei.value.name == "KV_ERR_BOUND"
+    torch.cuda.synchronize()
+    assert torch.equal(mem.cpu(), before)
