@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size for counter passes (0 = none)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
-    ap.add_argument("--no-extra", action="store_true", help="skip the long-context and 8-bit decode legs")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long-context, 8-bit, bf16, window and rotated legs")
     return ap.parse_args()
 
 
@@ -282,7 +282,7 @@ def q8_leg(reps: int):
             "decode_us_per_layer_call": avg * 1e3, "bytes_per_call": alg,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "one kv_attn_decode call per layer: decode_q8_mfma_kernel<128, 4> then merge_splits_kernel"},
+                         "kernel": "one kv_attn_decode call per layer: decode_q8_mfma_kernel<128, 4> then merge_splits8_kernel"},
             "kv_tokens_per_s": tokens * w.n_layers / (avg * 1e-3 * w.n_layers),
             "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
@@ -387,7 +387,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                              "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256, false, true> "
-                                       "then merge_splits_kernel"},
+                                       "then merge_splits8_kernel"},
                 "graph_ms_per_step": graph_ms, "graph_identical_to_eager": same,
                 "kv_tokens_per_s": B * L * ctx / (graph_ms * 1e-3),
                 "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
@@ -413,7 +413,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     pf_tflops = flops / (pf[0] * 1e-3) / 1e12
     log(f"{name} prefill: {pf[0]:.3f} ms per call, {pf_tflops:.0f} TFLOP/s useful")
     kernel = ("one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then decode_window_merge_kernel<256>"
-              if window else "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then merge_splits_kernel")
+              if window else "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then merge_splits8_kernel")
     return {"workload": f"27B-geometry batched decode, {name}: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
                         "8 lanes x 40960 tokens", "pool_bytes": n_pages * pb, "splits": sp,
             "decode_us_per_call": avg_ms * 1e3, "bytes_per_call": alg,
@@ -467,6 +467,30 @@ def oracle_baseline(w, budget_s: float):
         "sample": f"{len(units)} (layer, lane) units of {ctx} tokens x 4 KV heads x 16 query heads "
                   f"(dequantize + fp64 softmax attention), {spent:.1f} s",
     }
+
+
+def platform_info() -> dict:
+    """Device, runtime versions and the current DPM clock levels from sysfs
+    (the files rocm-smi reads; None where unavailable)."""
+    import glob
+
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    clocks = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device"))[:16]:
+        cur = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur[name[-4:]] = next((l.split(":", 1)[1].replace("*", "").strip() for l in f if "*" in l), None)
+            except OSError:
+                pass
+        if cur:
+            clocks.append(cur)
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip": torch.version.hip, "torch": torch.__version__,
+            "clocks": clocks or None}
 
 
 def main():
@@ -656,7 +680,7 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
-            "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then merge_splits_kernel",
+            "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then merge_splits8_kernel",
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": avg_launch_ms * 1e3,
         },
@@ -671,6 +695,7 @@ def main():
         "q2_window": win,
         "q2_rotated": rot,
         "cpu_baseline": cpu,
+        "platform": platform_info(),
     }
     print(json.dumps(res), flush=True)
 

@@ -17,7 +17,7 @@
 // Context", section "The cliff is in the accumulator"), scores and maxima in
 // base-2 units.  The four waves of a workgroup take every fourth page of the
 // split, each with its own online softmax, and combine in LDS at the end; the
-// partials go to the workspace for merge_splits_kernel.
+// partials go to the workspace for the split merge kernels.
 #include <type_traits>
 
 #include "decode_common.h"

@@ -9,7 +9,7 @@
 // Decode: the 2-bit split kernel covers the tokens before the window; the
 // kernel here computes the window's (max, sum, output) for one (sequence,
 // query head) and merges it with the split partials in fp32, like
-// merge_splits_kernel.  Prefill: a window partial per (query, head) row of the
+// the split merge kernels.  Prefill: a window partial per (query, head) row of the
 // queries that see the window goes after the splits' partials in the
 // workspace, and the prefill merge adds it to those rows.
 // Scores and maxima are in base-2 units (s * log2 e), as in the split kernels.
@@ -109,7 +109,7 @@ __device__ __forceinline__ void window_reduce(WindowLds<D>& L, const uint8_t* bl
 }
 
 // Decode: one workgroup per (sequence, query head): the window's partial,
-// merged in fp32 with the split partials (the first U of them loaded before
+// merged in fp32 with the split partials (the first U slots loaded before
 // the window's reduction) into the output.
 template <int D>
 __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, int layer, BatchDesc bd,
@@ -129,13 +129,15 @@ __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, i
     window_issue<D>(L, blk, q + (int64_t)row * D, vrow);
     const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + (int64_t)row * splits;
     const float* o = ws + (int64_t)row * splits * D + d;
+    // every slot below `splits` lies inside the workspace, so these loads do
+    // not wait for the live split count; unwritten slots are selected away
     float2 m0[U];
     float v0[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const bool ok = u < live;
-        m0[u] = ok ? ml[u] : make_float2(-INFINITY, 0.f);
-        v0[u] = ok ? o[(int64_t)u * D] : 0.f;
+        const bool in = u < splits;
+        m0[u] = in ? ml[u] : make_float2(-INFINITY, 0.f);
+        v0[u] = in ? o[(int64_t)u * D] : 0.f;
     }
     float M, den, acc;
     window_reduce<D>(L, blk, vrow, nw, sm, scores ? scores + (int64_t)row * sstride + c : nullptr, M, den, acc);
@@ -146,9 +148,9 @@ __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, i
         float v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (p0 == 0) {
-                m[u] = m0[u];
-                v[u] = v0[u];
+            if (p0 == 0) {  // select, never multiply, so that an unwritten slot cannot leak in
+                m[u] = u < live ? m0[u] : make_float2(-INFINITY, 0.f);
+                v[u] = u < live ? v0[u] : 0.f;
             } else {
                 const bool ok = p0 + u < live;
                 m[u] = ok ? ml[p0 + u] : make_float2(-INFINITY, 0.f);
