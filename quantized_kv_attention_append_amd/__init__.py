@@ -58,14 +58,37 @@ def _stream(stream) -> C.c_void_p:
     return C.c_void_p(stream.cuda_stream)
 
 
-def _dev(t: torch.Tensor, dtype, name: str):
+def _dev(t: torch.Tensor, dtype, name: str, shape=None, device=None):
+    """Device pointer of a contiguous tensor, after the checks that keep the
+    kernels inside it: device, dtype, layout and (where the library takes no
+    size for it) shape."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
-    if t.dtype != dtype:
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the pool on {device}")
+    if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(t.shape)}")
     return C.c_void_p(t.data_ptr())
+
+
+# Pools released while the current stream is capturing a HIP graph: their
+# destruction frees device memory, which would invalidate the capture, so it
+# waits for the next release or pool creation outside a capture.
+_deferred = []
+
+
+def _capturing() -> bool:
+    return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+
+
+def _flush_deferred():
+    while _deferred and not _capturing():
+        h, _memory = _deferred.pop()
+        check(lib.kv_pool_destroy(h))
 
 
 class Pool:
@@ -75,12 +98,16 @@ class Pool:
                  max_seq_tokens: int = 1 << 20, memory: Optional[torch.Tensor] = None):
         self.geom = _geom(geom)
         self.fmt = fmt
+        _flush_deferred()
         self._memory = memory  # keeps caller memory alive
+        self.device = torch.device("cuda", torch.cuda.current_device())  # the library allocates here
         h = C.c_void_p()
         d_mem = C.c_void_p(0)
         if memory is not None:
             if memory.dtype != torch.uint8 or not memory.is_cuda or not memory.is_contiguous():
                 raise TypeError("memory must be a contiguous uint8 device tensor")
+            if memory.device != self.device:
+                raise ValueError(f"memory is on {memory.device}, the current device is {self.device}")
             if memory.numel() < budget_bytes:
                 raise ValueError("memory is smaller than the budget")
             d_mem = C.c_void_p(memory.data_ptr())
@@ -90,9 +117,17 @@ class Pool:
 
     # ---------------------------------------------------------- lifetime --
     def close(self):
-        if getattr(self, "_h", None):
-            check(lib.kv_pool_destroy(self._h))
+        """Destroys the pool; inside a HIP graph capture on the current stream
+        (for instance when the garbage collector drops a pool there) the
+        destruction is deferred until a later release or pool creation."""
+        h = getattr(self, "_h", None)
+        if h:
             self._h = None
+            if _capturing():
+                _deferred.append((h, self._memory))
+                return
+            _flush_deferred()
+            check(lib.kv_pool_destroy(h))
 
     def __del__(self):
         try:
@@ -160,7 +195,8 @@ class Pool:
             if tuple(t.shape) != (rows, g.n_kv_heads, g.head_dim):
                 raise ValueError(f"{name} must be [{rows}][{g.n_kv_heads}][{g.head_dim}], got {tuple(t.shape)}")
         check(lib.kv_append_quant(self._h, int(layer), n, _i32(seqs), _i64(start_pos), _i32(n_new),
-                                  _dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"), _stream(stream)))
+                                  _dev(k, torch.bfloat16, "k", device=self.device),
+                                  _dev(v, torch.bfloat16, "v", device=self.device), _stream(stream)))
 
     def decode(self, layer: int, seqs, ctx_len, q: torch.Tensor, sm_scale: float, n_splits: int = 0,
                ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
@@ -178,11 +214,15 @@ class Pool:
             n_splits = sp
         sc_ptr, sc_stride = C.c_void_p(0), 0
         if scores is not None:
-            sc_ptr = _dev(scores, torch.float32, "scores")
+            if scores.dim() != 3:
+                raise ValueError("scores must be [n][Hq][stride]")
             sc_stride = scores.shape[-1]
-        check(lib.kv_attn_decode(self._h, int(layer), n, _i32(seqs), _i64(ctx_len), _dev(q, torch.bfloat16, "q"),
-                                 float(sm_scale), int(n_splits), C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
-                                 _dev(out, torch.float32, "out"), sc_ptr, int(sc_stride), _stream(stream)))
+            sc_ptr = _dev(scores, torch.float32, "scores", (n, g.n_q_heads, sc_stride), self.device)
+        check(lib.kv_attn_decode(self._h, int(layer), n, _i32(seqs), _i64(ctx_len),
+                                 _dev(q, torch.bfloat16, "q", device=self.device), float(sm_scale), int(n_splits),
+                                 _dev(ws, None, "ws", device=self.device), ws.numel() * ws.element_size(),
+                                 _dev(out, torch.float32, "out", (n, g.n_q_heads, g.head_dim), self.device), sc_ptr,
+                                 int(sc_stride), _stream(stream)))
         return out
 
     def prefill(self, layer: int, seq: int, q_start: int, q: torch.Tensor, sm_scale: float, n_splits: int = 0,
@@ -196,15 +236,18 @@ class Pool:
             out = torch.empty((n_q, g.n_q_heads, g.head_dim), dtype=torch.float32, device=q.device)
         if ws is None:
             ws = torch.empty(self.workspace_bytes(OP_PREFILL, n_q, n_splits), dtype=torch.uint8, device=q.device)
-        check(lib.kv_attn_prefill(self._h, int(layer), int(seq), int(q_start), int(n_q), _dev(q, torch.bfloat16, "q"),
-                                  float(sm_scale), int(n_splits), C.c_void_p(ws.data_ptr()),
-                                  ws.numel() * ws.element_size(), _dev(out, torch.float32, "out"), _stream(stream)))
+        check(lib.kv_attn_prefill(self._h, int(layer), int(seq), int(q_start), int(n_q),
+                                  _dev(q, torch.bfloat16, "q", device=self.device), float(sm_scale), int(n_splits),
+                                  _dev(ws, None, "ws", device=self.device), ws.numel() * ws.element_size(),
+                                  _dev(out, torch.float32, "out", (n_q, g.n_q_heads, g.head_dim), self.device),
+                                  _stream(stream)))
         return out
 
     def dequant_page(self, page: int, layer: int, head: int, kv: int, out: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
         if out is None:
-            out = torch.empty((PAGE, self.geom.head_dim), dtype=torch.float32, device="cuda")
-        check(lib.kv_dequant_page(self._h, int(page), int(layer), int(head), int(kv), _dev(out, torch.float32, "out"),
+            out = torch.empty((PAGE, self.geom.head_dim), dtype=torch.float32, device=self.device)
+        check(lib.kv_dequant_page(self._h, int(page), int(layer), int(head), int(kv),
+                                  _dev(out, torch.float32, "out", (PAGE, self.geom.head_dim), self.device),
                                   _stream(stream)))
         return out

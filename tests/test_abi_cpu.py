@@ -70,3 +70,17 @@ def test_limits_and_byte_count_overflow():
         kvq.pool_bytes_for_tokens((16, 4, 256, 16), kvq.FMT_Q2, 2 ** 62)
     assert ei.value.name == "KV_ERR_ARG"
     assert kvq.pool_bytes_for_tokens((16, 4, 256, 16), kvq.FMT_Q2, 2 ** 40) == 2 ** 40 * 9216
+
+
+def test_binding_refuses_host_tensors():
+    """A host tensor never reaches the library as a device pointer: the
+    binding raises before the call, since a kernel reading host memory
+    through such a pointer would fault."""
+    import torch
+    from quantized_kv_attention_append_amd import _dev
+    for t, dtype in ((torch.zeros(4), torch.float32), (torch.zeros(4, dtype=torch.uint8), None),
+                     (torch.zeros(2, 3, dtype=torch.bfloat16), torch.bfloat16)):
+        with pytest.raises(TypeError):
+            _dev(t, dtype, "x")
+    with pytest.raises(TypeError):
+        _dev(None, torch.float32, "x")

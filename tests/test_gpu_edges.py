@@ -12,6 +12,8 @@ from oracle import attention, pool as opool
 from synth import Workload, kv_rows, queries
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
 
+PAGE_TOKENS = 64
+
 pytestmark = pytest.mark.gpu
 
 # 1 layer x 2 KV heads x 128 dims, 8 query heads (group 4)
@@ -134,3 +136,79 @@ def test_positions_beyond_2_31_refused():
         assert ei.value.name == "KV_ERR_BOUND"
     torch.cuda.synchronize()
     assert torch.equal(mem.cpu(), before)
+
+
+def test_binding_refuses_mismatched_buffers():
+    """The binding checks what the C ABI takes no size for (out, scores) and
+    where every buffer lives before anything is launched."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    pool, mem = make_pool(W, 4, kvq.FMT_Q2, fill=0x5A)
+    seq = pool.reserve(200)
+    k, v = kv_rows(W, 0, 0, 100)
+    pool.append(0, [seq], [0], [100], k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    before = mem.cpu().clone()
+    q = queries(W, 0, 1).cuda()
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, 1, 2), dtype=torch.uint8, device="cuda")
+    bad = [
+        dict(ws=ws.cpu()),                                                   # host workspace
+        dict(ws=ws, out=torch.empty((1, W.n_q_heads, W.head_dim - 1), device="cuda")),  # short out
+        dict(ws=ws, out=torch.empty((1, W.n_q_heads, W.head_dim), device="cuda")[:, ::2]),  # strided
+        dict(ws=ws, scores=torch.empty((1, W.n_q_heads - 1, 100), device="cuda")),    # too few score rows
+        dict(ws=ws, scores=torch.empty((W.n_q_heads, 100), device="cuda")),           # not [n][Hq][stride]
+    ]
+    for kw in bad:
+        with pytest.raises((TypeError, ValueError)):
+            pool.decode(0, [seq], [100], q, W.sm_scale, n_splits=2, **kw)
+    with pytest.raises(TypeError):
+        pool.decode(0, [seq], [100], q.cpu(), W.sm_scale)                    # host query
+    with pytest.raises(TypeError):
+        pool.append(0, [seq], [100], [4], k[:4], v[:4])                      # host rows
+    with pytest.raises(ValueError):
+        pool.prefill(0, seq, 96, queries(W, 0, 4, stream=1).cuda(), W.sm_scale,
+                     out=torch.empty((3, W.n_q_heads, W.head_dim), device="cuda"))
+    with pytest.raises(ValueError):
+        pool.dequant_page(0, 0, 0, 0, out=torch.empty((PAGE_TOKENS, W.head_dim + 1), device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(mem.cpu(), before)
+    say("binding refusals: no byte changed")
+
+
+def test_pool_dropped_inside_a_graph_capture():
+    """A pool dropped while a HIP graph is captured on the current stream (as
+    the garbage collector may do at any allocation) neither breaks the capture
+    nor leaks: its destruction waits for the next pool creation outside it."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    pool, mem = make_pool(W, 4, kvq.FMT_Q2)
+    seq = pool.reserve(128)
+    k, v = kv_rows(W, 0, 0, 100)
+    pool.append(0, [seq], [0], [100], k.cuda(), v.cuda())
+    q = queries(W, 0, 1).cuda()
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, 1, 2), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, W.n_q_heads, W.head_dim), dtype=torch.float32, device="cuda")
+    pool.decode(0, [seq], [100], q, W.sm_scale, n_splits=2, ws=ws, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    doomed, _ = make_pool(W, 2, kvq.FMT_Q2)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pool.decode(0, [seq], [100], q, W.sm_scale, n_splits=2, ws=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        pool.decode(0, [seq], [100], q, W.sm_scale, n_splits=2, ws=ws, out=out)
+        del doomed                                   # destroyed here: deferred
+    assert len(kvq._deferred) == 1
+    for _ in range(2):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+    fresh, _ = make_pool(W, 2, kvq.FMT_Q2)          # outside the capture: the deferred pool goes
+    assert not kvq._deferred
+    fresh.close()
+    say("pool dropped inside a capture: capture intact, destroyed afterwards")
