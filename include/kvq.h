@@ -151,7 +151,8 @@ kv_status kv_pool_bytes_for_tokens(const kv_geom* geom, kv_format fmt, int64_t t
 kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int32_t max_seqs,
                          int64_t max_seq_tokens, void* d_mem, kv_pool** out);
 
-/* Destroy a pool; frees only memory the library allocated. */
+/* Destroy a pool; frees only memory the library allocated (with hipFree, so
+ * not while a HIP graph capture is active: that would invalidate it). */
 kv_status kv_pool_destroy(kv_pool* pool);
 
 kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);

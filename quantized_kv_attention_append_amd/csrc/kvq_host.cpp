@@ -504,8 +504,8 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 // least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
 // at least that many workgroups, and splits of about sixteen page pairs of the
 // longest sequence (eight pages per wavefront), since several of its smaller
-// workgroups share a compute unit (measured on 24 lanes of 16..124 pages:
-// 4 splits 67 us a layer, 2 splits 88 us, 8 splits 71 us).
+// workgroups share a compute unit (measured on 24 lanes of 16..124 pages, us
+// a layer call: 2 splits 88, 3 71, 4 67, 5 81, 6 83, 7 77, 8 71).
 int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     int64_t max_pages = 1;
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
