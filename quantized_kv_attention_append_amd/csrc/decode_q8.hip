@@ -19,7 +19,7 @@
 //   softmax: wave j % 4 takes heads j;
 //   p.v:     thread (d, half) takes dim d over tokens [32 half, 32 half + 32)
 //            (D = 128) or all 64 tokens (D = 256) for every head.
-// Partial (m, l, o) go to the workspace; merge_splits8_kernel or merge_splits32_kernel merges them.
+// Partial (m, l, o) go to the workspace; merge_splits8_kernel or merge_splits_wide_kernel merges them.
 #include <type_traits>
 
 #include "decode_common.h"
