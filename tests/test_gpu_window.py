@@ -210,3 +210,20 @@ def test_window_refusals_before_any_byte_moves():
     assert ei.value.name == "KV_ERR_WORKSPACE"
     torch.cuda.synchronize()
     assert torch.equal(mem.cpu(), before)
+
+
+@pytest.mark.parametrize("ctx_off", [0, 1, 70])
+def test_window_decode_many_splits(ctx_off):
+    """More than 8 live splits (20 and 64): the window merge folds the split
+    partials in several groups after the window's own partial; the context
+    ends at the last token, one short of it, or before the window."""
+    need_gpu()
+    total = 5000
+    n_pages = -(-total // 64) + 1
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages, salt=7)[:-1]
+    seq = pool.reserve(total, pages=bt)
+    k, v = kv_rows(TINY, 0, 0, total)
+    op = opool.OraclePool("q2w", 1, 4, 256, n_pages, fill=NAN_FILL)
+    _append_both(pool, op, 0, seq, 0, bt, k, v, (2000, 1999, 1001))
+    _decode_check(pool, op, TINY, 0, seq, 0, bt, total - ctx_off, [20, 64], f"window many splits, ctx={total - ctx_off}")
