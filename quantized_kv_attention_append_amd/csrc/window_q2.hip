@@ -109,14 +109,20 @@ __device__ __forceinline__ void window_reduce(WindowLds<D>& L, const uint8_t* bl
 }
 
 // Decode: one workgroup per (sequence, query head): the window's partial,
-// merged in fp32 with the split partials (the first U slots loaded before
-// the window's reduction) into the output.
-template <int D>
+// merged in fp32 with the split partials into the output.  Up to 8 splits:
+// the split partials are loaded before the window's reduction and folded in
+// one group.  More (WIDE): groups of 64 splits, lane t of each wave holding
+// split p0 + t's (max, sum), reduced across the wave, and each thread folding
+// its dim's 64 partial outputs with weights passed through the wave's row of
+// LDS; the first group is loaded before the window's reduction.  Only slots
+// below `splits` (inside the workspace) are loaded, and slots of splits that
+// hold no page (never written in this call) are selected away.
+template <int D, bool WIDE>
 __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                   const uint16_t* __restrict__ q, float sm, int splits,
                                                                   const float* __restrict__ ws, float* __restrict__ out,
                                                                   float* __restrict__ scores, int64_t sstride) {
-    constexpr int U = 8;
+    constexpr int U = WIDE ? 64 : 8;
     const int row = blockIdx.x;  // e * Hq + h
     const int Hq = pv.Hq, e = row / Hq, h = row % Hq, g = h / (Hq / pv.Hkv);
     const int d = threadIdx.x;
@@ -129,47 +135,78 @@ __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, i
     window_issue<D>(L, blk, q + (int64_t)row * D, vrow);
     const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + (int64_t)row * splits;
     const float* o = ws + (int64_t)row * splits * D + d;
-    // every slot below `splits` lies inside the workspace, so these loads do
-    // not wait for the live split count; unwritten slots are selected away
-    float2 m0[U];
-    float v0[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const bool in = u < splits;
-        m0[u] = in ? ml[u] : make_float2(-INFINITY, 0.f);
-        v0[u] = in ? o[(int64_t)u * D] : 0.f;
-    }
-    float M, den, acc;
-    window_reduce<D>(L, blk, vrow, nw, sm, scores ? scores + (int64_t)row * sstride + c : nullptr, M, den, acc);
+    float* srow = scores ? scores + (int64_t)row * sstride + c : nullptr;
+    float M, den, acc;  // running (max, sum, output) in base-2 units, the window's first
 
-    // ---- merge with the split partials (running max over groups of U splits) ----
-    for (int p0 = 0; p0 < live; p0 += U) {
+    if constexpr (WIDE) {
+        __shared__ __align__(16) float fs[D / 64][U];  // split weights, one row per wave
+        const int lane = d & 63, wave = d >> 6;
+        float2 mine;
+        float v[U];
+        auto load_group = [&](int p0) {
+            const int n = splits - p0;  // slots of this group inside the workspace
+            mine = lane < n ? ml[p0 + lane] : make_float2(-INFINITY, 0.f);
+            const float* base = o + (int64_t)p0 * D;
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = u < n ? base[u * D] : 0.f;
+        };
+        load_group(0);
+        window_reduce<D>(L, blk, vrow, nw, sm, srow, M, den, acc);
+        for (int p0 = 0; p0 < live; p0 += U) {  // the same trip count for every thread
+            if (p0 > 0) load_group(p0);
+            const bool mine_live = p0 + lane < live;
+            const float mx = mine_live ? mine.x : -INFINITY;
+            const float Mg = fmaxf(M, wave_max(mx));
+            const float r = exp2f(M - Mg);   // no window tokens (M = -inf): r = 0
+            const float f = exp2f(mx - Mg);  // 0 past the live splits
+            den = den * r + wave_sum(mine_live ? f * mine.y : 0.f);
+            acc *= r;
+            fs[wave][lane] = f;
+            __syncthreads();
+            const float4* f4 = reinterpret_cast<const float4*>(fs[wave]);
+#pragma unroll
+            for (int k = 0; k < U / 4; ++k) {
+                const float4 w = f4[k];
+                const float fw[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int u = 4 * k + i;
+                    acc = p0 + u < live ? fmaf(fw[i], v[u], acc) : acc;  // select: an unwritten slot may hold NaN
+                }
+            }
+            __syncthreads();  // the next group rewrites fs
+            M = Mg;
+        }
+    } else {
+        // every slot below `splits` lies inside the workspace, so these loads do
+        // not wait for the live split count; unwritten slots are selected away
         float2 m[U];
         float v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (p0 == 0) {  // select, never multiply, so that an unwritten slot cannot leak in
-                m[u] = u < live ? m0[u] : make_float2(-INFINITY, 0.f);
-                v[u] = u < live ? v0[u] : 0.f;
-            } else {
-                const bool ok = p0 + u < live;
-                m[u] = ok ? ml[p0 + u] : make_float2(-INFINITY, 0.f);
-                v[u] = ok ? o[(int64_t)(p0 + u) * D] : 0.f;
+            const bool in = u < splits;
+            m[u] = in ? ml[u] : make_float2(-INFINITY, 0.f);
+            v[u] = in ? o[(int64_t)u * D] : 0.f;
+        }
+        window_reduce<D>(L, blk, vrow, nw, sm, srow, M, den, acc);
+        if (live > 0) {
+            float Mg = M;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {  // select, never multiply, so that an unwritten slot cannot leak in
+                m[u] = u < live ? m[u] : make_float2(-INFINITY, 0.f);
+                v[u] = u < live ? v[u] : 0.f;
+                Mg = fmaxf(Mg, m[u].x);
+            }
+            const float r = exp2f(M - Mg);  // no window tokens (M = -inf): r = 0
+            den *= r;
+            acc *= r;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float f = exp2f(m[u].x - Mg);
+                den += f * m[u].y;
+                acc += f * v[u];
             }
         }
-        float Mg = M;
-#pragma unroll
-        for (int u = 0; u < U; ++u) Mg = fmaxf(Mg, m[u].x);
-        const float r = exp2f(M - Mg);  // M = -inf (no window tokens) on the first group: r = 0
-        den *= r;
-        acc *= r;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const float f = exp2f(m[u].x - Mg);
-            den += f * m[u].y;
-            acc += f * v[u];
-        }
-        M = Mg;
     }
     out[(int64_t)row * D + d] = acc / den;
 }
@@ -177,12 +214,14 @@ __global__ __launch_bounds__(256) void decode_window_merge_kernel(PoolView pv, i
 hipError_t launch_decode_window_merge(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q,
                                       float sm, int splits, const float* ws, float* out, float* scores,
                                       int64_t sstride, hipStream_t s) {
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3(bd.n * pv.Hq), dim3(pv.D), 0, s, pv, layer, bd, q, sm, splits, ws, out,
+                           scores, sstride);
+    };
     if (pv.D == 256)
-        hipLaunchKernelGGL(decode_window_merge_kernel<256>, dim3(bd.n * pv.Hq), dim3(256), 0, s, pv, layer, bd, q, sm,
-                           splits, ws, out, scores, sstride);
+        splits > 8 ? go(decode_window_merge_kernel<256, true>) : go(decode_window_merge_kernel<256, false>);
     else
-        hipLaunchKernelGGL(decode_window_merge_kernel<128>, dim3(bd.n * pv.Hq), dim3(128), 0, s, pv, layer, bd, q, sm,
-                           splits, ws, out, scores, sstride);
+        splits > 8 ? go(decode_window_merge_kernel<128, true>) : go(decode_window_merge_kernel<128, false>);
     return hipGetLastError();
 }
 
