@@ -159,6 +159,18 @@ struct Tile {
     uint4 meta[2];           // K and V metadata (scale, min) of tokens 2l and 2l + 1 of the pair
 };
 
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+// Code and metadata words are read once per call: streaming (nontemporal) loads.
+__device__ __forceinline__ uint4 stream_load4(const uint8_t* p) {
+    const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ uint2 stream_load2(const uint8_t* p) {
+    const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
+    return make_uint2(w.x, w.y);
+}
+
 template <int D>
 __device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, const uint8_t* base1, int l) {
     constexpr int NW = D / 64;
@@ -167,20 +179,19 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, cons
     for (int m = 0; m < 8; ++m) {
         const uint8_t* src = (m < 4 ? base0 : base1) + (16 * (m & 3) + j) * (D / 4) + 4 * NW * grp;
         if constexpr (NW == 4) {
-            const uint4 w = *reinterpret_cast<const uint4*>(src);
+            const uint4 w = stream_load4(src);
             t.kc[m][0] = w.x; t.kc[m][1] = w.y; t.kc[m][2] = w.z; t.kc[m][3] = w.w;
         } else {
-            const uint2 w = *reinterpret_cast<const uint2*>(src);
+            const uint2 w = stream_load2(src);
             t.kc[m][0] = w.x; t.kc[m][1] = w.y;
         }
     }
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-        t.vc[c] = *reinterpret_cast<const uint4*>((grp < 2 ? base0 : base1) + q2_vcodes_off(D) +
-                                                  q2_vword_off(D, 32 * c + j, 2 * (grp & 1)));
+        t.vc[c] = stream_load4((grp < 2 ? base0 : base1) + q2_vcodes_off(D) + q2_vword_off(D, 32 * c + j, 2 * (grp & 1)));
     const uint8_t* mb = (l < 32 ? base0 : base1) + 16 * (l & 31);
-    t.meta[0] = *reinterpret_cast<const uint4*>(mb + q2_kmeta_off(D));
-    t.meta[1] = *reinterpret_cast<const uint4*>(mb + q2_vmeta_off(D));
+    t.meta[0] = stream_load4(mb + q2_kmeta_off(D));
+    t.meta[1] = stream_load4(mb + q2_vmeta_off(D));
 }
 
 template <int D>
