@@ -130,15 +130,15 @@ __global__ __launch_bounds__(256, TB == 2 ? 2 : 1) void decode_bf16_kernel(PoolV
             for (int m = 0; m < NM; ++m)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    kraw[tb][2 * m + h] = *reinterpret_cast<const uint4*>(
-                        blk + 2 * ((t0 + 16 * tb + col) * D + 64 * m + 16 * grp + 8 * h));
+                    kraw[tb][2 * m + h] =
+                        stream_load4(blk + 2 * ((t0 + 16 * tb + col) * D + 64 * m + 16 * grp + 8 * h));
         uint4 vraw[NDB][KS];  // dim 16db + col, tokens t0 + 8 KS grp + 8h .. +7
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int h = 0; h < KS; ++h)
-                vraw[db][h] = *reinterpret_cast<const uint4*>(
-                    blk + 128 * D + 2 * ((16 * db + col) * PAGE + t0 + 8 * KS * grp + 8 * h));
+                vraw[db][h] =
+                    stream_load4(blk + 128 * D + 2 * ((16 * db + col) * PAGE + t0 + 8 * KS * grp + 8 * h));
 
         // ---- S^T: row 4grp + r (head 2grp + r/2 when r is even), column = token t0 + 16tb + col ----
         f32x4_t st[TB];

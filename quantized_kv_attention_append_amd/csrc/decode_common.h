@@ -22,6 +22,19 @@ namespace kvq {
 
 constexpr int MAX_SPLITS = 256;
 
+// Streaming loads for what a decode call reads once (codes, metadata, bf16
+// rows): nontemporal, so that they do not displace what the caches hold.
+typedef uint32_t stream_v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t stream_v2u __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 stream_load4(const uint8_t* p) {
+    const stream_v4u w = __builtin_nontemporal_load(reinterpret_cast<const stream_v4u*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ uint2 stream_load2(const uint8_t* p) {
+    const stream_v2u w = __builtin_nontemporal_load(reinterpret_cast<const stream_v2u*>(p));
+    return make_uint2(w.x, w.y);
+}
+
 // Splits p < live_splits(...) hold at least one page; the rest are empty and
 // leave their partials unwritten (split_range gives every split the same
 // whole number of page pairs, so empty splits only trail).

@@ -159,18 +159,6 @@ struct Tile {
     uint4 meta[2];           // K and V metadata (scale, min) of tokens 2l and 2l + 1 of the pair
 };
 
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));
-// Code and metadata words are read once per call: streaming (nontemporal) loads.
-__device__ __forceinline__ uint4 stream_load4(const uint8_t* p) {
-    const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-    return make_uint4(w.x, w.y, w.z, w.w);
-}
-__device__ __forceinline__ uint2 stream_load2(const uint8_t* p) {
-    const v2u w = __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p));
-    return make_uint2(w.x, w.y);
-}
-
 template <int D>
 __device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, const uint8_t* base1, int l) {
     constexpr int NW = D / 64;

@@ -493,11 +493,11 @@ __global__ __launch_bounds__(256, 2) void decode_q8_mfma_kernel(PoolView pv, int
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
             for (int m = 0; m < NM; ++m)
-                kraw[tb][m] = *reinterpret_cast<const uint4*>(blk + (16 * tb + col) * D + 64 * m + 16 * grp);
+                kraw[tb][m] = stream_load4(blk + (16 * tb + col) * D + 64 * m + 16 * grp);
         uint4 vraw[NDB];  // dim 16db + col, tokens 16grp .. +15
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-            vraw[db] = *reinterpret_cast<const uint4*>(blk + q8_vcodes_off(D) + (16 * db + col) * PAGE + 16 * grp);
+            vraw[db] = stream_load4(blk + q8_vcodes_off(D) + (16 * db + col) * PAGE + 16 * grp);
         float vsc[4];  // scale of token 16tb + col
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) vsc[tb] = reinterpret_cast<const float*>(blk + q8_vscale_off(D))[16 * tb + col];
