@@ -162,9 +162,12 @@ kv_status kv_pool_stats(const kv_pool* pool, kv_pool_stats_t* out);
 kv_status kv_pool_device_ptr(const kv_pool* pool, void** d_pages, int64_t* bytes);
 
 /* Admission: reserve ceil(max_tokens / 64) pages for a new sequence's whole
- * bound and upload its block table once.  pages: NULL to take free pages, or
- * an explicit list of that many distinct free page ids (logical page i ->
- * physical pages[i]).  Errors: KV_ERR_ARG, KV_ERR_BOUND (max_tokens above the
+ * bound and upload its block table once ("KV at 9 KB a token", section "How
+ * it works": the pool cannot run dry halfway through a reply; "The KV cache
+ * and prompt reuse", section "What a sequence is made of": one pool shared by
+ * every lane).  pages: NULL to take free pages, or an explicit list of
+ * exactly ceil(max_tokens / 64) distinct free page ids (logical page i ->
+ * physical pages[i]); the library reads that many entries.  Errors: KV_ERR_ARG, KV_ERR_BOUND (max_tokens above the
  * pool's max_seq_tokens), KV_ERR_NO_SPACE (not enough free pages or no free
  * sequence slot), KV_ERR_DEVICE. */
 kv_status kv_seq_reserve(kv_pool* pool, int64_t max_tokens, const int32_t* pages, int32_t* seq);
@@ -194,10 +197,25 @@ kv_status kv_seq_fork(kv_pool* pool, int32_t parent, int64_t n_tokens, int64_t m
  * holder left returns to the free list. */
 kv_status kv_seq_release(kv_pool* pool, int32_t seq);
 
+/* The device block table of a live sequence: *d_bt receives the device
+ * address of its int32 page ids (logical page i -> physical page d_bt[i]),
+ * the array every kernel walks, and *n_pages their count,
+ * ceil(bound / 64), all reserved at admission ("KV at 9 KB a token",
+ * section "How it works": a request reserves the pages of its whole bound
+ * when it is admitted).  The array is owned by the pool and stays valid and
+ * unchanged until the sequence is released; the caller must not write it.
+ * Errors: KV_ERR_ARG (NULL argument, sequence not live). */
+kv_status kv_seq_block_table(const kv_pool* pool, int32_t seq, const int32_t** d_bt, int32_t* n_pages);
+
 /* Host copy of a sequence's block table: writes up to cap page ids. */
 kv_status kv_seq_pages(const kv_pool* pool, int32_t seq, int32_t* pages, int32_t cap, int32_t* n_pages);
 
-/* Quantize-on-append for one layer.  For entry i, rows
+/* Quantize-on-append for one layer: every new token costs a fixed number of
+ * bytes in its page slot ("KV at 9 KB a token", section "How it works": per
+ * head per token, 64 B of 2-bit code and an 8-byte metadata row at 256 dims;
+ * the 8-bit variant follows "Half the Cache, Twice the Context", section
+ * "What the cache loses when you round it": the symmetric absmax quantizer,
+ * K scaled per channel, V per token).  For entry i, rows
  * d_k[row_i .. row_i + n_new[i]) (bf16 [rows][Hkv][D], row_i = sum of earlier
  * n_new) go to positions start_pos[i] .. start_pos[i] + n_new[i] - 1 of
  * sequence seqs[i]; same for d_v.  Each token's K and V rows are quantized in
@@ -224,7 +242,9 @@ kv_status kv_append_quant(kv_pool* pool, int32_t layer, int32_t n, const int32_t
 
 enum { KV_OP_DECODE = 0, KV_OP_PREFILL = 1 };
 
-/* Workspace bytes for an attention call: decode with n_rows sequences, or
+/* Workspace bytes for an attention call ("KV at 9 KB a token", section "How
+ * it works": the workspace needs no zeroing, since every byte a launch reads
+ * it has written first): decode with n_rows sequences, or
  * prefill with n_rows chunk queries, and n_splits splits of the context.
  * n_splits = 0 asks for enough bytes for the split count the library picks
  * by itself (decode: any count up to 256; prefill: the count it picks for
@@ -235,9 +255,16 @@ kv_status kv_workspace_bytes(const kv_pool* pool, int32_t op, int32_t n_rows, in
 /* Split-count the library picks for a decode batch when n_splits = 0. */
 kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_len, int32_t* n_splits);
 
-/* One decode step for n sequences of one layer.  d_q: bf16 [n][Hq][D], one
+/* One decode step for n sequences of one layer, reading the compressed pages
+ * directly through the block tables ("KV at 9 KB a token", opening section
+ * and "How it works": attention reads the compressed cache, priced per token
+ * in section "The numbers"), with every long sum in fp32 registers ("Half the
+ * Cache, Twice the Context", section "The cliff is in the accumulator, not
+ * the storage": a low-precision accumulator loses the mass of long flat
+ * contexts).  d_q: bf16 [n][Hq][D], one
  * query per sequence; sequence i attends to its tokens 0 .. ctx_len[i]-1
- * (ctx_len >= 1, within the reserved bound).  Scores are sm_scale x q.k^ over
+ * (ctx_len >= 1, within the reserved bound; n, seqs and ctx_len hold n
+ * entries).  Scores are sm_scale x q.k^ (sm_scale finite and > 0) over
  * the dequantized keys; softmax and all sums are kept in fp32; the contexts
  * are split into ranges of whole page pairs (flash-decoding), all of one size:
  * ceil(page pairs of the longest context / n_splits), n_splits in 1..256
@@ -265,7 +292,9 @@ kv_status kv_attn_decode(kv_pool* pool, int32_t layer, int32_t n, const int32_t*
  * exact from its bf16 rows, through a third kernel whose partials the merge
  * adds; the chunk must lie within the tokens appended).  Scores are
  * sm_scale x q.k^,
- * softmax and sums in fp32; both contractions run on bf16 matrix cores with
+ * sm_scale finite and > 0; softmax and sums in fp32 ("Half the Cache, Twice
+ * the Context", section "The cliff is in the accumulator, not the storage");
+ * both contractions run on bf16 matrix cores with
  * exact code operands and 16-bit softmax weights.  The keys of each block of
  * queries are split into n_splits ranges (1..64, 0 = the library's choice)
  * whose partials go to d_ws and are merged by a second kernel.
@@ -278,7 +307,11 @@ kv_status kv_attn_prefill(kv_pool* pool, int32_t layer, int32_t seq, int64_t q_s
                           float* d_out, kv_stream_t stream);
 
 /* Dequantize the 64 token slots of one (page, layer, KV head, K or V) plane
- * into d_out fp32 [64][D] (kv: 0 = K, 1 = V).  Slots never written hold
+ * into d_out fp32 [64][D] (kv: 0 = K, 1 = V): each row's codes through its
+ * metadata row ("KV at 9 KB a token", section "How it works": a row is its
+ * 2-bit codes plus an 8-byte metadata row; here fmaf(code, scale, min)), or
+ * code x scale for 8-bit rows ("Half the Cache, Twice the Context", section
+ * "What the cache loses when you round it"), or the stored bf16 values.  Slots never written hold
  * whatever the decoding of their bytes gives. */
 kv_status kv_dequant_page(const kv_pool* pool, int32_t page, int32_t layer, int32_t head, int32_t kv, float* d_out,
                           kv_stream_t stream);

@@ -52,6 +52,14 @@ def _i64(xs):
     return (C.c_int64 * len(xs))(*[int(x) for x in xs])
 
 
+def _same_length(n: int, **lists):
+    """The library reads one entry per sequence from each per-sequence array
+    (it takes no length for them): a shorter list would be read past its end."""
+    for name, xs in lists.items():
+        if len(xs) != n:
+            raise ValueError(f"{name} has {len(xs)} entries for {n} sequences")
+
+
 def _stream(stream) -> C.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -154,7 +162,13 @@ class Pool:
 
     def reserve(self, max_tokens: int, pages: Optional[Sequence[int]] = None) -> int:
         seq = C.c_int32()
-        arr = _i32(pages) if pages is not None else None
+        arr = None
+        if pages is not None:
+            need = -(-int(max_tokens) // PAGE)
+            if len(pages) != need:
+                # the library reads exactly ceil(max_tokens / 64) ids
+                raise ValueError(f"pages must list {need} page ids for {max_tokens} tokens, got {len(pages)}")
+            arr = _i32(pages)
         check(lib.kv_seq_reserve(self._h, int(max_tokens), arr, C.byref(seq)))
         return seq.value
 
@@ -167,6 +181,13 @@ class Pool:
 
     def release(self, seq: int):
         check(lib.kv_seq_release(self._h, int(seq)))
+
+    def block_table(self, seq: int):
+        """(device address, page count) of the sequence's block table: the
+        int32 page ids the kernels walk, logical page i at element i."""
+        p, n = C.c_void_p(), C.c_int32()
+        check(lib.kv_seq_block_table(self._h, int(seq), C.byref(p), C.byref(n)))
+        return p.value, n.value
 
     def pages(self, seq: int):
         n = C.c_int32()
@@ -190,6 +211,7 @@ class Pool:
         """Quantize-append bf16 rows k, v [sum(n_new)][Hkv][D] for one layer."""
         n = len(seqs)
         g = self.geom
+        _same_length(n, start_pos=start_pos, n_new=n_new)
         rows = sum(int(x) for x in n_new)
         for t, name in ((k, "k"), (v, "v")):
             if tuple(t.shape) != (rows, g.n_kv_heads, g.head_dim):
@@ -204,6 +226,7 @@ class Pool:
         """One decode step; q bf16 [n][Hq][D] -> fp32 [n][Hq][D]."""
         n = len(seqs)
         g = self.geom
+        _same_length(n, ctx_len=ctx_len)
         if tuple(q.shape) != (n, g.n_q_heads, g.head_dim):
             raise ValueError(f"q must be [{n}][{g.n_q_heads}][{g.head_dim}], got {tuple(q.shape)}")
         if out is None:

@@ -54,6 +54,7 @@ SIGNATURES = {
     "kv_seq_fork": [_P, _I32, _I64, _I64, _P, _PI32],
     "kv_seq_release": [_P, _I32],
     "kv_seq_pages": [_P, _I32, _PI32, _I32, _PI32],
+    "kv_seq_block_table": [_P, _I32, C.POINTER(_P), _PI32],
     "kv_append_quant": [_P, _I32, _I32, _PI32, _PI64, _PI32, _P, _P, _P],
     "kv_workspace_bytes": [_P, _I32, _I32, _I32, _PI64],
     "kv_decode_splits": [_P, _I32, _PI64, _PI32],

@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstdarg>
 #include <cstdio>
@@ -474,6 +475,16 @@ kv_status kv_seq_release(kv_pool* p, int32_t seq) {
     });
 }
 
+kv_status kv_seq_block_table(const kv_pool* p, int32_t seq, const int32_t** d_bt, int32_t* n_pages) {
+    return guarded([&]() -> kv_status {
+        if (!p || !d_bt || !n_pages) return fail(KV_ERR_ARG, "NULL argument");
+        if (seq < 0 || seq >= p->max_seqs || !p->seqs[(size_t)seq].live) return fail(KV_ERR_ARG, "sequence %d is not live", seq);
+        *d_bt = p->d_bt + (size_t)seq * p->bt_stride;
+        *n_pages = (int32_t)p->seqs[(size_t)seq].pages.size();
+        return KV_OK;
+    });
+}
+
 kv_status kv_seq_pages(const kv_pool* p, int32_t seq, int32_t* pages, int32_t cap, int32_t* n_pages) {
     return guarded([&]() -> kv_status {
         if (!p || !n_pages) return fail(KV_ERR_ARG, "NULL argument");
@@ -670,6 +681,7 @@ kv_status kv_attn_decode(kv_pool* p, int32_t layer, int32_t n, const int32_t* se
         if (!seqs || !ctx_len || !d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
         if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
         if (n_splits < 0 || n_splits > 256) return fail(KV_ERR_ARG, "n_splits %d out of range (0..256)", n_splits);
+        if (!(sm_scale > 0.f) || !(sm_scale < INFINITY)) return fail(KV_ERR_ARG, "sm_scale must be finite and positive");
         BatchDesc bd;
         memset(&bd, 0, sizeof bd);
         bd.n = n;
@@ -735,6 +747,7 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
         if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
         if (q_start > INT32_MAX) return fail(KV_ERR_BOUND, "q_start %lld is not below 2^31", (long long)q_start);
         if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
+        if (!(sm_scale > 0.f) || !(sm_scale < INFINITY)) return fail(KV_ERR_ARG, "sm_scale must be finite and positive");
         if (layer < 0 || layer >= p->geom.n_layers) return fail(KV_ERR_ARG, "layer %d out of range", layer);
         kv_status st = check_seq(p, seq, q_start + n_q, "prefill");
         if (st != KV_OK) return st;

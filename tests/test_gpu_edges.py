@@ -170,9 +170,51 @@ def test_binding_refuses_mismatched_buffers():
                      out=torch.empty((3, W.n_q_heads, W.head_dim), device="cuda"))
     with pytest.raises(ValueError):
         pool.dequant_page(0, 0, 0, 0, out=torch.empty((PAGE_TOKENS, W.head_dim + 1), device="cuda"))
+    # per-sequence arrays shorter than the batch (the library takes no length
+    # for them and would read past their end)
+    kd, vd = k[:4].cuda(), v[:4].cuda()
+    with pytest.raises(ValueError):
+        pool.append(0, [seq], [100, 104], [4], kd, vd)
+    with pytest.raises(ValueError):
+        pool.append(0, [seq], [100], [], kd, vd)
+    with pytest.raises(ValueError):
+        pool.decode(0, [seq, seq], [100], torch.cat([q, q]), W.sm_scale, n_splits=2)
+    with pytest.raises(ValueError):
+        pool.reserve(200, pages=[0, 1])          # 200 tokens need 4 page ids
+    # a scale that is not finite and positive is refused by the library
+    for sm in (0.0, -W.sm_scale, float("nan"), float("inf")):
+        with pytest.raises(kvq.KvError) as ei:
+            pool.decode(0, [seq], [100], q, sm, n_splits=2, ws=ws)
+        assert ei.value.name == "KV_ERR_ARG"
+        with pytest.raises(kvq.KvError) as ei:
+            pool.prefill(0, seq, 96, queries(W, 0, 4, stream=1).cuda(), sm)
+        assert ei.value.name == "KV_ERR_ARG"
     torch.cuda.synchronize()
     assert torch.equal(mem.cpu(), before)
     say("binding refusals: no byte changed")
+
+
+def test_block_table_is_the_reserved_pages():
+    """kv_seq_block_table hands out the device array the kernels walk: read
+    back from the device it lists the reserved pages in logical order."""
+    need_gpu()
+    import ctypes as C
+    import quantized_kv_attention_append_amd as kvq
+    hip = C.CDLL("libamdhip64.so")
+    pool, mem = make_pool(W, 12, kvq.FMT_Q2, fill=0x5A, max_seqs=3)
+    a = pool.reserve(200, pages=[7, 2, 9, 4])
+    b = pool.reserve(130)
+    for seq, want in ((a, [7, 2, 9, 4]), (b, pool.pages(b))):
+        ptr, n = pool.block_table(seq)
+        assert n == len(want) and ptr
+        host = (C.c_int32 * n)()
+        assert hip.hipMemcpy(host, C.c_void_p(ptr), C.c_size_t(4 * n), 2) == 0  # device to host
+        assert list(host) == list(want)
+    assert len(set(pool.pages(b)) & {7, 2, 9, 4}) == 0
+    pool.release(a)
+    with pytest.raises(kvq.KvError) as ei:
+        pool.block_table(a)
+    assert ei.value.name == "KV_ERR_ARG"
 
 
 def test_pool_dropped_inside_a_graph_capture():
