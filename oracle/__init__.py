@@ -24,8 +24,28 @@ Sources (the three pages this library is built from):
     formula, the symmetric absmax quantizer, per-channel K / per-token V
     scaling, the outlier recipe, the accumulator-precision model.
 
-Parity status of every function is stated in its module docstring; there is
-no function marked "parity unpinned".
+Pins: every function is checked against something other than itself, in
+the ``-m "not gpu"`` suite:
+  * accounting: the pages' byte figures (9,216 vs 65,536 B a token, 7.11x,
+    12.5 %, 3.02 GB vs 20.0 GiB) and the sizing table of "Half the Cache,
+    Twice the Context" (tests/golden/block1_sizing.txt, kv_bytes.txt);
+  * bf16, codec.sym_*: that page's printed reconstruction, needle and
+    flat-sum tables reproduced digit for digit (tests/golden/block2_*.txt,
+    block3_flat_sum.txt);
+  * codec (2-bit, 8-bit, rotation): closed-form invariants, round-half-even
+    ties, constant rows, exact rational arithmetic for the fused
+    multiply-add, scipy's Hadamard matrix;
+  * layout: byte positions worked out by hand (tests/golden/layout_cases.txt)
+    and a frozen block image (tests/golden/q2_block_d128.hex);
+  * pool: permutation invariance, untouched fill bytes, the bf16 block read
+    back by hand, fork and window identities;
+  * attention.decode / prefill / split and merge: closed forms (one key,
+    equal keys, a dominant key, the 131,072-token flat case), a pure-Python
+    loop on small inputs, the split-merge identity, prefill rows against
+    decode; attention.scores: the GQA head mapping and basis-key closed
+    forms, and softmax of the scores against decode; planted_rank: worked
+    ties.
+No function is left "parity unpinned".
 """
 
 from . import accounting, bf16, codec, layout, pool, attention, experiments  # noqa: F401

@@ -16,10 +16,14 @@ split p of the keys keeps (m_p, l_p, o_p) = (max score, sum of exp(s - m_p),
 sum of exp(s - m_p) V^), and the merge rescales by exp(m_p - M).  In exact
 arithmetic the merge equals the unsplit softmax; that invariant pins it.
 
-Pins (tests/test_oracle_attention.py): ctx_len = 1 gives o = V^_0; constant
-scores give the mean of V^; a dominant key returns its value row; a loop
-reference on tiny shapes; the split/merge identity; prefill's last row equals
-decode at the same length.
+Pins (tests/test_oracle_pool_attention.py): ctx_len = 1 gives o = V^_0;
+constant scores give the mean of V^; a dominant key returns its value row; a
+loop reference on tiny shapes; the split/merge identity; prefill's last row
+equals decode at the same length.  scores: with K[t, g] = (g + 1) * ones and
+unit queries every score of head h is sm * D * (h // G + 1) (the GQA
+mapping); unit-vector keys return the scaled query row; keys parallel to the
+query give sm * c * |q|^2; softmax of the scores applied to V is decode's
+output.  planted_rank: worked cases with ties.
 """
 
 from __future__ import annotations

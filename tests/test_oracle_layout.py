@@ -95,3 +95,77 @@ def test_v_plane_word_offsets_tile_the_plane():
                     a = layout.v_word_offset(D, d, 2 * half)
                     assert layout.v_word_offset(D, d, 2 * half + 1) == a + 4
                     assert layout.v_word_offset(D, d + 16, 2 * half) == a + 8  # dims d, d+16 adjacent
+
+
+def _golden_rows(golden, kind):
+    return [r[1:] for r in golden("layout_cases.txt") if r[0] == kind]
+
+
+def test_hand_derived_code_positions(golden):
+    """One code in an all-zero block sets exactly the byte worked out by hand
+    in tests/golden/layout_cases.txt (independently of the oracle's index
+    arithmetic)."""
+    rows = _golden_rows(golden, "code")
+    assert len(rows) >= 10
+    for fmt, D, plane, slot, dim, code, byte, value, *_ in rows:
+        D, slot, dim, code, byte, value = int(D), int(slot), int(dim), int(code), int(byte), int(value, 16)
+        if fmt == "q2":
+            buf = np.zeros(layout.q2_block_bytes(D), np.uint8)
+            blk = layout.Q2Block(buf, D)
+            row = np.zeros(D, np.uint8)
+            row[dim] = code
+            (blk.write_k if plane == "K" else blk.write_v)(slot, row, np.float32(0), np.float32(0))
+        else:
+            buf = np.zeros(layout.q8_block_bytes(D), np.uint8)
+            blk = layout.Q8Block(buf, D)
+            if plane == "K":
+                blk.k_codes[slot, dim] = code
+            else:
+                blk.v_codes[dim, slot] = code
+        nz = np.nonzero(buf)[0]
+        assert list(nz) == [byte], (fmt, D, plane, slot, dim, list(nz))
+        assert int(buf[byte]) == value
+
+
+def test_hand_derived_metadata_positions(golden):
+    for fmt, D, field, slot, scale, mn, off, hexbytes, *_ in _golden_rows(golden, "meta"):
+        D, slot, off = int(D), int(slot), int(off)
+        buf = np.zeros(layout.q2_block_bytes(D), np.uint8)
+        blk = layout.Q2Block(buf, D)
+        (blk.write_k if field == "K" else blk.write_v)(slot, np.zeros(D, np.uint8), np.float32(scale), np.float32(mn))
+        assert buf[off:off + 8].tobytes().hex() == hexbytes
+        assert np.count_nonzero(buf) == np.count_nonzero(np.frombuffer(bytes.fromhex(hexbytes), np.uint8))
+    for fmt, D, field, idx, x, off, hexbytes, *_ in _golden_rows(golden, "scale"):
+        D, idx, off = int(D), int(idx), int(off)
+        buf = np.zeros(layout.q8_block_bytes(D), np.uint8)
+        blk = layout.Q8Block(buf, D)
+        (blk.k_scale if field == "K" else blk.v_scale)[idx] = np.float32(x)
+        assert buf[off:off + 4].tobytes().hex() == hexbytes
+        assert np.count_nonzero(buf) == np.count_nonzero(np.frombuffer(bytes.fromhex(hexbytes), np.uint8))
+
+
+def test_block_image_is_frozen():
+    """The whole 2-bit block image of a fixed code pattern equals the stored
+    vector (tests/golden/q2_block_d128.hex, written by
+    tests/golden/make_layout_golden.py through the oracle): a change of the
+    block format anywhere shows as a difference here."""
+    import importlib.util
+    import os
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    spec = importlib.util.spec_from_file_location("make_layout_golden", os.path.join(here, "make_layout_golden.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    buf = mod.pattern_block()
+    stored = bytearray()
+    with open(os.path.join(here, "q2_block_d128.hex")) as f:
+        for line in f:
+            if line.startswith("#"):
+                continue
+            off, hx = line.split()
+            assert int(off) == len(stored)
+            stored += bytes.fromhex(hx)
+    assert bytes(stored) == buf.tobytes()
+    # spot checks by hand: K row 0 of codes (0, 3, 2, 1, ...) packs to 0x6c;
+    # K metadata of slot 1 is (2.0, -0.125)
+    assert stored[0] == 0 | 3 << 2 | 2 << 4 | 1 << 6 == 0x6C
+    assert np.frombuffer(bytes(stored[32 * 128 + 8:32 * 128 + 16]), np.float32).tolist() == [2.0, -0.125]

@@ -196,3 +196,54 @@ def test_c0_pipeline_oracle_runs():
     q = queries(w, 0, 1)[0].float().numpy()
     o = attention.decode(q, K, V, w.sm_scale)
     assert o.shape == (16, 256) and np.all(np.isfinite(o))
+
+
+def test_scores_gqa_head_mapping_closed_form():
+    """Query head h reads KV head h // G: with K[t, g] = (g + 1) * ones and
+    q_h = ones, every score of head h is sm * D * (h // G + 1).  Reading
+    KV head h % Hkv instead, or the wrong axis, changes the values."""
+    T, Hkv, G, D, sm = 5, 2, 4, 8, 0.3
+    K = np.stack([np.full((T, D), g + 1.0) for g in range(Hkv)], axis=1)
+    q = np.ones((Hkv * G, D))
+    s = attention.scores(q, K, sm)
+    assert s.shape == (Hkv * G, T)
+    for h in range(Hkv * G):
+        assert np.all(s[h] == sm * D * (h // G + 1))
+
+
+def test_scores_against_basis_keys_and_parallel_keys():
+    """Keys that are the unit vectors e_t give scores sm * q_h[t] (the query
+    row itself, so a transposed operand fails); keys c_t * q_h give
+    sm * c_t * |q_h|^2."""
+    rng = np.random.default_rng(31)
+    D, sm = 6, 0.125
+    q = rng.standard_normal((2, D))                     # Hq = 2, Hkv = 1
+    K = np.eye(D)[:, None, :]                           # [T = D][1][D]
+    s = attention.scores(q, K, sm)
+    assert np.array_equal(s, sm * q)
+    c = np.array([0.5, -2.0, 3.0])
+    K2 = (c[:, None] * q[0][None, :])[:, None, :]       # three keys parallel to q_0
+    s2 = attention.scores(q[:1], K2, sm)[0]
+    assert np.allclose(s2, sm * c * np.dot(q[0], q[0]), rtol=1e-15, atol=0)
+
+
+def test_scores_give_the_decode_weights():
+    """softmax of the raw logits, applied to V, is the decode output (decode
+    itself is pinned by its own closed forms above)."""
+    w, k, v = _c0_rows(200)
+    q = queries(w, 0, 1)[0].float().numpy()
+    K, V = pool.dequantized_rows("q2", k, v)
+    s = attention.scores(q, K, w.sm_scale)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    G = w.group
+    out = np.stack([p[h] @ np.asarray(V[:, h // G], np.float64) for h in range(w.n_q_heads)])
+    assert np.allclose(out, attention.decode(q, K, V, w.sm_scale), rtol=1e-12, atol=1e-14)
+
+
+def test_planted_rank_counts_strictly_higher_scores():
+    s = np.array([0.1, 0.5, 0.5, 0.3])
+    assert attention.planted_rank(s, 1) == 1   # tied with slot 2: ties favour the planted key
+    assert attention.planted_rank(s, 2) == 1
+    assert attention.planted_rank(s, 3) == 3   # 0.5 and 0.5 above it
+    assert attention.planted_rank(s, 0) == 4
