@@ -332,11 +332,11 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
     }
 }
 
-template <int D, bool SCORES, bool ROT, bool GENERAL>
+template <int D, bool SCORES, bool ROT, bool GENERAL, bool FUSE>
 __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int layer, const BatchDesc& bd,
                                                     const uint16_t* __restrict__ q, float sm, int splits,
-                                                    float* __restrict__ ws, float* __restrict__ scores,
-                                                    int64_t sstride, int h0, int nh) {
+                                                    float* __restrict__ ws, float* __restrict__ out,
+                                                    float* __restrict__ scores, int64_t sstride, int h0, int nh) {
     // The kernel takes four query heads of a KV head's group at a time: heads
     // h0 .. h0 + nh - 1.  Without GENERAL the group is exactly these four
     // (group 4, h0 = 0, nh = 4, all known when compiling); with it the group
@@ -572,80 +572,119 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
             float o = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) o += f[v] * (o_s[v][h][d] + ml_s[v][h][2]);
-            if (!GENERAL || h < nh) w.o[row * D + d] = o;
+            if (!GENERAL || h < nh) {
+                if constexpr (FUSE) store_agent(&w.o[row * D + d], o);
+                else w.o[row * D + d] = o;
+            }
         }
         if (l == 0 && (!GENERAL || h < nh)) {
-            w.ml[2 * row] = M;
-            w.ml[2 * row + 1] = lsum;
+            if constexpr (FUSE) {
+                store_agent(&w.ml[2 * row], M);
+                store_agent(&w.ml[2 * row + 1], lsum);
+            } else {
+                w.ml[2 * row] = M;
+                w.ml[2 * row + 1] = lsum;
+            }
         }
+    }
+    if constexpr (FUSE) {
+        // The last of the sequence's live splits to get here merges them all.
+        // Partials travel through agent-scope (L2-coherent) stores and loads
+        // only, so no cache writeback or invalidation is needed: every
+        // thread's partial stores have completed before the workgroup counts
+        // itself, and the merging workgroup loads them after the count shows
+        // every split done.
+        __shared__ int last_s;
+        wait_stores();
+        __syncthreads();
+        const int live = live_splits(ctx, bd.per);
+        int32_t* cnt = pv.cnt + ((int64_t)e * Hkv + g) * 2 + (h0 >> 2);
+        if (threadIdx.x == 0) {
+            const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int is_last = before == live - 1;
+            if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
+            last_s = is_last;
+        }
+        __syncthreads();
+        if (!last_s) return;
+        const int h = threadIdx.x >> 6;
+        if (GENERAL && h >= nh) return;
+        merge_live_splits<D / 64>(w, (head0 + h) * splits, live, l, out + (head0 + h) * D);
     }
 }
 
-// Group 4: the four heads of each KV head's group in one launch.
-template <int D, bool SCORES, bool ROT>
+// Group 4: the four heads of each KV head's group in one launch.  FUSE: the
+// last split of each (sequence, KV head) to finish merges the partials into
+// out (at most FUSED_MERGE_MAX_SPLITS splits).
+template <int D, bool SCORES, bool ROT, bool FUSE>
 __global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                              const uint16_t* __restrict__ q, float sm, int splits,
-                                                             float* __restrict__ ws, float* __restrict__ scores,
-                                                             int64_t sstride) {
-    decode_q2_mfma_body<D, SCORES, ROT, false>(pv, layer, bd, q, sm, splits, ws, scores, sstride, 0, 4);
+                                                             float* __restrict__ ws, float* __restrict__ out,
+                                                             float* __restrict__ scores, int64_t sstride) {
+    decode_q2_mfma_body<D, SCORES, ROT, false, FUSE>(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, 0, 4);
 }
 
 // Other groups: heads h0 .. h0 + nh - 1 of each KV head's group.
-template <int D, bool SCORES, bool ROT>
+template <int D, bool SCORES, bool ROT, bool FUSE>
 __global__ __launch_bounds__(256) void decode_q2_mfma_group_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                    const uint16_t* __restrict__ q, float sm,
                                                                    int splits, float* __restrict__ ws,
+                                                                   float* __restrict__ out,
                                                                    float* __restrict__ scores, int64_t sstride,
                                                                    int h0, int nh) {
-    decode_q2_mfma_body<D, SCORES, ROT, true>(pv, layer, bd, q, sm, splits, ws, scores, sstride, h0, nh);
+    decode_q2_mfma_body<D, SCORES, ROT, true, FUSE>(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, h0, nh);
 }
 
-hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
-                                     int splits, float* ws, float* scores, int64_t sstride, hipStream_t s, bool rot) {
+// The split kernels of a decode call; fuse: each launch also merges (out).
+static hipError_t launch_decode_q2_splits(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q,
+                                          float sm, int splits, float* ws, float* out, float* scores,
+                                          int64_t sstride, hipStream_t s, bool rot, bool fuse) {
     dim3 grid(bd.n * pv.Hkv, splits);
     const float smk = rot ? sm / (float)pv.D : sm;  // H q . H k = D q . k
     const int Gq = pv.Hq / pv.Hkv;
     using D128 = std::integral_constant<int, 128>;
     using D256 = std::integral_constant<int, 256>;
+    using T = std::true_type;
+    using F = std::false_type;
+    // template flags: head dim, scores, rotated, fused merge
+    auto flags = [&](auto&& go) {
+        auto f3 = [&](auto d, auto sc, auto r) { fuse ? go(d, sc, r, T{}) : go(d, sc, r, F{}); };
+        auto f2 = [&](auto d, auto sc) { rot ? f3(d, sc, T{}) : f3(d, sc, F{}); };
+        auto f1 = [&](auto d) { scores ? f2(d, T{}) : f2(d, F{}); };
+        pv.D == 256 ? f1(D256{}) : f1(D128{});
+    };
     if (Gq == 4) {
-        auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, scores, sstride);
-        };
-        auto pick = [&](auto d_tag) {
-            constexpr int DD = decltype(d_tag)::value;
-            if (rot)
-                scores ? go(decode_q2_mfma_kernel<DD, true, true>) : go(decode_q2_mfma_kernel<DD, false, true>);
-            else
-                scores ? go(decode_q2_mfma_kernel<DD, true, false>) : go(decode_q2_mfma_kernel<DD, false, false>);
-        };
-        pv.D == 256 ? pick(D256{}) : pick(D128{});
+        flags([&](auto d, auto sc, auto r, auto fu) {
+            hipLaunchKernelGGL((decode_q2_mfma_kernel<decltype(d)::value, decltype(sc)::value, decltype(r)::value,
+                                                      decltype(fu)::value>),
+                               grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores, sstride);
+        });
         return hipGetLastError();
     }
     // other groups: up to four query heads per launch (two launches for group 8)
     for (int h0 = 0; h0 < Gq; h0 += 4) {
         const int nh = Gq - h0 < 4 ? Gq - h0 : 4;
-        auto go = [&](auto kernel) {
-            hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, scores, sstride, h0,
+        flags([&](auto d, auto sc, auto r, auto fu) {
+            hipLaunchKernelGGL((decode_q2_mfma_group_kernel<decltype(d)::value, decltype(sc)::value,
+                                                            decltype(r)::value, decltype(fu)::value>),
+                               grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores, sstride, h0,
                                nh);
-        };
-        auto pick = [&](auto d_tag) {
-            constexpr int DD = decltype(d_tag)::value;
-            if (rot)
-                scores ? go(decode_q2_mfma_group_kernel<DD, true, true>)
-                       : go(decode_q2_mfma_group_kernel<DD, false, true>);
-            else
-                scores ? go(decode_q2_mfma_group_kernel<DD, true, false>)
-                       : go(decode_q2_mfma_group_kernel<DD, false, false>);
-        };
-        pv.D == 256 ? pick(D256{}) : pick(D128{});
+        });
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
 }
 
+hipError_t launch_decode_q2_partials(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
+                                     int splits, float* ws, float* scores, int64_t sstride, hipStream_t s, bool rot) {
+    return launch_decode_q2_splits(pv, layer, bd, q, sm, splits, ws, nullptr, scores, sstride, s, rot, false);
+}
+
 hipError_t launch_decode_q2(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm, int splits,
                             float* ws, float* out, float* scores, int64_t sstride, hipStream_t s, bool rot) {
+    if (splits <= FUSED_MERGE_MAX_SPLITS && pv.cnt)
+        return launch_decode_q2_splits(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, s, rot, true);
     const hipError_t err = launch_decode_q2_partials(pv, layer, bd, q, sm, splits, ws, scores, sstride, s, rot);
     return err != hipSuccess ? err : launch_merge_splits(bd, pv.Hq, pv.D, splits, ws, out, s);
 }

@@ -109,6 +109,7 @@ struct kv_pool {
     int32_t* d_bt = nullptr;     // [max_seqs][bt_stride]
     uint16_t* d_stage = nullptr; // 8-bit exact-K window
     uint8_t* d_win = nullptr;    // 2-bit window pools: exact rows of the last page, per (seq, layer, head)
+    int32_t* d_cnt = nullptr;    // split arrival counters of the fused decode merge, zero between calls
     int device = 0;
     // host metadata
     std::vector<int32_t> refs;       // page -> sequences holding it (0: free)
@@ -142,6 +143,7 @@ struct kv_pool {
         v.bt_stride = bt_stride;
         v.stage = d_stage;
         v.win = d_win;
+        v.cnt = d_cnt;
         return v;
     }
 };
@@ -248,6 +250,14 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
             size_t wb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * 256 * (size_t)geom->head_dim;
             e = hipMalloc((void**)&p->d_win, wb);
         }
+        if (e == hipSuccess) {
+            // one counter per (batch entry, KV head, launch of four query heads); each
+            // fused decode launch returns every counter it used to zero
+            const size_t cb = decode_counters(geom->n_kv_heads) * sizeof(int32_t);
+            e = hipMalloc((void**)&p->d_cnt, cb);
+            if (e == hipSuccess) e = hipMemset(p->d_cnt, 0, cb);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
+        }
         if (e != hipSuccess) {
             kv_status r = hip_fail(e, "hipMalloc(block tables / window)");
             kv_pool_destroy(p);
@@ -279,6 +289,7 @@ kv_status kv_pool_destroy(kv_pool* p) {
         if (p->d_bt) (void)hipFree(p->d_bt);
         if (p->d_stage) (void)hipFree(p->d_stage);
         if (p->d_win) (void)hipFree(p->d_win);
+        if (p->d_cnt) (void)hipFree(p->d_cnt);
         delete p;
         return KV_OK;
     });

@@ -21,7 +21,16 @@ struct PoolView {
     int32_t bt_stride;
     uint16_t* stage;       // 8-bit pools: exact K window, bf16 [max_seqs][L][Hkv][64][D]
     uint8_t* win;          // 2-bit window pools: one bf16 block (K [64][D], V [D][64]) per (seq, layer, head)
+    int32_t* cnt;          // fused decode merge: arrival counters [KV_MAX_BATCH][Hkv][2], zero between calls
 };
+
+// Arrival counters a pool keeps for the fused decode merge: one per (batch
+// entry, KV head, launch of four query heads; group 8 takes two launches).
+inline int64_t decode_counters(int Hkv) { return (int64_t)KV_MAX_BATCH * Hkv * 2; }
+// Largest split count whose merge runs inside the split kernel (the last
+// workgroup of a (sequence, KV head) to finish merges them); more splits are
+// merged by a kernel of their own.
+constexpr int FUSED_MERGE_MAX_SPLITS = 8;
 
 // The window block of (seq, layer, head) in a 2-bit window pool.
 __host__ __device__ inline uint8_t* window_block(const PoolView& pv, int seq, int layer, int head) {
