@@ -30,11 +30,13 @@
 // accumulation "Half the Cache, Twice the Context" asks for in section "The
 // cliff is in the accumulator").
 //
-// One workgroup of four wavefronts per (sequence, KV head, split); wave w
-// takes every fourth pair of pages of the split (128 tokens = one k-block of
-// the instruction), keeping the next two pairs' loads in flight while it
-// computes the current one, and the four waves combine their partial results
-// in LDS.  Token t of the pair sits at page t/64, slot t%64.  Operand lane
+// One workgroup of eight wavefronts per (sequence, KV head, split); wave w
+// takes every eighth pair of pages of the split (128 tokens = one k-block of
+// the instruction).  A pair's two (layer, KV head) blocks are copied into the
+// wave's LDS slot by DMA loads (global -> LDS), read from there into
+// registers, and the next pair's DMA goes out while the wave computes; the
+// eight waves combine their partial results in LDS.  Token t of the pair
+// sits at page t/64, slot t%64.  Operand lane
 // layouts of the instruction: fp4 lane group g holds k = 32g..32g+31; fp8
 // lane group g holds k = 16g..16g+15 and 64+16g..64+16g+15; the result lane l
 // holds column l%16, rows 4(l/16)..+3.
@@ -152,34 +154,141 @@ constexpr float LN2 = 0.6931471805599453f;
 // 2^8 in weight, so the running sums are rescaled rarely (weights stay < 2^8).
 constexpr float RESCALE_LOG2 = 8.0f;
 
+// A tile is a pair of pages: the two (layer, KV head) blocks, byte for byte
+// as they sit in the pool, copied into an LDS slot of the wave by DMA loads
+// (global -> LDS, no registers held while they are in flight).
 template <int D>
-struct Tile {
-    uint32_t kc[8][D / 64];  // K code words of token 16m + l%16 of the pair, this lane group's D/16 bytes
-    uint4 vc[D / 32];        // V words of dims 32c + l%16 and 32c + 16 + l%16 for this lane group's k-range
-    uint4 meta[2];           // K and V metadata (scale, min) of tokens 2l and 2l + 1 of the pair
+struct TileShape {
+    static constexpr int BLK = (int)q2_block_bytes(D);  // 9,216 at D = 256
+    static constexpr int BYTES = 2 * BLK;
+    static constexpr int DMA = 2 * BLK / 1024;          // 16-byte DMA loads per lane and tile
+};
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// One (layer, KV head) block copied to LDS at `lds` by one wave: lane l moves
+// bytes 16 l + 1024 i.  The loads are issued in inline asm so that the
+// compiler sees no LDS write in flight (it would otherwise wait for every
+// outstanding DMA before any LDS read); the kernel places the waits itself.
+// The instruction's immediate offset applies to both addresses (M0 + offset +
+// 16 lane in LDS, base + voff + offset in memory) and is below 4,096, so the
+// block goes in groups of four loads.  It first waits for every earlier LDS
+// read of the wave to return, since the slot may be the one just read.  M0
+// is saved and restored.
+template <int D>
+__device__ __forceinline__ void dma_block(const uint8_t* base, uint32_t v0, uint32_t lds) {
+    const uint32_t v1 = v0 + 4096, l1 = lds + 4096;
+    uint32_t saved;
+    if constexpr (D == 256) {
+        const uint32_t v2 = v0 + 8192, l2 = lds + 8192;
+        asm volatile(
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "s_mov_b32 %[sv], m0\n\t"
+            "s_mov_b32 m0, %[l0]\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:1024 nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:2048 nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:3072 nt\n\t"
+            "s_mov_b32 m0, %[l1]\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] nt\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] offset:1024 nt\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] offset:2048 nt\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] offset:3072 nt\n\t"
+            "s_mov_b32 m0, %[l2]\n\t"
+            "global_load_lds_dwordx4 %[v2], %[b] nt\n\t"
+            "s_mov_b32 m0, %[sv]"
+            : [sv] "=&s"(saved)
+            : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [l0] "s"(lds), [l1] "s"(l1), [l2] "s"(l2)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "s_mov_b32 %[sv], m0\n\t"
+            "s_mov_b32 m0, %[l0]\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:1024 nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:2048 nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:3072 nt\n\t"
+            "s_mov_b32 m0, %[l1]\n\t"
+            "global_load_lds_dwordx4 %[v1], %[b] nt\n\t"
+            "s_mov_b32 m0, %[sv]"
+            : [sv] "=&s"(saved)
+            : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [l0] "s"(lds), [l1] "s"(l1)
+            : "memory");
+    }
+}
+static_assert(q2_block_bytes(256) == 9 * 1024 && q2_block_bytes(128) == 5 * 1024, "blocks are whole KiB");
+
+// Waits until at most N of this wave's vector memory operations are
+// outstanding.  Loads complete in issue order, so with the next tile's DMA
+// (N loads) issued after this tile's, vmcnt(N) means this tile has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Loads and stores at an LDS byte address (plain scalar and vector types:
+// HIP's vector structs do not bind to LDS-qualified references).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T*>((uintptr_t)addr);
+}
+template <typename T>
+__device__ __forceinline__ void lds_store(uint32_t addr, T v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T*>((uintptr_t)addr) = v;
+}
+__device__ __forceinline__ uint4 lds_load4(uint32_t addr) {
+    const u32x4 w = lds_load<u32x4>(addr);
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ float2 lds_loadf2(uint32_t addr) {
+    const u32x2 w = lds_load<u32x2>(addr);
+    return make_float2(__uint_as_float(w.x), __uint_as_float(w.y));
+}
+
+// The registers a tile is computed from: lane (j, grp) holds the K code words
+// of token 16m + j for this lane group's D/16 bytes (q.k operands), the V
+// words of dims 32c + j and 32c + 16 + j for its k-range (p.v operands), and
+// the (scale, min) rows of token 16m + j.
+template <int D>
+struct TileRegs {
+    uint32_t kc[8][D / 64];
+    uint4 vc[D / 32];
+    float2 km[8];
+    float2 vm[8];
 };
 
 template <int D>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const uint8_t* base0, const uint8_t* base1, int l) {
-    constexpr int NW = D / 64;
+__device__ __forceinline__ void read_tile(TileRegs<D>& t, uint32_t slot, int l) {
+    constexpr int NW = D / 64, B = TileShape<D>::BLK;
     const int j = l & 15, grp = l >> 4;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const uint8_t* src = (m < 4 ? base0 : base1) + (16 * (m & 3) + j) * (D / 4) + 4 * NW * grp;
+        const uint32_t src = slot + (m < 4 ? 0 : B) + (16 * (m & 3) + j) * (D / 4) + 4 * NW * grp;
         if constexpr (NW == 4) {
-            const uint4 w = stream_load4(src);
+            const uint4 w = lds_load4(src);
             t.kc[m][0] = w.x; t.kc[m][1] = w.y; t.kc[m][2] = w.z; t.kc[m][3] = w.w;
         } else {
-            const uint2 w = stream_load2(src);
+            const u32x2 w = lds_load<u32x2>(src);
             t.kc[m][0] = w.x; t.kc[m][1] = w.y;
         }
     }
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-        t.vc[c] = stream_load4((grp < 2 ? base0 : base1) + q2_vcodes_off(D) + q2_vword_off(D, 32 * c + j, 2 * (grp & 1)));
-    const uint8_t* mb = (l < 32 ? base0 : base1) + 16 * (l & 31);
-    t.meta[0] = stream_load4(mb + q2_kmeta_off(D));
-    t.meta[1] = stream_load4(mb + q2_vmeta_off(D));
+        t.vc[c] = lds_load4(slot + (grp < 2 ? 0 : B) + q2_vcodes_off(D) + q2_vword_off(D, 32 * c + j, 2 * (grp & 1)));
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const uint32_t mb = slot + (m < 4 ? 0 : B) + 8 * (16 * (m & 3) + j);
+        t.km[m] = lds_loadf2(mb + q2_kmeta_off(D));
+        t.vm[m] = lds_loadf2(mb + q2_vmeta_off(D));
+    }
 }
 
 template <int D>
@@ -197,40 +306,31 @@ struct QConst {
     float cB;     // log2(e) * sm: raw q.k^ -> log2 units
 };
 
-// Per-wave LDS: the tile's metadata as {k scale, k min, v scale, v min} per
-// token, and the weight-digit transpose: for head h and digit i, 32 words at
+// The weight-digit transpose of a wave: for head h and digit i, 32 words at
 // wdig_base(h, i); word c (c < 16) holds the digits of tokens 16m + c for
-// m = 0..3, word 16 + c those for m = 4..7.
-struct WaveLds {
-    float4 meta[2 * PAGE];
-    uint32_t wdig[4 * 4 * 32 + 16 * 3];
-};
-__device__ __forceinline__ int wdig_base(int h, int i) { return (4 * h + i) * 32 + 16 * h; }
+// m = 0..3, word 16 + c those for m = 4..7.  With four waves a workgroup the
+// rows of the four heads are staggered by 16 words (fewer bank conflicts);
+// eight waves take the unpadded 2,048 bytes so that the workgroup fits LDS.
+template <bool PAD>
+__device__ __forceinline__ int wdig_base(int h, int i) { return (4 * h + i) * 32 + (PAD ? 16 * h : 0); }
+template <bool PAD>
+constexpr int WDIG_BYTES = 4 * (4 * 4 * 32 + (PAD ? 16 * 3 : 0));
 
-template <int D, bool FULL, bool SCORES>
-__device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int l, const v8i* qop,
+template <int D, bool FULL, bool SCORES, bool PAD>
+__device__ __forceinline__ void compute_tile(const TileRegs<D>& t, uint32_t wdig, int l, const v8i* qop,
                                              const QConst& qc, WaveState<D>& st, int tok0, int ctx,
                                              float* __restrict__ srow) {
     constexpr int NC = D / 128, NB = D / 16;
     const int j = l & 15, grp = l >> 4;
-    {
-        const uint4 k = t.meta[0], v = t.meta[1];
-        lds.meta[2 * l] = make_float4(__uint_as_float(k.x), __uint_as_float(k.y), __uint_as_float(v.x),
-                                      __uint_as_float(v.y));
-        lds.meta[2 * l + 1] = make_float4(__uint_as_float(k.z), __uint_as_float(k.w), __uint_as_float(v.z),
-                                          __uint_as_float(v.w));
-    }
     // ---- q.k: raw scores q.k^ of tokens 16m + j, head grp ----
     float s[8];
-    float4 mt[8];
     float tmax = -INFINITY;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         v4f cq = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NC; ++c) cq = mma_qk(qop[c], fp4_operand(t.kc[m][2 * c], t.kc[m][2 * c + 1]), cq, qc.scale_a);
-        mt[m] = lds.meta[16 * m + j];
-        float x = fmaf(mt[m].x, (cq[0] + cq[1]) + (cq[2] + cq[3]), mt[m].y * qc.qsum);
+        float x = fmaf(t.km[m].x, (cq[0] + cq[1]) + (cq[2] + cq[3]), t.km[m].y * qc.qsum);
         if (!FULL && tok0 + 16 * m + j >= ctx) x = -INFINITY;
         s[m] = x;
         tmax = fmaxf(tmax, x);
@@ -259,12 +359,12 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
         const float p = __builtin_amdgcn_exp2f(fmaf(s[m], qc.cB, -st.cbm));
         float x;
         if (FULL) {
-            x = p * mt[m].z;
-            st.c_run = fmaf(p, mt[m].w, st.c_run);
+            x = p * t.vm[m].x;
+            st.c_run = fmaf(p, t.vm[m].y, st.c_run);
         } else {
             const bool valid = tok0 + 16 * m + j < ctx;
-            x = valid ? p * mt[m].z : 0.f;
-            st.c_run += valid ? p * mt[m].w : 0.f;
+            x = valid ? p * t.vm[m].x : 0.f;
+            st.c_run += valid ? p * t.vm[m].y : 0.f;
         }
         st.l_run += p;
         w[m] = x;
@@ -304,19 +404,19 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
     const uint32_t d1a = __builtin_amdgcn_perm(H[1], H[0], 0x06040200u), d1b = __builtin_amdgcn_perm(H[3], H[2], 0x06040200u);
     const uint32_t d3a = __builtin_amdgcn_perm(H[1], H[0], 0x07050301u), d3b = __builtin_amdgcn_perm(H[3], H[2], 0x07050301u);
     {
-        uint32_t* wd = lds.wdig;
-        wd[wdig_base(grp, 0) + j] = d0a; wd[wdig_base(grp, 0) + 16 + j] = d0b;
-        wd[wdig_base(grp, 1) + j] = d1a; wd[wdig_base(grp, 1) + 16 + j] = d1b;
-        wd[wdig_base(grp, 2) + j] = d2a; wd[wdig_base(grp, 2) + 16 + j] = d2b;
-        wd[wdig_base(grp, 3) + j] = d3a; wd[wdig_base(grp, 3) + 16 + j] = d3b;
+        auto put = [&](int i, int half, uint32_t v) { lds_store<uint32_t>(wdig + 4 * (wdig_base<PAD>(grp, i) + 16 * half + j), v); };
+        put(0, 0, d0a); put(0, 1, d0b);
+        put(1, 0, d1a); put(1, 1, d1b);
+        put(2, 0, d2a); put(2, 1, d2b);
+        put(3, 0, d3a); put(3, 1, d3b);
     }
     // p.v operand of column j = 4h + i: k = 16 grp + s <- word 4 grp + s/4 byte s%4,
     // k = 64 + 16 grp + s <- word 16 + 4 grp + s/4 byte s%4
     v8i wop;
     {
-        const int base = wdig_base(j >> 2, j & 3) + 4 * grp;
-        const uint4 lo = *reinterpret_cast<const uint4*>(&lds.wdig[base]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&lds.wdig[base + 16]);
+        const uint32_t base = wdig + 4 * (wdig_base<PAD>(j >> 2, j & 3) + 4 * grp);
+        const uint4 lo = lds_load4(base);
+        const uint4 hi = lds_load4(base + 64);
         wop[0] = (int)lo.x; wop[1] = (int)lo.y; wop[2] = (int)lo.z; wop[3] = (int)lo.w;
         wop[4] = (int)hi.x; wop[5] = (int)hi.y; wop[6] = (int)hi.z; wop[7] = (int)hi.w;
     }
@@ -332,7 +432,22 @@ __device__ __forceinline__ void compute_tile(const Tile<D>& t, WaveLds& lds, int
     }
 }
 
-template <int D, bool SCORES, bool ROT, bool GENERAL, bool FUSE>
+// LDS of a split workgroup of W waves: SLOTS tile slots per wave, then one
+// area per wave for its query rows (before the first tile) and its
+// weight-digit transpose (after); at the end, the waves' partial results
+// reuse the tile slots.
+template <int D, int W, int SLOTS>
+struct SplitLds {
+    static constexpr bool PAD = W == 4;
+    static constexpr int AREA = WDIG_BYTES<PAD>;
+    static constexpr int SLOTS_BYTES = W * SLOTS * TileShape<D>::BYTES;
+    static constexpr int BYTES = SLOTS_BYTES + W * AREA;
+    static_assert(4 * D * 2 <= AREA, "the query rows of four heads fit a wave's area");
+    static_assert(BYTES <= 160 * 1024, "a workgroup's LDS fits the compute unit");
+    static_assert((W * 4 * D + W * 4 * 3) * 4 + 4 <= SLOTS_BYTES, "the waves' partials fit the tile slots");
+};
+
+template <int D, bool SCORES, bool ROT, bool GENERAL, bool FUSE, int W, int SLOTS>
 __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int layer, const BatchDesc& bd,
                                                     const uint16_t* __restrict__ q, float sm, int splits,
                                                     float* __restrict__ ws, float* __restrict__ out,
@@ -345,6 +460,9 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
     constexpr int G = 4;
     constexpr int NC = D / 128;  // k-chunks of the q.k product
     constexpr int NB = D / 16;   // 16-dim blocks of the p.v product
+    using LdsT = SplitLds<D, W, SLOTS>;
+    constexpr bool PAD = LdsT::PAD;
+    constexpr int TB = TileShape<D>::BYTES;
     const int Hkv = pv.Hkv, Hq = pv.Hq;
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int Gq = GENERAL ? Hq / Hkv : G;  // the pool's GQA group
@@ -358,128 +476,121 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
     split_range(ctx, bd.per, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
 
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63;
     const int j = l & 15, grp = l >> 4;
     const int hq = j >> 2, iq = j & 3;  // this lane's q.k row: digit iq of head hq
 
-    __shared__ __align__(16) WaveLds lds_s[4];
-    __shared__ float o_s[4][G][D];
-    __shared__ float ml_s[4][G][3];
+    __shared__ __align__(16) uint8_t smem[LdsT::BYTES];
+    const uint32_t slot0 = lds_addr(smem) + wave * SLOTS * TB;
+    const uint32_t area = lds_addr(smem) + LdsT::SLOTS_BYTES + wave * LdsT::AREA;
+    auto slot_of = [&](int t) { return slot0 + (SLOTS == 2 ? (t & 1) * TB : 0); };
 
-    const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
     const int n_pages = (ctx + PAGE - 1) / PAGE;
     float* srow = scores && (!GENERAL || grp < nh) ? scores + (head0 + grp) * sstride : nullptr;
-    WaveLds& lds = lds_s[wave];
+    // the block table through the constant address space: page ids are
+    // uniform across a wave, so they come in by scalar loads, which do not
+    // queue behind the tiles' DMA loads
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(pv.bt + (int64_t)bd.seq[e] * pv.bt_stride);
 
-    // ---- this wave's tiles: page pairs pg0/2 + wave + 4i, i < T ----
+    // ---- this wave's tiles: page pairs pg0/2 + wave + W i, i < T ----
     const int pr_first = pg0 / 2 + wave;
     const int pr_end = (pg1 + 1) / 2;
-    const int T = pr_first < pr_end ? (pr_end - pr_first + 3) / 4 : 0;
-    // the last tile of the sequence may be partly past ctx; it is done on its own
-    const bool last_partial = T > 0 && 2 * (pr_first + 4 * (T - 1)) * PAGE + 2 * PAGE > ctx;
+    const int T = pr_first < pr_end ? (pr_end - pr_first + W - 1) / W : 0;
+    // the last tile of the sequence may be partly past ctx (and its second
+    // page past the last page: it then re-reads the first)
+    const bool last_partial = T > 0 && 2 * (pr_first + W * (T - 1)) * PAGE + 2 * PAGE > ctx;
     const int TF = last_partial ? T - 1 : T;  // full tiles
-    auto tok0_of = [&](int t) { return 2 * (pr_first + 4 * t) * PAGE; };
+    auto tok0_of = [&](int t) { return 2 * (pr_first + W * t) * PAGE; };
+    const uint32_t voff = 16 * l;
+    auto issue = [&](int t) {  // tile t's DMA into slot t % SLOTS
+        const int pair = pr_first + W * t;
+        const int id0 = bt[2 * pair], id1 = bt[min(2 * pair + 1, n_pages - 1)];
+        const uint32_t slot = slot_of(t);
+        dma_block<D>(pv.pages + (int64_t)id0 * pv.page_bytes + lhoff, voff, slot);
+        dma_block<D>(pv.pages + (int64_t)id1 * pv.page_bytes + lhoff, voff, slot + TileShape<D>::BLK);
+    };
 
-    // Tiles go in chunks of 64: lane k of pid0/pid1 holds the physical ids of
-    // the two pages of tile c0 + k.  Two tile buffers keep one tile in flight
-    // while the other is computed; every load is issued unconditionally
-    // (indices clamped to the chunk's last tile, re-read from cache), and the
-    // loop runs whole two-tile rounds with fixed buffer roles so that no
-    // buffer is ever copied (a copy would wait for its load).
-    Tile<D> ta, tb;
-    int pid0 = 0, pid1 = 0, Tc = 0;
-    auto fetch_ids = [&](int c0) {
-        Tc = min(64, TF - c0);
-        pid0 = pid1 = 0;
-        if (l < Tc) {
-            const int pair = pr_first + 4 * (c0 + l);
-            pid0 = bt[2 * pair];
-            pid1 = bt[2 * pair + 1];
-        }
-    };
-    auto load = [&](Tile<D>& tile, int t) {
-        const int tt = min(t, Tc - 1);
-        load_tile<D>(tile, pv.pages + (int64_t)__builtin_amdgcn_readlane(pid0, tt) * pv.page_bytes + lhoff,
-                     pv.pages + (int64_t)__builtin_amdgcn_readlane(pid1, tt) * pv.page_bytes + lhoff, l);
-    };
-    // The query rows of the group's G heads (contiguous, G D bf16) are loaded
-    // first, in 16-byte pieces, so that preparing the query operand waits for
-    // them only while the first tile is still in flight; they pass through
-    // this wave's metadata area of LDS, unused until the first tile.
+    // The query rows of the group's G heads (contiguous, G D bf16) go to the
+    // wave's area of LDS before any tile is in flight (the compiler's wait
+    // for them must not be taken after a DMA load); the rotated variant
+    // widens them to fp32 and transforms them in the wave's last tile slot
+    // before that slot's first DMA.
     constexpr int QPIECES = G * D * 2 / 16 / 64;  // 16-byte pieces per lane
-    static_assert(G * D * 2 <= sizeof(WaveLds::meta), "query rows fit the metadata area");
-    uint4 qraw[QPIECES];
     {
+        uint4 qraw[QPIECES];
         const uint4* qsrc = reinterpret_cast<const uint4*>(q + head0 * D);
 #pragma unroll
         for (int i = 0; i < QPIECES; ++i) {  // piece p holds bf16 8p .. 8p + 7 of the four rows
             const int p = l + 64 * i;
             qraw[i] = !GENERAL || 8 * p < nh * D ? qsrc[p] : make_uint4(0u, 0u, 0u, 0u);
         }
-    }
-    if (TF > 0) {
-        fetch_ids(0);
-        load(ta, 0);
-    }
-    // The rotated variant scores H q against the codes of H k (the launcher
-    // passes sm / D): the rows are widened to fp32 over this wave's whole LDS
-    // area and transformed there, stages h = 1 .. D/2 as on append.
-    static_assert(!ROT || sizeof(WaveLds) >= G * D * sizeof(float), "fp32 query rows fit the wave's LDS area");
-    if constexpr (ROT) {
-        float* qf = reinterpret_cast<float*>(&lds);
+        if constexpr (ROT) {
+            const uint32_t qf = slot0 + (SLOTS - 1) * TB;  // fp32 [G][D]
 #pragma unroll
-        for (int i = 0; i < QPIECES; ++i) {
-            const uint32_t u[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
+            for (int i = 0; i < QPIECES; ++i) {
+                const uint32_t u[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                qf[8 * (l + 64 * i) + 2 * k] = bf16lo(u[k]);
-                qf[8 * (l + 64 * i) + 2 * k + 1] = bf16hi(u[k]);
+                for (int k = 0; k < 4; ++k) {
+                    lds_store<float>(qf + 4 * (8 * (l + 64 * i) + 2 * k), bf16lo(u[k]));
+                    lds_store<float>(qf + 4 * (8 * (l + 64 * i) + 2 * k + 1), bf16hi(u[k]));
+                }
             }
+        } else {
+#pragma unroll
+            for (int i = 0; i < QPIECES; ++i)
+                lds_store<u32x4>(area + 16 * (l + 64 * i), u32x4{qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w});
         }
-        __syncthreads();
-        for (int h = 1; h < D; h *= 2) {  // additions only: nothing to contract
+    }
+    // (with one slot a wave, the rotated rows sit in the slot of tile 0)
+    if (T > 0 && !(ROT && SLOTS == 1)) issue(0);
+    if (ROT) {
+        // stages h = 1 .. D/2 as on append, additions only: nothing to contract
+        const uint32_t qf = slot0 + (SLOTS - 1) * TB;
+        auto at = [&](int i) { return qf + 4 * i; };
+        for (int h = 1; h < D; h *= 2) {
             float a[G * D / 128], b[G * D / 128];
             int ia[G * D / 128];
 #pragma unroll
             for (int k = 0; k < G * D / 128; ++k) {  // pair p = l + 64 k of the G D / 2 pairs
                 const int pr = l + 64 * k, row = pr / (D / 2), jj = pr % (D / 2);
                 ia[k] = row * D + (jj / h) * 2 * h + jj % h;
-                a[k] = qf[ia[k]];
-                b[k] = qf[ia[k] + h];
+                a[k] = lds_load<float>(at(ia[k]));
+                b[k] = lds_load<float>(at(ia[k] + h));
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int k = 0; k < G * D / 128; ++k) {
-                qf[ia[k]] = a[k] + b[k];
-                qf[ia[k] + h] = a[k] - b[k];
+                lds_store<float>(at(ia[k]), a[k] + b[k]);
+                lds_store<float>(at(ia[k] + h), a[k] - b[k]);
             }
-            __syncthreads();
+            __builtin_amdgcn_wave_barrier();
         }
-    } else {
-        uint4* qdst = reinterpret_cast<uint4*>(lds.meta);
-#pragma unroll
-        for (int i = 0; i < QPIECES; ++i) qdst[l + 64 * i] = qraw[i];
-        __syncthreads();
     }
 
     // ---- query operand: 19-bit fixed point per head, row 4 hq + iq = digit iq of head hq ----
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(lds.meta) + hq * D;
-    const float* qrow_f = reinterpret_cast<const float*>(&lds) + hq * D;
     float qv[NC][32];
     float amax = 0.f, qsum = 0.f;
+    {
+        const uint32_t qrows = ROT ? slot0 + (SLOTS - 1) * TB : area;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int s = 0; s < 32; ++s) {
-            // k of byte s; the K operand puts dim(k) at nibble k % 32 of lane group k / 32
-            const int k = fp8_k(grp, s), ga = k >> 5, n = k & 31;
-            const int dim = 32 * NC * ga + 32 * c + 16 * (n >> 4) + 2 * (n & 7) + ((n >> 3) & 1);
-            const float x = ROT ? qrow_f[dim] : bf16_to_f32(qrow[dim]);
-            qv[c][s] = x;
-            amax = fmaxf(amax, fabsf(x));
-            qsum += x;
-        }
+            for (int s = 0; s < 32; ++s) {
+                // k of byte s; the K operand puts dim(k) at nibble k % 32 of lane group k / 32
+                const int k = fp8_k(grp, s), ga = k >> 5, n = k & 31;
+                const int dim = 32 * NC * ga + 32 * c + 16 * (n >> 4) + 2 * (n & 7) + ((n >> 3) & 1);
+                const float x = ROT ? lds_load<float>(qrows + 4 * (hq * D + dim))
+                                    : bf16_to_f32(lds_load<uint16_t>(qrows + 2 * (hq * D + dim)));
+                qv[c][s] = x;
+                amax = fmaxf(amax, fabsf(x));
+                qsum += x;
+            }
+    }
+    // the rotated rows sat in the last slot: its first DMA goes out now
+    if (ROT && SLOTS == 1 && T > 0) issue(0);
+    if (SLOTS == 2 && T > 1) issue(1);
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     qsum += __shfl_xor(qsum, 16);
@@ -506,62 +617,61 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
     st.l_run = 0.f;
     st.c_run = 0.f;
 
-    for (int c0 = 0; c0 < TF; c0 += 64) {
-        if (c0 > 0) {
-            fetch_ids(c0);
-            load(ta, 0);
-        }
-        auto run = [&](const Tile<D>& tile, int t) {
-            compute_tile<D, true, SCORES>(tile, lds, l, qop, qc, st, tok0_of(c0 + t), ctx, srow);
-        };
-        int t = 0;
-        for (; t + 2 <= Tc; t += 2) {
-            load(tb, t + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            run(ta, t);
-            load(ta, t + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            run(tb, t + 1);
-        }
-        // at most one tile left, already loaded into ta
-        if (t < Tc) run(ta, t);
+    // ---- the tiles: DMA of tile t + SLOTS in flight while tile t is computed ----
+    // (score stores may complete out of order with loads: with scores every
+    // wait is for all outstanding operations)
+    constexpr int DMA = TileShape<D>::DMA;
+    auto wait_tile = [&](int t) {
+        if (!SCORES && SLOTS == 2 && t + 1 < T) wait_vm<DMA>();
+        else wait_vm<0>();
+    };
+    for (int t = 0; t < TF; ++t) {
+        wait_tile(t);
+        TileRegs<D> tr;
+        read_tile<D>(tr, slot_of(t), l);
+        if (t + SLOTS < T) issue(t + SLOTS);
+        compute_tile<D, true, SCORES, PAD>(tr, area, l, qop, qc, st, tok0_of(t), ctx, srow);
     }
     if (last_partial) {
-        const int pair = pr_first + 4 * (T - 1);
-        const int p1 = 2 * pair + 1 < n_pages ? 2 * pair + 1 : 2 * pair;
-        load_tile<D>(ta, pv.pages + (int64_t)bt[2 * pair] * pv.page_bytes + lhoff,
-                     pv.pages + (int64_t)bt[p1] * pv.page_bytes + lhoff, l);
-        compute_tile<D, false, SCORES>(ta, lds, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
+        wait_tile(T - 1);
+        TileRegs<D> tr;
+        read_tile<D>(tr, slot_of(T - 1), l);
+        compute_tile<D, false, SCORES, PAD>(tr, area, l, qop, qc, st, tok0_of(T - 1), ctx, srow);
     }
 
     // ---- this wave's partial: sum the digit columns, and each head's lanes ----
     const float l_run = row_sum16(st.l_run), c_run = row_sum16(st.c_run);  // head grp
+    float4 o4[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        o4[b].x = quad_sum(st.acc[b][0]);
+        o4[b].y = quad_sum(st.acc[b][1]);
+        o4[b].z = quad_sum(st.acc[b][2]);
+        o4[b].w = quad_sum(st.acc[b][3]);
+    }
+    __syncthreads();  // every wave is done with its tile slots, which the partials reuse
+    float(*o_s)[G][D] = reinterpret_cast<float(*)[G][D]>(smem);
+    float(*ml_s)[G][3] = reinterpret_cast<float(*)[G][3]>(smem + W * G * D * 4);
     if (j == 0) {
         ml_s[wave][grp][0] = st.cbm;  // log2 units
         ml_s[wave][grp][1] = l_run;
         ml_s[wave][grp][2] = c_run;
     }
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        float4 o;
-        o.x = quad_sum(st.acc[b][0]);
-        o.y = quad_sum(st.acc[b][1]);
-        o.z = quad_sum(st.acc[b][2]);
-        o.w = quad_sum(st.acc[b][3]);
-        if (iq == 0) *reinterpret_cast<float4*>(&o_s[wave][hq][16 * b + 4 * grp]) = o;
-    }
+    for (int b = 0; b < NB; ++b)
+        if (iq == 0) *reinterpret_cast<float4*>(&o_s[wave][hq][16 * b + 4 * grp]) = o4[b];
     __syncthreads();
 
-    // ---- combine the four waves, write this split's partial ----
+    // ---- combine the W waves, write this split's partial ----
     DecodeWs w(ws, bd.n, Hq, D, splits);
-    {
+    if (threadIdx.x < 64 * G) {
         const int h = threadIdx.x >> 6;
         float M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_s[v][h][0]);
-        float f[4], lsum = 0.f;
+        for (int v = 0; v < W; ++v) M = fmaxf(M, ml_s[v][h][0]);
+        float f[W], lsum = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < W; ++v) {
             f[v] = __builtin_amdgcn_exp2f(ml_s[v][h][0] - M);
             lsum += f[v] * ml_s[v][h][1];
         }
@@ -571,7 +681,7 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
             const int d = l + 64 * k;
             float o = 0.f;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) o += f[v] * (o_s[v][h][d] + ml_s[v][h][2]);
+            for (int v = 0; v < W; ++v) o += f[v] * (o_s[v][h][d] + ml_s[v][h][2]);
             if (!GENERAL || h < nh) {
                 if constexpr (FUSE) store_agent(&w.o[row * D + d], o);
                 else w.o[row * D + d] = o;
@@ -594,7 +704,7 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
         // thread's partial stores have completed before the workgroup counts
         // itself, and the merging workgroup loads them after the count shows
         // every split done.
-        __shared__ int last_s;
+        int* last_s = reinterpret_cast<int*>(smem + W * G * (D + 3) * 4);  // past the partials
         wait_stores();
         __syncthreads();
         const int live = live_splits(ctx, bd.per);
@@ -603,36 +713,47 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
             const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const int is_last = before == live - 1;
             if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
-            last_s = is_last;
+            *last_s = is_last;
         }
         __syncthreads();
-        if (!last_s) return;
+        if (!*last_s || threadIdx.x >= 64 * G) return;
         const int h = threadIdx.x >> 6;
         if (GENERAL && h >= nh) return;
         merge_live_splits<D / 64>(w, (head0 + h) * splits, live, l, out + (head0 + h) * D);
     }
 }
 
+// Workgroup shape of the split kernel: eight waves (two per SIMD, 244
+// registers a wave) with one tile slot each fill the compute unit's 160 KiB
+// of LDS; while a wave computes one tile the DMA of its next is in flight,
+// and the SIMD's other wave covers the first's stalls.  (Four waves with two
+// slots each, one wave per SIMD, measured 41.3 against 38.9 us a 27B-geometry
+// decode call: 296 registers a wave, moved through the accumulation
+// registers.)
+constexpr int SPLIT_WAVES = 8, SPLIT_SLOTS = 1;
+
 // Group 4: the four heads of each KV head's group in one launch.  FUSE: the
 // last split of each (sequence, KV head) to finish merges the partials into
 // out (at most FUSED_MERGE_MAX_SPLITS splits).
-template <int D, bool SCORES, bool ROT, bool FUSE>
-__global__ __launch_bounds__(256) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
-                                                             const uint16_t* __restrict__ q, float sm, int splits,
-                                                             float* __restrict__ ws, float* __restrict__ out,
-                                                             float* __restrict__ scores, int64_t sstride) {
-    decode_q2_mfma_body<D, SCORES, ROT, false, FUSE>(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, 0, 4);
+template <int D, bool SCORES, bool ROT, bool FUSE, int W, int SLOTS>
+__global__ __launch_bounds__(64 * W) void decode_q2_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                                const uint16_t* __restrict__ q, float sm, int splits,
+                                                                float* __restrict__ ws, float* __restrict__ out,
+                                                                float* __restrict__ scores, int64_t sstride) {
+    decode_q2_mfma_body<D, SCORES, ROT, false, FUSE, W, SLOTS>(pv, layer, bd, q, sm, splits, ws, out, scores, sstride,
+                                                               0, 4);
 }
 
 // Other groups: heads h0 .. h0 + nh - 1 of each KV head's group.
-template <int D, bool SCORES, bool ROT, bool FUSE>
-__global__ __launch_bounds__(256) void decode_q2_mfma_group_kernel(PoolView pv, int layer, BatchDesc bd,
-                                                                   const uint16_t* __restrict__ q, float sm,
-                                                                   int splits, float* __restrict__ ws,
-                                                                   float* __restrict__ out,
-                                                                   float* __restrict__ scores, int64_t sstride,
-                                                                   int h0, int nh) {
-    decode_q2_mfma_body<D, SCORES, ROT, true, FUSE>(pv, layer, bd, q, sm, splits, ws, out, scores, sstride, h0, nh);
+template <int D, bool SCORES, bool ROT, bool FUSE, int W, int SLOTS>
+__global__ __launch_bounds__(64 * W) void decode_q2_mfma_group_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                                      const uint16_t* __restrict__ q, float sm,
+                                                                      int splits, float* __restrict__ ws,
+                                                                      float* __restrict__ out,
+                                                                      float* __restrict__ scores, int64_t sstride,
+                                                                      int h0, int nh) {
+    decode_q2_mfma_body<D, SCORES, ROT, true, FUSE, W, SLOTS>(pv, layer, bd, q, sm, splits, ws, out, scores, sstride,
+                                                              h0, nh);
 }
 
 // The split kernels of a decode call; fuse: each launch also merges (out).
@@ -656,8 +777,9 @@ static hipError_t launch_decode_q2_splits(const PoolView& pv, int layer, const B
     if (Gq == 4) {
         flags([&](auto d, auto sc, auto r, auto fu) {
             hipLaunchKernelGGL((decode_q2_mfma_kernel<decltype(d)::value, decltype(sc)::value, decltype(r)::value,
-                                                      decltype(fu)::value>),
-                               grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores, sstride);
+                                                      decltype(fu)::value, SPLIT_WAVES, SPLIT_SLOTS>),
+                               grid, dim3(64 * SPLIT_WAVES), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores,
+                               sstride);
         });
         return hipGetLastError();
     }
@@ -666,9 +788,10 @@ static hipError_t launch_decode_q2_splits(const PoolView& pv, int layer, const B
         const int nh = Gq - h0 < 4 ? Gq - h0 : 4;
         flags([&](auto d, auto sc, auto r, auto fu) {
             hipLaunchKernelGGL((decode_q2_mfma_group_kernel<decltype(d)::value, decltype(sc)::value,
-                                                            decltype(r)::value, decltype(fu)::value>),
-                               grid, dim3(256), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores, sstride, h0,
-                               nh);
+                                                            decltype(r)::value, decltype(fu)::value, SPLIT_WAVES,
+                                                            SPLIT_SLOTS>),
+                               grid, dim3(64 * SPLIT_WAVES), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores,
+                               sstride, h0, nh);
         });
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
