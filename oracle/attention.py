@@ -81,6 +81,29 @@ def prefill(q, K, V, sm: float, q_start: int, rows=None):
     return out
 
 
+def prefill_dense(q, K, V, sm: float, q_start: int):
+    """The same causal prefill as ``prefill``, as one fp64 matrix product per
+    query head over the whole chunk: scores [n][T] with keys past a row's
+    position masked out, row softmax, then the product with V.  For checking
+    every row of a long chunk (one product per head instead of a vector product
+    per row and head); pinned against ``prefill`` in
+    tests/test_oracle_pool_attention.py."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    n, Hq, D = q.shape
+    T = q_start + n
+    G = Hq // K.shape[1]
+    visible = np.arange(T)[None, :] <= (q_start + np.arange(n))[:, None]       # [n][T]
+    out = np.empty((n, Hq, D), np.float64)
+    for h in range(Hq):
+        g = h // G
+        s = sm * (q[:, h, :] @ K[:T, g, :].T)
+        s = np.where(visible, s, -np.inf)
+        out[:, h, :] = _softmax(s) @ V[:T, g, :]
+    return out
+
+
 def split_partials(s, Vg, bounds):
     """Per split [a, b): (m, l, o) for scores s [T] and values Vg [T][D]."""
     parts = []

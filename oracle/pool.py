@@ -53,7 +53,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import bf16, codec
+from . import bf16, codec, layout
 from .accounting import page_bytes
 from .layout import PAGE, Bf16Block, Q2Block, Q8Block, block_bytes, block_offset
 
@@ -272,3 +272,50 @@ def dequantized_rows(fmt: str, k_rows, v_rows):
         c, s = codec.q8_quantize_k_page(k[p0:p0 + PAGE])
         K[p0:p0 + PAGE] = codec.q8_dequantize(c, s[None])
     return K, V
+
+
+def sequence_blocks(fmt: str, k_rows, v_rows):
+    """Byte images of the (layer, KV head) blocks of a sequence appended from
+    position 0 in whole pages: [T / 64][H][block_bytes] uint8 for rows
+    k_rows, v_rows [T][H][D] (fp32 values of bf16, T a multiple of 64).
+
+    The same codec and layout as OraclePool.append (the 2-bit codec and its
+    block layout; the 8-bit codec with K per channel over each page's 64
+    tokens and V per token), applied to all pages at once, so that whole pools
+    of the large workloads can be checked byte for byte.  Pinned against
+    OraclePool's token-by-token image in tests/test_oracle_pool_attention.py.
+    """
+    k = np.asarray(k_rows, np.float32)
+    v = np.asarray(v_rows, np.float32)
+    T, H, D = k.shape
+    assert T % PAGE == 0 and v.shape == k.shape
+    P = T // PAGE
+    out = np.empty((P, H, block_bytes(fmt, D)), np.uint8)
+    if fmt == "q2":
+        ck, sk, mk = codec.q2_quantize(k)
+        cv, sv, mv = codec.q2_quantize(v)
+        # K codes token-major: [P][H][64][D/4]
+        kp = layout.pack2(ck).reshape(P, PAGE, H, D // 4).transpose(0, 2, 1, 3)
+        out[:, :, :16 * D] = kp.reshape(P, H, 16 * D)
+        # V codes: each dim's 64 slots packed in the V-row word layout, then
+        # placed where the plane puts that dim's words
+        vrows = layout.pack2_vrow(cv.reshape(P, PAGE, H, D).transpose(0, 2, 3, 1))   # [P][H][D][16]
+        plane = np.empty((P, H, 16 * D), np.uint8)
+        plane[:, :, layout.v_plane_index(D)] = vrows
+        out[:, :, 16 * D:32 * D] = plane
+        for off, sc, mn in ((32 * D, sk, mk), (32 * D + 512, sv, mv)):
+            meta = np.stack([sc, mn], axis=-1).astype(np.float32)                  # [T][H][2]
+            meta = meta.reshape(P, PAGE, H, 2).transpose(0, 2, 1, 3)              # [P][H][64][2]
+            out[:, :, off:off + 512] = np.ascontiguousarray(meta).view(np.uint8).reshape(P, H, 512)
+        return out
+    if fmt == "q8":
+        cv, sv = codec.q8_quantize_v(v)                                            # [T][H][D], [T][H]
+        ck, skc = codec.sym_quantize(k.reshape(P, PAGE, H, D), 8, axis=1, dtype=np.float32)
+        out[:, :, :64 * D] = ck.astype(np.int8).transpose(0, 2, 1, 3).reshape(P, H, 64 * D).view(np.uint8)
+        vd = cv.reshape(P, PAGE, H, D).transpose(0, 2, 3, 1)                       # [P][H][D][64]
+        out[:, :, 64 * D:128 * D] = np.ascontiguousarray(vd).reshape(P, H, 64 * D).view(np.uint8)
+        out[:, :, 128 * D:132 * D] = np.ascontiguousarray(skc[:, 0].astype(np.float32)).view(np.uint8).reshape(P, H, 4 * D)
+        vsc = sv.reshape(P, PAGE, H).transpose(0, 2, 1).astype(np.float32)          # [P][H][64]
+        out[:, :, 132 * D:132 * D + 256] = np.ascontiguousarray(vsc).view(np.uint8).reshape(P, H, 256)
+        return out
+    raise ValueError(fmt)

@@ -71,9 +71,12 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
     // 6.6e-7 of the correctly rounded quotient (rcp within one ulp, the product
     // within half an ulp, the quotient below 3.000001), so unless it lies
     // within 2e-6 of a half-integer both round to the same code.  The rare
-    // element that does takes the correctly rounded division.
+    // element that does takes the correctly rounded division, and so does
+    // every element of a row whose scale lies outside [2^-120, 2^120]: there
+    // the reciprocal can overflow (a subnormal scale) or lose its bound (a
+    // subnormal reciprocal).
     const float inv = __builtin_amdgcn_rcpf(sc);
-    bool near = false;
+    bool near = !(sc >= 0x1p-120f && sc <= 0x1p120f);
     float d[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k) {

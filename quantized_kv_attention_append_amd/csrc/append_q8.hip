@@ -34,12 +34,14 @@ namespace kvq {
 // rounded quotient (rcp within one ulp, the product within half an ulp, the
 // quotient at most 127.0001 in size), so unless it lies within 1e-4 of a
 // half-integer both round to the same integer; the rare element that does
-// takes the correctly rounded division.
+// takes the correctly rounded division, and so does every element whose
+// scale lies outside [2^-120, 2^120] (where the reciprocal can overflow or be
+// subnormal).
 __device__ __forceinline__ int8_t q8_code(float x, float s, float inv) {
 #pragma clang fp contract(off)
     const float qa = x * inv;
     float r = rintf(qa);
-    if (fabsf(qa - r) > 0.5f - 1e-4f) r = rintf(x / s);
+    if (!(s >= 0x1p-120f && s <= 0x1p120f) || fabsf(qa - r) > 0.5f - 1e-4f) r = rintf(x / s);
     return (int8_t)fminf(fmaxf(r, -127.0f), 127.0f);
 }
 

@@ -5,16 +5,21 @@
   normalised query of the group's first head; split counts 16, 32, 64, 128,
   each with a 0xFF-filled workspace.  Outputs against the fp64 oracle, and the
   planted key's attention rank against the oracle's rank.
-* 27B-geometry batched decode: 16 layers x 8 lanes x 40,960 tokens in one
-  pool, decoded layer by layer in the launch configuration bench.py times;
-  sampled (layer, lane) outputs against the oracle.
+  The whole 75.5 MB pool is compared byte for byte with the oracle's image.
+* The flat case of "Half the Cache, Twice the Context" (section "The cliff
+  is in the accumulator, not the storage"): 131,072 keys that are all the
+  same row, so every weight is equal and the output is the mean of the 131,072
+  dequantized value rows; a 16-bit running sum would keep a few thousandths
+  of that mass.  At 1 split (one workgroup's running sums over every token),
+  16 and the library's choice.
+(The 27B-geometry workload is checked whole in tests/test_gpu_fullsize.py.)
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle import attention, codec
+from oracle import attention, codec, pool as opool
 from synth import WORKLOADS, kv_rows, page_permutation, planted_position, queries
 from synth.workloads import plant_key
 from tests.gpu_helpers import assert_close, make_pool, need_gpu, say
@@ -42,7 +47,14 @@ def test_long_split_k_decode_planted_key():
     pool, mem = make_pool(w, n_pages, 1, max_seqs=1, max_seq_tokens=ctx)
     seq = pool.reserve(ctx, pages=page_permutation(w, n_pages))
     pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
+    torch.cuda.synchronize()
     say("long decode: oracle")
+    kf, vf = k.float().numpy(), v.float().numpy()
+    blocks = opool.sequence_blocks("q2", kf, vf)                  # [2048][4][9216]; one layer: a page is 4 blocks
+    got = mem.view(n_pages, -1)[torch.as_tensor(page_permutation(w, n_pages).astype(np.int64), device="cuda")]
+    bad = int(np.count_nonzero(got.cpu().numpy() != blocks.reshape(n_pages, -1)))
+    assert bad == 0, f"131072 tokens: {bad} pool bytes differ from the oracle"
+    say(f"long decode: the whole pool ({mem.numel() / 1e6:.1f} MB) bit-exact")
     K, V = _oracle_rows(k, v)
     qn = q[0].float().numpy()
     ref = attention.decode(qn, K, V, w.sm_scale)
@@ -76,34 +88,22 @@ def test_long_split_k_decode_planted_key():
 
 
 @pytest.mark.timeout(600)
-def test_27b_geometry_batched_decode_sampled():
+def test_flat_131072_tokens_output_is_the_mean():
     need_gpu()
-    import quantized_kv_attention_append_amd as kvq
-    w = WORKLOADS["27b"]
-    L, B, ctx = w.n_layers, w.lanes, w.ctx
-    ppl = ctx // 64
-    n_pages = B * ppl
-    _, pb = kvq.token_bytes((L, w.n_kv_heads, w.head_dim, w.n_q_heads), kvq.FMT_Q2)
-    assert n_pages * pb == 3_019_898_880
-    pool = kvq.Pool(n_pages * pb, (L, w.n_kv_heads, w.head_dim, w.n_q_heads), kvq.FMT_Q2, max_seqs=B, max_seq_tokens=ctx)
-    perm = page_permutation(w, n_pages)
-    seqs = [pool.reserve(ctx, pages=perm[i * ppl:(i + 1) * ppl]) for i in range(B)]
-    for layer in range(L):
-        kv = [kv_rows(w, layer, lane, ctx, device="cuda") for lane in range(B)]
-        pool.append(layer, seqs, [0] * B, [ctx] * B, torch.cat([a for a, _ in kv]), torch.cat([b for _, b in kv]))
-        del kv
-    st = pool.stats()
-    assert st["used_pages"] == n_pages and st["free_pages"] == 0
-    sp = pool.decode_splits([ctx] * B)
-    say(f"27B geometry: populated, splits={sp}")
-    samples = {(0, 0), (7, 3), (15, 7)}
-    for layer in range(L):
-        q = queries(w, layer, B, device="cuda")
-        out = pool.decode(layer, seqs, [ctx] * B, q, w.sm_scale, n_splits=sp)
-        for lane in range(B):
-            if (layer, lane) not in samples:
-                continue
-            k, v = kv_rows(w, layer, lane, ctx, device="cuda")
-            K, V = _oracle_rows(k.cpu(), v.cpu())
-            ref = attention.decode(q[lane].float().cpu().numpy(), K, V, w.sm_scale)
-            assert_close(out[lane].cpu().numpy(), ref, f"27B layer {layer} lane {lane}")
+    w = WORKLOADS["long"]
+    ctx = w.ctx
+    _, v = kv_rows(w, 0, 0, ctx)
+    kr, _ = kv_rows(w, 0, 1, 1)
+    k = kr.expand(ctx, -1, -1).contiguous()                      # every key the same row: equal weights
+    q = queries(w, 0, 1)
+    n_pages = ctx // 64
+    pool, mem = make_pool(w, n_pages, 1, max_seqs=1, max_seq_tokens=ctx)
+    seq = pool.reserve(ctx, pages=page_permutation(w, n_pages))
+    pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
+    V = codec.q2_dequantize(*codec.q2_quantize(v.float().numpy()))
+    mean = V.astype(np.float64).mean(axis=0)                      # [Hkv][D]
+    ref = np.repeat(mean, w.group, axis=0)                        # query head h reads KV head h // 4
+    for sp in (1, 16, 0):
+        out = pool.decode(0, [seq], [ctx], q.cuda(), w.sm_scale, n_splits=sp)
+        torch.cuda.synchronize()
+        assert_close(out[0].cpu().numpy(), ref, f"flat 131072 tokens, splits={sp or pool.decode_splits([ctx])}")

@@ -176,48 +176,67 @@ def test_decode_q8_small(w, lens):
                          f"8-bit scores lane {i}", rel_l2=1e-5)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_q8_batch_decode_then_append():
     """Full 8-bit workload: populate 32 layers x 24 lanes, decode every layer,
-    append one token per lane, decode again; sampled (layer, lane) pairs against
-    the oracle, both decodes."""
+    append one token per lane, decode again.  For layers 0, 13 and 31: every
+    lane's full pages byte for byte against the oracle's image, the page the
+    appended token opens against the oracle pool's image of it, and the whole
+    decode output of all 24 lanes (before and after the append) against the
+    oracle."""
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
     w = Q8B
-    lens = q8_batch_lengths(w)
+    lens = [int(x) for x in q8_batch_lengths(w)]
     geom = geom_of(w)
     _, pb = kvq.token_bytes(geom, kvq.FMT_Q8)
-    n_pages = int(sum(-(-(int(L) + 1) // 64) for L in lens))
-    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q8, max_seqs=w.lanes, max_seq_tokens=int(lens.max()) + 64)
+    n_pages = int(sum(-(-(L + 1) // 64) for L in lens))
+    mem = torch.full((n_pages * pb,), 0xA5, dtype=torch.uint8, device="cuda")
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q8, max_seqs=w.lanes, max_seq_tokens=max(lens) + 64, memory=mem)
     perm = page_permutation(w, n_pages)
-    seqs, off = [], 0
+    seqs, bts, off = [], [], 0
     for L in lens:
-        npg = -(-(int(L) + 1) // 64)
-        seqs.append(pool.reserve(int(L) + 1, pages=perm[off:off + npg]))
+        npg = -(-(L + 1) // 64)
+        bts.append(perm[off:off + npg])
+        seqs.append(pool.reserve(L + 1, pages=bts[-1]))
         off += npg
-    say(f"8-bit workload: {n_pages} pages, {n_pages * pb / 1e9:.2f} GB, lengths {lens.min()}..{lens.max()}")
-    B = w.lanes
+    say(f"8-bit workload: {n_pages} pages, {n_pages * pb / 1e9:.2f} GB, lengths {min(lens)}..{max(lens)}")
+    B, H, D = w.lanes, w.n_kv_heads, w.head_dim
+    block = 132 * D + 256
     ws = torch.empty(pool.workspace_bytes(0, B, 0), dtype=torch.uint8, device="cuda")
-    samples = {(0, 0), (13, 7), (31, 23), (31, int(np.argmax(lens)))}
+    pages_of = lambda lane, lp: torch.as_tensor(np.asarray(bts[lane][lp], np.int64), device="cuda")
     for layer in range(w.n_layers):
-        kv = [kv_rows(w, layer, i, int(lens[i]) + 1, device="cuda") for i in range(B)]
-        pool.append(layer, seqs, [0] * B, [int(L) for L in lens],
+        kv = [kv_rows(w, layer, i, lens[i] + 1, device="cuda") for i in range(B)]
+        pool.append(layer, seqs, [0] * B, lens,
                     torch.cat([k[:L] for (k, _), L in zip(kv, lens)]), torch.cat([v[:L] for (_, v), L in zip(kv, lens)]))
         q = queries(w, layer, B, device="cuda")
-        out1 = pool.decode(layer, seqs, [int(L) for L in lens], q, w.sm_scale, ws=ws).cpu()
-        pool.append(layer, seqs, [int(L) for L in lens], [1] * B,
+        out1 = pool.decode(layer, seqs, lens, q, w.sm_scale, ws=ws).cpu().numpy()
+        check = layer in (0, 13, 31)
+        if check:   # the full pages before the next token opens a page
+            full = [mem.view(-1, pb).index_select(0, pages_of(i, slice(0, lens[i] // 64)))[
+                :, layer * H * block:(layer + 1) * H * block].cpu().numpy() for i in range(B)]
+        pool.append(layer, seqs, lens, [1] * B,
                     torch.cat([k[L:L + 1] for (k, _), L in zip(kv, lens)]),
                     torch.cat([v[L:L + 1] for (_, v), L in zip(kv, lens)]))
-        out2 = pool.decode(layer, seqs, [int(L) + 1 for L in lens], q, w.sm_scale, ws=ws).cpu()
-        for (sl, lane) in samples:
-            if sl != layer:
-                continue
-            k, v = (t.cpu().float().numpy() for t in kv[lane])
-            qi = q[lane].float().cpu().numpy()
-            L = int(lens[lane])
-            K, V = opool.dequantized_rows("q8", k[:L], v[:L])
-            assert_close(out1[lane].numpy(), attention.decode(qi, K, V, w.sm_scale), f"8-bit layer {layer} lane {lane} ctx {L}")
-            K, V = opool.dequantized_rows("q8", k, v)
-            assert_close(out2[lane].numpy(), attention.decode(qi, K, V, w.sm_scale),
-                         f"8-bit layer {layer} lane {lane} ctx {L + 1} after append")
+        out2 = pool.decode(layer, seqs, [L + 1 for L in lens], q, w.sm_scale, ws=ws).cpu().numpy()
+        if check:
+            qh = q.float().cpu().numpy()
+            ref1, ref2 = [], []
+            for i, L in enumerate(lens):
+                k, v = (t.cpu().float().numpy() for t in kv[i])
+                blocks = opool.sequence_blocks("q8", k[:L], v[:L])
+                bad = int(np.count_nonzero(full[i] != blocks.reshape(L // 64, H * block)))
+                assert bad == 0, f"8-bit layer {layer} lane {i}: {bad} bytes of the full pages differ"
+                one = opool.OraclePool("q8", w.n_layers, H, D, 1, fill=0xA5)
+                one.append(layer, 0, [0], 0, k[L:L + 1], v[L:L + 1])
+                got = mem.view(-1, pb)[int(bts[i][L // 64])][layer * H * block:(layer + 1) * H * block].cpu().numpy()
+                assert np.array_equal(got, one.data[0, layer * H * block:(layer + 1) * H * block]), \
+                    f"8-bit layer {layer} lane {i}: the page of token {L} differs"
+                K, V = opool.dequantized_rows("q8", k[:L], v[:L])
+                ref1.append(attention.decode(qh[i], K, V, w.sm_scale))
+                K, V = opool.dequantized_rows("q8", k, v)
+                ref2.append(attention.decode(qh[i], K, V, w.sm_scale))
+            assert_close(out1, np.stack(ref1), f"8-bit layer {layer}, all 24 lanes")
+            assert_close(out2, np.stack(ref2), f"8-bit layer {layer}, all 24 lanes after one more token")
+            say(f"8-bit layer {layer}: pages bit-exact, whole outputs within tolerance")
         del kv

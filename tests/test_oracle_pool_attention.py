@@ -247,3 +247,36 @@ def test_planted_rank_counts_strictly_higher_scores():
     assert attention.planted_rank(s, 2) == 1
     assert attention.planted_rank(s, 3) == 3   # 0.5 and 0.5 above it
     assert attention.planted_rank(s, 0) == 4
+
+
+@pytest.mark.parametrize("fmt,D", [("q2", 256), ("q2", 128), ("q8", 128), ("q8", 256)])
+def test_sequence_blocks_equal_the_token_by_token_pool(fmt, D):
+    """The whole-sequence page images equal the pool image that appends one
+    token at a time (OraclePool), block by block."""
+    w, k, v = _c0_rows(192)
+    k, v = k[..., :D].copy(), v[..., :D].copy()
+    H = k.shape[1]
+    bt = np.array([2, 0, 1], np.int32)
+    p = pool.OraclePool(fmt, 2, H, D, 3, fill=0x3C)
+    start = 0
+    for n in (70, 1, 57, 64):
+        p.append(1, 0, bt, start, k[start:start + n], v[start:start + n])
+        start += n
+    blocks = pool.sequence_blocks(fmt, k, v)
+    assert blocks.shape == (3, H, layout.block_bytes(fmt, D))
+    bb = layout.block_bytes(fmt, D)
+    for lp in range(3):
+        for h in range(H):
+            off = (1 * H + h) * bb                       # layer 1
+            assert np.array_equal(p.data[bt[lp], off:off + bb], blocks[lp, h]), (lp, h)
+
+
+def test_prefill_dense_equals_the_row_loop():
+    rng = np.random.default_rng(41)
+    n, T0, Hq, Hkv, D = 9, 23, 4, 2, 16
+    q = rng.standard_normal((n, Hq, D))
+    K = rng.standard_normal((T0 + n, Hkv, D))
+    V = rng.standard_normal((T0 + n, Hkv, D))
+    a = attention.prefill(q, K, V, 0.25, T0)
+    b = attention.prefill_dense(q, K, V, 0.25, T0)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-13)
