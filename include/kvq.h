@@ -284,6 +284,26 @@ kv_status kv_attn_decode(kv_pool* pool, int32_t layer, int32_t n, const int32_t*
                          const uint16_t* d_q, float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes,
                          float* d_out, float* d_scores, int64_t scores_stride, kv_stream_t stream);
 
+/* Bytes of the static device array kv_attn_decode_static uses as its
+ * workspace (one per device). */
+#define KV_STATIC_SCRATCH_BYTES (16ll << 20)
+
+/* kv_attn_decode for callers that cannot allocate device memory at call time
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results as kv_attn_decode (and the same
+ * split count for n_splits = 0), with the workspace a file-scope device array
+ * of KV_STATIC_SCRATCH_BYTES per device instead of d_ws.  Nothing is
+ * allocated: the array's device address is looked up once per device on the
+ * first call there, with the pool's device current.  A batch whose workspace
+ * (kv_workspace_bytes) exceeds the array is refused with KV_ERR_WORKSPACE.
+ * All calls on one device share the array: calls that overlap on a device
+ * (other streams, other pools) race and must be ordered by the caller.
+ * Errors: those of kv_attn_decode, KV_ERR_ARG (the current device is not the
+ * pool's), KV_ERR_WORKSPACE (batch too large for the array). */
+kv_status kv_attn_decode_static(kv_pool* pool, int32_t layer, int32_t n, const int32_t* seqs, const int64_t* ctx_len,
+                                const uint16_t* d_q, float sm_scale, int32_t n_splits, float* d_out, float* d_scores,
+                                int64_t scores_stride, kv_stream_t stream);
+
 /* Causal prefill of a chunk of n_q queries of one sequence that sit at
  * positions q_start .. q_start + n_q - 1, after the chunk's own K/V have been
  * appended ("KV at 9 KB a token", opening section: prefill attention reads

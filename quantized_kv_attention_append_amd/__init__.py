@@ -248,6 +248,32 @@ class Pool:
                                  int(sc_stride), _stream(stream)))
         return out
 
+    def decode_static(self, layer: int, seqs, ctx_len, q: torch.Tensor, sm_scale: float, n_splits: int = 0,
+                      out: Optional[torch.Tensor] = None, scores: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+        """decode() with the library's static device workspace instead of ws
+        (kv_attn_decode_static): the library allocates nothing; out is
+        allocated here only when not given."""
+        n = len(seqs)
+        g = self.geom
+        _same_length(n, ctx_len=ctx_len)
+        if tuple(q.shape) != (n, g.n_q_heads, g.head_dim):
+            raise ValueError(f"q must be [{n}][{g.n_q_heads}][{g.head_dim}], got {tuple(q.shape)}")
+        if out is None:
+            out = torch.empty((n, g.n_q_heads, g.head_dim), dtype=torch.float32, device=q.device)
+        sc_ptr, sc_stride = C.c_void_p(0), 0
+        if scores is not None:
+            if scores.dim() != 3:
+                raise ValueError("scores must be [n][Hq][stride]")
+            sc_stride = scores.shape[-1]
+            sc_ptr = _dev(scores, torch.float32, "scores", (n, g.n_q_heads, sc_stride), self.device)
+        check(lib.kv_attn_decode_static(self._h, int(layer), n, _i32(seqs), _i64(ctx_len),
+                                        _dev(q, torch.bfloat16, "q", device=self.device), float(sm_scale),
+                                        int(n_splits),
+                                        _dev(out, torch.float32, "out", (n, g.n_q_heads, g.head_dim), self.device),
+                                        sc_ptr, int(sc_stride), _stream(stream)))
+        return out
+
     def prefill(self, layer: int, seq: int, q_start: int, q: torch.Tensor, sm_scale: float, n_splits: int = 0,
                 ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         """Causal prefill of a chunk q bf16 [n_q][Hq][D] at positions q_start.. -> fp32 [n_q][Hq][D]."""

@@ -59,6 +59,7 @@ SIGNATURES = {
     "kv_workspace_bytes": [_P, _I32, _I32, _I32, _PI64],
     "kv_decode_splits": [_P, _I32, _PI64, _PI32],
     "kv_attn_decode": [_P, _I32, _I32, _PI32, _PI64, _P, _F, _I32, _P, _I64, _P, _P, _I64, _P],
+    "kv_attn_decode_static": [_P, _I32, _I32, _PI32, _PI64, _P, _F, _I32, _P, _P, _I64, _P],
     "kv_attn_prefill": [_P, _I32, _I32, _I64, _I32, _P, _F, _I32, _P, _I64, _P, _P],
     "kv_dequant_page": [_P, _I32, _I32, _I32, _I32, _P, _P],
     "kv_last_error": [],

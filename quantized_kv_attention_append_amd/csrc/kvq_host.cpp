@@ -40,6 +40,14 @@ kv_status fail(kv_status s, const char* fmt, ...) {
     return s;
 }
 
+}  // namespace
+
+namespace kvq {
+kv_status set_error(kv_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace kvq
+
+namespace {
+
 kv_status hip_fail(hipError_t e, const char* what) {
     return fail(KV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
@@ -158,6 +166,10 @@ void push_free(kv_pool* p, int32_t pg) {
     }
 }
 }  // namespace
+
+namespace kvq {
+int pool_device(const kv_pool* p) { return p ? p->device : -1; }
+}  // namespace kvq
 
 extern "C" {
 

@@ -125,6 +125,11 @@ hipError_t launch_copy_ranges(const CopyRange* r, int n, hipStream_t s);
 hipError_t launch_dequant_page(const PoolView& pv, int fmt, int page, int layer, int head, int kv, float* out,
                                hipStream_t s);
 
+// Sets the calling thread's last-error message and returns s.
+kv_status set_error(kv_status s, const char* msg);
+// The device a pool was created on (-1 for NULL).
+int pool_device(const kv_pool* p);
+
 // Decode workspace: partial outputs [n][Hq][splits][D] then (max, sum) pairs [n][Hq][splits][2].
 inline int64_t decode_ws_floats(int n, int Hq, int D, int splits) {
     return (int64_t)n * Hq * splits * (D + 2);
