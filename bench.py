@@ -11,16 +11,23 @@ one decode launch per layer for all 8 lanes (16 launches), one bf16 query per
 lane per layer.
 
 Prints one JSON line: KV tokens attended per second (lane x layer x token
-triples), the per-launch roofline of the decode kernel against 8 TB/s HBM, and
-the CPU oracle timed on a bounded sample of the same work.
+triples), the per-launch roofline of the decode kernel against 8 TB/s HBM
+and against a measured probe of the same reads, and the CPU oracle timed on a
+bounded sample of the same work.
 
-    python bench.py [--steps K] [--warmup W] [--splits P] [--no-cpu] [--copy-mib M]
-                    [--no-prefill] [--no-extra]
+    python bench.py [--steps K] [--warmup W] [--splits P] [--no-cpu] [--cpu-units U]
+                    [--copy-mib M] [--no-prefill] [--no-extra]
 
-Besides the headline line's decode, the same JSON line holds the chunked
-prefill (65,536 + 1,024 tokens), the 131,072-token split-K decode at 16..128
-splits (cache-warm and after a 1 GiB flush) and the 8-bit 24-lane x 32-layer
-decode, each with its own figures.
+Besides the headline decode, the same JSON line holds: probes of the chip's
+streaming read rate, of the decode's read pattern without arithmetic and of
+the bf16 matrix cores; the chunked prefill (65,536 + 1,024 tokens); the
+131,072-token split-K decode at 16..128 splits (cache-warm and after a 1 GiB
+flush) with the planted key's rank; the 8-bit 24-lane x 32-layer decode and
+its layer step (decode, then one appended token per lane); the bf16, exact-
+window and rotated 2-bit formats over the 27B batch; and the oracle baseline
+(a pool of worker processes, one BLAS thread each) for the 27B decode and
+populate, the long context per split count, the prefill chunk and the 8-bit
+layer step.
 
 The roofline's "traffic" (HBM bytes a decode call really moves, from the
 FETCH_SIZE and WRITE_SIZE counters scaled by a copy of known size) is read
@@ -43,8 +50,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "quantized_kv_attention_append_amd", "csrc")
-# sources of the two kernels of a 2-bit decode call (split kernel + merge)
-DECODE_SOURCES = ("decode_q2_mfma.hip", "merge_splits.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
+# sources of the kernel of a 2-bit decode call at 8 splits (split partials and their merge)
+DECODE_SOURCES = ("decode_q2_mfma.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q2_mfma_27b_geometry_traffic.md")
 METRIC = "decode attention: KV tokens attended/s and achieved HBM GB/s (% of peak), 2-bit"
 
@@ -55,7 +62,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--splits", type=int, default=0, help="split-K partitions per (lane, KV head); 0 = library choice")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget for the oracle sample")
+    ap.add_argument("--cpu-units", type=int, default=32, help="27B (layer, lane) units in the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0, help="calibration copy size for counter passes (0 = none)")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill leg")
@@ -130,6 +137,7 @@ def prefill_leg(steps: int, warmup: int):
         e1.synchronize()
         ms.append(e0.elapsed_time(e1))
     avg = sum(ms) / len(ms)
+    med = sorted(ms)[len(ms) // 2]
     flops = 4.0 * w.head_dim * w.n_q_heads * sum(prior + i + 1 for i in range(n_q))
     tflops = flops / (avg * 1e-3) / 1e12
     log(f"prefill: {avg:.3f} ms per call, {tflops:.0f} TFLOP/s useful ({100 * tflops / MFMA_BF16_TFLOPS:.1f}% of bf16 peak)")
@@ -137,13 +145,21 @@ def prefill_leg(steps: int, warmup: int):
         "workload": "chunked prefill, 2-bit: 65536 prior + 1024 chunk tokens, 1 layer x 4 KV heads x 256 dims, "
                     "16 query heads",
         "ms_per_call": avg,
+        "ms_median": med,
         "ms_min": min(ms),
+        "median_tflops": flops / (med * 1e-3) / 1e12,
         "useful_flops": flops,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_TFLOPS, "traffic": None,
                      "kernel": "one kv_attn_prefill call: prefill_kernel<256, 1> then prefill_merge_kernel"},
         "chunk_append_ms": chunk_append_ms,
     }
+
+
+def _stats_us(ms):
+    """mean / median / min of a list of millisecond times, in microseconds."""
+    ms = sorted(ms)
+    return {"us_mean": 1e3 * sum(ms) / len(ms), "us_median": 1e3 * ms[len(ms) // 2], "us_min": 1e3 * ms[0]}
 
 
 def _call_ms(fn, reps: int, flush=None):
@@ -186,11 +202,23 @@ def long_context_leg(reps: int):
     n_pages = ctx // 64
     pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q2, max_seqs=1, max_seq_tokens=ctx)
     seq = pool.reserve(ctx, pages=page_permutation(w, n_pages))
-    k, v = kv_rows(w, 0, 0, ctx, device="cuda")
-    q = queries(w, 0, 1, device="cuda")
+    # drawn on the host (as the parity test and the oracle baseline draw them),
+    # so that the oracle's rank of the planted key is over the same rows
+    k, v = kv_rows(w, 0, 0, ctx)
+    q = queries(w, 0, 1)
     plant_key(k, q[0], planted_position(w, ctx), w.group)
+    k, v, q = k.cuda(), v.cuda(), q.cuda()
     pool.append(0, [seq], [0], [ctx], k, v)
     del k, v
+    pos = planted_position(w, ctx)
+    # the planted key's rank among the raw logits of each group's first query
+    # head (1 + keys scoring strictly higher), from the kernel's own scores
+    scores = torch.empty((1, w.n_q_heads, ctx), dtype=torch.float32, device="cuda")
+    pool.decode(0, [seq], [ctx], q, w.sm_scale, scores=scores)
+    sc = scores[0, ::w.group]
+    gpu_rank = [int(x) for x in (1 + (sc > sc[:, pos:pos + 1]).sum(dim=1)).cpu()]
+    del scores, sc
+    log(f"long context: planted key at {pos}, rank among the GPU's logits per KV head {gpu_rank}")
     out = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     alg = ctx * w.n_kv_heads * 2 * (w.head_dim // 4 + 8) + w.n_q_heads * w.head_dim * (2 + 4)
@@ -204,15 +232,18 @@ def long_context_leg(reps: int):
         cold = _call_ms(call, reps, flush=lambda: scratch.fill_(sp))
         res.append({"splits": sp,
                     "us_mean": warm[0] * 1e3, "us_min": warm[1] * 1e3, "us_median": warm[2] * 1e3,
-                    "gbs_mean": alg / (warm[0] * 1e-3) / 1e9,
+                    "gbs_mean": alg / (warm[0] * 1e-3) / 1e9, "gbs_median": alg / (warm[2] * 1e-3) / 1e9,
                     "flushed_us_mean": cold[0] * 1e3, "flushed_us_min": cold[1] * 1e3,
-                    "flushed_gbs_mean": alg / (cold[0] * 1e-3) / 1e9})
+                    "flushed_us_median": cold[2] * 1e3,
+                    "flushed_gbs_median": alg / (cold[2] * 1e-3) / 1e9})
         log(f"long context, splits={sp}: {warm[0] * 1e3:.1f} us ({alg / (warm[0] * 1e-3) / 1e9:.0f} GB/s), "
             f"after a 1 GiB flush {cold[0] * 1e3:.1f} us ({alg / (cold[0] * 1e-3) / 1e9:.0f} GB/s)")
     del scratch
     return {"workload": "long split-K decode, 2-bit: 1 lane x 131072 tokens, 1 layer x 4 KV heads x 256 dims, "
                         "16 query heads, planted key",
-            "bytes_per_call": alg, "per_splits": res}
+            "bytes_per_call": alg, "per_splits": res, "default_splits": pool.decode_splits([ctx]),
+            "planted_position": pos,
+            "planted_rank": {"gpu": gpu_rank, "heads": list(range(0, w.n_q_heads, w.group))}}
 
 
 def q8_leg(reps: int):
@@ -220,7 +251,10 @@ def q8_leg(reps: int):
     heads x 128 dims, 32 query heads.  Populate every layer (timed, HBM bytes
     of bf16 rows read and codes written), then decode every layer (one call per
     layer for all lanes, HIP events); algorithmic bytes 268 per (token, KV
-    head) plus q and out."""
+    head) plus q and out.  Then the workload's own unit, a layer step: the
+    layer's decode for all lanes followed by the quantize-append of one new
+    token per lane (which re-derives the open page's channel scales and codes
+    from its exact rows), steps of all 32 layers timed per layer."""
     import torch
 
     import quantized_kv_attention_append_amd as kvq
@@ -228,15 +262,16 @@ def q8_leg(reps: int):
 
     w = WORKLOADS["q8"]
     lens = [int(x) for x in q8_batch_lengths(w)]
+    extra = reps + 2                       # tokens appended by the timed layer steps
     geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
     _, pb = kvq.token_bytes(geom, kvq.FMT_Q8)
-    n_pages = sum(-(-L // 64) for L in lens)
-    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q8, max_seqs=w.lanes, max_seq_tokens=max(lens))
+    n_pages = sum(-(-(L + extra) // 64) for L in lens)
+    pool = kvq.Pool(n_pages * pb, geom, kvq.FMT_Q8, max_seqs=w.lanes, max_seq_tokens=max(lens) + extra)
     perm = page_permutation(w, n_pages)
     seqs, off = [], 0
     for L in lens:
-        npg = -(-L // 64)
-        seqs.append(pool.reserve(L, pages=perm[off:off + npg]))
+        npg = -(-(L + extra) // 64)
+        seqs.append(pool.reserve(L + extra, pages=perm[off:off + npg]))
         off += npg
     B = w.lanes
     stream = torch.cuda.current_stream()
@@ -270,20 +305,43 @@ def q8_leg(reps: int):
             e1.record(stream)
             ev.append((e0, e1))
     torch.cuda.synchronize()
-    avg = sum(e0.elapsed_time(e1) for e0, e1 in ev) / len(ev)
+    dec = _stats_us([e0.elapsed_time(e1) for e0, e1 in ev])
+    avg = dec["us_mean"] * 1e-3
     alg = tokens * w.n_kv_heads * 268 + B * w.n_q_heads * w.head_dim * (2 + 4)
+    # ---- layer steps: decode at the current length, then one new token per lane ----
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4)
+    new_rows = torch.randn((extra, w.n_layers, 2, B, w.n_kv_heads, w.head_dim), generator=g, device="cuda",
+                           dtype=torch.float32).to(torch.bfloat16)
+    cur = list(lens)
+    step_ms = []
+    for r in range(reps + 1):              # the first round is a warm-up
+        for layer in range(w.n_layers):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pool.decode(layer, seqs, cur, qs[layer], w.sm_scale, ws=ws, out=outs[layer])
+            pool.append(layer, seqs, cur, [1] * B, new_rows[r, layer, 0], new_rows[r, layer, 1])
+            e1.record(stream)
+            step_ms.append((r, e0, e1))
+        cur = [c + 1 for c in cur]
+    torch.cuda.synchronize()
+    layer_step = _stats_us([e0.elapsed_time(e1) for r, e0, e1 in step_ms if r > 0])
     app_bytes = w.n_layers * tokens * w.n_kv_heads * 2 * (2 * w.head_dim) + w.n_layers * tokens * w.n_kv_heads * (
         2 * w.head_dim + 8)
     gbs = alg / (avg * 1e-3) / 1e9
     log(f"8-bit: populate {w.n_layers} layers x {tokens} tokens in {app_ms:.1f} ms; decode {avg * 1e3:.1f} us a layer "
-        f"call, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), splits={sp}")
+        f"call (median {dec['us_median']:.1f}), {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s), splits={sp}; "
+        f"layer step (decode + 1-token append per lane) {layer_step['us_mean']:.1f} us")
     return {"workload": "8-bit decode, 24 lanes x 64*U[16,128] tokens, 32 layers x 8 KV heads x 128 dims, 32 query heads",
             "tokens_per_layer": tokens, "pool_bytes": n_pages * pb, "splits": sp,
-            "decode_us_per_layer_call": avg * 1e3, "bytes_per_call": alg,
+            "decode_us_per_layer_call": avg * 1e3, "decode_us_median": dec["us_median"], "bytes_per_call": alg,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None,
                          "kernel": "one kv_attn_decode call per layer: decode_q8_mfma_kernel<128, 4> then merge_splits8_kernel"},
             "kv_tokens_per_s": tokens * w.n_layers / (avg * 1e-3 * w.n_layers),
+            "layer_step": {"what": "per layer: decode of all 24 lanes, then quantize-append of 1 token per lane",
+                           **layer_step,
+                           "step_ms_32_layers": layer_step["us_mean"] * w.n_layers * 1e-3},
             "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
 
 
@@ -425,48 +483,287 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
             "prefill_ms_per_call": pf[0], "prefill_ms_min": pf[1], "prefill_useful_tflops": pf_tflops}
 
 
-def oracle_baseline(w, budget_s: float):
-    """The oracle's decode (dequantize the lane's codes, fp64 softmax attention)
-    timed on (layer, lane) units of the same workload until the budget is spent."""
-    import numpy as np
+def probe_leg(pool, perm, reps: int = 10):
+    """Measured ceilings for the headline kernels (libkvq_probe.so):
+      * read_stream: a plain streaming read of one layer's 188.7 MB worth of
+        the pool, 16 windows rotated through the 3.02 GB pool so that the
+        256 MB last-level cache does not serve it;
+      * read_pattern: the 2-bit decode's reads without its arithmetic: the
+        (layer, KV head) blocks of every lane's 640 pages through the same
+        page permutation, the decode's grid (8 lanes x 4 KV heads x 8 splits
+        of 4 waves), the 16 layers in turn;
+      * mfma_bf16: back-to-back bf16 matrix-core products in every wave, no
+        memory traffic.
+    Each call timed with HIP events, calls back to back."""
+    import ctypes as C
+
     import torch
-    from threadpoolctl import threadpool_info
+
+    path = os.path.join(ROOT, "quantized_kv_attention_append_amd", "libkvq_probe.so")
+    lib = C.CDLL(path)
+    lib.kvq_probe_read_stream.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+    lib.kvq_probe_read_blocks.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64,
+                                          C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+    lib.kvq_probe_read_blocks_lds.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64,
+                                              C.c_int64, C.c_void_p, C.c_void_p]
+    lib.kvq_probe_mfma_bf16.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    base, pool_bytes = pool.device_ptr()
+    L, H, D, B, PPL = 16, 4, 256, 8, 640
+    block = 32 * D + 1024
+    page_bytes = L * H * block
+    layer_bytes = B * PPL * H * block                      # 188,743,680
+    bt = torch.as_tensor(perm.astype("int32"), device="cuda")
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: {rc}")
+
+    def timed(fn):
+        for layer in range(L):
+            fn(layer)
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            for layer in range(L):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn(layer)
+                e1.record(stream)
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return _stats_us([e0.elapsed_time(e1) for e0, e1 in ev])
+
+    stream_t = timed(lambda layer: check(lib.kvq_probe_read_stream(C.c_void_p(base + layer * layer_bytes), layer_bytes,
+                                                                   16384, C.c_void_p(sink.data_ptr()), sp)))
+    pattern_t = timed(lambda layer: check(lib.kvq_probe_read_blocks(
+        C.c_void_p(base), C.c_void_p(bt.data_ptr()), B, PPL, H, 8, page_bytes, layer * H * block, block,
+        C.c_void_p(sink.data_ptr()), sp)))
+    pattern_lds_t = timed(lambda layer: check(lib.kvq_probe_read_blocks_lds(
+        C.c_void_p(base), C.c_void_p(bt.data_ptr()), B, PPL, H, 8, page_bytes, layer * H * block,
+        C.c_void_p(sink.data_ptr()), sp)))
+    grid, iters = 1024, 2000
+    mfma = []
+    for shape, chains in ((0, 4), (0, 8), (1, 2), (1, 4)):
+        go = lambda: check(lib.kvq_probe_mfma_bf16(shape, chains, grid, iters, C.c_void_p(sink.data_ptr()), sp))
+        go()
+        t = _call_ms(go, 10)
+        fl = grid * 4 * iters * chains * 32768
+        mfma.append((fl / (t[2] * 1e-3) / 1e12, shape, chains, fl, t[2]))
+    best = max(mfma)
+    best_pattern = min(pattern_t, pattern_lds_t, key=lambda t: t["us_median"])
+    res = {
+        "read_stream": {"bytes": layer_bytes, **stream_t, "gbs_median": layer_bytes / stream_t["us_median"] / 1e3},
+        "read_pattern": {"bytes": layer_bytes, **best_pattern,
+                         "gbs_median": layer_bytes / best_pattern["us_median"] / 1e3,
+                         "what": "the 2-bit decode's block reads at its grid (8 lanes x 4 KV heads x 8 splits of 4 "
+                                 "waves), no arithmetic: the faster of register loads (two blocks in flight a wave) "
+                                 "and LDS DMA staging (two page pairs in flight a wave)",
+                         "register_us_median": pattern_t["us_median"], "lds_dma_us_median": pattern_lds_t["us_median"]},
+        "mfma_bf16": {"flops": best[3], "us_median": best[4] * 1e3, "tflops_median": best[0],
+                      "what": f"the fastest of 16x16x32 and 32x32x16 bf16 products, 2 to 8 independent chains a "
+                              f"wave, 1024 x 4 waves: {'16x16x32' if best[1] == 0 else '32x32x16'} x {best[2]} chains",
+                      "all_tflops": {f"{'16x16x32' if m[1] == 0 else '32x32x16'} x {m[2]}": m[0] for m in mfma}},
+    }
+    log(f"probes: stream read {res['read_stream']['gbs_median']:.0f} GB/s, decode read pattern "
+        f"{res['read_pattern']['gbs_median']:.0f} GB/s, bf16 matrix cores {res['mfma_bf16']['tflops_median']:.0f} TFLOP/s")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# The oracle baseline: the oracle as it stands, timed on the host's cores, over
+# independent units of the same workloads in a pool of worker processes with
+# one BLAS thread each.  Workers never touch the GPU: each draws its unit's
+# rows on the host from the workload's seeded recipe (outside the timed
+# region) and times only the oracle's step.
+
+def _cpu_init():
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    if ROOT not in sys.path:
+        sys.path.insert(0, ROOT)
+    import torch
+    torch.set_num_threads(1)
+    from threadpoolctl import threadpool_limits
+    globals()["_cpu_limits"] = threadpool_limits(1)
+
+
+def _cpu_q2_unit(layer, lane):
+    """27B workload, one (layer, lane): per KV head, the append (quantize and
+    pack the head's K and V rows into page blocks) and the decode (dequantize,
+    fp64 softmax attention of the group's 4 query heads)."""
+    import numpy as np
+
+    from oracle import attention, codec, pool as opool
+    from synth import WORKLOADS, kv_rows, queries
+    w = WORKLOADS["27b"]
+    k, v = kv_rows(w, layer, lane, w.ctx)
+    q = queries(w, layer, w.lanes)[lane].float().numpy()
+    kf, vf = k.float().numpy(), v.float().numpy()
+    t_app = t_dec = 0.0
+    for g in range(w.n_kv_heads):
+        kh, vh = np.ascontiguousarray(kf[:, g:g + 1]), np.ascontiguousarray(vf[:, g:g + 1])
+        t0 = time.perf_counter()
+        opool.sequence_blocks("q2", kh, vh)
+        t1 = time.perf_counter()
+        ck, cv = codec.q2_quantize(kh), codec.q2_quantize(vh)           # the codes the pages hold (untimed)
+        t2 = time.perf_counter()
+        K, V = codec.q2_dequantize(*ck), codec.q2_dequantize(*cv)
+        attention.decode(q[g * w.group:(g + 1) * w.group], K, V, w.sm_scale)
+        t3 = time.perf_counter()
+        t_app += t1 - t0
+        t_dec += t3 - t2
+    return {"tokens": w.ctx, "rows": 2 * w.ctx * w.n_kv_heads, "append_s": t_app, "decode_s": t_dec}
+
+
+def _cpu_long_head(g):
+    """Long split-K workload, KV head g: the decode of its 4 query heads with
+    the keys split as the GPU splits them (whole page pairs, the same count
+    in every split) at 16, 32, 64 and 128 splits; and the planted key's rank
+    among the logits of query head 4g over the dequantized keys (the oracle's)
+    and over the exact bf16 keys."""
+    import numpy as np
 
     from oracle import attention, codec
-    from synth import kv_rows, queries
-
+    from synth import WORKLOADS, kv_rows, planted_position, queries
+    from synth.workloads import plant_key
+    w = WORKLOADS["long"]
     ctx = w.ctx
-    done_tokens, spent, units = 0, 0.0, []
-    # (layer, lane) units in an order that spreads the sample over layers and
-    # lanes, until the budget of oracle time is spent
-    order = [(layer, (layer + s) % w.lanes) for s in range(w.lanes) for layer in range(w.n_layers)]
-    for layer, lane in order:
-        k, v = kv_rows(w, layer, lane, ctx, device="cuda")
-        kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
-        del k, v
-        ck = codec.q2_quantize(kf)
-        cv = codec.q2_quantize(vf)
-        q = queries(w, layer, w.lanes, device="cuda")[lane].float().cpu().numpy()
+    k, v = kv_rows(w, 0, 0, ctx)
+    q = queries(w, 0, 1)
+    pos = planted_position(w, ctx)
+    plant_key(k, q[0], pos, w.group)
+    kh, vh = k[:, g:g + 1].float().numpy(), v[:, g:g + 1].float().numpy()
+    qh = q[0, g * w.group:(g + 1) * w.group].float().numpy()
+    ck, cv = codec.q2_quantize(kh), codec.q2_quantize(vh)
+    res = {}
+    for sp in (16, 32, 64, 128):
         t0 = time.perf_counter()
-        K = codec.q2_dequantize(*ck)
-        V = codec.q2_dequantize(*cv)
-        attention.decode(q, K, V, w.sm_scale)
-        dt = time.perf_counter() - t0
-        spent += dt
-        done_tokens += ctx
-        units.append((layer, lane))
-        log(f"oracle unit layer={layer} lane={lane}: {dt:.2f} s")
-        if spent >= budget_s:
-            break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {
-        "value": done_tokens / spent,
+        K, V = codec.q2_dequantize(*ck)[:, 0], codec.q2_dequantize(*cv)[:, 0]
+        s = attention.scores(qh, K[:, None], w.sm_scale)
+        per = -(-((ctx // 64 + 1) // 2) // sp)          # page pairs a split, as the library sizes them
+        bounds = [(p * per * 128, min((p + 1) * per * 128, ctx)) for p in range(sp)]
+        for h in range(w.group):
+            attention.merge_partials(attention.split_partials(s[h], np.asarray(V, np.float64), bounds))
+        res[sp] = time.perf_counter() - t0
+    K = codec.q2_dequantize(*ck)
+    s_o = attention.scores(qh[:1], K, w.sm_scale)[0]
+    s_x = attention.scores(qh[:1], kh, w.sm_scale)[0]
+    return {"seconds": res, "rank_oracle": attention.planted_rank(s_o, pos), "rank_exact": attention.planted_rank(s_x, pos)}
+
+
+def _cpu_prefill_head(g, rows):
+    """Chunked prefill workload, KV head g: the chunk's append (quantize the
+    1,024 new K and V rows), the read of all 66,560 keys (dequantize) and the
+    causal attention of `rows` chunk rows for the group's 4 query heads."""
+    import numpy as np
+
+    from oracle import attention, codec
+    from synth import WORKLOADS, kv_rows, queries
+    w = WORKLOADS["prefill"]
+    prior, n_q = w.ctx, w.chunk
+    k, v = kv_rows(w, 0, 0, prior + n_q)
+    q = queries(w, 0, n_q, stream=1)
+    kh, vh = k[:, g:g + 1].float().numpy(), v[:, g:g + 1].float().numpy()
+    ck_p, cv_p = codec.q2_quantize(kh[:prior]), codec.q2_quantize(vh[:prior])
+    t0 = time.perf_counter()
+    ck_c, cv_c = codec.q2_quantize(kh[prior:]), codec.q2_quantize(vh[prior:])
+    t1 = time.perf_counter()
+    K = np.concatenate([codec.q2_dequantize(*ck_p), codec.q2_dequantize(*ck_c)])
+    V = np.concatenate([codec.q2_dequantize(*cv_p), codec.q2_dequantize(*cv_c)])
+    t2 = time.perf_counter()
+    sample = list(range(0, n_q, n_q // rows))[:rows]
+    attention.prefill(q[:, g * w.group:(g + 1) * w.group].float().numpy(), K, V, w.sm_scale, prior, rows=sample)
+    t3 = time.perf_counter()
+    return {"append_s": t1 - t0, "read_s": t2 - t1, "rows": len(sample), "attend_s": t3 - t2}
+
+
+def _cpu_q8_lane(lane):
+    """8-bit workload, layer 0, one lane: the decode (dequantize every page,
+    fp64 attention of 32 query heads) and the append of one more token (its V
+    row; the open page's K channels re-derived from its exact rows)."""
+    import numpy as np
+
+    from oracle import attention, codec, pool as opool
+    from synth import WORKLOADS, kv_rows, q8_batch_lengths, queries
+    w = WORKLOADS["q8"]
+    L = int(q8_batch_lengths(w)[lane])
+    k, v = kv_rows(w, 0, lane, L + 1)
+    q = queries(w, 0, w.lanes)[lane].float().numpy()
+    kf, vf = k.float().numpy(), v.float().numpy()
+    t0 = time.perf_counter()
+    K, V = opool.dequantized_rows("q8", kf[:L], vf[:L])
+    attention.decode(q, K, V, w.sm_scale)
+    t1 = time.perf_counter()
+    codec.q8_quantize_v(vf[L:L + 1])
+    codec.q8_quantize_k_page(kf[L - L % 64:L + 1])
+    t2 = time.perf_counter()
+    return {"tokens": L, "decode_s": t1 - t0, "append_s": t2 - t1}
+
+
+def cpu_baseline(budget_units: int = 32):
+    """The oracle on the host's cores (see the functions above), all units in
+    one pool of worker processes, one BLAS thread each."""
+    import multiprocessing as mp
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t_start = time.perf_counter()
+    with mp.get_context("spawn").Pool(workers, initializer=_cpu_init) as pool:
+        # the 27B units: (layer, lane) pairs spread over layers and lanes
+        units = [(layer, (layer + s) % 8) for s in range(8) for layer in range(16)][:budget_units]
+        jobs27 = [pool.apply_async(_cpu_q2_unit, u) for u in units]
+        jobs_long = [pool.apply_async(_cpu_long_head, (g,)) for g in range(4)]
+        jobs_pf = [pool.apply_async(_cpu_prefill_head, (g, 16)) for g in range(4)]
+        jobs_q8 = [pool.apply_async(_cpu_q8_lane, (i,)) for i in range(24)]
+        r27 = [j.get() for j in jobs27]
+        rl = [j.get() for j in jobs_long]
+        rp = [j.get() for j in jobs_pf]
+        r8 = [j.get() for j in jobs_q8]
+    wall = time.perf_counter() - t_start
+    dec_s = sum(r["decode_s"] for r in r27)
+    app_s = sum(r["append_s"] for r in r27)
+    tokens = sum(r["tokens"] for r in r27)
+    rows = sum(r["rows"] for r in r27)
+    value = tokens / dec_s * workers     # worker-seconds spread over the pool's cores
+    ctx_long = 131072
+    par = min(workers, 4)                 # the 4 KV-head units run side by side
+    long = {f"splits_{sp}": {"seconds_per_call": sum(r["seconds"][sp] for r in rl) / par,
+                             "kv_tokens_per_s": ctx_long / (sum(r["seconds"][sp] for r in rl) / par)}
+            for sp in (16, 32, 64, 128)}
+    pf_rows = 1024
+    pf_attend = sum(r["attend_s"] / r["rows"] for r in rp) * pf_rows      # worker-seconds for the whole chunk
+    pf_append = sum(r["append_s"] for r in rp)
+    pf_read = sum(r["read_s"] for r in rp)
+    q8_dec = sum(r["decode_s"] for r in r8)
+    q8_app = sum(r["append_s"] for r in r8)
+    q8_tokens = sum(r["tokens"] for r in r8)
+    res = {
+        "value": value,
         "unit": "KV tokens/s",
-        "cores": threads,
+        "cores": workers,
         "kind": "oracle",
-        "sample": f"{len(units)} (layer, lane) units of {ctx} tokens x 4 KV heads x 16 query heads "
-                  f"(dequantize + fp64 softmax attention), {spent:.1f} s",
+        "sample": (f"27B-geometry 2-bit decode: {len(units)} (layer, lane) units of 40960 tokens x 4 KV heads "
+                   f"(dequantize + fp64 softmax attention of 16 query heads), {dec_s:.1f} worker-seconds on "
+                   f"{workers} worker processes with one BLAS thread each; value = tokens / worker-seconds x "
+                   f"workers; rows drawn on the host from the workload's seeds, outside the timed region"),
+        "wall_s": wall,
+        "populate": {"rows_per_s": rows / app_s * workers,
+                     "what": "quantize + pack K and V rows into page blocks, the same units"},
+        "long_context": {**long, "what": "131,072-token decode of 16 query heads split as the GPU splits it, "
+                                         "4 KV-head units on 4 workers"},
+        "prefill": {"chunk_s": (pf_append + pf_read + pf_attend) / min(workers, 4),
+                    "what": "65,536 + 1,024 chunk: append, read and causal attention of all 1,024 rows "
+                            "(extrapolated from 16 sampled rows a KV head), 4 KV-head units on 4 workers"},
+        "q8": {"layer_step_s": (q8_dec + q8_app) / workers, "decode_kv_tokens_per_s": q8_tokens / q8_dec * workers,
+               "what": "8-bit layer 0: decode of 24 lanes then one appended token each, on the pool"},
+        "planted_rank": {"oracle": [r["rank_oracle"] for r in rl], "exact_bf16": [r["rank_exact"] for r in rl]},
     }
+    log(f"oracle baseline on {workers} workers ({wall:.1f} s wall): decode {value:.3g} KV tokens/s, populate "
+        f"{res['populate']['rows_per_s']:.3g} rows/s, planted rank oracle {res['planted_rank']['oracle']} "
+        f"exact {res['planted_rank']['exact_bf16']}")
+    return res
 
 
 def platform_info() -> dict:
@@ -566,6 +863,7 @@ def main():
     region_ms = ev[0][0][0].elapsed_time(ev[-1][-1][1])
     ms_per_step = region_ms / args.steps
     avg_launch_ms = sum(launch_ms) / len(launch_ms)
+    launch_stats = _stats_us(launch_ms)
 
     kv_bytes_per_launch = B * pages_per_lane * H * 64 * (2 * (D // 4 + 8))   # K and V rows read
     io_bytes_per_launch = B * Hq * D * 2 + B * Hq * D * 4                      # q in, fp32 out
@@ -619,6 +917,9 @@ def main():
         log(f"calibration copy: 3 x {args.copy_mib} MiB int32 -> fp32")
         del src, dst
 
+    probes = probe_leg(pool, perm)
+    median_gbs = bytes_per_launch / (launch_stats["us_median"] * 1e-6) / 1e9
+
     prefill = None if args.no_prefill else prefill_leg(max(3, args.steps // 4), 2)
     long_ctx = None if args.no_extra else long_context_leg(10)
     q8 = None if args.no_extra else q8_leg(5)
@@ -648,9 +949,17 @@ def main():
         log(f"2-bit rotated against 2-bit: decode step {rot['step_time_vs_q2']:.3f}x the time, "
             f"populate {rot['populate_time_vs_q2']:.3f}x")
 
+    if prefill is not None:
+        pt = probes["mfma_bf16"]["tflops_median"]
+        prefill["roofline"]["probe"] = pt
+        prefill["roofline"]["frac_of_probe"] = prefill["roofline"]["achieved"] / pt
+
     cpu = None
     if not args.no_cpu:
-        cpu = oracle_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(args.cpu_units)
+        if long_ctx is not None:
+            long_ctx["planted_rank"]["oracle"] = cpu["planted_rank"]["oracle"]
+            long_ctx["planted_rank"]["exact_bf16"] = cpu["planted_rank"]["exact_bf16"]
 
     res = {
         "metric": METRIC,
@@ -680,10 +989,18 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
-            "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then merge_splits8_kernel",
+            "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256, false, false, true, 8, 1> "
+                      "(split-K partials and their merge in one launch)",
             "bytes_per_launch": bytes_per_launch,
             "avg_launch_us": avg_launch_ms * 1e3,
+            "median_launch_us": launch_stats["us_median"],
+            "min_launch_us": launch_stats["us_min"],
+            "median_frac": median_gbs / HBM_PEAK_GBS,
+            "probe": probes["read_pattern"]["gbs_median"],
+            "frac_of_probe": achieved / probes["read_pattern"]["gbs_median"],
+            "probe_what": "the decode's block reads at its grid without arithmetic, GB/s (median)",
         },
+        "probes": probes,
         "step_mode": step_mode,
         "eager": eager,
         "graph": graph,

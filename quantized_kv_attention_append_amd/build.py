@@ -3,7 +3,9 @@
     python -m quantized_kv_attention_append_amd.build [-v]
 
 Compiles every csrc/*.hip and csrc/*.cpp with hipcc (one object each, in
-parallel) and links them into quantized_kv_attention_append_amd/libkvq.so.
+parallel) and links them into quantized_kv_attention_append_amd/libkvq.so;
+also builds the measurement probes bench.py uses (probes/probes.hip ->
+libkvq_probe.so, outside the library's C ABI).
 Packed-fp32 instruction selection is switched off for all device code.
 """
 
@@ -65,7 +67,26 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probes(verbose)
     return LIB
+
+
+PROBE_SRC = os.path.join(PKG, "probes", "probes.hip")
+PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
+
+
+def build_probes(verbose: bool = False) -> str:
+    """The measurement probes bench.py loads (a library of their own, outside
+    the C ABI of include/kvq.h)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc()] + common_flags() + ["-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
