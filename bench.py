@@ -355,8 +355,8 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     window=True runs the same legs over 2-bit pools with the exact window of
     the last page: each lane's last 64 tokens are read as bf16 rows, the rest
     as 2-bit rows (the pool's pages are the 2-bit 3.02 GB).  rotated=True runs
-    the decode legs over the 2-bit pool of Hadamard-rotated K rows (same pages; no
-    prefill for that format)."""
+    them over the 2-bit pool of Hadamard-rotated K rows (same pages; the
+    prefill rotates the chunk's queries first)."""
     import torch
 
     import quantized_kv_attention_append_amd as kvq
@@ -438,19 +438,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
         f"(identical to eager: {same})")
     del pool, ws, outs, qs, eager_outs
     torch.cuda.empty_cache()
-    if rotated:
-        return {"workload": f"27B-geometry batched decode, {name}: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
-                            "8 lanes x 40960 tokens", "pool_bytes": n_pages * pb, "splits": sp,
-                "decode_us_per_call": avg_ms * 1e3, "bytes_per_call": alg,
-                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                             "kernel": "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256, false, true> "
-                                       "then merge_splits8_kernel"},
-                "graph_ms_per_step": graph_ms, "graph_identical_to_eager": same,
-                "kv_tokens_per_s": B * L * ctx / (graph_ms * 1e-3),
-                "populate_ms": app_ms, "populate_gbs": app_bytes / app_ms / 1e6}
-
-    # ---- chunked prefill over a bf16 pool: 65,536 prior + 1,024 chunk ----
+    # ---- chunked prefill over a pool of the same format: 65,536 prior + 1,024 chunk ----
     w3 = WORKLOADS["prefill"]
     prior, n_q = w3.ctx, w3.chunk
     total = prior + n_q
@@ -471,7 +459,9 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     pf_tflops = flops / (pf[0] * 1e-3) / 1e12
     log(f"{name} prefill: {pf[0]:.3f} ms per call, {pf_tflops:.0f} TFLOP/s useful")
     kernel = ("one kv_attn_decode call per layer: decode_q2_mfma_kernel<256> then decode_window_merge_kernel<256>"
-              if window else "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then merge_splits8_kernel")
+              if window else
+              "one kv_attn_decode call per layer: decode_q2_mfma_kernel<256, false, true, true, 8, 1> (merge inside)"
+              if rotated else "one kv_attn_decode call per layer: decode_bf16_kernel<256, 4> then merge_splits8_kernel")
     return {"workload": f"27B-geometry batched decode, {name}: 16 layers x 4 KV heads x 256 dims, 16 query heads, "
                         "8 lanes x 40960 tokens", "pool_bytes": n_pages * pb, "splits": sp,
             "decode_us_per_call": avg_ms * 1e3, "bytes_per_call": alg,
@@ -946,8 +936,11 @@ def main():
         # the price of the rotation: the query transform, butterflies on the K rows of append
         rot["step_time_vs_q2"] = rot["graph_ms_per_step"] / ms_per_step
         rot["populate_time_vs_q2"] = rot["populate_ms"] / app_ms
+        if prefill is not None:
+            rot["prefill_time_vs_q2"] = rot["prefill_ms_per_call"] / prefill["ms_per_call"]
         log(f"2-bit rotated against 2-bit: decode step {rot['step_time_vs_q2']:.3f}x the time, "
-            f"populate {rot['populate_time_vs_q2']:.3f}x")
+            f"populate {rot['populate_time_vs_q2']:.3f}x"
+            + (f", prefill {rot['prefill_time_vs_q2']:.3f}x" if prefill is not None else ""))
 
     if prefill is not None:
         pt = probes["mfma_bf16"]["tflops_median"]

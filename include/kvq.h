@@ -95,9 +95,11 @@ typedef enum {
      * Cache, Twice the Context" names in its closing notes, applied where its
      * outliers are channels (K), which the rotation spreads over the row
      * before the per-token range is taken.  Decode rotates the query the same
-     * way and scores with sm_scale / D (H q . H k = D q . k).  Prefill is
-     * not implemented for it (KV_ERR_FORMAT); kv_dequant_page returns K rows
-     * in the rotated basis. */
+     * way and scores with sm_scale / D (H q . H k = D q . k); prefill
+     * rotates the chunk's query rows the same way and takes them as two
+     * bf16 terms (the rounded value and the rounded residual), which its
+     * workspace holds.  kv_dequant_page returns K rows in the rotated
+     * basis. */
     KV_FMT_Q2_ROT = 5
 } kv_format;
 
@@ -249,7 +251,9 @@ enum { KV_OP_DECODE = 0, KV_OP_PREFILL = 1 };
  * n_splits = 0 asks for enough bytes for the split count the library picks
  * by itself (decode: any count up to 256; prefill: the count it picks for
  * n_rows queries, about one workgroup per compute unit).  A KV_FMT_Q2_WINDOW
- * prefill needs one more split's worth for the window's partials. */
+ * prefill needs one more split's worth for the window's partials, a
+ * KV_FMT_Q2_ROT prefill 4 x n_rows x Hq x D more bytes for the rotated
+ * query's two bf16 terms. */
 kv_status kv_workspace_bytes(const kv_pool* pool, int32_t op, int32_t n_rows, int32_t n_splits, int64_t* bytes);
 
 /* Split-count the library picks for a decode batch when n_splits = 0. */
@@ -306,21 +310,22 @@ kv_status kv_attn_decode_static(kv_pool* pool, int32_t layer, int32_t n, const i
 
 /* Causal prefill of a chunk of n_q queries of one sequence that sit at
  * positions q_start .. q_start + n_q - 1, after the chunk's own K/V have been
- * appended ("KV at 9 KB a token", opening section: prefill attention reads
- * the compressed cache): query i attends to tokens 0 .. q_start + i, all read
- * from the pool, 2-bit, bf16 and 2-bit window pools (the window's keys come
- * exact from its bf16 rows, through a third kernel whose partials the merge
- * adds; the chunk must lie within the tokens appended).  Scores are
- * sm_scale x q.k^,
- * sm_scale finite and > 0; softmax and sums in fp32 ("Half the Cache, Twice
- * the Context", section "The cliff is in the accumulator, not the storage");
- * both contractions run on bf16 matrix cores with
- * exact code operands and 16-bit softmax weights.  The keys of each block of
- * queries are split into n_splits ranges (1..64, 0 = the library's choice)
- * whose partials go to d_ws and are merged by a second kernel.
- * d_q: bf16 [n_q][Hq][D]; d_out: fp32 [n_q][Hq][D].  The workspace needs no
- * clearing: every byte read is written first within the call.  Errors:
- * KV_ERR_ARG, KV_ERR_BOUND, KV_ERR_FORMAT (an 8-bit pool), KV_ERR_WORKSPACE,
+ * appended ("KV at 9 KB a token", opening section and "How it works":
+ * prefill attention reads the compressed cache directly): query i attends to
+ * tokens 0 .. q_start + i, all read from the pool.  2-bit, bf16, 2-bit window
+ * pools (the window's keys come exact from its bf16 rows, through a third
+ * kernel whose partials the merge adds; the chunk must lie within the tokens
+ * appended) and rotated 2-bit pools (the chunk's query rows are rotated first
+ * and enter as two bf16 terms).  Scores are sm_scale x q.k^ (sm_scale finite
+ * and > 0); softmax and sums in fp32 ("Half the Cache, Twice the Context",
+ * section "The cliff is in the accumulator, not the storage"); both
+ * contractions run on bf16 matrix cores with exact code operands and 16-bit
+ * softmax weights.  The keys of each block of queries are split into
+ * n_splits ranges (1..64, 0 = the library's choice) whose partials go to d_ws
+ * and are merged by a second kernel.  d_q: bf16 [n_q][Hq][D]; d_out: fp32
+ * [n_q][Hq][D].  The workspace (kv_workspace_bytes) needs no clearing: every
+ * byte read is written first within the call.  Errors: KV_ERR_ARG,
+ * KV_ERR_BOUND, KV_ERR_FORMAT (an 8-bit pool), KV_ERR_WORKSPACE,
  * KV_ERR_DEVICE. */
 kv_status kv_attn_prefill(kv_pool* pool, int32_t layer, int32_t seq, int64_t q_start, int32_t n_q,
                           const uint16_t* d_q, float sm_scale, int32_t n_splits, void* d_ws, int64_t ws_bytes,

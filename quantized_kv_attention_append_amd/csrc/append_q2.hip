@@ -113,34 +113,6 @@ __device__ __forceinline__ void load_bf16_rows(const uint16_t* p, float (&x)[N])
     }
 }
 
-// Unnormalised Walsh-Hadamard transform of a row spread over the 16 lanes of a
-// DPP row (lane c holds dims c DPL .. c DPL + DPL - 1), for the rotated
-// variant: stages h = 1, 2, .., D/2 in that order, each replacing (x_i,
-// x_{i+h}) by (x_i + x_{i+h}, x_i - x_{i+h}) with one fp32 rounding; stages
-// h < DPL stay inside the lane, the others pair lane c with lane c ^ (h / DPL).
-template <int DPL>
-__device__ __forceinline__ void hadamard_row16(float (&x)[DPL], int c) {
-#pragma clang fp contract(off)
-#pragma unroll
-    for (int h = 1; h < DPL; h *= 2)
-#pragma unroll
-        for (int i = 0; i < DPL; ++i)
-            if (!(i & h)) {
-                const float a = x[i], b = x[i + h];
-                x[i] = a + b;
-                x[i + h] = a - b;
-            }
-#pragma unroll
-    for (int m = 1; m < 16; m *= 2) {
-        const bool upper = (c & m) != 0;
-#pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-            const float o = __shfl_xor(x[i], m);
-            x[i] = upper ? o - x[i] : x[i] + o;
-        }
-    }
-}
-
 template <int D, bool ROT>
 __global__ __launch_bounds__(256) void append_q2_kernel(PoolView pv, int layer, BatchDesc bd,
                                                         const uint16_t* __restrict__ kin,

@@ -684,9 +684,10 @@ kv_status kv_workspace_bytes(const kv_pool* p, int32_t op, int32_t n_rows, int32
             int sp = n_splits > 0 ? n_splits : 256;
             *bytes = 4 * decode_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
         } else if (op == KV_OP_PREFILL) {
-            int sp = n_splits > 0 ? n_splits : (n_rows > 0 ? prefill_auto_splits(n_rows, p->geom.n_q_heads, p->geom.n_kv_heads) : 1);
-            if (p->fmt == KV_FMT_Q2_WINDOW) ++sp;  // the window's partials
-            *bytes = 4 * prefill_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp);
+            const int sp = n_splits > 0 ? n_splits
+                         : (n_rows > 0 ? prefill_auto_splits(n_rows, p->geom.n_q_heads, p->geom.n_kv_heads, p->fmt) : 1);
+            *bytes = 4 * (prefill_ws_floats(n_rows, p->geom.n_q_heads, p->geom.head_dim, sp) +
+                          prefill_extra_floats(p->fmt, n_rows, p->geom.n_q_heads, p->geom.head_dim));
         } else {
             return fail(KV_ERR_ARG, "unknown op %d", op);
         }
@@ -765,8 +766,8 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
                           kv_stream_t stream) {
     return guarded([&]() -> kv_status {
         if (!p) return fail(KV_ERR_ARG, "pool is NULL");
-        if (p->fmt == KV_FMT_Q8 || p->fmt == KV_FMT_Q2_ROT)
-            return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit, bf16 and 2-bit window formats only");
+        if (p->fmt == KV_FMT_Q8)
+            return fail(KV_ERR_FORMAT, "prefill is implemented for the 2-bit, bf16, 2-bit window and rotated formats only");
         if (n_q <= 0 || q_start < 0) return fail(KV_ERR_ARG, "bad chunk");
         if (q_start > INT32_MAX) return fail(KV_ERR_BOUND, "q_start %lld is not below 2^31", (long long)q_start);
         if (!d_q || !d_out) return fail(KV_ERR_ARG, "NULL argument");
@@ -783,9 +784,9 @@ kv_status kv_attn_prefill(kv_pool* p, int32_t layer, int32_t seq, int64_t q_star
                             (long long)(q_start + n_q), (long long)A, layer);
             w0 = (int)(PAGE * ((A - 1) / PAGE));
         }
-        int sp = n_splits > 0 ? n_splits : prefill_auto_splits(n_q, p->geom.n_q_heads, p->geom.n_kv_heads);
-        int64_t need = 4 * prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim,
-                                             sp + (p->fmt == KV_FMT_Q2_WINDOW ? 1 : 0));
+        int sp = n_splits > 0 ? n_splits : prefill_auto_splits(n_q, p->geom.n_q_heads, p->geom.n_kv_heads, p->fmt);
+        int64_t need = 4 * (prefill_ws_floats(n_q, p->geom.n_q_heads, p->geom.head_dim, sp) +
+                            prefill_extra_floats(p->fmt, n_q, p->geom.n_q_heads, p->geom.head_dim));
         if (!d_ws || ws_bytes < need)
             return fail(KV_ERR_WORKSPACE, "prefill needs %lld workspace bytes, got %lld", (long long)need, (long long)ws_bytes);
         hipError_t e = launch_prefill(p->view(), (int)p->fmt, layer, seq, (int)q_start, n_q, d_q, sm_scale, sp,

@@ -108,13 +108,23 @@ hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, 
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
 hipError_t launch_decode_bf16(const PoolView& pv, int layer, const BatchDesc& bd, const uint16_t* q, float sm,
                               int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s);
-// Prefill over a 2-bit, bf16 or 2-bit window pool (fmt).  Window pools: keys
-// from w0 = 64 * floor((A - 1) / 64) on come from the window block, and the
-// window's partials sit after the splits' in ws (one more split's worth).
+// Prefill over a 2-bit, bf16, 2-bit window or rotated 2-bit pool (fmt).
+// Window pools: keys from w0 = 64 * floor((A - 1) / 64) on come from the
+// window block, and the window's partials sit after the splits' in ws (one
+// more split's worth).  Rotated pools: the rotated query's two bf16 terms
+// sit after the splits' partials.
 hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
                           float sm, int splits, float* ws, float* out, int w0, hipStream_t s);
-// Split count a prefill of n_q chunk queries takes when the caller passes 0.
-int prefill_auto_splits(int n_q, int Hq, int Hkv);
+// Split count a prefill of n_q chunk queries takes when the caller passes 0,
+// for a pool of format fmt (the rotated format takes 64 (query, head) rows a
+// workgroup, the others 128).
+int prefill_auto_splits(int n_q, int Hq, int Hkv, int fmt);
+// Floats a prefill workspace holds beyond the splits' partials: the window's
+// partials (2-bit window pools) or the rotated query's two bf16 terms
+// (rotated pools).
+inline int64_t prefill_extra_floats(int fmt, int n_q, int Hq, int D) {
+    return fmt == KV_FMT_Q2_WINDOW ? (int64_t)n_q * Hq * (D + 2) : fmt == KV_FMT_Q2_ROT ? (int64_t)n_q * Hq * D : 0;
+}
 // Device-to-device copies of byte ranges (multiples of 16 bytes, 16-byte aligned).
 struct CopyRange {
     const uint8_t* src;

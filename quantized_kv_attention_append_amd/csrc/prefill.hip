@@ -50,8 +50,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
-constexpr int NCB = 2;            // 16-column blocks per wave
-constexpr int ROWS = 4 * NCB * 16;  // (query, head) rows per workgroup
+// A wave owns NCB 16-column blocks of (query, head) rows, a workgroup four
+// waves: 4 NCB 16 rows.  Two blocks a wave in general; one when the query
+// enters as two bf16 terms (the rotated format), which doubles the q.k
+// products and their query registers.
+template <bool ROTQ>
+constexpr int PREFILL_NCB = ROTQ ? 1 : 2;
+template <bool ROTQ>
+constexpr int PREFILL_ROWS = 4 * PREFILL_NCB<ROTQ> * 16;
 constexpr int KROW = 8;           // padding of a K~ row, bf16 elements (16 B: the 16 rows a read group
                                   // touches start in distinct 16-byte bank slots)
 constexpr int VROW = 12;          // padding of a V~ row, bf16 elements (24 B; 0 is 2.5x slower at
@@ -259,10 +265,15 @@ __device__ __forceinline__ void prefill_split_range(int pos_max, int splits, int
     *pg1 = min(sp * per + per, n_pages);
 }
 
-template <int D, int FMT>
+// ROTQ (the rotated 2-bit format): q holds each (query, head) row as two bf16
+// terms of its rotated values, [n_q][Hq][2][D] (rounded value, then rounded
+// residual), and both enter the q.k product; the scale passed is sm / D.
+template <int D, int FMT, bool ROTQ>
 __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, int seq, int q_start, int n_q,
                                                       const uint16_t* __restrict__ q, float sm, int splits,
                                                       int kpl, float* __restrict__ ws) {
+    constexpr int NCB = PREFILL_NCB<ROTQ>, ROWS = PREFILL_ROWS<ROTQ>;
+    constexpr int QTERMS = ROTQ ? 2 : 1;
     constexpr int KSTEPS = D / 32, DB = D / 16;
     constexpr int KS = PrefillLds<D>::KS, VS = PrefillLds<D>::VS;
     const int Hkv = pv.Hkv, Hq = pv.Hq, G = Hq / Hkv;
@@ -288,32 +299,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, in
     int qi[NCB], pos[NCB];
     bool live[NCB];
     float qsum[NCB];
-    bf16x8 qop[NCB][KSTEPS];
+    bf16x8 qop[NCB][QTERMS][KSTEPS];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         const int col = 16 * (NCB * wave + cb) + j;
         qi[cb] = q_first + col / G;
         live[cb] = qi[cb] < n_q;
         pos[cb] = q_start + min(qi[cb], n_q - 1);
-        const uint16_t* qrow = q + ((int64_t)min(qi[cb], n_q - 1) * Hq + g * G + col % G) * D;
+        const uint16_t* qrow = q + ((int64_t)min(qi[cb], n_q - 1) * Hq + g * G + col % G) * QTERMS * D;
         float s = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            // kappa = 32 ks + 8 grp + e; dims of kappa .. kappa + 7: two runs of four
-            const int kap = 32 * ks + 8 * grp, d0 = kappa_dim(kap);
-            const uint2 a = *reinterpret_cast<const uint2*>(qrow + d0);      // dims d0 .. d0+3
-            const uint2 b = *reinterpret_cast<const uint2*>(qrow + d0 + 8);  // dims d0+8 .. d0+11
-            // interleave: kappa order d0, d0+8, d0+1, d0+9, ...
-            const uint4 u = make_uint4(__builtin_amdgcn_perm(b.x, a.x, 0x05040100u),
-                                       __builtin_amdgcn_perm(b.x, a.x, 0x07060302u),
-                                       __builtin_amdgcn_perm(b.y, a.y, 0x05040100u),
-                                       __builtin_amdgcn_perm(b.y, a.y, 0x07060302u));
-            qop[cb][ks] = as_bf16x8(u);
-            s += bf16_to_f32((uint16_t)(a.x & 0xFFFF)) + bf16_to_f32((uint16_t)(a.x >> 16)) +
-                 bf16_to_f32((uint16_t)(a.y & 0xFFFF)) + bf16_to_f32((uint16_t)(a.y >> 16)) +
-                 bf16_to_f32((uint16_t)(b.x & 0xFFFF)) + bf16_to_f32((uint16_t)(b.x >> 16)) +
-                 bf16_to_f32((uint16_t)(b.y & 0xFFFF)) + bf16_to_f32((uint16_t)(b.y >> 16));
-        }
+        for (int tm = 0; tm < QTERMS; ++tm)
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                // kappa = 32 ks + 8 grp + e; dims of kappa .. kappa + 7: two runs of four
+                const int kap = 32 * ks + 8 * grp, d0 = kappa_dim(kap);
+                const uint2 a = *reinterpret_cast<const uint2*>(qrow + tm * D + d0);      // dims d0 .. d0+3
+                const uint2 b = *reinterpret_cast<const uint2*>(qrow + tm * D + d0 + 8);  // dims d0+8 .. d0+11
+                // interleave: kappa order d0, d0+8, d0+1, d0+9, ...
+                const uint4 u = make_uint4(__builtin_amdgcn_perm(b.x, a.x, 0x05040100u),
+                                           __builtin_amdgcn_perm(b.x, a.x, 0x07060302u),
+                                           __builtin_amdgcn_perm(b.y, a.y, 0x05040100u),
+                                           __builtin_amdgcn_perm(b.y, a.y, 0x07060302u));
+                qop[cb][tm][ks] = as_bf16x8(u);
+                s += bf16_to_f32((uint16_t)(a.x & 0xFFFF)) + bf16_to_f32((uint16_t)(a.x >> 16)) +
+                     bf16_to_f32((uint16_t)(a.y & 0xFFFF)) + bf16_to_f32((uint16_t)(a.y >> 16)) +
+                     bf16_to_f32((uint16_t)(b.x & 0xFFFF)) + bf16_to_f32((uint16_t)(b.x >> 16)) +
+                     bf16_to_f32((uint16_t)(b.y & 0xFFFF)) + bf16_to_f32((uint16_t)(b.y >> 16));
+            }
         s += __shfl_xor(s, 16);
         s += __shfl_xor(s, 32);
         qsum[cb] = s;
@@ -367,7 +380,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, in
             if (idx + LDS_AHEAD < NQK) fk[(idx + LDS_AHEAD) % (LDS_AHEAD + 1)] = kfrag(idx + LDS_AHEAD);
             const int kb = idx / KSTEPS, ks = idx % KSTEPS;
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) st[cb][kb] = mma(fk[idx % (LDS_AHEAD + 1)], qop[cb][ks], st[cb][kb]);
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int tm = 0; tm < QTERMS; ++tm) st[cb][kb] = mma(fk[idx % (LDS_AHEAD + 1)], qop[cb][tm][ks], st[cb][kb]);
         }
         // ---- scores and the page's maximum per row (column j) ----
         constexpr bool MASKED = decltype(masked_tag)::value;
@@ -519,12 +534,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PoolView pv, int layer, in
 // [n_q][Hq][D], then (max, sum) pairs; the window starts at key 64 kpl) count
 // for the rows whose position reaches the window, the only rows written.
 __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q, int Hq, int Hkv, int D, int splits,
-                                                            int kpl, const float* __restrict__ ws,
+                                                            int kpl, int rows_per_block, const float* __restrict__ ws,
                                                             const float* __restrict__ win, float* __restrict__ out) {
     const int row = blockIdx.x;  // i * Hq + h
     const int i = row / Hq, G = Hq / Hkv;
     const int d = threadIdx.x;
-    const int QB = ROWS / G, qb = i / QB;
+    const int QB = rows_per_block / G, qb = i / QB;
     const int pos = q_start + i;
     const int pos_max = q_start + min(qb * QB + QB, n_q) - 1;
     const int n_pages = min(pos_max / PAGE + 1, kpl);
@@ -558,11 +573,43 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q
     out[(int64_t)row * D + d] = acc / den;
 }
 
-int prefill_auto_splits(int n_q, int Hq, int Hkv) {
-    const int QB = ROWS / (Hq / Hkv);
+int prefill_rows_per_block(int fmt) { return fmt == KV_FMT_Q2_ROT ? PREFILL_ROWS<true> : PREFILL_ROWS<false>; }
+
+int prefill_auto_splits(int n_q, int Hq, int Hkv, int fmt) {
+    const int QB = prefill_rows_per_block(fmt) / (Hq / Hkv);
     const int blocks = ((n_q + QB - 1) / QB) * Hkv;
     const int want = (256 + blocks - 1) / blocks;  // about one workgroup per compute unit
     return want < 1 ? 1 : want > 64 ? 64 : want;
+}
+
+// The rotated format's query rows: H q in fp32 butterflies (the stages of the
+// rotated append, H the unnormalised Walsh-Hadamard matrix), each row written
+// as two bf16 terms, the rotated value rounded to nearest and the rounded
+// residual: [n_q][Hq][2][D].  A row on the 16 lanes of a DPP row, sixteen rows
+// a workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void rotate_query_kernel(const uint16_t* __restrict__ q, int rows,
+                                                           uint16_t* __restrict__ qr) {
+    constexpr int DPL = D / 16;
+    const int row = blockIdx.x * 16 + (threadIdx.x >> 4), c = threadIdx.x & 15;
+    const bool in = row < rows;  // every lane takes part in the row shuffles
+    float x[DPL];
+    const uint16_t* src = q + (int64_t)min(row, rows - 1) * D + c * DPL;
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) x[k] = bf16_to_f32(src[k]);
+    hadamard_row16<DPL>(x, c);
+    uint32_t hi[DPL / 2], lo[DPL / 2];
+#pragma unroll
+    for (int k = 0; k < DPL / 2; ++k) split_hi_lo(x[2 * k], x[2 * k + 1], hi[k], lo[k]);
+    if (in) {
+        uint32_t* dh = reinterpret_cast<uint32_t*>(qr + (int64_t)row * 2 * D + c * DPL);
+        uint32_t* dl = reinterpret_cast<uint32_t*>(qr + (int64_t)row * 2 * D + D + c * DPL);
+#pragma unroll
+        for (int k = 0; k < DPL / 2; ++k) {
+            dh[k] = hi[k];
+            dl[k] = lo[k];
+        }
+    }
 }
 
 hipError_t launch_prefill_window(const PoolView& pv, int layer, int seq, int q_start, int n_q, int w0,
@@ -570,24 +617,38 @@ hipError_t launch_prefill_window(const PoolView& pv, int layer, int seq, int q_s
 
 hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
                           float sm, int splits, float* ws, float* out, int w0, hipStream_t s) {
-    const int G = pv.Hq / pv.Hkv, QB = ROWS / G;
+    const int G = pv.Hq / pv.Hkv, rows = prefill_rows_per_block(fmt), QB = rows / G;
     const bool window = fmt == KV_FMT_Q2_WINDOW;
     const int kpl = window ? w0 / PAGE : INT_MAX;
     dim3 grid(((n_q + QB - 1) / QB) * pv.Hkv, splits);
     if (fmt == KV_FMT_BF16) {
         if (pv.D == 256)
-            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_BF16>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
-                               q, sm, splits, kpl, ws);
+            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_BF16, false>), grid, dim3(256), 0, s, pv, layer, seq,
+                               q_start, n_q, q, sm, splits, kpl, ws);
         else
-            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_BF16>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
-                               q, sm, splits, kpl, ws);
+            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_BF16, false>), grid, dim3(256), 0, s, pv, layer, seq,
+                               q_start, n_q, q, sm, splits, kpl, ws);
+    } else if (fmt == KV_FMT_Q2_ROT) {
+        // the rotated query terms sit after the splits' partials
+        uint16_t* qr = reinterpret_cast<uint16_t*>(ws + prefill_ws_floats(n_q, pv.Hq, pv.D, splits));
+        const int qrows = n_q * pv.Hq;
+        const float smr = sm / (float)pv.D;  // H q . H k = D q . k
+        if (pv.D == 256) {
+            hipLaunchKernelGGL(rotate_query_kernel<256>, dim3((qrows + 15) / 16), dim3(256), 0, s, q, qrows, qr);
+            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_Q2, true>), grid, dim3(256), 0, s, pv, layer, seq, q_start,
+                               n_q, qr, smr, splits, kpl, ws);
+        } else {
+            hipLaunchKernelGGL(rotate_query_kernel<128>, dim3((qrows + 15) / 16), dim3(256), 0, s, q, qrows, qr);
+            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_Q2, true>), grid, dim3(256), 0, s, pv, layer, seq, q_start,
+                               n_q, qr, smr, splits, kpl, ws);
+        }
     } else if (kpl > 0) {
         if (pv.D == 256)
-            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
-                               q, sm, splits, kpl, ws);
+            hipLaunchKernelGGL((prefill_kernel<256, KV_FMT_Q2, false>), grid, dim3(256), 0, s, pv, layer, seq, q_start,
+                               n_q, q, sm, splits, kpl, ws);
         else
-            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_Q2>), grid, dim3(256), 0, s, pv, layer, seq, q_start, n_q,
-                               q, sm, splits, kpl, ws);
+            hipLaunchKernelGGL((prefill_kernel<128, KV_FMT_Q2, false>), grid, dim3(256), 0, s, pv, layer, seq, q_start,
+                               n_q, q, sm, splits, kpl, ws);
     }
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -598,7 +659,7 @@ hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q
         if (err != hipSuccess) return err;
     }
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(n_q * pv.Hq), dim3(pv.D), 0, s, q_start, n_q, pv.Hq, pv.Hkv, pv.D,
-                       splits, kpl, ws, win, out);
+                       splits, kpl, rows, ws, win, out);
     return hipGetLastError();
 }
 

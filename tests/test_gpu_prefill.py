@@ -117,3 +117,36 @@ def test_c3_chunked_prefill_full_size():
     ref = attention.prefill_dense(q.float().cpu().numpy(), K, V, w.sm_scale, prior)
     assert_close(out, ref, "65536 + 1024 chunk, all 1024 rows x 16 heads")
     say("PREFILL prefill: the whole pool bit-exact, every chunk row within tolerance")
+
+
+@pytest.mark.timeout(900)
+def test_c3_chunked_prefill_full_size_rotated():
+    """The 65,536 + 1,024 chunk over a rotated 2-bit pool: the whole pool byte
+    for byte against the oracle's image (the 2-bit pages of the rotated K rows
+    and of the V rows), and every chunk row against the oracle's causal
+    prefill over the pool read back in the original basis."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    from oracle import codec
+    w = PREFILL
+    prior, n_q = w.ctx, w.chunk
+    total = prior + n_q
+    n_pages = total // 64
+    pool, mem = make_pool(w, n_pages, kvq.FMT_Q2_ROT, max_seqs=1, max_seq_tokens=total)
+    perm = page_permutation(w, n_pages)
+    seq = pool.reserve(total, pages=perm)
+    k, v = kv_rows(w, 0, 0, total, device="cuda")
+    pool.append(0, [seq], [0], [prior], k[:prior], v[:prior])
+    pool.append(0, [seq], [prior], [n_q], k[prior:], v[prior:])
+    q = queries(w, 0, n_q, device="cuda", stream=1)
+    ws = torch.full((pool.workspace_bytes(kvq.OP_PREFILL, n_q, 0),), 0xFF, dtype=torch.uint8, device="cuda")
+    out = pool.prefill(0, seq, prior, q, w.sm_scale, ws=ws).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
+    blocks = opool.sequence_blocks("q2", codec.hadamard_rows(kf), vf)
+    got = mem.view(n_pages, -1)[torch.as_tensor(perm.astype(np.int64), device="cuda")].cpu().numpy()
+    bad = int(np.count_nonzero(got != blocks.reshape(n_pages, -1)))
+    assert bad == 0, f"rotated 65536 + 1024: {bad} pool bytes differ from the oracle"
+    K, V = opool.dequantized_rows("q2r", kf, vf)
+    ref = attention.prefill_dense(q.float().cpu().numpy(), K, V, w.sm_scale, prior)
+    assert_close(out, ref, "rotated 65536 + 1024 chunk, all 1024 rows x 16 heads")

@@ -148,16 +148,62 @@ def test_rotated_lowers_the_decode_error_against_the_exact_rows():
     assert errs["q2r"] < errs["q2"]
 
 
-def test_rotated_refusals():
+def _rotated_prefill_case(w, layer, prior, n_q, splits_list, salt=0):
+    """Prefill over a rotated pool against the oracle's attention over the
+    rotated pool read back in the original basis (rows are the pages of a
+    seeded permutation; the workspace is filled with 0xFF)."""
+    import quantized_kv_attention_append_amd as kvq
+    total = prior + n_q
+    n_pages = -(-total // 64) + 1
+    pool, mem = make_pool(w, n_pages, _fmt())
+    bt = page_permutation(w, n_pages, salt=salt)[:-1]
+    seq = pool.reserve(total, pages=bt)
+    k, v = kv_rows(w, layer, 0, total)
+    if prior:
+        pool.append(layer, [seq], [0], [prior], k[:prior].cuda(), v[:prior].cuda())
+    pool.append(layer, [seq], [prior], [n_q], k[prior:].cuda(), v[prior:].cuda())
+    q = queries(w, layer, n_q, stream=1)
+    K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
+    ref = attention.prefill(q.float().numpy(), K, V, w.sm_scale, q_start=prior)
+    for sp in splits_list:
+        ws = torch.full((pool.workspace_bytes(kvq.OP_PREFILL, n_q, sp),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = pool.prefill(layer, seq, prior, q.cuda(), w.sm_scale, n_splits=sp, ws=ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref, f"rotated prefill {w.name} prior={prior} n_q={n_q} splits={sp}")
+
+
+def test_rotated_prefill_small():
+    need_gpu()
+    _rotated_prefill_case(TINY, 0, 100, 45, [1, 2, 3, 0])
+    _rotated_prefill_case(TINY, 0, 0, 77, [1, 2])
+
+
+@pytest.mark.parametrize("w", [Workload(96, "rotated prefill, D=128 group 4", "q2r", 2, 2, 128, 8, 1, 300),
+                               Workload(96, "rotated prefill, D=256 group 2", "q2r", 1, 4, 256, 8, 1, 300),
+                               Workload(96, "rotated prefill, D=128 group 8", "q2r", 1, 2, 128, 16, 1, 300)],
+                         ids=lambda w: w.name)
+def test_rotated_prefill_geometries(w):
+    need_gpu()
+    _rotated_prefill_case(w, w.n_layers - 1, 130, 64, [1, 4, 0], salt=3)
+
+
+def test_rotated_prefill_last_row_equals_decode():
     need_gpu()
     import quantized_kv_attention_append_amd as kvq
-    pool, _ = make_pool(TINY, 4, _fmt())
-    seq = pool.reserve(128)
-    k, v = kv_rows(TINY, 0, 0, 128)
-    pool.append(0, [seq], [0], [128], k.cuda(), v.cuda())
-    with pytest.raises(kvq.KvError) as ei:
-        pool.prefill(0, seq, 64, queries(TINY, 0, 64, stream=1).cuda(), TINY.sm_scale)
-    assert ei.value.name == "KV_ERR_FORMAT"
+    prior, n_q = 200, 40
+    pool, mem = make_pool(TINY, 5, _fmt())
+    seq = pool.reserve(prior + n_q)
+    k, v = kv_rows(TINY, 0, 0, prior + n_q)
+    pool.append(0, [seq], [0], [prior + n_q], k.cuda(), v.cuda())
+    q = queries(TINY, 0, n_q, stream=1).cuda()
+    out = pool.prefill(0, seq, prior, q, TINY.sm_scale)
+    dec = pool.decode(0, [seq], [prior + n_q], q[-1:].contiguous(), TINY.sm_scale)
+    torch.cuda.synchronize()
+    K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
+    ref = attention.decode(q[-1].float().cpu().numpy(), K, V, TINY.sm_scale)
+    assert_close(out[-1].cpu().numpy(), ref, "rotated prefill last row against the oracle's decode")
+    assert_close(dec[0].cpu().numpy(), ref, "rotated decode at the same length against the oracle")
+    assert_close(out[-1].cpu().numpy(), dec[0].cpu().numpy().astype(np.float64), "rotated prefill last row vs decode")
 
 
 @pytest.mark.parametrize("w", [Workload(94, "rotated, group 8, D=128", "q2r", 1, 2, 128, 16, 2, 300),
