@@ -23,6 +23,7 @@
 
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "kvq_rt.h"
 
 using namespace kvq;
 
@@ -49,7 +50,7 @@ kv_status set_error(kv_status s, const char* msg) { return fail(s, "%s", msg); }
 namespace {
 
 kv_status hip_fail(hipError_t e, const char* what) {
-    return fail(KV_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+    return fail(KV_ERR_DEVICE, "%s: %s", what, rt::error_string(e));
 }
 
 // Runs an entry point's body so that no C++ exception crosses the C ABI: a
@@ -236,7 +237,7 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
         p->block_bytes = block_bytes_of(fmt, geom->head_dim);
         p->max_seqs = max_seqs;
         p->bt_stride = (int32_t)((max_seq_tokens + PAGE - 1) / PAGE);
-        hipError_t e = hipGetDevice(&p->device);
+        hipError_t e = rt::current_device(&p->device);
         if (e != hipSuccess) {
             delete p;
             return hip_fail(e, "hipGetDevice");
@@ -244,34 +245,32 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
         if (d_mem) {
             p->d_pages = (uint8_t*)d_mem;
         } else {
-            e = hipMalloc((void**)&p->d_pages, (size_t)(n_pages * pb));
+            e = rt::alloc((void**)&p->d_pages, (size_t)(n_pages * pb));
             if (e != hipSuccess) {
                 delete p;
-                return hip_fail(e, "hipMalloc(pool pages)");
+                return hip_fail(e, "pool page allocation");
             }
             p->own_pages = true;
         }
-        e = hipMalloc((void**)&p->d_bt, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
-        if (e == hipSuccess) e = hipMemset(p->d_bt, 0, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
-        if (e == hipSuccess) e = hipDeviceSynchronize();
+        e = rt::alloc((void**)&p->d_bt, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
+        if (e == hipSuccess) e = rt::zero(p->d_bt, (size_t)max_seqs * p->bt_stride * sizeof(int32_t));
         if (e == hipSuccess && fmt == KV_FMT_Q8) {
             size_t sb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * PAGE * geom->head_dim * sizeof(uint16_t);
-            e = hipMalloc((void**)&p->d_stage, sb);
+            e = rt::alloc((void**)&p->d_stage, sb);
         }
         if (e == hipSuccess && fmt == KV_FMT_Q2_WINDOW) {
             size_t wb = (size_t)max_seqs * geom->n_layers * geom->n_kv_heads * 256 * (size_t)geom->head_dim;
-            e = hipMalloc((void**)&p->d_win, wb);
+            e = rt::alloc((void**)&p->d_win, wb);
         }
         if (e == hipSuccess) {
             // one counter per (batch entry, KV head, launch of four query heads); each
             // fused decode launch returns every counter it used to zero
             const size_t cb = decode_counters(geom->n_kv_heads) * sizeof(int32_t);
-            e = hipMalloc((void**)&p->d_cnt, cb);
-            if (e == hipSuccess) e = hipMemset(p->d_cnt, 0, cb);
-            if (e == hipSuccess) e = hipDeviceSynchronize();
+            e = rt::alloc((void**)&p->d_cnt, cb);
+            if (e == hipSuccess) e = rt::zero(p->d_cnt, cb);
         }
         if (e != hipSuccess) {
-            kv_status r = hip_fail(e, "hipMalloc(block tables / window)");
+            kv_status r = hip_fail(e, "block table / window / counter allocation");
             kv_pool_destroy(p);
             return r;
         }
@@ -297,11 +296,11 @@ kv_status kv_pool_create(int64_t bytes, const kv_geom* geom, kv_format fmt, int3
 kv_status kv_pool_destroy(kv_pool* p) {
     return guarded([&]() -> kv_status {
         if (!p) return fail(KV_ERR_ARG, "pool is NULL");
-        if (p->own_pages && p->d_pages) (void)hipFree(p->d_pages);
-        if (p->d_bt) (void)hipFree(p->d_bt);
-        if (p->d_stage) (void)hipFree(p->d_stage);
-        if (p->d_win) (void)hipFree(p->d_win);
-        if (p->d_cnt) (void)hipFree(p->d_cnt);
+        if (p->own_pages && p->d_pages) (void)rt::release(p->d_pages);
+        if (p->d_bt) (void)rt::release(p->d_bt);
+        if (p->d_stage) (void)rt::release(p->d_stage);
+        if (p->d_win) (void)rt::release(p->d_win);
+        if (p->d_cnt) (void)rt::release(p->d_cnt);
         delete p;
         return KV_OK;
     });
@@ -378,12 +377,11 @@ kv_status kv_seq_reserve(kv_pool* p, int64_t max_tokens, const int32_t* pages, i
                 if (p->refs[(size_t)pg] == 0) got.push_back(pg);
             }
         }
-        hipError_t e = hipMemcpy(p->d_bt + (size_t)slot * p->bt_stride, got.data(), got.size() * sizeof(int32_t),
-                                 hipMemcpyHostToDevice);
+        hipError_t e = rt::upload(p->d_bt + (size_t)slot * p->bt_stride, got.data(), got.size() * sizeof(int32_t));
         if (e != hipSuccess) {
             if (!pages)
                 for (int32_t pg : got) push_free(p, pg);
-            return hip_fail(e, "hipMemcpy(block table)");
+            return hip_fail(e, "block table upload");
         }
         for (int32_t pg : got) p->refs[(size_t)pg] = 1;
         p->free_count -= need;
@@ -448,8 +446,7 @@ kv_status kv_seq_fork(kv_pool* p, int32_t parent, int64_t n, int64_t max_tokens,
             if (p->refs[(size_t)pg] == 0) got.push_back(pg);
         }
         pages.insert(pages.end(), got.begin(), got.end());
-        hipError_t e = hipMemcpy(p->d_bt + (size_t)slot * p->bt_stride, pages.data(), pages.size() * sizeof(int32_t),
-                                 hipMemcpyHostToDevice);
+        hipError_t e = rt::upload(p->d_bt + (size_t)slot * p->bt_stride, pages.data(), pages.size() * sizeof(int32_t));
         CopyRange r[3];
         int nr = 0;
         if (copy)

@@ -115,10 +115,17 @@ hipError_t launch_decode_bf16(const PoolView& pv, int layer, const BatchDesc& bd
 // sit after the splits' partials.
 hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
                           float sm, int splits, float* ws, float* out, int w0, hipStream_t s);
-// Split count a prefill of n_q chunk queries takes when the caller passes 0,
-// for a pool of format fmt (the rotated format takes 64 (query, head) rows a
-// workgroup, the others 128).
-int prefill_auto_splits(int n_q, int Hq, int Hkv, int fmt);
+// (query, head) rows a prefill workgroup takes: 64 for the rotated format
+// (its query enters as two bf16 terms), 128 for the others.
+inline int prefill_rows_per_block(int fmt) { return fmt == KV_FMT_Q2_ROT ? 64 : 128; }
+// Split count a prefill of n_q chunk queries takes when the caller passes 0:
+// about one workgroup per compute unit (256 on MI355X).
+inline int prefill_auto_splits(int n_q, int Hq, int Hkv, int fmt) {
+    const int QB = prefill_rows_per_block(fmt) / (Hq / Hkv);
+    const int blocks = ((n_q + QB - 1) / QB) * Hkv;
+    const int want = (256 + blocks - 1) / blocks;
+    return want < 1 ? 1 : want > 64 ? 64 : want;
+}
 // Floats a prefill workspace holds beyond the splits' partials: the window's
 // partials (2-bit window pools) or the rotated query's two bf16 terms
 // (rotated pools).

@@ -573,14 +573,7 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q
     out[(int64_t)row * D + d] = acc / den;
 }
 
-int prefill_rows_per_block(int fmt) { return fmt == KV_FMT_Q2_ROT ? PREFILL_ROWS<true> : PREFILL_ROWS<false>; }
-
-int prefill_auto_splits(int n_q, int Hq, int Hkv, int fmt) {
-    const int QB = prefill_rows_per_block(fmt) / (Hq / Hkv);
-    const int blocks = ((n_q + QB - 1) / QB) * Hkv;
-    const int want = (256 + blocks - 1) / blocks;  // about one workgroup per compute unit
-    return want < 1 ? 1 : want > 64 ? 64 : want;
-}
+static_assert(PREFILL_ROWS<true> == 64 && PREFILL_ROWS<false> == 128, "prefill_rows_per_block() matches the kernels");
 
 // The rotated format's query rows: H q in fp32 butterflies (the stages of the
 // rotated append, H the unnormalised Walsh-Hadamard matrix), each row written
