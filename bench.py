@@ -131,6 +131,7 @@ def prefill_leg(steps: int, warmup: int):
     torch.cuda.synchronize()
     ms = []
     for _ in range(steps):
+        _hold(4)
         e0.record(stream)
         pool.prefill(0, seq, prior, q, w.sm_scale, ws=ws, out=out)
         e1.record(stream)
@@ -162,6 +163,28 @@ def _stats_us(ms):
     return {"us_mean": 1e3 * sum(ms) / len(ms), "us_median": 1e3 * ms[len(ms) // 2], "us_min": 1e3 * ms[0]}
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def _hold(n_calls: int):
+    """Keep the current stream busy (a spin kernel) for about 0.25 ms per call
+    about to be queued, plus 5 ms, so that the host enqueues those calls before
+    the GPU reaches them: event pairs around each call then time the GPU's work
+    back to back, not the host's launch pace or a pause of the interpreter."""
+    global _SLEEP_CYCLES_PER_MS
+    import torch
+    if _SLEEP_CYCLES_PER_MS is None:
+        stream = torch.cuda.current_stream()
+        torch.cuda._sleep(1000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.cuda._sleep(2_000_000)
+        e1.record(stream)
+        e1.synchronize()
+        _SLEEP_CYCLES_PER_MS = 2_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int((5.0 + 0.25 * n_calls) * _SLEEP_CYCLES_PER_MS))
+
+
 def _call_ms(fn, reps: int, flush=None):
     """Average, minimum and median of HIP-event times of fn() on the current
     stream, the calls enqueued back to back (one synchronisation at the end,
@@ -170,6 +193,7 @@ def _call_ms(fn, reps: int, flush=None):
     import torch
     stream = torch.cuda.current_stream()
     ev = []
+    _hold(reps * (2 if flush is not None else 1))
     for _ in range(reps):
         if flush is not None:
             flush()
@@ -297,6 +321,7 @@ def q8_leg(reps: int):
         pool.decode(layer, seqs, lens, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
     torch.cuda.synchronize()
     ev = []
+    _hold(reps * w.n_layers)
     for _ in range(reps):  # steps of one call per layer, back to back, an event pair around each call
         for layer in range(w.n_layers):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -315,6 +340,7 @@ def q8_leg(reps: int):
                            dtype=torch.float32).to(torch.bfloat16)
     cur = list(lens)
     step_ms = []
+    _hold(2 * (reps + 1) * w.n_layers)
     for r in range(reps + 1):              # the first round is a warm-up
         for layer in range(w.n_layers):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -401,6 +427,7 @@ def bf16_leg(reps: int, window: bool = False, rotated: bool = False):
     step()
     torch.cuda.synchronize()
     ev = []
+    _hold(reps * L)
     for _ in range(reps):
         for layer in range(L):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -516,6 +543,7 @@ def probe_leg(pool, perm, reps: int = 10):
             fn(layer)
         torch.cuda.synchronize()
         ev = []
+        _hold(reps * L)
         for _ in range(reps):
             for layer in range(L):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -844,11 +872,10 @@ def main():
     ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    _hold(args.steps * L)
     for s in range(args.steps):
         step(ev[s])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(args.steps) for l in range(L)]
     region_ms = ev[0][0][0].elapsed_time(ev[-1][-1][1])
     ms_per_step = region_ms / args.steps
@@ -862,7 +889,7 @@ def main():
     tokens_per_step = B * L * ctx
     value = tokens_per_step / (ms_per_step * 1e-3)
     log(f"splits={sp} avg decode launch {avg_launch_ms * 1e3:.1f} us, step {ms_per_step:.3f} ms, "
-        f"{achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s), wall {wall:.3f} s")
+        f"{achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of 8 TB/s)")
 
     # ---- the same step captured once as a HIP graph and replayed (no host
     # launch work, no dispatch gaps between calls); its outputs must equal the

@@ -23,6 +23,7 @@
 
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "prefill.h"
 #include "kvq_rt.h"
 
 using namespace kvq;

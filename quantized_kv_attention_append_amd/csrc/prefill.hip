@@ -40,6 +40,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "prefill.h"
 
 namespace kvq {
 

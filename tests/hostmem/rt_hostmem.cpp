@@ -17,6 +17,7 @@
 
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "prefill.h"
 #include "kvq_rt.h"
 
 namespace kvq {
