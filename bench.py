@@ -568,7 +568,7 @@ def probe_leg(pool, perm, reps: int = 10):
         go = lambda: check(lib.kvq_probe_mfma_bf16(shape, chains, grid, iters, C.c_void_p(sink.data_ptr()), sp))
         go()
         t = _call_ms(go, 10)
-        fl = grid * 4 * iters * chains * 32768
+        fl = grid * 4 * iters * chains * (16384 if shape == 0 else 32768)  # 2 M N K flops an instruction
         mfma.append((fl / (t[2] * 1e-3) / 1e12, shape, chains, fl, t[2]))
     best = max(mfma)
     best_pattern = min(pattern_t, pattern_lds_t, key=lambda t: t["us_median"])

@@ -13,9 +13,8 @@ namespace kvq {
 // sit after the splits' partials.
 hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q_start, int n_q, const uint16_t* q,
                           float sm, int splits, float* ws, float* out, int w0, hipStream_t s);
-// (query, head) rows a prefill workgroup takes: 64 for the rotated format
-// (its query enters as two bf16 terms), 128 for the others.
-inline int prefill_rows_per_block(int fmt) { return fmt == KV_FMT_Q2_ROT ? 64 : 128; }
+// (query, head) rows a prefill workgroup takes, in every format.
+inline int prefill_rows_per_block(int /*fmt*/) { return 128; }
 // Split count a prefill of n_q chunk queries takes when the caller passes 0:
 // about one workgroup per compute unit (256 on MI355X).
 inline int prefill_auto_splits(int n_q, int Hq, int Hkv, int fmt) {
