@@ -152,7 +152,7 @@ def prefill_leg(steps: int, warmup: int):
         "useful_flops": flops,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / MFMA_BF16_TFLOPS, "traffic": None,
-                     "kernel": "one kv_attn_prefill call: prefill_kernel<256, 1> then prefill_merge_kernel"},
+                     "kernel": "one kv_attn_prefill call: prefill_ws_kernel<256, false> then prefill_merge_kernel"},
         "chunk_append_ms": chunk_append_ms,
     }
 
