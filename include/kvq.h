@@ -13,9 +13,9 @@
  *    figures (pages, used pages, page bytes).
  *  - "The KV cache and prompt reuse" (ignis, concepts), section "What a
  *    sequence is made of": one pool shared by all lanes, a lane is charged for
- *    the pages it holds; the window of exact recent keys the compressed format
- *    keeps.  Section "When reuse misses": a format mismatch is refused before
- *    any byte moves.
+ *    the pages it holds; the most recent keys are held unquantized by the
+ *    compressed format.  Section "When reuse misses": a format mismatch is
+ *    rejected with nothing copied.
  *  - "Half the Cache, Twice the Context" (ml.co.ke): the symmetric absmax
  *    quantizer with per-channel K and per-token V scaling (section "What the
  *    cache loses when you round it"), accumulation in real FP32 (section "The
@@ -75,9 +75,9 @@ typedef enum {
      * it, control it": the format is hq-e8-2b or bf16), in the same paged
      * pool and through the same calls. */
     KV_FMT_BF16 = 3,
-    /* KV_FMT_Q2 pages plus the window of exact recent keys that "The KV
-     * cache and prompt reuse" (section "What a sequence is made of") has the
-     * compressed format keep, read as one page: for each (sequence, layer, KV
+    /* KV_FMT_Q2 pages plus the unquantized recent keys that "The KV cache
+     * and prompt reuse" (section "What a sequence is made of") has the
+     * compressed format hold, read as one page: for each (sequence, layer, KV
      * head) the bf16 K and V rows of the last page appended to.  With A
      * tokens of a (sequence, layer) appended, decode and prefill read tokens
      * 64 * floor((A - 1) / 64) .. A - 1 exact and every earlier token from

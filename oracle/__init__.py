@@ -19,7 +19,7 @@ Sources (the three pages this library is built from):
     reservation, prefill reading the compressed cache, the garbage-filled
     workspace check.
   * "The KV cache and prompt reuse" (ignis, concepts): one pool shared by all
-    lanes, fixed 64-token pages, the window of exact recent keys.
+    lanes, fixed 64-token pages, recent keys held unquantized.
   * "Half the Cache, Twice the Context" (ml.co.ke): the bytes-per-token
     formula, the symmetric absmax quantizer, per-channel K / per-token V
     scaling, the outlier recipe, the accumulator-precision model.

@@ -2,8 +2,8 @@
 
 Follows "KV at 9 KB a token" (How it works: fixed-size 64-token pages, a pool
 that is a byte budget) and "The KV cache and prompt reuse" (What a sequence is
-made of: one pool shared by all lanes; the window of exact recent keys the
-compressed format keeps).  A sequence owns a block table: logical page i of the
+made of: one pool shared by all lanes; the most recent keys, which the
+compressed format holds unquantized).  A sequence owns a block table: logical page i of the
 sequence lives in physical page ``bt[i]``; token t sits in slot t % 64 of page
 ``bt[t // 64]``.
 
@@ -33,8 +33,8 @@ kept for it.
 
 The 2-bit format with an exact window ("q2w") keeps, besides the 2-bit pages,
 the exact rows of the last page a (sequence, layer) has appended to: the
-"window of exact recent keys that the compressed KV format keeps" of "The KV
-cache and prompt reuse" (What a sequence is made of), read here as one page.
+recent keys that "The KV cache and prompt reuse" (What a sequence is made of)
+has the compressed format hold unquantized, read here as one page.
 With A tokens appended, every reader sees tokens 64 * floor((A - 1) / 64) ..
 A - 1 exact and every earlier token through the 2-bit codec; the pages
 themselves hold exactly what a plain 2-bit pool holds.  Appends are then

@@ -14,7 +14,7 @@
 // exact window of a 2-bit window pool: the block of the last page an append
 // reaches goes to the (sequence, layer, head) window block instead of the
 // page ("The KV cache and prompt reuse", section "What a sequence is made
-// of": the window of exact recent keys).
+// of": the most recent keys are held unquantized).
 #include "kvq_device.h"
 #include "kvq_internal.h"
 

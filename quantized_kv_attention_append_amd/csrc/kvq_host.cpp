@@ -5,8 +5,8 @@
 // sequence reserves the pages of its whole bound when it is admitted, so an
 // append inside the bound can never run out of pages ("KV at 9 KB a token",
 // section "How it works"; "The KV cache and prompt reuse", section "What a
-// sequence is made of").  Every check runs before anything is launched, and a
-// mismatch is refused before any byte moves ("The KV cache and prompt reuse",
+// sequence is made of").  Every check runs before anything is launched, so a
+// refused call has copied or written nothing ("The KV cache and prompt reuse",
 // section "When reuse misses"); nothing falls back to another path ("Half the
 // Cache, Twice the Context", section "How to apply this", item 6).
 #include <hip/hip_runtime.h>

@@ -1,7 +1,8 @@
 // Attention over the exact window of a 2-bit window pool: the bf16 K and V
 // rows of the last page a (sequence, layer) has appended to, kept beside the
-// 2-bit pages (the window of exact recent keys of "The KV cache and prompt
-// reuse", section "What a sequence is made of").  A window block has the bf16
+// 2-bit pages (the most recent keys, which the compressed format of "The KV
+// cache and prompt reuse", section "What a sequence is made of", holds
+// unquantized).  A window block has the bf16
 // page layout: K token-major (slot t at 2Dt), V dim-major (dim d at
 // 128D + 128d).  Slots past the appended tokens hold stale rows, so every
 // product with them is selected away, never multiplied by a zero weight.

@@ -4,7 +4,7 @@ After the child and the parent each append their own continuation, the whole
 pool image equals the oracle's bit for bit (shared pages untouched, the copied
 page carried on by the child), both decode within tolerance of the oracle,
 page accounting counts shared pages once, and appends into shared pages are
-refused before any byte moves."""
+refused with the pool unchanged."""
 
 import numpy as np
 import pytest

@@ -12,7 +12,7 @@ for a request's whole bound when it is admitted; "The KV cache and prompt
 reuse", section "What a sequence is made of": a lane is charged for the
 pages it holds, shared prefix pages once), that every refused call leaves
 the pool's bytes and the launch log unchanged ("The KV cache and prompt
-reuse", section "When reuse misses": refused before any byte moves), and
+reuse", section "When reuse misses": a refusal copies nothing), and
 the launch plans.  test_host_runtime_under_address_sanitizer runs this file
 again with the library built with -fsanitize=address.
 """

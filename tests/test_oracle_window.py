@@ -1,7 +1,7 @@
 """Oracle pins: the 2-bit format with an exact window of the last page.
 
 "The KV cache and prompt reuse" (What a sequence is made of) has the
-compressed format keep a window of exact recent keys.  Read here: with A
+compressed format hold its most recent keys unquantized.  Read here: with A
 tokens of a (sequence, layer) appended, the tokens of page floor((A - 1) / 64)
 are read exact, every earlier token through the 2-bit codec.  Pinned by:
   * the pages equal a plain 2-bit pool's byte for byte (the body is the 2-bit
