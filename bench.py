@@ -53,6 +53,9 @@ CSRC = os.path.join(ROOT, "quantized_kv_attention_append_amd", "csrc")
 # sources of the kernel of a 2-bit decode call at 8 splits (split partials and their merge)
 DECODE_SOURCES = ("decode_q2_mfma.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q2_mfma_27b_geometry_traffic.md")
+# sources of an 8-bit decode call's two kernels (split partials, merge) and of its split count
+Q8_SOURCES = ("decode_q8.hip", "merge_splits.hip", "decode_common.h", "kvq_device.h", "kvq_internal.h", "kvq_host.cpp")
+Q8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_q8_mfma_24_lanes_32_layers.md")
 METRIC = "decode attention: KV tokens attended/s and achieved HBM GB/s (% of peak), 2-bit"
 
 
@@ -74,24 +77,24 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def decode_source_hash() -> str:
+def decode_source_hash(names=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per decode call from the committed counter summary, or None
-    when it is absent or was taken on other decode sources."""
+def measured_traffic(path=TRAFFIC_FILE, names=DECODE_SOURCES):
+    """HBM bytes per decode call from a committed counter summary, or None
+    when it is absent or was taken on other sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             fields = dict(line.split(":", 1) for line in f if line.startswith(("source_sha256:", "traffic_bytes_per_call:")))
     except OSError:
         return None
-    if fields.get("source_sha256", "").strip() != decode_source_hash():
-        log("traffic: counter summary is for other decode sources; reporting null")
+    if fields.get("source_sha256", "").strip() != decode_source_hash(names):
+        log(f"traffic: {os.path.basename(path)} is for other sources; reporting null")
         return None
     return int(fields["traffic_bytes_per_call"].strip())
 
@@ -362,7 +365,7 @@ def q8_leg(reps: int):
             "tokens_per_layer": tokens, "pool_bytes": n_pages * pb, "splits": sp,
             "decode_us_per_layer_call": avg * 1e3, "decode_us_median": dec["us_median"], "bytes_per_call": alg,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic(Q8_TRAFFIC_FILE, Q8_SOURCES),
                          "kernel": "one kv_attn_decode call per layer: decode_q8_mfma_kernel<128, 4> then merge_splits8_kernel"},
             "kv_tokens_per_s": tokens * w.n_layers / (avg * 1e-3 * w.n_layers),
             "layer_step": {"what": "per layer: decode of all 24 lanes, then quantize-append of 1 token per lane",

@@ -385,7 +385,12 @@ __global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int
 //         tokens, two k-steps); lane group g accumulates the rows of heads
 //         2g and 2g + 1, the same heads as its softmax, so the rescale is local.
 // The sum over dims and over tokens is order-free, so each k-step takes the
-// dims (tokens) that one 16-byte load per lane delivers.
+// dims (tokens) that one 16-byte load per lane delivers.  A wave holds one
+// page in registers at a time and waits for it, so the loads in flight come
+// from the other waves: three workgroups share a compute unit (168 registers
+// a wave), the group's fp32 query rows sit in LDS rather than in registers
+// (read once a page, for the channel-scale products), and the host picks the
+// split count that fills those slots in one round.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -442,7 +447,7 @@ __device__ __forceinline__ float row_sum16(float v) {
 }  // namespace
 
 template <int D, int G, bool SCORES>
-__global__ __launch_bounds__(256, 2) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+__global__ __launch_bounds__(256, 3) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                 const uint16_t* __restrict__ q, float sm, int splits,
                                                                 float* __restrict__ ws, float* __restrict__ out,
                                                                 float* __restrict__ scores, int64_t sstride) {
@@ -463,20 +468,19 @@ __global__ __launch_bounds__(256, 2) void decode_q8_mfma_kernel(PoolView pv, int
     __shared__ __align__(16) uint16_t w_s[4][16][WROW];  // per wave: weight rows 2j + h over the page's tokens
     __shared__ __align__(16) float o_s[4][G][D];
     __shared__ float ml_s[4][G][2];
+    __shared__ __align__(16) float q_s[G][D];  // the group's query rows, fp32
 
     // rows 2G.. of the weight operand stay zero
     for (int i = lane; i < 16 * WROW; i += 64)
         if (i / WROW >= 2 * G) w_s[wave][i / WROW][i % WROW] = 0;
 
-    // this lane's query row: head col / 2, term col % 2; dims 64m + 16grp + i
+    // this lane's query row: head col / 2, term col % 2; dims 64m + 16grp + i,
+    // read once a page from the workgroup's fp32 copy of the group's rows
     const int aj = col >> 1, ah = col & 1;
     const bool arow = col < 2 * G;
-    float qv[NM][16];
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            qv[m][i] = arow ? bf16_to_f32(q[((int64_t)e * Hq + g * G + aj) * D + 64 * m + 16 * grp + i]) : 0.f;
+    for (int i = tid; i < G * D; i += 256) q_s[i / D][i % D] = bf16_to_f32(q[((int64_t)e * Hq + g * G) * D + i]);
+    __syncthreads();
+    const float* qrow = &q_s[arow ? aj : 0][0];
 
     f32x4_t acc[NDB];
 #pragma unroll
@@ -510,10 +514,11 @@ __global__ __launch_bounds__(256, 2) void decode_q8_mfma_kernel(PoolView pv, int
             for (int c4 = 0; c4 < 4; ++c4) {
                 const float4 k4 =
                     *reinterpret_cast<const float4*>(blk + q8_kscale_off(D) + 4 * (64 * m + 16 * grp + 4 * c4));
-                x[4 * c4] = qv[m][4 * c4] * k4.x;
-                x[4 * c4 + 1] = qv[m][4 * c4 + 1] * k4.y;
-                x[4 * c4 + 2] = qv[m][4 * c4 + 2] * k4.z;
-                x[4 * c4 + 3] = qv[m][4 * c4 + 3] * k4.w;
+                const float4 q4 = *reinterpret_cast<const float4*>(qrow + 64 * m + 16 * grp + 4 * c4);
+                x[4 * c4] = arow ? q4.x * k4.x : 0.f;
+                x[4 * c4 + 1] = arow ? q4.y * k4.y : 0.f;
+                x[4 * c4 + 2] = arow ? q4.z * k4.z : 0.f;
+                x[4 * c4 + 3] = arow ? q4.w * k4.w : 0.f;
             }
             qa[2 * m] = make_uint4(bf16_term2(x[0], x[1], ah), bf16_term2(x[2], x[3], ah), bf16_term2(x[4], x[5], ah),
                                    bf16_term2(x[6], x[7], ah));

@@ -534,17 +534,35 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 // Default split count for a decode batch.  2-bit and bf16: about one workgroup per
 // compute unit (256 on MI355X) over all (sequence, KV head) pairs, with at
 // least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
-// at least that many workgroups, and splits of about sixteen page pairs of the
-// longest sequence (eight pages per wavefront), since several of its smaller
-// workgroups share a compute unit (measured on 24 lanes of 16..124 pages, us
-// a layer call: 2 splits 88, 3 71, 4 67, 5 81, 6 83, 7 77, 8 71).
+// its decode holds three workgroups on each compute unit at 128 dims (two at
+// 256), and a workgroup whose split holds no page ends at once; the split
+// count is the largest whose workgroups with pages all fit in those slots
+// together, so that none waits for a second round, going no further once a
+// split is down to one page pair (measured at 128 dims on 24 lanes of 16..128
+// pages, us a layer call: 4 splits 68, 6 56, 8 65 with 883 such workgroups
+// for 768 slots, 12 60, 16 61).
 int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     int64_t max_pages = 1;
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
     const int64_t base = (int64_t)n * p->geom.n_kv_heads;
     const int64_t want = (256 + base - 1) / base;
-    if (p->fmt == KV_FMT_Q8)
-        return (int)std::max<int64_t>(1, std::min<int64_t>(256, std::max<int64_t>(want, ((max_pages + 1) / 2 + 15) / 16)));
+    if (p->fmt == KV_FMT_Q8) {
+        const int64_t SLOTS = (p->geom.head_dim == 128 ? 3 : 2) * 256;
+        const int64_t max_pairs = (max_pages + 1) / 2;
+        int best = 1;
+        for (int s = 1; s <= 256; ++s) {
+            const int64_t per = (max_pairs + s - 1) / s;
+            int64_t live = 0;  // workgroups with pages
+            for (int i = 0; i < n; ++i) {
+                const int64_t pairs = ((ctx[i] + PAGE - 1) / PAGE + 1) / 2;
+                live += (pairs + per - 1) / per;
+            }
+            if (s > 1 && live * p->geom.n_kv_heads > SLOTS) break;
+            best = s;
+            if (per == 1) break;
+        }
+        return best;
+    }
     const int64_t cap = std::max<int64_t>(1, ((max_pages + 1) / 2) / 8);
     return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, 256}));
 }
