@@ -214,8 +214,10 @@ __global__ __launch_bounds__(256) void decode_q8_kernel(PoolView pv, int layer, 
 //            the wave's LDS and read as broadcasts;
 //   softmax: wave-wide max and sum per head, weights p_t vscale_t to LDS;
 //   p.v:     o_j,d += sum_t w_j(t) c_dt over the page's 64 tokens.
+// (the variant that also stores the raw logits takes one workgroup a compute
+// unit: it spills at two)
 template <int D, int G, bool SCORES>
-__global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int layer, BatchDesc bd,
+__global__ __launch_bounds__(256, SCORES ? 1 : 2) void decode_q8_wave_kernel(PoolView pv, int layer, BatchDesc bd,
                                                              const uint16_t* __restrict__ q, float sm, int splits,
                                                              float* __restrict__ ws, float* __restrict__ out,
                                                              float* __restrict__ scores, int64_t sstride) {
@@ -297,10 +299,15 @@ __global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int
             if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
         // ---- online softmax per head; slots past ctx weigh nothing (their bytes may be anything) ----
+        if constexpr (SCORES) {  // a variant of its own: the branch costs the other variant registers
+            if (valid) {
+                float* srow = scores + ((int64_t)e * Hq + g * G) * sstride + pg * PAGE + lane;
+#pragma unroll
+                for (int j = 0; j < G; ++j) srow[j * sstride] = sm * s[j];
+            }
+        }
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            if constexpr (SCORES)  // a variant of its own: the branch costs the other variant registers
-                if (valid) scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + lane] = sm * s[j];
             const float x = valid ? s[j] * cs : -INFINITY;
             const float m_new = fmaxf(m[j], wave_max(x));  // finite: every page of the split holds a token
             const float alpha = __builtin_amdgcn_exp2f(m[j] - m_new);
@@ -387,10 +394,11 @@ __global__ __launch_bounds__(256, 2) void decode_q8_wave_kernel(PoolView pv, int
 // The sum over dims and over tokens is order-free, so each k-step takes the
 // dims (tokens) that one 16-byte load per lane delivers.  A wave holds one
 // page in registers at a time and waits for it, so the loads in flight come
-// from the other waves: three workgroups share a compute unit (168 registers
-// a wave), the group's fp32 query rows sit in LDS rather than in registers
-// (read once a page, for the channel-scale products), and the host picks the
-// split count that fills those slots in one round.
+// from the other waves: three workgroups share a compute unit up to group 4
+// (168 registers a wave; two at group 8), the group's fp32 query rows sit in
+// LDS rather than in registers (read once a page, for the channel-scale
+// products), and the host picks the split count that fills those slots in
+// one round.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -446,8 +454,13 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 }  // namespace
 
+// workgroups a compute unit holds: three up to group 4 (168 registers a wave),
+// two at group 8 (its eight heads' rows take more) and in the variant that
+// also stores the raw logits, so that no variant spills
+constexpr int Q8_MFMA_WGS_PER_CU(int G, bool scores) { return G <= 4 && !scores ? 3 : 2; }
+
 template <int D, int G, bool SCORES>
-__global__ __launch_bounds__(256, 3) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+__global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                 const uint16_t* __restrict__ q, float sm, int splits,
                                                                 float* __restrict__ ws, float* __restrict__ out,
                                                                 float* __restrict__ scores, int64_t sstride) {
@@ -539,6 +552,16 @@ __global__ __launch_bounds__(256, 3) void decode_q8_mfma_kernel(PoolView pv, int
         }
         // ---- online softmax of heads 2grp, 2grp + 1 over the page's tokens ----
         const int n_tok = min(PAGE, ctx - pg * PAGE);
+        if constexpr (SCORES) {  // raw logits, stored apart from the softmax (a branch inside it costs registers)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int j = 2 * grp + hh;
+                float* srow = scores + ((int64_t)e * Hq + g * G + min(j, G - 1)) * sstride + pg * PAGE + col;
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    if (j < G && 16 * tb + col < n_tok) srow[16 * tb] = sm * (st[tb][2 * hh] + st[tb][2 * hh + 1]);
+            }
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int j = 2 * grp + hh;
@@ -548,8 +571,6 @@ __global__ __launch_bounds__(256, 3) void decode_q8_mfma_kernel(PoolView pv, int
             for (int tb = 0; tb < 4; ++tb) {
                 const bool valid = 16 * tb + col < n_tok;
                 const float raw = st[tb][2 * hh] + st[tb][2 * hh + 1];
-                if constexpr (SCORES)
-                    if (live && valid) scores[((int64_t)e * Hq + g * G + j) * sstride + pg * PAGE + 16 * tb + col] = sm * raw;
                 sv[tb] = valid && live ? raw * cs : -INFINITY;
                 mt = fmaxf(mt, sv[tb]);
             }

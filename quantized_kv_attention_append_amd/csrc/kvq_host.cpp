@@ -534,8 +534,9 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 // Default split count for a decode batch.  2-bit and bf16: about one workgroup per
 // compute unit (256 on MI355X) over all (sequence, KV head) pairs, with at
 // least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
-// its decode holds three workgroups on each compute unit at 128 dims (two at
-// 256), and a workgroup whose split holds no page ends at once; the split
+// its decode holds three workgroups on each compute unit at 128 dims up to
+// group 4 (two at group 8 and at 256 dims), and a workgroup whose split holds
+// no page ends at once; the split
 // count is the largest whose workgroups with pages all fit in those slots
 // together, so that none waits for a second round, going no further once a
 // split is down to one page pair (measured at 128 dims on 24 lanes of 16..128
@@ -547,7 +548,8 @@ int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     const int64_t base = (int64_t)n * p->geom.n_kv_heads;
     const int64_t want = (256 + base - 1) / base;
     if (p->fmt == KV_FMT_Q8) {
-        const int64_t SLOTS = (p->geom.head_dim == 128 ? 3 : 2) * 256;
+        const int G = p->geom.n_q_heads / p->geom.n_kv_heads;
+        const int64_t SLOTS = (p->geom.head_dim == 128 && G <= 4 ? 3 : 2) * 256;
         const int64_t max_pairs = (max_pages + 1) / 2;
         int best = 1;
         for (int s = 1; s <= 256; ++s) {
