@@ -443,6 +443,7 @@ struct SplitLds {
     static constexpr int SLOTS_BYTES = W * SLOTS * TileShape<D>::BYTES;
     static constexpr int BYTES = SLOTS_BYTES + W * AREA;
     static_assert(4 * D * 2 <= AREA, "the query rows of four heads fit a wave's area");
+    static_assert(64 * 8 * 4 <= AREA, "a pass of the rotated rows (eight fp32 a lane) fits a wave's area");
     static_assert(BYTES <= 160 * 1024, "a workgroup's LDS fits the compute unit");
     static_assert((W * 4 * D + W * 4 * 3) * 4 + 4 <= SLOTS_BYTES, "the waves' partials fit the tile slots");
 };
@@ -514,82 +515,116 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
 
     // The query rows of the group's G heads (contiguous, G D bf16) go to the
     // wave's area of LDS before any tile is in flight (the compiler's wait
-    // for them must not be taken after a DMA load); the rotated variant
-    // widens them to fp32 and transforms them in the wave's last tile slot
-    // before that slot's first DMA.
+    // for them must not be taken after a DMA load).  The rotated variant
+    // instead widens each lane's pieces to fp32 in registers, issues the first
+    // DMA, and then transforms them there: butterfly stages h = 1, 2, 4 inside
+    // a lane's eight dims, h = 8m across the lanes l ^ m of one head's row,
+    // with the additions of the append's transform in the same order.  The
+    // rotated rows then pass through the wave's area (2 KB) a half at a time.
     constexpr int QPIECES = G * D * 2 / 16 / 64;  // 16-byte pieces per lane
+    // piece i of lane l: bf16 8p .. 8p + 7 of the four rows, p = l + 64 i, i.e.
+    // dims 8 (l % (D/8)) .. of head 8p / D
+    float qr[ROT ? QPIECES : 1][8];
     {
         uint4 qraw[QPIECES];
         const uint4* qsrc = reinterpret_cast<const uint4*>(q + head0 * D);
 #pragma unroll
-        for (int i = 0; i < QPIECES; ++i) {  // piece p holds bf16 8p .. 8p + 7 of the four rows
+        for (int i = 0; i < QPIECES; ++i) {
             const int p = l + 64 * i;
             qraw[i] = !GENERAL || 8 * p < nh * D ? qsrc[p] : make_uint4(0u, 0u, 0u, 0u);
         }
         if constexpr (ROT) {
-            const uint32_t qf = slot0 + (SLOTS - 1) * TB;  // fp32 [G][D]
 #pragma unroll
             for (int i = 0; i < QPIECES; ++i) {
                 const uint32_t u[4] = {qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    lds_store<float>(qf + 4 * (8 * (l + 64 * i) + 2 * k), bf16lo(u[k]));
-                    lds_store<float>(qf + 4 * (8 * (l + 64 * i) + 2 * k + 1), bf16hi(u[k]));
+                    qr[i][2 * k] = bf16lo(u[k]);
+                    qr[i][2 * k + 1] = bf16hi(u[k]);
                 }
             }
+            // the values are taken (and the loads waited for) before the DMA below
+#pragma unroll
+            for (int i = 0; i < QPIECES; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(qr[i][k]));
         } else {
 #pragma unroll
             for (int i = 0; i < QPIECES; ++i)
                 lds_store<u32x4>(area + 16 * (l + 64 * i), u32x4{qraw[i].x, qraw[i].y, qraw[i].z, qraw[i].w});
         }
     }
-    // (with one slot a wave, the rotated rows sit in the slot of tile 0)
-    if (T > 0 && !(ROT && SLOTS == 1)) issue(0);
-    if (ROT) {
+    if (T > 0) issue(0);
+    if constexpr (ROT) {
         // stages h = 1 .. D/2 as on append, additions only: nothing to contract
-        const uint32_t qf = slot0 + (SLOTS - 1) * TB;
-        auto at = [&](int i) { return qf + 4 * i; };
-        for (int h = 1; h < D; h *= 2) {
-            float a[G * D / 128], b[G * D / 128];
-            int ia[G * D / 128];
 #pragma unroll
-            for (int k = 0; k < G * D / 128; ++k) {  // pair p = l + 64 k of the G D / 2 pairs
-                const int pr = l + 64 * k, row = pr / (D / 2), jj = pr % (D / 2);
-                ia[k] = row * D + (jj / h) * 2 * h + jj % h;
-                a[k] = lds_load<float>(at(ia[k]));
-                b[k] = lds_load<float>(at(ia[k] + h));
-            }
-            __builtin_amdgcn_wave_barrier();
+        for (int h = 1; h < 8; h *= 2)
 #pragma unroll
-            for (int k = 0; k < G * D / 128; ++k) {
-                lds_store<float>(at(ia[k]), a[k] + b[k]);
-                lds_store<float>(at(ia[k] + h), a[k] - b[k]);
-            }
-            __builtin_amdgcn_wave_barrier();
+            for (int i = 0; i < QPIECES; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if ((k & h) == 0) {
+                        const float a = qr[i][k], b = qr[i][k + h];
+                        qr[i][k] = a + b;
+                        qr[i][k + h] = a - b;
+                    }
+#pragma unroll
+        for (int m = 1; m < D / 8; m *= 2) {  // h = 8m: the partner is lane l ^ m
+            const bool upper = (l & m) != 0;   // this lane holds the element i + h of its pairs
+#pragma unroll
+            for (int i = 0; i < QPIECES; ++i)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float o = __shfl_xor(qr[i][k], m);
+                    qr[i][k] = upper ? o - qr[i][k] : qr[i][k] + o;
+                }
         }
     }
 
     // ---- query operand: 19-bit fixed point per head, row 4 hq + iq = digit iq of head hq ----
     float qv[NC][32];
     float amax = 0.f, qsum = 0.f;
-    {
-        const uint32_t qrows = ROT ? slot0 + (SLOTS - 1) * TB : area;
+    // byte s of chunk c: k of byte s; the K operand puts dim(k) at nibble k % 32 of lane group k / 32
+    auto dim_of = [&](int c, int s) {
+        const int k = fp8_k(grp, s), ga = k >> 5, n = k & 31;
+        return 32 * NC * ga + 32 * c + 16 * (n >> 4) + 2 * (n & 7) + ((n >> 3) & 1);
+    };
+    if constexpr (!ROT) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int s = 0; s < 32; ++s) {
-                // k of byte s; the K operand puts dim(k) at nibble k % 32 of lane group k / 32
-                const int k = fp8_k(grp, s), ga = k >> 5, n = k & 31;
-                const int dim = 32 * NC * ga + 32 * c + 16 * (n >> 4) + 2 * (n & 7) + ((n >> 3) & 1);
-                const float x = ROT ? lds_load<float>(qrows + 4 * (hq * D + dim))
-                                    : bf16_to_f32(lds_load<uint16_t>(qrows + 2 * (hq * D + dim)));
+                const float x = bf16_to_f32(lds_load<uint16_t>(area + 2 * (hq * D + dim_of(c, s))));
                 qv[c][s] = x;
                 amax = fmaxf(amax, fabsf(x));
                 qsum += x;
             }
+    } else {
+        // piece `pass` of every lane holds heads HPP pass .. HPP pass + HPP - 1, at float 8 l of the area
+        constexpr int NPASS = QPIECES, HPP = G / NPASS;
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass) {
+            lds_store<u32x4>(area + 32 * l, u32x4{__float_as_uint(qr[pass][0]), __float_as_uint(qr[pass][1]),
+                                                  __float_as_uint(qr[pass][2]), __float_as_uint(qr[pass][3])});
+            lds_store<u32x4>(area + 32 * l + 16, u32x4{__float_as_uint(qr[pass][4]), __float_as_uint(qr[pass][5]),
+                                                       __float_as_uint(qr[pass][6]), __float_as_uint(qr[pass][7])});
+            const bool mine = hq / HPP == pass;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int s = 0; s < 32; ++s) {
+                    const float x = lds_load<float>(area + 4 * ((hq % HPP) * D + dim_of(c, s)));
+                    if (mine) qv[c][s] = x;
+                }
+        }
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int s = 0; s < 32; ++s) {
+                amax = fmaxf(amax, fabsf(qv[c][s]));
+                qsum += qv[c][s];
+            }
     }
-    // the rotated rows sat in the last slot: its first DMA goes out now
-    if (ROT && SLOTS == 1 && T > 0) issue(0);
     if (SLOTS == 2 && T > 1) issue(1);
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
