@@ -56,19 +56,21 @@ __global__ __launch_bounds__(256) void merge_splits8_kernel(BatchDesc bd, int Hq
     out[row * D + d] = acc / den;
 }
 
-// More than 8 splits, in groups of 64: lane t of every wave holds the (max,
-// sum) of split p0 + t, the wave reduces them, and each thread folds its
-// dim's 64 partial outputs with the split weights, which go through the
-// wave's own row of LDS.  Only slots below `splits` (inside the workspace)
-// are loaded and results past the live splits are selected away; the first
-// group's loads go out before the live split count is known.
+// More than 8 splits, in groups of 64, one wave per (sequence, query head,
+// 64 dims): lane t holds the (max, sum) of split p0 + t, the wave reduces
+// them, and each lane folds its dim's 64 partial outputs with the split
+// weights, which go through the wave's row of LDS.  (A row's dims spread over
+// D / 64 workgroups, so that a long sequence's few rows still read their
+// partials on many compute units.)  Only slots below `splits` (inside the
+// workspace) are loaded and results past the live splits are selected away;
+// the first group's loads go out before the live split count is known.
 template <int D>
-__global__ __launch_bounds__(256) void merge_splits_wide_kernel(BatchDesc bd, int Hq, int splits,
-                                                                const float* __restrict__ ws,
-                                                                float* __restrict__ out) {
+__global__ __launch_bounds__(64) void merge_splits_wide_kernel(BatchDesc bd, int Hq, int splits,
+                                                               const float* __restrict__ ws,
+                                                               float* __restrict__ out) {
     constexpr int U = 64;
-    __shared__ __align__(16) float fs[4][U];  // split weights, one row per wave
-    const int d = threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __align__(16) float fs[1][U];  // split weights
+    const int lane = threadIdx.x, wave = 0, d = 64 * blockIdx.y + lane;
     const int64_t row = blockIdx.x;  // e * Hq + h
     const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)bd.n * Hq * splits * D) + row * splits;
     const float* o = ws + row * splits * D + d;
@@ -113,13 +115,13 @@ __global__ __launch_bounds__(256) void merge_splits_wide_kernel(BatchDesc bd, in
 }
 
 hipError_t launch_merge_splits(const BatchDesc& bd, int Hq, int D, int splits, float* ws, float* out, hipStream_t s) {
-    const dim3 grid(bd.n * Hq), block(D);
+    const dim3 grid(bd.n * Hq), block(D), wide_grid(bd.n * Hq, D / 64);
     if (splits <= 8)
         hipLaunchKernelGGL(merge_splits8_kernel, grid, block, 0, s, bd, Hq, D, splits, ws, out);
     else if (D == 256)
-        hipLaunchKernelGGL(merge_splits_wide_kernel<256>, grid, block, 0, s, bd, Hq, splits, ws, out);
+        hipLaunchKernelGGL(merge_splits_wide_kernel<256>, wide_grid, dim3(64), 0, s, bd, Hq, splits, ws, out);
     else
-        hipLaunchKernelGGL(merge_splits_wide_kernel<128>, grid, block, 0, s, bd, Hq, splits, ws, out);
+        hipLaunchKernelGGL(merge_splits_wide_kernel<128>, wide_grid, dim3(64), 0, s, bd, Hq, splits, ws, out);
     return hipGetLastError();
 }
 
