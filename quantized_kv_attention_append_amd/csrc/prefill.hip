@@ -893,7 +893,12 @@ __global__ __launch_bounds__(WS_NT) void prefill_ws_kernel(PoolView pv, int laye
     }
 }
 
-// Merge of the prefill partials: one workgroup per (query, head); split p
+// rows a merge workgroup takes, one after another (tiny workgroups, one a row,
+// were bound by their launch rate)
+constexpr int PREFILL_MERGE_ROWS = 8;
+
+// Merge of the prefill partials: PREFILL_MERGE_ROWS (query, head) rows a
+// workgroup, thread d taking dim d of each; split p
 // counts for query i when its first page starts at or before i's position and
 // holds a page below kpl.  A window pool's window partials (win: outputs
 // [n_q][Hq][D], then (max, sum) pairs; the window starts at key 64 kpl) count
@@ -901,41 +906,46 @@ __global__ __launch_bounds__(WS_NT) void prefill_ws_kernel(PoolView pv, int laye
 __global__ __launch_bounds__(256) void prefill_merge_kernel(int q_start, int n_q, int Hq, int Hkv, int D, int splits,
                                                             int kpl, int rows_per_block, const float* __restrict__ ws,
                                                             const float* __restrict__ win, float* __restrict__ out) {
-    const int row = blockIdx.x;  // i * Hq + h
-    const int i = row / Hq, G = Hq / Hkv;
-    const int d = threadIdx.x;
-    const int QB = rows_per_block / G, qb = i / QB;
-    const int pos = q_start + i;
-    const int pos_max = q_start + min(qb * QB + QB, n_q) - 1;
-    const int n_pages = min(pos_max / PAGE + 1, kpl);
-    int live = 0;
-    if (n_pages > 0) {
-        const int per = (n_pages + splits - 1) / splits;
-        live = min(min(splits, pos / (per * PAGE) + 1), (n_pages + per - 1) / per);
+    const int G = Hq / Hkv, d = threadIdx.x;
+    const int QB = rows_per_block / G;
+    const float2* mlb = reinterpret_cast<const float2*>(ws + (int64_t)n_q * Hq * splits * D);
+#pragma unroll
+    for (int rr = 0; rr < PREFILL_MERGE_ROWS; ++rr) {
+        const int row = blockIdx.x * PREFILL_MERGE_ROWS + rr;  // i * Hq + h
+        if (row >= n_q * Hq) break;
+        const int i = row / Hq, qb = i / QB;
+        const int pos = q_start + i;
+        const int pos_max = q_start + min(qb * QB + QB, n_q) - 1;
+        const int n_pages = min(pos_max / PAGE + 1, kpl);
+        int live = 0;
+        if (n_pages > 0) {
+            const int per = (n_pages + splits - 1) / splits;
+            live = min(min(splits, pos / (per * PAGE) + 1), (n_pages + per - 1) / per);
+        }
+        const float2* ml = mlb + (int64_t)row * splits;
+        const float* o = ws + (int64_t)row * splits * D + d;
+        float M = -INFINITY, wm = -INFINITY, wl = 0.f, wo = 0.f;
+        if (win && pos >= kpl * PAGE) {
+            const float2 w = reinterpret_cast<const float2*>(win + (int64_t)n_q * Hq * D)[row];
+            wm = w.x;
+            wl = w.y;
+            wo = win[(int64_t)row * D + d];
+            M = wm;
+        }
+        for (int p = 0; p < live; ++p) M = fmaxf(M, ml[p].x);
+        float den = 0.f, acc = 0.f;
+        if (wl > 0.f) {
+            const float f = exp2f(wm - M);
+            den = f * wl;
+            acc = f * wo;
+        }
+        for (int p = 0; p < live; ++p) {
+            const float f = exp2f(ml[p].x - M);
+            den += f * ml[p].y;
+            acc += f * o[(int64_t)p * D];
+        }
+        out[(int64_t)row * D + d] = acc / den;
     }
-    const float2* ml = reinterpret_cast<const float2*>(ws + (int64_t)n_q * Hq * splits * D) + (int64_t)row * splits;
-    const float* o = ws + (int64_t)row * splits * D + d;
-    float M = -INFINITY, wm = -INFINITY, wl = 0.f, wo = 0.f;
-    if (win && pos >= kpl * PAGE) {
-        const float2 w = reinterpret_cast<const float2*>(win + (int64_t)n_q * Hq * D)[row];
-        wm = w.x;
-        wl = w.y;
-        wo = win[(int64_t)row * D + d];
-        M = wm;
-    }
-    for (int p = 0; p < live; ++p) M = fmaxf(M, ml[p].x);
-    float den = 0.f, acc = 0.f;
-    if (wl > 0.f) {
-        const float f = exp2f(wm - M);
-        den = f * wl;
-        acc = f * wo;
-    }
-    for (int p = 0; p < live; ++p) {
-        const float f = exp2f(ml[p].x - M);
-        den += f * ml[p].y;
-        acc += f * o[(int64_t)p * D];
-    }
-    out[(int64_t)row * D + d] = acc / den;
 }
 
 static_assert(PREFILL_ROWS == 128 && WS_ROWS == 128, "prefill_rows_per_block() matches the kernels");
@@ -1016,8 +1026,8 @@ hipError_t launch_prefill(const PoolView& pv, int fmt, int layer, int seq, int q
         err = launch_prefill_window(pv, layer, seq, q_start, n_q, w0, q, sm, win, win + (int64_t)n_q * pv.Hq * pv.D, s);
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(prefill_merge_kernel, dim3(n_q * pv.Hq), dim3(pv.D), 0, s, q_start, n_q, pv.Hq, pv.Hkv, pv.D,
-                       splits, kpl, rows, ws, win, out);
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3((n_q * pv.Hq + PREFILL_MERGE_ROWS - 1) / PREFILL_MERGE_ROWS),
+                       dim3(pv.D), 0, s, q_start, n_q, pv.Hq, pv.Hkv, pv.D, splits, kpl, rows, ws, win, out);
     return hipGetLastError();
 }
 
