@@ -380,8 +380,10 @@ __global__ __launch_bounds__(256, SCORES ? 1 : 2) void decode_q8_wave_kernel(Poo
 // bf16; the query times the page's channel scales enters as two bf16 terms
 // (rounded, then the rounded residual), and so do the weights p_t vscale_t,
 // so both products run on v_mfma_f32_16x16x32_bf16 with a row per (head,
-// term): row 2j + h.  The four waves of a workgroup take every fourth page;
-// per page and wave:
+// term): row 2j + h.  The W waves of a workgroup take every W-th page, each
+// through its own LDS slot: the page's block arrives there by DMA while the
+// wave computes the page before, whose operands it has already read from the
+// slot into registers.  Per page and wave:
 //   S^T = Q~ K^T for each block of 16 tokens: A = the query rows, B = K codes
 //         (lane l: token 16tb + l%16, 16 consecutive dims, two k-steps), so
 //         lane group g ends with the scores of heads 2g and 2g + 1 for the
@@ -392,13 +394,10 @@ __global__ __launch_bounds__(256, SCORES ? 1 : 2) void decode_q8_wave_kernel(Poo
 //         tokens, two k-steps); lane group g accumulates the rows of heads
 //         2g and 2g + 1, the same heads as its softmax, so the rescale is local.
 // The sum over dims and over tokens is order-free, so each k-step takes the
-// dims (tokens) that one 16-byte load per lane delivers.  A wave holds one
-// page in registers at a time and waits for it, so the loads in flight come
-// from the other waves: three workgroups share a compute unit up to group 4
-// (168 registers a wave; two at group 8), the group's fp32 query rows sit in
-// LDS rather than in registers (read once a page, for the channel-scale
-// products), and the host picks the split count that fills those slots in
-// one round.
+// dims (tokens) that one 16-byte read per lane delivers.  Up to group 4 a
+// workgroup has four waves and two share a compute unit, so that one streams
+// pages while the other combines its waves and ends; the host picks the split
+// count that fills those slots in one round.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -454,34 +453,94 @@ __device__ __forceinline__ float row_sum16(float v) {
 
 }  // namespace
 
-// workgroups a compute unit holds: three up to group 4 (168 registers a wave),
-// two at group 8 (its eight heads' rows take more) and in the variant that
-// also stores the raw logits, so that no variant spills
-constexpr int Q8_MFMA_WGS_PER_CU(int G, bool scores) { return G <= 4 && !scores ? 3 : 2; }
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t q8_lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// One (layer, KV head) block of an 8-bit page at 128 dims (17,152 bytes) copied
+// to LDS at `lds` by one wave with DMA loads (global -> LDS, no registers held
+// while they are in flight): lane l moves bytes 16 l + 1024 i, sixteen whole
+// pieces in groups of four (the instruction's immediate offset applies to both
+// addresses and stays below 4,096), then the last 768 bytes by lanes 0 .. 47.
+// The loads are issued in inline asm so that the compiler sees no LDS write in
+// flight (it would otherwise wait for the DMA before every LDS read); the
+// kernel places the waits.  It first waits for every earlier LDS read of the
+// wave to return, since the slot may be the one just read.  M0 is saved and
+// restored.
+constexpr int Q8_BLOCK_128 = (int)q8_block_bytes(128);
+static_assert(Q8_BLOCK_128 == 16 * 1024 + 768, "sixteen whole KiB and 768 bytes");
+__device__ __forceinline__ void q8_dma_block(const uint8_t* base_any, uint32_t v0, uint32_t lds, int lane) {
+    // the base address is wave-uniform; scalar registers say so to the compiler
+    const uint64_t b64 = (uint64_t)(uintptr_t)base_any;
+    const uint8_t* base = (const uint8_t*)(uintptr_t)(
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64));
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+        const uint32_t vv = v0 + 4096 * gq, ll = __builtin_amdgcn_readfirstlane(lds + 4096 * gq);
+        uint32_t saved;
+        asm volatile(
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "s_mov_b32 %[sv], m0\n\t"
+            "s_mov_b32 m0, %[l0]\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:1024 nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:2048 nt\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] offset:3072 nt\n\t"
+            "s_mov_b32 m0, %[sv]"
+            : [sv] "=&s"(saved)
+            : [b] "s"(base), [v0] "v"(vv), [l0] "s"(ll)
+            : "memory");
+    }
+    if (lane < 48) {
+        const uint32_t vv = v0 + 16384, ll = __builtin_amdgcn_readfirstlane(lds + 16384);
+        uint32_t saved;
+        asm volatile(
+            "s_waitcnt lgkmcnt(0)\n\t"
+            "s_mov_b32 %[sv], m0\n\t"
+            "s_mov_b32 m0, %[l0]\n\t"
+            "global_load_lds_dwordx4 %[v0], %[b] nt\n\t"
+            "s_mov_b32 m0, %[sv]"
+            : [sv] "=&s"(saved)
+            : [b] "s"(base), [v0] "v"(vv), [l0] "s"(ll)
+            : "memory");
+    }
+}
+
+// Waves a workgroup, one page slot of LDS each: four up to group 4, so that
+// two workgroups share a compute unit's LDS (one streams while the other
+// finishes); eight at group 8, whose query rows and weights take more.
+constexpr int Q8_WAVES(int G) { return G <= 4 ? 4 : 8; }
 
 template <int D, int G, bool SCORES>
-__global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
+__global__ __launch_bounds__(64 * Q8_WAVES(G), G <= 4 ? 2 : 1) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                 const uint16_t* __restrict__ q, float sm, int splits,
                                                                 float* __restrict__ ws, float* __restrict__ out,
                                                                 float* __restrict__ scores, int64_t sstride) {
     static_assert(2 * G <= 16, "two rows per head in a 16-row block");
+    static_assert(D == 128, "the 8-bit matrix-core form runs at 128 dims");
     constexpr float LOG2E = 1.4426950408889634f;
     constexpr int NM = D / 64;   // 16-byte K chunks of a lane's token row (two k-steps each)
     constexpr int NDB = D / 16;  // 16-dim blocks of the p.v product
     constexpr int WROW = PAGE + 8;  // padded weight row, bf16 elements
+    constexpr int W = Q8_WAVES(G), BLK = Q8_BLOCK_128;
     const int Hkv = pv.Hkv, Hq = pv.Hq;
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
     const int ctx = bd.pos[e];
     int pg0, pg1;
     split_range(ctx, bd.per, sp, &pg0, &pg1);
     if (pg0 >= pg1) return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
 
-    __shared__ __align__(16) uint16_t w_s[4][16][WROW];  // per wave: weight rows 2j + h over the page's tokens
-    __shared__ __align__(16) float o_s[4][G][D];
-    __shared__ float ml_s[4][G][2];
+    __shared__ __align__(16) uint8_t slots[W][BLK];      // per wave: one page's block, as stored
+    __shared__ __align__(16) uint16_t w_s[W][16][WROW];  // per wave: weight rows 2j + h over the page's tokens
+    __shared__ float ml_s[W][G][2];
     __shared__ __align__(16) float q_s[G][D];  // the group's query rows, fp32
+    static_assert(W * BLK + W * 16 * WROW * 2 + W * G * 2 * 4 + G * D * 4 <= (G <= 4 ? 80 : 160) * 1024,
+                  "the workgroups of a compute unit fit its LDS");
+    static_assert(W * G * D * 4 <= W * BLK, "the waves' partial outputs fit the page slots");
 
     // rows 2G.. of the weight operand stay zero
     for (int i = lane; i < 16 * WROW; i += 64)
@@ -491,7 +550,7 @@ __global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_
     // read once a page from the workgroup's fp32 copy of the group's rows
     const int aj = col >> 1, ah = col & 1;
     const bool arow = col < 2 * G;
-    for (int i = tid; i < G * D; i += 256) q_s[i / D][i % D] = bf16_to_f32(q[((int64_t)e * Hq + g * G) * D + i]);
+    for (int i = tid; i < G * D; i += 64 * W) q_s[i / D][i % D] = bf16_to_f32(q[((int64_t)e * Hq + g * G) * D + i]);
     __syncthreads();
     const float* qrow = &q_s[arow ? aj : 0][0];
 
@@ -500,24 +559,49 @@ __global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_
     for (int db = 0; db < NDB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};  // heads 2grp, 2grp + 1
     const float cs = sm * LOG2E;
-    const int32_t* bt = pv.bt + (int64_t)bd.seq[e] * pv.bt_stride;
+    // page ids through the constant address space (scalar loads): the DMA takes
+    // its base address from scalar registers
+    const __attribute__((address_space(4))) int32_t* bt =
+        (const __attribute__((address_space(4))) int32_t*)(pv.bt + (int64_t)bd.seq[e] * pv.bt_stride);
     const int64_t lhoff = ((int64_t)layer * Hkv + g) * pv.block_bytes;
+    const uint32_t slot = __builtin_amdgcn_readfirstlane(q8_lds_addr(slots[wave]));
+    auto issue = [&](int pg) { q8_dma_block(pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff, 16 * lane, slot, lane); };
+    typedef uint32_t lds_u4 __attribute__((ext_vector_type(4)));
+    typedef float lds_f4 __attribute__((ext_vector_type(4)));
+    auto lds_u4_at = [&](uint32_t a) {
+        const lds_u4 w = *reinterpret_cast<const __attribute__((address_space(3))) lds_u4*>((uintptr_t)a);
+        return make_uint4(w.x, w.y, w.z, w.w);
+    };
+    auto lds_f4_at = [&](uint32_t a) {
+        const lds_f4 w = *reinterpret_cast<const __attribute__((address_space(3))) lds_f4*>((uintptr_t)a);
+        return make_float4(w.x, w.y, w.z, w.w);
+    };
+    auto lds_f_at = [&](uint32_t a) { return *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)a); };
 
-    for (int pg = pg0 + wave; pg < pg1; pg += 4) {
-        const uint8_t* blk = pv.pages + (int64_t)bt[pg] * pv.page_bytes + lhoff;
+    // wave w takes pages pg0 + w + W k; page k + 1's DMA is in flight while page k is computed
+    if (pg0 + wave < pg1) issue(pg0 + wave);
+    for (int pg = pg0 + wave; pg < pg1; pg += W) {
+        // every outstanding load: the page's DMA (and with scores the score stores)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         uint4 kraw[4][NM];  // token 16tb + col, dims 64m + 16grp .. +15
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-            for (int m = 0; m < NM; ++m)
-                kraw[tb][m] = stream_load4(blk + (16 * tb + col) * D + 64 * m + 16 * grp);
+            for (int m = 0; m < NM; ++m) kraw[tb][m] = lds_u4_at(slot + (16 * tb + col) * D + 64 * m + 16 * grp);
         uint4 vraw[NDB];  // dim 16db + col, tokens 16grp .. +15
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-            vraw[db] = stream_load4(blk + q8_vcodes_off(D) + (16 * db + col) * PAGE + 16 * grp);
+            vraw[db] = lds_u4_at(slot + (uint32_t)q8_vcodes_off(D) + (16 * db + col) * PAGE + 16 * grp);
         float vsc[4];  // scale of token 16tb + col
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) vsc[tb] = reinterpret_cast<const float*>(blk + q8_vscale_off(D))[16 * tb + col];
+        for (int tb = 0; tb < 4; ++tb) vsc[tb] = lds_f_at(slot + (uint32_t)q8_vscale_off(D) + 4 * (16 * tb + col));
+        float4 ksc[NM][4];  // channel scales of dims 64m + 16grp + 4c4 .. +3
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+                ksc[m][c4] = lds_f4_at(slot + (uint32_t)q8_kscale_off(D) + 4 * (64 * m + 16 * grp + 4 * c4));
+        if (pg + W < pg1) issue(pg + W);
         // ---- A: the query row times the channel scales, term ah ----
         uint4 qa[2 * NM];
 #pragma unroll
@@ -525,8 +609,7 @@ __global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_
             float x[16];
 #pragma unroll
             for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 k4 =
-                    *reinterpret_cast<const float4*>(blk + q8_kscale_off(D) + 4 * (64 * m + 16 * grp + 4 * c4));
+                const float4 k4 = ksc[m][c4];
                 const float4 q4 = *reinterpret_cast<const float4*>(qrow + 64 * m + 16 * grp + 4 * c4);
                 x[4 * c4] = arow ? q4.x * k4.x : 0.f;
                 x[4 * c4 + 1] = arow ? q4.y * k4.y : 0.f;
@@ -608,7 +691,11 @@ __global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_
         }
     }
 
-    // ---- combine the four waves (a wave without pages holds m = -inf, l = 0, o = 0) ----
+    // ---- combine the waves (a wave without pages holds m = -inf, l = 0, o = 0) ----
+    // the partial outputs reuse the page slots once every wave is past its last page
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    float(*o_s)[G][D] = reinterpret_cast<float(*)[G][D]>(&slots[0][0]);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int j = 2 * grp + hh;
@@ -623,14 +710,14 @@ __global__ __launch_bounds__(256, Q8_MFMA_WGS_PER_CU(G, SCORES)) void decode_q8_
     }
     __syncthreads();
     DecodeWs w(ws, bd.n, Hq, D, splits);
-    for (int idx = tid; idx < G * D; idx += 256) {
+    for (int idx = tid; idx < G * D; idx += 64 * W) {
         const int j = idx / D, d = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) M = fmaxf(M, ml_s[v][j][0]);
+        for (int v = 0; v < W; ++v) M = fmaxf(M, ml_s[v][j][0]);
         float accum = 0.f, L = 0.f;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < W; ++v) {
             const float f = ml_s[v][j][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml_s[v][j][0] - M);
             accum += f * o_s[v][j][d];
             L += f * ml_s[v][j][1];
@@ -648,13 +735,14 @@ hipError_t launch_decode_q8(const PoolView& pv, int layer, const BatchDesc& bd, 
                             int splits, float* ws, float* out, float* scores, int64_t sstride, hipStream_t s) {
     dim3 grid(bd.n * pv.Hkv, splits);
     const int G = pv.Hq / pv.Hkv;
-    auto go = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
+    auto go = [&](auto kernel, int threads = 256) {
+        hipLaunchKernelGGL(kernel, grid, dim3(threads), 0, s, pv, layer, bd, q, sm, splits, ws, out, scores, sstride);
     };
     auto wave_form = [&](auto d_tag, auto g_tag) {
         constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
         if constexpr (Q8_MATRIX_CORES && DD == 128)  // at 256 dims its registers spill: the VALU form runs
-            scores ? go(decode_q8_mfma_kernel<DD, GG, true>) : go(decode_q8_mfma_kernel<DD, GG, false>);
+            scores ? go(decode_q8_mfma_kernel<DD, GG, true>, 64 * Q8_WAVES(GG))
+                   : go(decode_q8_mfma_kernel<DD, GG, false>, 64 * Q8_WAVES(GG));
         else
             scores ? go(decode_q8_wave_kernel<DD, GG, true>) : go(decode_q8_wave_kernel<DD, GG, false>);
     };
