@@ -22,6 +22,7 @@ SMALL8_256 = Workload(92, "small 8-bit D=256 geometry", "q8", 1, 4, 256, 8, 2, 2
 # the other group sizes of the wave-parallel decode (1, 8; 4 at D = 256) and the
 # one that takes the workgroup-per-page form (8 at D = 256)
 G1 = Workload(94, "8-bit group 1", "q8", 1, 4, 128, 4, 2, 300)
+G2 = Workload(96, "8-bit group 2", "q8", 1, 4, 128, 8, 2, 300)
 G8 = Workload(95, "8-bit group 8", "q8", 1, 2, 128, 16, 2, 300)
 G4_256 = Workload(97, "8-bit D=256 group 4", "q8", 1, 2, 256, 8, 2, 200)
 G8_256 = Workload(98, "8-bit D=256 group 8", "q8", 1, 1, 256, 8, 2, 200)
@@ -147,8 +148,11 @@ def test_append_q8_must_be_sequential():
     assert torch.equal(mem, before)
 
 
+# lanes of 1,100 and 1,300 tokens give each wave of the matrix-core form several
+# pages, one in LDS while the next arrives (four waves up to group 4, eight at 8)
 @pytest.mark.parametrize("w,lens", [(SMALL8, [300, 130, 64]), (SMALL8_256, [200, 65]), (G1, [300, 70]),
-                                    (G8, [300, 129]), (G4_256, [200, 65]), (G8_256, [130, 200])])
+                                    (G1, [1100, 300]), (G2, [300, 70]), (G8, [300, 129]), (G8, [1300, 129]),
+                                    (G4_256, [200, 65]), (G8_256, [130, 200])])
 def test_decode_q8_small(w, lens):
     need_gpu()
     n_pages = sum(-(-L // 64) for L in lens) + 2
