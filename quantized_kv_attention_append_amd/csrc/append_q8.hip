@@ -65,11 +65,17 @@ __global__ __launch_bounds__(256) void append_q8_kernel(PoolView pv, int layer, 
     auto in_row = [&](int s) { return ((int64_t)bd.row0[e] + (lp * PAGE + s - start)) * pv.Hkv + head; };
 
     // exact K rows of slots [0, slot_hi) as bf16 bits: earlier slots from the
-    // staging page, the new ones from the input
-    __shared__ uint16_t k_s[PAGE][D];
-    for (int i = tid; i < slot_hi * D; i += 256) {
-        const int s = i / D, d = i - s * D;
-        k_s[s][d] = s < slot_lo ? stage[(int64_t)s * D + d] : kin[in_row(s) * D + d];
+    // staging page (16-byte pieces: the staging rows are the bulk of a short
+    // append), the new ones from the input
+    __shared__ __align__(16) uint16_t k_s[PAGE][D];
+    constexpr int PR = D / 8;  // 16-byte pieces of a row
+    for (int i = tid; i < slot_lo * PR; i += 256) {
+        const int s = i / PR, c = i - s * PR;
+        *reinterpret_cast<uint4*>(&k_s[s][8 * c]) = *reinterpret_cast<const uint4*>(stage + (int64_t)s * D + 8 * c);
+    }
+    for (int i = tid; i < (slot_hi - slot_lo) * D; i += 256) {
+        const int s = slot_lo + i / D, d = i % D;
+        k_s[s][d] = kin[in_row(s) * D + d];
     }
     __syncthreads();
     // the page stays open: keep its new exact rows for the next append
