@@ -376,61 +376,72 @@ __global__ __launch_bounds__(256, SCORES ? 1 : 2) void decode_q8_wave_kernel(Poo
     }
 }
 
-// Matrix-core form for G in {1, 2, 4, 8}.  Codes -127..127 are exact in
-// bf16; the query times the page's channel scales enters as two bf16 terms
-// (rounded, then the rounded residual), and so do the weights p_t vscale_t,
-// so both products run on v_mfma_f32_16x16x32_bf16 with a row per (head,
-// term): row 2j + h.  The W waves of a workgroup take every W-th page, each
-// through its own LDS slot: the page's block arrives there by DMA while the
-// wave computes the page before, whose operands it has already read from the
-// slot into registers.  Per page and wave:
-//   S^T = Q~ K^T for each block of 16 tokens: A = the query rows, B = K codes
-//         (lane l: token 16tb + l%16, 16 consecutive dims, two k-steps), so
-//         lane group g ends with the scores of heads 2g and 2g + 1 for the
-//         lane's token (hi and lo terms in adjacent rows, summed in-lane);
+// Matrix-core form for G in {1, 2, 4, 8} at 128 dims, on the int8 products
+// (v_mfma_i32_16x16x64_i8).  The codes -127..127 enter as they are stored.
+// The query times the page's channel scales, and the weights p_t vscale_t,
+// enter as three balanced radix-128 digits each: for a row (a head's 128
+// scaled query dims, or a head's 64 weights of the page) with largest
+// magnitude in [2^k, 2^(k+1)), e = k - 5 and n = rint(x 2^(14 - e)) (|n| <
+// 2^20) = 16384 d0 + 128 d1 + d2 with d1, d2 in -64..63 and |d0| <= 64, so x
+// is within 2^(e - 15) <= 2^-20 max|x| of 2^(e - 14) n.  One fused
+// multiply-add, x 2^(14 - e) + (2^23 + 3,153,984), leaves n + 3,153,984 =
+// (d0 + 192) 128^2 + (d1 + 64) 128 + (d2 + 64) in the low mantissa bits
+// (rounded to nearest even), so each digit is one bit-field extract and one
+// subtraction.  Row 4j + i of an operand is digit i of head j (row 4j + 3
+// zero), four heads a 16-row block; the int32 products are exact and are
+// combined in fp32 as 2^(e - 14) (16384 A0 + 128 A1 + A2).  The W waves of a
+// workgroup take every W-th page, each through its own LDS slot: the page's
+// block arrives there by DMA while the wave computes the page before, whose
+// operands it has already read from the slot into registers.  Per page, wave
+// and block of four heads:
+//   S^T = Q~ K^T for each block of 16 tokens: A = the query digit rows, B = K
+//         codes (lane l: token 16tb + l%16, 16 consecutive dims, two k-steps
+//         of 64), so lane group g ends with the three digit products of head
+//         g for the lane's token;
 //   softmax per head over the 64 tokens in the 16 lanes of its group;
-//   O += W~ V for each block of 16 dims: A = the weight rows (through the
-//         wave's LDS), B = V codes (lane l: dim 16db + l%16, 16 consecutive
-//         tokens, two k-steps); lane group g accumulates the rows of heads
-//         2g and 2g + 1, the same heads as its softmax, so the rescale is local.
+//   O += W~ V for each block of 16 dims: A = the weight digit rows (through
+//         the wave's LDS), B = V codes (lane l: dim 16db + l%16, 16 consecutive
+//         tokens, one k-step); lane group g gets head g's three digit products
+//         for the lane's dim, the same head as its softmax, so the rescale and
+//         the weights' scale are local.
 // The sum over dims and over tokens is order-free, so each k-step takes the
 // dims (tokens) that one 16-byte read per lane delivers.  Up to group 4 a
 // workgroup has four waves and two share a compute unit, so that one streams
 // pages while the other combines its waves and ends; the host picks the split
 // count that fills those slots in one round.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 namespace {
 
-__device__ __forceinline__ f32x4_t mma_bf16(const uint4& a, const uint4& b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                   0, 0, 0);
+__device__ __forceinline__ i32x4_t mma_i8(const uint4& a, const uint4& b, i32x4_t c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a), __builtin_bit_cast(i32x4_t, b), c, 0,
+                                                  0, 0);
 }
-// two int8 codes (bytes b, b + 1 of w) -> two bf16, exact
-__device__ __forceinline__ uint32_t i8x2_bf16(uint32_t w, int b) {
-    const float x = (float)(int8_t)(w >> (8 * b)), y = (float)(int8_t)(w >> (8 * b + 8));
-    return __builtin_amdgcn_perm(__float_as_uint(y), __float_as_uint(x), 0x07060302u);
+// 2^23 + 64 (1 + 128 + 128^2) + 128^3: x 2^s + Q8_DIGIT_BIAS, rounded to an
+// integer in [2^23, 2^24), holds rint(x 2^s) + 3,153,984 in its low 23 bits
+constexpr float Q8_DIGIT_BIAS = 11542592.0f;
+// 2^e for a normal result, and the unbiased exponent field of x
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+__device__ __forceinline__ int exponent_of(float x) { return (int)((__float_as_uint(x) >> 23) & 0xFF) - 127; }
+// the scale exponent e of a row whose largest magnitude is amax (see above),
+// kept where 2^(14 - e) and 2^(e - 14) are normal floats
+__device__ __forceinline__ int q8_digit_exp(float amax) {
+    return amax > 0.f ? max(exponent_of(amax) - 5, -112) : 0;
 }
-// eight int8 codes (two words) -> the bf16 operand
-__device__ __forceinline__ uint4 i8x8_bf16(uint32_t w0, uint32_t w1) {
-    return make_uint4(i8x2_bf16(w0, 0), i8x2_bf16(w0, 2), i8x2_bf16(w1, 0), i8x2_bf16(w1, 2));
+// digit i (0: most significant) of the biased integer in the low bits of y
+__device__ __forceinline__ int q8_digit(float y, int i) {
+    const uint32_t u = __float_as_uint(y);
+    return i == 0 ? (int)((u >> 14) & 511u) - 192 : (int)((u >> (7 * (2 - i))) & 127u) - 64;
 }
-// the bf16 term h (0: x rounded; 1: the rounded residual) of two values
-__device__ __forceinline__ uint32_t bf16_term2(float x, float y, int h) {
-    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x, y}, bf16x2_t));
-    const float rx = x - __uint_as_float(hi << 16), ry = y - __uint_as_float(hi & 0xFFFF0000u);  // exact
-    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){rx, ry}, bf16x2_t));
-    return h ? lo : hi;
+// four digits -> their two's-complement bytes in one word
+__device__ __forceinline__ uint32_t pack_i8x4(int a, int b, int c, int d) {
+    const uint32_t lo = __builtin_amdgcn_perm((uint32_t)b, (uint32_t)a, 0x0c0c0400u);  // a.b0, b.b0
+    const uint32_t hi = __builtin_amdgcn_perm((uint32_t)d, (uint32_t)c, 0x04000c0cu);  // c.b0, d.b0 in bytes 2, 3
+    return lo | hi;
 }
-// one value as its bf16 term (low half) and the rounded residual (high half)
-__device__ __forceinline__ uint32_t bf16_hi_lo(float x) {
-    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x, 0.f}, bf16x2_t)) & 0xFFFFu;
-    const float r = x - __uint_as_float(hi << 16);  // exact
-    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){r, 0.f}, bf16x2_t));
-    return hi | (lo << 16);
+// the fp32 value of a digit row triple: 16384 A0 + 128 A1 + A2
+__device__ __forceinline__ float q8_digits_value(const i32x4_t& a) {
+    return fmaf((float)a[0], 16384.0f, fmaf((float)a[1], 128.0f, (float)a[2]));
 }
 // Max / sum over each 16-lane row with DPP: quad butterflies, then the row
 // rotated by 4 and by 8 (every lane ends with the row's result).
@@ -513,17 +524,20 @@ __device__ __forceinline__ void q8_dma_block(const uint8_t* base_any, uint32_t v
 // finishes); eight at group 8, whose query rows and weights take more.
 constexpr int Q8_WAVES(int G) { return G <= 4 ? 4 : 8; }
 
+
 template <int D, int G, bool SCORES>
 __global__ __launch_bounds__(64 * Q8_WAVES(G), G <= 4 ? 2 : 1) void decode_q8_mfma_kernel(PoolView pv, int layer, BatchDesc bd,
                                                                 const uint16_t* __restrict__ q, float sm, int splits,
                                                                 float* __restrict__ ws, float* __restrict__ out,
                                                                 float* __restrict__ scores, int64_t sstride) {
-    static_assert(2 * G <= 16, "two rows per head in a 16-row block");
     static_assert(D == 128, "the 8-bit matrix-core form runs at 128 dims");
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "groups 1, 2, 4, 8");
     constexpr float LOG2E = 1.4426950408889634f;
-    constexpr int NM = D / 64;   // 16-byte K chunks of a lane's token row (two k-steps each)
-    constexpr int NDB = D / 16;  // 16-dim blocks of the p.v product
-    constexpr int WROW = PAGE + 8;  // padded weight row, bf16 elements
+    constexpr int NRB = (G + 3) / 4;  // 16-row blocks of four heads
+    constexpr int HPB = G < 4 ? G : 4;  // heads of a block
+    constexpr int NM = D / 64;   // 64-dim k-steps of q.k
+    constexpr int NDB = D / 16;  // 16-dim blocks of p.v
+    constexpr int WROW = PAGE + 16;  // padded weight digit row, bytes
     constexpr int W = Q8_WAVES(G), BLK = Q8_BLOCK_128;
     const int Hkv = pv.Hkv, Hq = pv.Hq;
     const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
@@ -534,30 +548,38 @@ __global__ __launch_bounds__(64 * Q8_WAVES(G), G <= 4 ? 2 : 1) void decode_q8_mf
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int col = lane & 15, grp = lane >> 4;
 
-    __shared__ __align__(16) uint8_t slots[W][BLK];      // per wave: one page's block, as stored
-    __shared__ __align__(16) uint16_t w_s[W][16][WROW];  // per wave: weight rows 2j + h over the page's tokens
+    __shared__ __align__(16) uint8_t slots[W][BLK];           // per wave: one page's block, as stored
+    __shared__ __align__(16) int8_t w_s[W][NRB][16][WROW];    // per wave: weight digit rows 4j + i over the page's tokens
     __shared__ float ml_s[W][G][2];
     __shared__ __align__(16) float q_s[G][D];  // the group's query rows, fp32
-    static_assert(W * BLK + W * 16 * WROW * 2 + W * G * 2 * 4 + G * D * 4 <= (G <= 4 ? 80 : 160) * 1024,
+    static_assert(W * BLK + W * NRB * 16 * WROW + W * G * 2 * 4 + G * D * 4 <= (G <= 4 ? 80 : 160) * 1024,
                   "the workgroups of a compute unit fit its LDS");
     static_assert(W * G * D * 4 <= W * BLK, "the waves' partial outputs fit the page slots");
 
-    // rows 2G.. of the weight operand stay zero
-    for (int i = lane; i < 16 * WROW; i += 64)
-        if (i / WROW >= 2 * G) w_s[wave][i / WROW][i % WROW] = 0;
+    // every weight digit row starts at zero: rows 4j + 3 and the rows of heads
+    // past the group stay so
+    for (int i = lane; i < NRB * 16 * WROW / 4; i += 64) reinterpret_cast<uint32_t*>(&w_s[wave][0][0][0])[i] = 0u;
 
-    // this lane's query row: head col / 2, term col % 2; dims 64m + 16grp + i,
-    // read once a page from the workgroup's fp32 copy of the group's rows
-    const int aj = col >> 1, ah = col & 1;
-    const bool arow = col < 2 * G;
+    // this lane's query operand row in block rb: digit ad of head 4 rb + aj
+    const int aj = col >> 2, ad = col & 3;
+    const bool arow = aj < HPB && ad < 3;
+    // its digit as a bit field of the biased integer: offset, width, bias
+    const uint32_t a_off = ad == 0 ? 14u : 7u * (2u - (uint32_t)min(ad, 2)), a_wid = ad == 0 ? 9u : 7u;
+    const int a_bias = ad == 0 ? 192 : 64;
     for (int i = tid; i < G * D; i += 64 * W) q_s[i / D][i % D] = bf16_to_f32(q[((int64_t)e * Hq + g * G) * D + i]);
     __syncthreads();
-    const float* qrow = &q_s[arow ? aj : 0][0];
 
-    f32x4_t acc[NDB];
+    float o[NRB][NDB];  // head 4 rb + grp, dim 16 db + col
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};  // heads 2grp, 2grp + 1
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) o[rb][db] = 0.f;
+    float m_run[NRB], l_run[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+    }
     const float cs = sm * LOG2E;
     // page ids through the constant address space (scalar loads): the DMA takes
     // its base address from scalar registers
@@ -602,92 +624,107 @@ __global__ __launch_bounds__(64 * Q8_WAVES(G), G <= 4 ? 2 : 1) void decode_q8_mf
             for (int c4 = 0; c4 < 4; ++c4)
                 ksc[m][c4] = lds_f4_at(slot + (uint32_t)q8_kscale_off(D) + 4 * (64 * m + 16 * grp + 4 * c4));
         if (pg + W < pg1) issue(pg + W);
-        // ---- A: the query row times the channel scales, term ah ----
-        uint4 qa[2 * NM];
+        const int n_tok = min(PAGE, ctx - pg * PAGE);
+
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            float x[16];
+        for (int rb = 0; rb < NRB; ++rb) {
+            // ---- A: digit ad of the query row of head 4 rb + aj times the channel scales ----
+            const float* qrow = &q_s[arow ? 4 * rb + aj : 0][0];
+            float x[NM][16];
+            float amax = 0.f;
 #pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const float4 k4 = ksc[m][c4];
-                const float4 q4 = *reinterpret_cast<const float4*>(qrow + 64 * m + 16 * grp + 4 * c4);
-                x[4 * c4] = arow ? q4.x * k4.x : 0.f;
-                x[4 * c4 + 1] = arow ? q4.y * k4.y : 0.f;
-                x[4 * c4 + 2] = arow ? q4.z * k4.z : 0.f;
-                x[4 * c4 + 3] = arow ? q4.w * k4.w : 0.f;
-            }
-            qa[2 * m] = make_uint4(bf16_term2(x[0], x[1], ah), bf16_term2(x[2], x[3], ah), bf16_term2(x[4], x[5], ah),
-                                   bf16_term2(x[6], x[7], ah));
-            qa[2 * m + 1] = make_uint4(bf16_term2(x[8], x[9], ah), bf16_term2(x[10], x[11], ah),
-                                       bf16_term2(x[12], x[13], ah), bf16_term2(x[14], x[15], ah));
-        }
-        // ---- S^T: row 4grp + r = (head 2grp + r/2, term r%2), column = token 16tb + col ----
-        f32x4_t st[4];
+            for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-            st[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int c4 = 0; c4 < 4; ++c4) {
+                    const float4 k4 = ksc[m][c4];
+                    const float4 q4 = *reinterpret_cast<const float4*>(qrow + 64 * m + 16 * grp + 4 * c4);
+                    x[m][4 * c4] = q4.x * k4.x;
+                    x[m][4 * c4 + 1] = q4.y * k4.y;
+                    x[m][4 * c4 + 2] = q4.z * k4.z;
+                    x[m][4 * c4 + 3] = q4.w * k4.w;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(x[m][4 * c4 + i]));
+                }
+            // the head's 128 dims are spread over the four lane groups
+            amax = fmaxf(amax, __shfl_xor(amax, 16));
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            const int ea = q8_digit_exp(amax);
+            const float amul = pow2f(14 - ea);
+            uint4 qa[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) {
-                const uint4 r = kraw[tb][m];
-                st[tb] = mma_bf16(qa[2 * m], i8x8_bf16(r.x, r.y), st[tb]);
-                st[tb] = mma_bf16(qa[2 * m + 1], i8x8_bf16(r.z, r.w), st[tb]);
-            }
-        }
-        // ---- online softmax of heads 2grp, 2grp + 1 over the page's tokens ----
-        const int n_tok = min(PAGE, ctx - pg * PAGE);
-        if constexpr (SCORES) {  // raw logits, stored apart from the softmax (a branch inside it costs registers)
+                uint32_t wv[4];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const int j = 2 * grp + hh;
+                for (int w4 = 0; w4 < 4; ++w4) {
+                    int d[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float y = fmaf(x[m][4 * w4 + i], amul, Q8_DIGIT_BIAS);
+                        d[i] = (int)__builtin_amdgcn_ubfe(__float_as_uint(y), a_off, a_wid) - a_bias;
+                    }
+                    wv[w4] = arow ? pack_i8x4(d[0], d[1], d[2], d[3]) : 0u;
+                }
+                qa[m] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+            }
+            // the score scale of head 4 rb + grp (the q.k result rows of lane group grp)
+            const float qs = pow2f(__shfl(ea, 4 * grp) - 14);
+
+            // ---- S^T: rows 4grp + i = digit i of head 4 rb + grp, column = token 16tb + col ----
+            float sv[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+                i32x4_t st = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < NM; ++m) st = mma_i8(qa[m], kraw[tb][m], st);
+                sv[tb] = qs * q8_digits_value(st);  // the raw logit over sm
+            }
+            const int j = 4 * rb + grp;
+            const bool live = grp < HPB;
+            if constexpr (SCORES) {  // raw logits, stored apart from the softmax
                 float* srow = scores + ((int64_t)e * Hq + g * G + min(j, G - 1)) * sstride + pg * PAGE + col;
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
-                    if (j < G && 16 * tb + col < n_tok) srow[16 * tb] = sm * (st[tb][2 * hh] + st[tb][2 * hh + 1]);
+                    if (live && 16 * tb + col < n_tok) srow[16 * tb] = sm * sv[tb];
             }
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int j = 2 * grp + hh;
-            const bool live = j < G;
-            float sv[4], mt = -INFINITY;
+            // ---- online softmax of head j over the page's tokens, and the weight digits ----
+            float mt = -INFINITY;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 const bool valid = 16 * tb + col < n_tok;
-                const float raw = st[tb][2 * hh] + st[tb][2 * hh + 1];
-                sv[tb] = valid && live ? raw * cs : -INFINITY;
+                sv[tb] = valid && live ? sv[tb] * cs : -INFINITY;
                 mt = fmaxf(mt, sv[tb]);
             }
-            const float m_new = fmaxf(m_run[hh], row_max16(mt));
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[hh] - m_new);
-            float psum = 0.f;
+            const float m_new = fmaxf(m_run[rb], row_max16(mt));
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+            float psum = 0.f, wgt[4], wmax = 0.f;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 // slots past ctx weigh nothing (their codes and scales may be any bytes)
                 const float p = sv[tb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[tb] - m_new);
                 psum += p;
-                const float wgt = p != 0.f ? p * vsc[tb] : 0.f;
-                const uint32_t hl = bf16_hi_lo(wgt);
-                if (live) {
-                    w_s[wave][2 * j][16 * tb + col] = (uint16_t)(hl & 0xFFFF);
-                    w_s[wave][2 * j + 1][16 * tb + col] = (uint16_t)(hl >> 16);
+                wgt[tb] = p != 0.f ? p * vsc[tb] : 0.f;
+                wmax = fmaxf(wmax, wgt[tb]);
+            }
+            l_run[rb] = l_run[rb] * alpha + row_sum16(psum);
+            m_run[rb] = m_new;
+            const int ew = q8_digit_exp(row_max16(wmax));
+            const float wmul = pow2f(14 - ew), wsc = pow2f(ew - 14);
+            if (live) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const float y = fmaf(wgt[tb], wmul, Q8_DIGIT_BIAS);
+                    w_s[wave][rb][4 * grp][16 * tb + col] = (int8_t)q8_digit(y, 0);
+                    w_s[wave][rb][4 * grp + 1][16 * tb + col] = (int8_t)q8_digit(y, 1);
+                    w_s[wave][rb][4 * grp + 2][16 * tb + col] = (int8_t)q8_digit(y, 2);
                 }
             }
-            l_run[hh] = l_run[hh] * alpha + row_sum16(psum);
-            m_run[hh] = m_new;
+            // ---- O += W~ V: A = weight digit row col, tokens 16grp .. +15 (the wave's LDS is read in order) ----
+            const uint4 wa = *reinterpret_cast<const uint4*>(&w_s[wave][rb][col][16 * grp]);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                acc[db][2 * hh] *= alpha;
-                acc[db][2 * hh + 1] *= alpha;
+                const i32x4_t pv4 = mma_i8(wa, vraw[db], i32x4_t{0, 0, 0, 0});
+                o[rb][db] = fmaf(o[rb][db], alpha, wsc * q8_digits_value(pv4));
             }
-        }
-        // ---- O += W~ V: A = weight row col, tokens 16grp .. +15 (the wave's LDS is read in order) ----
-        const uint4 wa0 = *reinterpret_cast<const uint4*>(&w_s[wave][col][16 * grp]);
-        const uint4 wa1 = *reinterpret_cast<const uint4*>(&w_s[wave][col][16 * grp + 8]);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-            const uint4 r = vraw[db];
-            acc[db] = mma_bf16(wa0, i8x8_bf16(r.x, r.y), acc[db]);
-            acc[db] = mma_bf16(wa1, i8x8_bf16(r.z, r.w), acc[db]);
         }
     }
 
@@ -697,14 +734,14 @@ __global__ __launch_bounds__(64 * Q8_WAVES(G), G <= 4 ? 2 : 1) void decode_q8_mf
     __syncthreads();
     float(*o_s)[G][D] = reinterpret_cast<float(*)[G][D]>(&slots[0][0]);
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int j = 2 * grp + hh;
-        if (j < G) {
+    for (int rb = 0; rb < NRB; ++rb) {
+        const int j = 4 * rb + grp;
+        if (grp < HPB) {
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) o_s[wave][j][16 * db + col] = acc[db][2 * hh] + acc[db][2 * hh + 1];
+            for (int db = 0; db < NDB; ++db) o_s[wave][j][16 * db + col] = o[rb][db];
             if (col == 0) {
-                ml_s[wave][j][0] = m_run[hh];
-                ml_s[wave][j][1] = l_run[hh];
+                ml_s[wave][j][0] = m_run[rb];
+                ml_s[wave][j][1] = l_run[rb];
             }
         }
     }
