@@ -1,25 +1,24 @@
-// Split-K decode attention over the 8-bit pool on the vector ALUs (any GQA
-// group G <= 8, head_dim 128 or 256).
+// Split-K decode attention over the 8-bit pool (any GQA group G <= 8,
+// head_dim 128 or 256).
 //
 // The 8-bit format reads 268 bytes per (token, KV head) at D = 128 for 2 x G x
-// 128 multiply-adds, few enough that the vector ALUs keep up with HBM.  The
-// dequantization is folded into the operands: K is scaled per channel, so the
-// query is multiplied by the page's channel scales once per page
-// (q.k^_t = sum_d (q_d s_d) c_td), and V is scaled per token, so the
-// softmax weight absorbs it (sum_t p_t v^_td = sum_t (p_t s_t) c_dt).  Scores,
-// the online softmax and every running sum are fp32 (the two-level
+// 128 multiply-adds.  The dequantization is folded into the operands: K is
+// scaled per channel, so the query is multiplied by the page's channel scales
+// once per page (q.k^_t = sum_d (q_d s_d) c_td), and V is scaled per token,
+// so the softmax weight absorbs it (sum_t p_t v^_td = sum_t (p_t s_t) c_dt).
+// Scores, the online softmax and every running sum are fp32 (the two-level
 // accumulation of "Half the Cache, Twice the Context", section "The cliff is
-// in the accumulator"), in base-2 units inside the kernel.
+// in the accumulator"), in base-2 units inside the kernels.
 //
-// One workgroup of 256 threads per (sequence, KV head, split), one page of 64
-// tokens per step, the next page's bytes prefetched into registers while the
-// current one is computed:
-//   scores:  wave w takes dims [wD/4, (w+1)D/4) of token t = lane for every
-//            head; the four partial dots meet in LDS;
-//   softmax: wave j % 4 takes heads j;
-//   p.v:     thread (d, half) takes dim d over tokens [32 half, 32 half + 32)
-//            (D = 128) or all 64 tokens (D = 256) for every head.
-// Partial (m, l, o) go to the workspace; merge_splits8_kernel or merge_splits_wide_kernel merges them.
+// Three forms, one workgroup per (sequence, KV head, split) each:
+//   decode_q8_mfma_kernel (D = 128, G in {1, 2, 4, 8}): both products on the
+//     int8 matrix cores, pages staged in LDS by DMA;
+//   decode_q8_wave_kernel (D = 256, G in {1, 2, 4}): the vector ALUs, each
+//     wave its own pages and online softmax;
+//   decode_q8_kernel (the other groups): the vector ALUs, the workgroup on
+//     one page at a time.
+// Partial (m, l, o) go to the workspace; merge_splits8_kernel or
+// merge_splits_wide_kernel merges them.
 #include <type_traits>
 
 #include "decode_common.h"
@@ -71,6 +70,13 @@ __device__ __forceinline__ void load_page_q8(PageQ8<D>& pg, const uint8_t* blk, 
     pg.vscale = tid < PAGE ? reinterpret_cast<const float*>(blk + q8_vscale_off(D))[tid] : 0.f;
 }
 
+// Workgroup form: 256 threads, one page of 64 tokens per step, the next page's
+// bytes prefetched into registers while the current one is computed:
+//   scores:  wave w takes dims [wD/4, (w+1)D/4) of token t = lane for every
+//            head; the four partial dots meet in LDS;
+//   softmax: wave j % 4 takes heads j;
+//   p.v:     thread (d, half) takes dim d over tokens [32 half, 32 half + 32)
+//            (D = 128) or all 64 tokens (D = 256) for every head.
 template <int D>
 __global__ __launch_bounds__(256) void decode_q8_kernel(PoolView pv, int layer, BatchDesc bd,
                                                         const uint16_t* __restrict__ q, float sm, int splits,
