@@ -161,6 +161,29 @@ def test_decode_q2_ragged_lengths(ctx):
     _decode_case(TINY, ctx, [1, 4])
 
 
+@pytest.mark.parametrize("qscale", [64.0, 1.0 / 64.0])
+def test_decode_q2_peaked_and_flat(qscale):
+    """Queries scaled by 64 (a softmax concentrated on a few tokens, most
+    weights far below their block's largest) and by 1/64 (nearly flat
+    weights), at 256 and 128 dims: the fixed-point query digits and the 16-bit
+    weight digits of the decode kernel against the oracle's fp64 attention."""
+    need_gpu()
+    for w, ctx in ((TINY, 700), (SMALL128, 450)):
+        n_pages = -(-ctx // 64) + 1
+        pool, mem = make_pool(w, n_pages, 1)
+        bt = page_permutation(w, n_pages, salt=29)[:-1]
+        seq = pool.reserve(ctx, pages=bt)
+        k, v = kv_rows(w, 0, 0, ctx)
+        pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
+        q = (queries(w, 0, 1).float() * qscale).to(torch.bfloat16)
+        K, V = opool.dequantized_rows("q2", k.float().numpy(), v.float().numpy())
+        ref = attention.decode(q[0].float().numpy(), K, V, w.sm_scale)
+        for sp in (1, 3, 0):
+            out = pool.decode(0, [seq], [ctx], q.cuda(), w.sm_scale, n_splits=sp)
+            torch.cuda.synchronize()
+            assert_close(out[0].cpu().numpy(), ref, f"2-bit {w.name} q x {qscale:g} ctx={ctx} splits={sp}")
+
+
 def test_decode_q2_block_table_permutation_invariance():
     need_gpu()
     w, ctx = TINY, 256

@@ -180,6 +180,30 @@ def test_decode_q8_small(w, lens):
                          f"8-bit scores lane {i}", rel_l2=1e-5)
 
 
+@pytest.mark.parametrize("w,qscale", [(SMALL8, 64.0), (SMALL8, 1.0 / 64.0), (G8, 64.0), (G1, 1.0 / 64.0)])
+def test_decode_q8_peaked_and_flat(w, qscale):
+    """Queries scaled by 64 (a softmax concentrated on a few tokens, most weights
+    far below each page's largest) and by 1/64 (nearly flat weights): the
+    matrix-core form keeps the scaled query and the weights to 2^-20 of each
+    row's largest value, which the oracle's fp64 attention must confirm."""
+    need_gpu()
+    lens = [300, 190]
+    n_pages = sum(-(-L // 64) for L in lens) + 1
+    pool, mem, op, bts, seqs = _setup(w, lens, n_pages, salt=17)
+    layer = 0
+    ks = [kv_rows(w, layer, i, L)[0] for i, L in enumerate(lens)]
+    vs = [kv_rows(w, layer, i, L)[1] for i, L in enumerate(lens)]
+    _append_chunks(pool, op, layer, seqs, bts, [[(i, L) for i, L in enumerate(lens)]], ks, vs, [0] * len(lens))
+    q = (queries(w, layer, len(lens)).float() * qscale).to(torch.bfloat16)
+    for sp in (1, 0):
+        out = pool.decode(layer, seqs, lens, q.cuda(), w.sm_scale, n_splits=sp)
+        torch.cuda.synchronize()
+        for i, c in enumerate(lens):
+            K, V = op.gather(layer, bts[i], c)
+            ref = attention.decode(q[i].float().numpy(), K, V, w.sm_scale)
+            assert_close(out[i].cpu().numpy(), ref, f"8-bit q x {qscale:g}, lane {i} ctx={c} splits={sp}")
+
+
 @pytest.mark.timeout(900)
 def test_q8_batch_decode_then_append():
     """Full 8-bit workload: populate 32 layers x 24 lanes, decode every layer,
