@@ -204,6 +204,33 @@ def test_decode_q8_peaked_and_flat(w, qscale):
             assert_close(out[i].cpu().numpy(), ref, f"8-bit q x {qscale:g}, lane {i} ctx={c} splits={sp}")
 
 
+def test_decode_q8_long_lanes_many_splits():
+    """Two lanes of 9,000 and 2,500 tokens at 12 and 40 splits (the merge of more
+    than 8 splits, one split a lane of a wave) and at the library's count, with
+    the workspace pre-filled with 0xFF so that an unwritten partial would show."""
+    need_gpu()
+    import quantized_kv_attention_append_amd as kvq
+    w = SMALL8
+    lens = [9000, 2500]
+    n_pages = sum(-(-L // 64) for L in lens) + 1
+    pool, mem, op, bts, seqs = _setup(w, lens, n_pages, salt=23)
+    layer = 1
+    ks = [kv_rows(w, layer, i, L)[0] for i, L in enumerate(lens)]
+    vs = [kv_rows(w, layer, i, L)[1] for i, L in enumerate(lens)]
+    _append_chunks(pool, op, layer, seqs, bts, [[(i, L) for i, L in enumerate(lens)]], ks, vs, [0] * len(lens))
+    q = queries(w, layer, len(lens))
+    refs = []
+    for i, c in enumerate(lens):
+        K, V = op.gather(layer, bts[i], c)
+        refs.append(attention.decode(q[i].float().numpy(), K, V, w.sm_scale))
+    for sp in (12, 40, 0):
+        ws = torch.full((pool.workspace_bytes(kvq.OP_DECODE, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
+        out = pool.decode(layer, seqs, lens, q.cuda(), w.sm_scale, n_splits=sp, ws=ws)
+        torch.cuda.synchronize()
+        for i, c in enumerate(lens):
+            assert_close(out[i].cpu().numpy(), refs[i], f"8-bit long lane {i} ctx={c} splits={sp or pool.decode_splits(lens)}")
+
+
 @pytest.mark.timeout(900)
 def test_q8_batch_decode_then_append():
     """Full 8-bit workload: populate 32 layers x 24 lanes, decode every layer,
