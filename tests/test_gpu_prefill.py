@@ -19,7 +19,7 @@ PREFILL = WORKLOADS["prefill"]
 SMALL128 = Workload(90, "small D=128 geometry", "q2", 2, 2, 128, 8, 3, 300)
 
 
-def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):
+def _prefill_case(w, layer, prior, n_q, splits_list, salt=0, qscale=1.0):
     import quantized_kv_attention_append_amd as kvq
     total = prior + n_q
     n_pages = -(-total // 64) + 1
@@ -31,6 +31,8 @@ def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):
         pool.append(layer, [seq], [0], [prior], k[:prior].cuda(), v[:prior].cuda())
     pool.append(layer, [seq], [prior], [n_q], k[prior:].cuda(), v[prior:].cuda())
     q = queries(w, layer, n_q, stream=1)
+    if qscale != 1.0:
+        q = (q.float() * qscale).to(torch.bfloat16)
     K, V = opool.dequantized_rows("q2", k.float().numpy(), v.float().numpy())
     ref = attention.prefill(q.float().numpy(), K, V, w.sm_scale, q_start=prior)
     outs = []
@@ -38,7 +40,7 @@ def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):
         ws = torch.full((pool.workspace_bytes(kvq.OP_PREFILL, n_q, sp),), 0xFF, dtype=torch.uint8, device="cuda")
         out = pool.prefill(layer, seq, prior, q.cuda(), w.sm_scale, n_splits=sp, ws=ws)
         torch.cuda.synchronize()
-        assert_close(out.cpu().numpy(), ref, f"prefill prior={prior} n_q={n_q} splits={sp}")
+        assert_close(out.cpu().numpy(), ref, f"prefill prior={prior} n_q={n_q} splits={sp} q x {qscale:g}")
         outs.append(out.cpu())
     return pool, seq, q, outs
 
@@ -56,6 +58,16 @@ def test_prefill_small_d256_chunk_from_zero():
 def test_prefill_d128_group4():
     need_gpu()
     _prefill_case(SMALL128, 1, 130, 64, [1, 4])
+
+
+@pytest.mark.parametrize("qscale", [64.0, 1.0 / 64.0])
+def test_prefill_peaked_and_flat(qscale):
+    """Queries scaled by 64 (a sharply peaked softmax, the lazily rescaled
+    reference moving often) and by 1/64 (nearly flat weights), at 256 and 128
+    dims, against the oracle's fp64 causal attention."""
+    need_gpu()
+    _prefill_case(TINY, 0, 300, 70, [1, 2, 0], salt=5, qscale=qscale)
+    _prefill_case(SMALL128, 1, 200, 100, [1, 0], salt=6, qscale=qscale)
 
 
 def test_prefill_last_row_equals_decode():
