@@ -103,7 +103,7 @@ def test_dequant_page_bf16_returns_rows():
             assert np.array_equal(gv.view(np.uint32), V[64 * lp:64 * lp + 64, h].view(np.uint32))
 
 
-def _decode_case(w, ctx, splits_list, layer=0):
+def _decode_case(w, ctx, splits_list, layer=0, qscale=1.0):
     n_pages = -(-ctx // 64) + 2
     pool, mem = make_pool(w, n_pages, _fmt(), fill=NAN_FILL)
     bt = page_permutation(w, n_pages, salt=ctx)[:-2]
@@ -111,6 +111,8 @@ def _decode_case(w, ctx, splits_list, layer=0):
     k, v = kv_rows(w, layer, 0, ctx)
     pool.append(layer, [seq], [0], [ctx], k.cuda(), v.cuda())
     q = queries(w, layer, 1)
+    if qscale != 1.0:
+        q = (q.float() * qscale).to(torch.bfloat16)
     K, V = k.float().numpy(), v.float().numpy()
     ref = attention.decode(q[0].float().numpy(), K, V, w.sm_scale)
     ref_s = attention.scores(q[0].float().numpy(), K, w.sm_scale)
@@ -119,8 +121,17 @@ def _decode_case(w, ctx, splits_list, layer=0):
         ws = torch.full((pool.workspace_bytes(0, 1, sp),), 0xFF, dtype=torch.uint8, device="cuda")
         out = pool.decode(layer, [seq], [ctx], q.cuda(), w.sm_scale, n_splits=sp, ws=ws, scores=scores)
         torch.cuda.synchronize()
-        assert_close(out[0].cpu().numpy(), ref, f"bf16 decode {w.name} ctx={ctx} splits={sp}")
+        assert_close(out[0].cpu().numpy(), ref, f"bf16 decode {w.name} ctx={ctx} splits={sp} q x {qscale:g}")
         assert_close(scores[0].cpu().numpy(), ref_s, f"bf16 scores ctx={ctx} splits={sp}", max_abs=2e-3, rel_l2=1e-5)
+
+
+@pytest.mark.parametrize("qscale", [64.0, 1.0 / 64.0])
+def test_decode_bf16_peaked_and_flat(qscale):
+    """bf16 pools with queries scaled by 64 and by 1/64: the weights' two bf16
+    terms under a sharply peaked and a nearly flat softmax."""
+    need_gpu()
+    _decode_case(TINY, 700, [1, 3, 0], qscale=qscale)
+    _decode_case(SMALL128, 450, [1, 0], layer=1, qscale=qscale)
 
 
 @pytest.mark.parametrize("ctx", [1, 63, 65, 256, 1000])

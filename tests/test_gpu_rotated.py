@@ -103,6 +103,29 @@ def test_rotated_decode_ragged(ctx):
         assert rel <= 5e-5, f"rotated scores ctx={ctx} splits={sp}: rel L2 {rel:.2e}"
 
 
+@pytest.mark.parametrize("qscale", [64.0, 1.0 / 64.0])
+def test_rotated_decode_peaked_and_flat(qscale):
+    """The rotated decode with queries scaled by 64 (a sharply peaked softmax)
+    and by 1/64 (nearly flat weights): the query's fp32 butterflies and its
+    fixed-point digits against the oracle's fp64 attention over the rotated
+    rows."""
+    need_gpu()
+    ctx = 700
+    n_pages = -(-ctx // 64) + 1
+    pool, mem = make_pool(TINY, n_pages, _fmt(), fill=NAN_FILL)
+    bt = page_permutation(TINY, n_pages, salt=31)[:-1]
+    seq = pool.reserve(ctx, pages=bt)
+    k, v = kv_rows(TINY, 0, 0, ctx)
+    pool.append(0, [seq], [0], [ctx], k.cuda(), v.cuda())
+    q = (queries(TINY, 0, 1, stream=3).float() * qscale).to(torch.bfloat16)
+    K, V = opool.dequantized_rows("q2r", k.float().numpy(), v.float().numpy())
+    ref = attention.decode(q[0].float().numpy(), K, V, TINY.sm_scale)
+    for sp in (1, 3, 0):
+        out = pool.decode(0, [seq], [ctx], q.cuda(), TINY.sm_scale, n_splits=sp)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy()[0], ref, f"rotated decode q x {qscale:g} splits={sp}")
+
+
 def test_rotated_decode_batch_d128():
     need_gpu()
     w = SMALL128
