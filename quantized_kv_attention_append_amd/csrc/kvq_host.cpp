@@ -535,20 +535,23 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 // compute unit (256 on MI355X) over all (sequence, KV head) pairs, with at
 // least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
 // its decode holds two workgroups on each compute unit (at 128 dims and group
-// up to 4, four waves a workgroup, each with one page slot of LDS; at group 8
-// one of eight waves; at 256 dims two of four), and a workgroup whose split
-// holds no page ends at once; the split count is the largest whose workgroups
-// with pages all fit in 512 slots together, going no further once a split is
-// down to one page pair (measured at 128 dims on 24 lanes of 16..124 pages, us
-// a layer call: 3 splits 57.8 with 376 such workgroups, 4 52.3 with 472, 5
-// 60.9 with 568, 6 60.0, 8 56.4, 12 58.6).
+// up to 4, four waves a workgroup, each with one page slot of LDS; at 256 dims
+// two of four) or one (at 128 dims and group 8, eight waves), and a workgroup
+// whose split holds no page ends at once; the split count is the largest
+// whose workgroups with pages all fit in those slots (512 or 256) together,
+// going no further once a split is down to one page pair (measured on 24
+// lanes of 16..124 pages, us a layer call: group 4, 8 KV heads: 3 splits 51.5
+// with 376 such workgroups, 4 46.6 with 472, 5 51.9 with 568, 6 51.6, 8 49.3;
+// group 8, 4 KV heads: 2 splits 45.5, 3 36.7, 4 36.9 with 236, 6 44.7, 8 42.7,
+// 10 49.1 with 492).
 int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     int64_t max_pages = 1;
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
     const int64_t base = (int64_t)n * p->geom.n_kv_heads;
     const int64_t want = (256 + base - 1) / base;
     if (p->fmt == KV_FMT_Q8) {
-        const int64_t SLOTS = 2 * 256;
+        const int G = p->geom.n_q_heads / p->geom.n_kv_heads;
+        const int64_t SLOTS = (p->geom.head_dim == 128 && G == 8 ? 1 : 2) * 256;
         const int64_t max_pairs = (max_pages + 1) / 2;
         int best = 1;
         for (int s = 1; s <= 256; ++s) {

@@ -359,6 +359,14 @@ def test_launch_plans(lib):
     assert live(sp.value) <= 512 < live(sp.value + 1), (sp.value, live(sp.value), live(sp.value + 1))
     assert sp.value == 4
     g8.close()
+    # at group 8 (here 4 KV heads, 32 query heads) the decode holds one workgroup a
+    # compute unit, so the workgroups with pages must fit 256 slots
+    g8 = HostPool(lib, (32, 4, 128, 32), Q8, 4, max_seqs=24, max_seq_tokens=8192)
+    assert lib.kv_decode_splits(g8.h, 24, i64(lens), C.byref(sp)) == OK
+    live4 = lambda s: live(s) // 2  # live() counts 8 KV heads
+    assert live4(sp.value) <= 256 < live4(sp.value + 1), (sp.value, live4(sp.value), live4(sp.value + 1))
+    assert sp.value == 4
+    g8.close()
     ptr, npg = C.c_void_p(), C.c_int32()
     assert lib.kv_seq_block_table(g.h, seqs[3], C.byref(ptr), C.byref(npg)) == OK and npg.value == 640
     assert list((C.c_int32 * 640).from_address(ptr.value)) == g.pages(seqs[3])
