@@ -75,6 +75,11 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
     // every element of a row whose scale lies outside [2^-120, 2^120]: there
     // the reciprocal can overflow (a subnormal scale) or lose its bound (a
     // subnormal reciprocal).
+    // Here the clamp to 0..3 cannot bind: d = RN(x - mn) >= 0 and the reciprocal
+    // is positive, and d <= RN(mx - mn) with sc = RN(RN(mx - mn) / 3), so the
+    // quotient is below 3.000001 and rounds to at most 3 (a zero range gives
+    // d = 0; scales outside [2^-120, 2^120] take the division below, which
+    // clamps).
     const float inv = __builtin_amdgcn_rcpf(sc);
     bool near = !(sc >= 0x1p-120f && sc <= 0x1p120f);
     float d[DPL];
@@ -84,7 +89,7 @@ __device__ __forceinline__ void q2_quantize_row(const float (&x)[DPL], uint32_t 
         const float ta = d[k] * inv;
         const float ra = rintf(ta);
         near |= fabsf(ta - ra) > 0.5f - 2e-6f;  // within 2e-6 of a half-integer
-        c[k] = (uint32_t)fminf(fmaxf(ra, 0.0f), 3.0f);
+        c[k] = (uint32_t)ra;
     }
     if (__builtin_amdgcn_ballot_w64(near)) {
 #pragma unroll
