@@ -273,9 +273,10 @@ kv_status kv_decode_splits(const kv_pool* pool, int32_t n, const int64_t* ctx_le
  * are split into ranges of whole page pairs (flash-decoding), all of one size:
  * ceil(page pairs of the longest context / n_splits), n_splits in 1..256
  * (0 = kv_decode_splits' choice), so a shorter context fills fewer ranges.
- * The ranges' partial results (max, sum, unnormalised output) go to d_ws; a
- * second kernel on the same stream merges them in fp32 (two launches per
- * call).
+ * The ranges' partial results (max, sum, unnormalised output) go to d_ws and
+ * are merged in fp32: for KV_FMT_Q2 and KV_FMT_Q2_ROT at n_splits <= 8 by the
+ * last workgroup of the split kernel to finish a (sequence, KV head), else by
+ * a second kernel on the same stream.
  * KV_FMT_Q2_WINDOW: the ranges cover the tokens before the window; the merge
  * kernel also attends to the window's exact rows (ctx_len at most the tokens
  * appended to the layer, else KV_ERR_BOUND).

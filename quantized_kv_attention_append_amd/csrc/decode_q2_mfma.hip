@@ -1,7 +1,8 @@
 // Split-K decode attention over the 2-bit pool on the gfx950 matrix cores
-// (head_dim 128 or 256; four query heads of a KV head's group a launch, so
+// (head_dim 128 or 256; four query heads of a KV head's group a workgroup, so
 // groups 1 and 2 leave rows of the products empty and group 8 takes two
-// launches).
+// workgroups a split, launched together so that the second reads the pages
+// from L2).
 //
 // At group 4 and 256 dims a decode step does 2 x 4 x 256 multiply-adds for
 // every 144 bytes of K and V rows it reads, more than the vector ALUs can
@@ -178,48 +179,68 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // block goes in groups of four loads.  It first waits for every earlier LDS
 // read of the wave to return, since the slot may be the one just read.  M0
 // is saved and restored.
-template <int D>
+// NT: streaming (nontemporal) loads; without it the lines stay in L2 for a
+// second workgroup that reads the same block soon after.
+#define KVQ_DMA_256(NTS)                                                                     \
+    "s_waitcnt lgkmcnt(0)\n\t"                                                              \
+    "s_mov_b32 %[sv], m0\n\t"                                                               \
+    "s_mov_b32 m0, %[l0]\n\t"                                                               \
+    "global_load_lds_dwordx4 %[v0], %[b]" NTS "\n\t"                                        \
+    "global_load_lds_dwordx4 %[v0], %[b] offset:1024" NTS "\n\t"                            \
+    "global_load_lds_dwordx4 %[v0], %[b] offset:2048" NTS "\n\t"                            \
+    "global_load_lds_dwordx4 %[v0], %[b] offset:3072" NTS "\n\t"                            \
+    "s_mov_b32 m0, %[l1]\n\t"                                                               \
+    "global_load_lds_dwordx4 %[v1], %[b]" NTS "\n\t"                                        \
+    "global_load_lds_dwordx4 %[v1], %[b] offset:1024" NTS "\n\t"                            \
+    "global_load_lds_dwordx4 %[v1], %[b] offset:2048" NTS "\n\t"                            \
+    "global_load_lds_dwordx4 %[v1], %[b] offset:3072" NTS "\n\t"                            \
+    "s_mov_b32 m0, %[l2]\n\t"                                                               \
+    "global_load_lds_dwordx4 %[v2], %[b]" NTS "\n\t"                                        \
+    "s_mov_b32 m0, %[sv]"
+#define KVQ_DMA_128(NTS)                                                                     \
+    "s_waitcnt lgkmcnt(0)\n\t"                                                              \
+    "s_mov_b32 %[sv], m0\n\t"                                                               \
+    "s_mov_b32 m0, %[l0]\n\t"                                                               \
+    "global_load_lds_dwordx4 %[v0], %[b]" NTS "\n\t"                                        \
+    "global_load_lds_dwordx4 %[v0], %[b] offset:1024" NTS "\n\t"                            \
+    "global_load_lds_dwordx4 %[v0], %[b] offset:2048" NTS "\n\t"                            \
+    "global_load_lds_dwordx4 %[v0], %[b] offset:3072" NTS "\n\t"                            \
+    "s_mov_b32 m0, %[l1]\n\t"                                                               \
+    "global_load_lds_dwordx4 %[v1], %[b]" NTS "\n\t"                                        \
+    "s_mov_b32 m0, %[sv]"
+template <int D, bool NT = true>
 __device__ __forceinline__ void dma_block(const uint8_t* base, uint32_t v0, uint32_t lds) {
     const uint32_t v1 = v0 + 4096, l1 = lds + 4096;
     uint32_t saved;
     if constexpr (D == 256) {
         const uint32_t v2 = v0 + 8192, l2 = lds + 8192;
-        asm volatile(
-            "s_waitcnt lgkmcnt(0)\n\t"
-            "s_mov_b32 %[sv], m0\n\t"
-            "s_mov_b32 m0, %[l0]\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] nt\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] offset:1024 nt\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] offset:2048 nt\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] offset:3072 nt\n\t"
-            "s_mov_b32 m0, %[l1]\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b] nt\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b] offset:1024 nt\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b] offset:2048 nt\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b] offset:3072 nt\n\t"
-            "s_mov_b32 m0, %[l2]\n\t"
-            "global_load_lds_dwordx4 %[v2], %[b] nt\n\t"
-            "s_mov_b32 m0, %[sv]"
-            : [sv] "=&s"(saved)
-            : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [l0] "s"(lds), [l1] "s"(l1), [l2] "s"(l2)
-            : "memory");
+        if constexpr (NT)
+            asm volatile(KVQ_DMA_256(" nt")
+                         : [sv] "=&s"(saved)
+                         : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [l0] "s"(lds), [l1] "s"(l1),
+                           [l2] "s"(l2)
+                         : "memory");
+        else
+            asm volatile(KVQ_DMA_256("")
+                         : [sv] "=&s"(saved)
+                         : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [v2] "v"(v2), [l0] "s"(lds), [l1] "s"(l1),
+                           [l2] "s"(l2)
+                         : "memory");
     } else {
-        asm volatile(
-            "s_waitcnt lgkmcnt(0)\n\t"
-            "s_mov_b32 %[sv], m0\n\t"
-            "s_mov_b32 m0, %[l0]\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] nt\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] offset:1024 nt\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] offset:2048 nt\n\t"
-            "global_load_lds_dwordx4 %[v0], %[b] offset:3072 nt\n\t"
-            "s_mov_b32 m0, %[l1]\n\t"
-            "global_load_lds_dwordx4 %[v1], %[b] nt\n\t"
-            "s_mov_b32 m0, %[sv]"
-            : [sv] "=&s"(saved)
-            : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [l0] "s"(lds), [l1] "s"(l1)
-            : "memory");
+        if constexpr (NT)
+            asm volatile(KVQ_DMA_128(" nt")
+                         : [sv] "=&s"(saved)
+                         : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [l0] "s"(lds), [l1] "s"(l1)
+                         : "memory");
+        else
+            asm volatile(KVQ_DMA_128("")
+                         : [sv] "=&s"(saved)
+                         : [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1), [l0] "s"(lds), [l1] "s"(l1)
+                         : "memory");
     }
 }
+#undef KVQ_DMA_256
+#undef KVQ_DMA_128
 static_assert(q2_block_bytes(256) == 9 * 1024 && q2_block_bytes(128) == 5 * 1024, "blocks are whole KiB");
 
 // Waits until at most N of this wave's vector memory operations are
@@ -448,7 +469,7 @@ struct SplitLds {
     static_assert((W * 4 * D + W * 4 * 3) * 4 + 4 <= SLOTS_BYTES, "the waves' partials fit the tile slots");
 };
 
-template <int D, bool SCORES, bool ROT, bool GENERAL, bool FUSE, int W, int SLOTS>
+template <int D, bool SCORES, bool ROT, bool GENERAL, bool FUSE, int W, int SLOTS, bool PAIRED = false>
 __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int layer, const BatchDesc& bd,
                                                     const uint16_t* __restrict__ q, float sm, int splits,
                                                     float* __restrict__ ws, float* __restrict__ out,
@@ -465,11 +486,33 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
     constexpr bool PAD = LdsT::PAD;
     constexpr int TB = TileShape<D>::BYTES;
     const int Hkv = pv.Hkv, Hq = pv.Hq;
-    const int e = blockIdx.x / Hkv, g = blockIdx.x % Hkv, sp = blockIdx.y;
+    // PAIRED (group 8 in one launch): a one-dimensional grid of
+    // two workgroups per (sequence, KV head, split), the half h taking heads
+    // 4h ..  Each run of 16 workgroups holds both halves of 8 such triples, the
+    // second half 8 places after the first: workgroups go round the XCDs in
+    // dispatch order, so the two land on the same XCD at nearly the same time and
+    // the second reads the blocks mostly from that XCD's L2 (the DMA is then not
+    // nontemporal).  A last run of fewer than 16 keeps the halves r apart.
+    unsigned bx = blockIdx.x, by = blockIdx.y;
+    int half = 0;
+    if constexpr (PAIRED) {
+        const int M = bd.n * Hkv * splits;  // triples; the grid is 2 M
+        const int L = blockIdx.x, base = L & ~15, off = L & 15;
+        const int r = min(8, M - (base >> 1));
+        half = off >= r;
+        const int t = (base >> 1) + off - half * r;
+        bx = (unsigned)(t % (bd.n * Hkv));
+        by = (unsigned)(t / (bd.n * Hkv));
+    }
+    const int e = bx / Hkv, g = bx % Hkv, sp = (int)by;
     const int Gq = GENERAL ? Hq / Hkv : G;  // the pool's GQA group
     if constexpr (!GENERAL) {
         h0 = 0;
         nh = G;
+    }
+    if constexpr (PAIRED) {
+        h0 = 4 * half;
+        nh = min(4, Gq - h0);
     }
     const int64_t head0 = (int64_t)e * Hq + (int64_t)g * Gq + h0;  // first query row of this launch
     const int ctx = bd.pos[e];
@@ -509,8 +552,8 @@ __device__ __forceinline__ void decode_q2_mfma_body(const PoolView& pv, int laye
         const int pair = pr_first + W * t;
         const int id0 = bt[2 * pair], id1 = bt[min(2 * pair + 1, n_pages - 1)];
         const uint32_t slot = slot_of(t);
-        dma_block<D>(pv.pages + (int64_t)id0 * pv.page_bytes + lhoff, voff, slot);
-        dma_block<D>(pv.pages + (int64_t)id1 * pv.page_bytes + lhoff, voff, slot + TileShape<D>::BLK);
+        dma_block<D, !PAIRED>(pv.pages + (int64_t)id0 * pv.page_bytes + lhoff, voff, slot);
+        dma_block<D, !PAIRED>(pv.pages + (int64_t)id1 * pv.page_bytes + lhoff, voff, slot + TileShape<D>::BLK);
     };
 
     // The query rows of the group's G heads (contiguous, G D bf16) go to the
@@ -779,6 +822,17 @@ __global__ __launch_bounds__(64 * W) void decode_q2_mfma_kernel(PoolView pv, int
                                                                0, 4);
 }
 
+// Group 8: both halves of each KV head's group in one launch.
+template <int D, bool SCORES, bool ROT, bool FUSE, int W, int SLOTS>
+__global__ __launch_bounds__(64 * W) void decode_q2_mfma_pair_kernel(PoolView pv, int layer, BatchDesc bd,
+                                                                     const uint16_t* __restrict__ q, float sm,
+                                                                     int splits, float* __restrict__ ws,
+                                                                     float* __restrict__ out,
+                                                                     float* __restrict__ scores, int64_t sstride) {
+    decode_q2_mfma_body<D, SCORES, ROT, true, FUSE, W, SLOTS, true>(pv, layer, bd, q, sm, splits, ws, out, scores,
+                                                                    sstride, 0, 0);
+}
+
 // Other groups: heads h0 .. h0 + nh - 1 of each KV head's group.
 template <int D, bool SCORES, bool ROT, bool FUSE, int W, int SLOTS>
 __global__ __launch_bounds__(64 * W) void decode_q2_mfma_group_kernel(PoolView pv, int layer, BatchDesc bd,
@@ -818,7 +872,17 @@ static hipError_t launch_decode_q2_splits(const PoolView& pv, int layer, const B
         });
         return hipGetLastError();
     }
-    // other groups: up to four query heads per launch (two launches for group 8)
+    if (Gq == 8) {  // both halves of the group in one launch
+        const dim3 grid2(2 * bd.n * pv.Hkv * splits);
+        flags([&](auto d, auto sc, auto r, auto fu) {
+            hipLaunchKernelGGL((decode_q2_mfma_pair_kernel<decltype(d)::value, decltype(sc)::value, decltype(r)::value,
+                                                           decltype(fu)::value, SPLIT_WAVES, SPLIT_SLOTS>),
+                               grid2, dim3(64 * SPLIT_WAVES), 0, s, pv, layer, bd, q, smk, splits, ws, out, scores,
+                               sstride);
+        });
+        return hipGetLastError();
+    }
+    // other groups: up to four query heads per launch
     for (int h0 = 0; h0 < Gq; h0 += 4) {
         const int nh = Gq - h0 < 4 ? Gq - h0 : 4;
         flags([&](auto d, auto sc, auto r, auto fu) {

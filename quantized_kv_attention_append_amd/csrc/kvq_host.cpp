@@ -533,7 +533,8 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 
 // Default split count for a decode batch.  2-bit and bf16: about one workgroup per
 // compute unit (256 on MI355X) over all (sequence, KV head) pairs, with at
-// least eight page pairs per split (two per wavefront of a workgroup).  8-bit:
+// least eight page pairs per split (two per wavefront of a workgroup); the
+// 2-bit formats run group 8 as two workgroups a split.  8-bit:
 // its decode holds two workgroups on each compute unit (at 128 dims and group
 // up to 4, four waves a workgroup, each with one page slot of LDS; at 256 dims
 // two of four) or one (at 128 dims and group 8, eight waves), and a workgroup
@@ -547,10 +548,12 @@ kv_status check_seq(const kv_pool* p, int32_t seq, int64_t end_pos, const char* 
 int auto_splits(const kv_pool* p, int n, const int64_t* ctx) {
     int64_t max_pages = 1;
     for (int i = 0; i < n; ++i) max_pages = std::max<int64_t>(max_pages, (ctx[i] + PAGE - 1) / PAGE);
-    const int64_t base = (int64_t)n * p->geom.n_kv_heads;
+    const int G = p->geom.n_q_heads / p->geom.n_kv_heads;
+    // the 2-bit decode runs group 8 as two workgroups a split
+    const bool pair = (p->fmt == KV_FMT_Q2 || p->fmt == KV_FMT_Q2_ROT || p->fmt == KV_FMT_Q2_WINDOW) && G == 8;
+    const int64_t base = (int64_t)n * p->geom.n_kv_heads * (pair ? 2 : 1);
     const int64_t want = (256 + base - 1) / base;
     if (p->fmt == KV_FMT_Q8) {
-        const int G = p->geom.n_q_heads / p->geom.n_kv_heads;
         const int64_t SLOTS = (p->geom.head_dim == 128 && G == 8 ? 1 : 2) * 256;
         const int64_t max_pairs = (max_pages + 1) / 2;
         int best = 1;

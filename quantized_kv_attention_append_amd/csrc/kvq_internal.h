@@ -25,7 +25,7 @@ struct PoolView {
 };
 
 // Arrival counters a pool keeps for the fused decode merge: one per (batch
-// entry, KV head, launch of four query heads; group 8 takes two launches).
+// entry, KV head, four query heads; group 8 takes two).
 inline int64_t decode_counters(int Hkv) { return (int64_t)KV_MAX_BATCH * Hkv * 2; }
 // Largest split count whose merge runs inside the split kernel (the last
 // workgroup of a (sequence, KV head) to finish merges them); more splits are

@@ -244,7 +244,8 @@ def test_errors_refused_before_any_write():
 
 
 # GQA groups other than 4 run the same matrix-core kernel four query heads at
-# a time (group 8 in two launches; groups 1 and 2 with empty rows)
+# a time (group 8 as two workgroups a split in one launch; groups 1 and 2 with
+# empty rows)
 GROUPS = [
     Workload(93, "group 1, D=128", "q2", 1, 4, 128, 4, 2, 300),
     Workload(93, "group 2, D=256", "q2", 1, 2, 256, 4, 2, 300),
@@ -268,7 +269,7 @@ def test_decode_q2_other_groups(w):
         K, V = opool.dequantized_rows("q2", k.float().numpy(), v.float().numpy())
         refs.append(attention.decode(q[i].float().numpy(), K, V, w.sm_scale))
         refs_s.append(attention.scores(q[i].float().numpy(), K, w.sm_scale))
-    for sp in (1, 3):
+    for sp in (1, 3, 12):  # 12: more splits than the fused merge takes, most of them empty
         scores = torch.full((len(lens), w.n_q_heads, max(lens)), float("nan"), device="cuda")
         ws = torch.full((pool.workspace_bytes(0, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
         out = pool.decode(0, seqs, lens, q.cuda(), w.sm_scale, n_splits=sp, ws=ws, scores=scores)

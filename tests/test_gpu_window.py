@@ -18,6 +18,8 @@ TINY = WORKLOADS["tiny"]
 PREFILL = WORKLOADS["prefill"]
 # group 2 at 128 dims (the matrix-core split kernel with two empty query rows), 2 layers
 G2_128 = Workload(97, "group 2, D=128, window", "q2w", 2, 2, 128, 4, 3, 400)
+# group 8: the split kernel's two workgroups a split
+G8_128 = Workload(97, "group 8, D=128, window", "q2w", 2, 2, 128, 16, 3, 400)
 NAN_FILL = 0xFF
 
 
@@ -86,14 +88,14 @@ def test_window_decode_ragged(pieces):
         _decode_check(pool, op, TINY, 0, seq, 0, bt, ctx, [1, 3, 0], f"window pieces={pieces}")
 
 
-def test_window_decode_batched_group2_d128():
+@pytest.mark.parametrize("w", [G2_128, G8_128], ids=lambda w: w.name)
+def test_window_decode_batched_d128(w):
     need_gpu()
-    w = G2_128
     lens = [400, 64, 30, 129]
     n_pages = sum(-(-L // 64) for L in lens) + 1
     pool, mem = make_pool(w, n_pages, _fmt(), fill=NAN_FILL)
     perm = page_permutation(w, n_pages)
-    op = opool.OraclePool("q2w", 2, 2, 128, n_pages, fill=NAN_FILL)
+    op = opool.OraclePool("q2w", w.n_layers, w.n_kv_heads, w.head_dim, n_pages, fill=NAN_FILL)
     bts, seqs, off = [], [], 0
     for L in lens:
         npg = -(-L // 64)
@@ -111,7 +113,7 @@ def test_window_decode_batched_group2_d128():
         ws = torch.full((pool.workspace_bytes(0, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
         out = pool.decode(layer, seqs, ctxs, q.cuda(), w.sm_scale, n_splits=sp, ws=ws)
         torch.cuda.synchronize()
-        assert_close(out.cpu().numpy(), ref, f"window batched G2 D128 splits={sp}")
+        assert_close(out.cpu().numpy(), ref, f"window batched {w.name} splits={sp}")
 
 
 def _prefill_case(w, layer, prior, n_q, splits_list, salt=0):

@@ -344,6 +344,12 @@ def test_launch_plans(lib):
     seqs = [g.reserve(40960)[1] for _ in range(8)]
     sp = C.c_int32()
     assert lib.kv_decode_splits(g.h, 8, i64([40960] * 8), C.byref(sp)) == OK and sp.value == 8
+    # at group 8 the 2-bit decode runs two workgroups a split, so half the splits
+    g2 = HostPool(lib, (16, 4, 256, 32), Q2, 8 * 640, max_seq_tokens=40960)
+    for _ in range(8):
+        g2.reserve(40960)
+    assert lib.kv_decode_splits(g2.h, 8, i64([40960] * 8), C.byref(sp)) == OK and sp.value == 4
+    g2.close()
     # and for the 8-bit batch (24 lanes of 16..124 pages, 8 KV heads x 128 dims): the most splits whose
     # workgroups with pages fit two to each of 256 compute units (472 at 4 splits, 568 at 5)
     from synth import WORKLOADS, q8_batch_lengths
