@@ -109,7 +109,7 @@ def test_window_decode_batched_d128(w):
     q = queries(w, layer, len(lens))
     ref = np.stack([attention.decode(q[i].float().numpy(), *op.gather(layer, bts[i], ctxs[i], seq=i), w.sm_scale)
                     for i in range(len(lens))])
-    for sp in (1, 2, 0):
+    for sp in (1, 2, 0, 12):  # up to 8 splits the split kernel attends to the window too; 12: a merge kernel does
         ws = torch.full((pool.workspace_bytes(0, len(lens), sp),), 0xFF, dtype=torch.uint8, device="cuda")
         out = pool.decode(layer, seqs, ctxs, q.cuda(), w.sm_scale, n_splits=sp, ws=ws)
         torch.cuda.synchronize()
