@@ -273,6 +273,54 @@ def long_context_leg(reps: int):
             "planted_rank": {"gpu": gpu_rank, "heads": list(range(0, w.n_q_heads, w.group))}}
 
 
+def group8_leg(reps: int):
+    """2-bit decode at GQA group 8: the 27B lanes (8 x 40,960 tokens, 4 KV heads
+    x 256 dims) with 32 query heads, 4 layers.  The library runs both four-head
+    halves of each group in one launch, the second half reading the pages
+    mostly from L2; calls are timed with HIP events back to back at the
+    library's split count, cycling over the layers."""
+    import dataclasses
+
+    import torch
+
+    import quantized_kv_attention_append_amd as kvq
+    from synth import WORKLOADS, kv_rows, page_permutation, queries
+
+    w = dataclasses.replace(WORKLOADS["27b"], n_layers=4, n_q_heads=32)
+    L, H, D, Hq, B, ctx = w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads, w.lanes, w.ctx
+    geom = (L, H, D, Hq)
+    _, pb = kvq.token_bytes(geom, kvq.FMT_Q2)
+    ppl = ctx // 64
+    pool = kvq.Pool(B * ppl * pb, geom, kvq.FMT_Q2, max_seqs=B, max_seq_tokens=ctx)
+    perm = page_permutation(w, B * ppl)
+    seqs = [pool.reserve(ctx, pages=perm[i * ppl:(i + 1) * ppl]) for i in range(B)]
+    for layer in range(L):
+        kv = [kv_rows(w, layer, i, ctx, device="cuda") for i in range(B)]
+        pool.append(layer, seqs, [0] * B, [ctx] * B, torch.cat([k for k, _ in kv]), torch.cat([v for _, v in kv]))
+        del kv
+    ctxs = [ctx] * B
+    sp = pool.decode_splits(ctxs)
+    ws = torch.empty(pool.workspace_bytes(kvq.OP_DECODE, B, sp), dtype=torch.uint8, device="cuda")
+    qs = [queries(w, layer, B, device="cuda") for layer in range(L)]
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device="cuda") for _ in range(L)]
+    turn = [0]
+
+    def call():
+        layer = turn[0] % L
+        turn[0] += 1
+        pool.decode(layer, seqs, ctxs, qs[layer], w.sm_scale, n_splits=sp, ws=ws, out=outs[layer])
+
+    for _ in range(L):
+        call()
+    avg, mn, med = _call_ms(call, reps * L)
+    alg = B * ppl * H * 64 * 2 * (D // 4 + 8) + B * Hq * D * (2 + 4)
+    log(f"group 8: {avg * 1e3:.1f} us a call (median {med * 1e3:.1f}), splits={sp}, "
+        f"{alg / (avg * 1e-3) / 1e9:.0f} GB/s against one read of the pages")
+    return {"workload": "2-bit decode, 8 lanes x 40960 tokens, 4 layers x 4 KV heads x 256 dims, 32 query heads",
+            "bytes_per_call": alg, "splits": sp, "us_mean": avg * 1e3, "us_median": med * 1e3, "us_min": mn * 1e3,
+            "gbs_mean": alg / (avg * 1e-3) / 1e9}
+
+
 def q8_leg(reps: int):
     """The 8-bit format: 24 lanes of 64 x U[16, 128] tokens, 32 layers x 8 KV
     heads x 128 dims, 32 query heads.  Populate every layer (timed, HBM bytes
@@ -961,6 +1009,7 @@ def main():
         log(f"2-bit window against 2-bit: decode step {win['step_time_vs_q2']:.3f}x the time"
             + (f", prefill {win['prefill_time_vs_q2']:.3f}x" if prefill is not None else ""))
 
+    g8 = None if args.no_extra else group8_leg(5)
     rot = None if args.no_extra else bf16_leg(5, rotated=True)
     if rot is not None:
         # the price of the rotation: the query transform, butterflies on the K rows of append
@@ -1034,6 +1083,7 @@ def main():
         "bf16": bf16,
         "q2_window": win,
         "q2_rotated": rot,
+        "q2_group8": g8,
         "cpu_baseline": cpu,
         "platform": platform_info(),
     }
