@@ -4,7 +4,7 @@ and HIP-graph replays of decode in every format.
 * 2 of the 16 layers x 8 lanes x 40,960 tokens (the per-layer shape bench.py
   times), each layer's whole output (8 lanes) against the oracle: the window
   format reads each lane's last page exact; the rotated format reads rotated
-  rows.
+  rows.  The same lanes with 32 query heads (group 8), plain and window.
 * A decode step (two layers) captured in a HIP graph and replayed three times,
   with eager work and synchronizations between the replays: every replay's
   outputs equal the eager outputs bit for bit.  Decode records no memset.
@@ -52,6 +52,40 @@ def test_27b_geometry_whole_layers(name):
             K, V = opool.dequantized_rows(name, k.float().cpu().numpy(), v.float().cpu().numpy())
             refs.append(attention.decode(q[lane].float().cpu().numpy(), K, V, w.sm_scale))
         assert_close(out, np.stack(refs), f"27B {name} layer {layer}, all 8 lanes")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["q2", "q2w"])
+def test_27b_lanes_group8_whole_layer(name):
+    # the 27B lanes with 32 query heads over the 4 KV heads: both four-head
+    # halves of each group in one launch, at the library's split count
+    need_gpu()
+    import dataclasses
+
+    import quantized_kv_attention_append_amd as kvq
+    fmt = {"q2": kvq.FMT_Q2, "q2w": kvq.FMT_Q2_WINDOW}[name]
+    w = dataclasses.replace(WORKLOADS["27b"], n_layers=2, n_q_heads=32)
+    B, ctx = w.lanes, w.ctx
+    geom = (w.n_layers, w.n_kv_heads, w.head_dim, w.n_q_heads)
+    ppl = ctx // 64
+    _, pb = kvq.token_bytes(geom, fmt)
+    pool = kvq.Pool(B * ppl * pb, geom, fmt, max_seqs=B, max_seq_tokens=ctx)
+    perm = page_permutation(w, B * ppl)
+    seqs = [pool.reserve(ctx, pages=perm[i * ppl:(i + 1) * ppl]) for i in range(B)]
+    layer = 1
+    kv = [kv_rows(w, layer, lane, ctx, device="cuda") for lane in range(B)]
+    pool.append(layer, seqs, [0] * B, [ctx] * B, torch.cat([a for a, _ in kv]), torch.cat([b for _, b in kv]))
+    del kv
+    sp = pool.decode_splits([ctx] * B)
+    say(f"27B lanes, group 8, {name}: splits={sp}")
+    q = queries(w, layer, B, device="cuda")
+    out = pool.decode(layer, seqs, [ctx] * B, q, w.sm_scale, n_splits=sp).cpu().numpy()
+    refs = []
+    for lane in range(B):
+        k, v = kv_rows(w, layer, lane, ctx, device="cuda")
+        K, V = opool.dequantized_rows(name, k.float().cpu().numpy(), v.float().cpu().numpy())
+        refs.append(attention.decode(q[lane].float().cpu().numpy(), K, V, w.sm_scale))
+    assert_close(out, np.stack(refs), f"27B lanes group 8 {name} layer {layer}, all 8 lanes")
 
 
 # 2 layers x 4 KV heads x 128 dims, 16 query heads: every format at group 4
